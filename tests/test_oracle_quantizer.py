@@ -1,0 +1,375 @@
+"""Pins for the oracle's blockwise quantizer and MSE clip search.
+
+Every expectation here comes from the pages (worked examples, stated bounds and
+invariants), from hand derivation on constructed inputs, or from a brute-force
+search that does not reuse the oracle's formulas.  A plausible slip anywhere in
+the quantizer (a wrong sign of the zero point, a dropped term in the error sum,
+an off-by-one clamp, a swapped nibble) breaks at least one of them.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    out = {}
+    for line in open(os.path.join(GOLDEN, name)):
+        line = line.split("#", 1)[0].strip()
+        if line:
+            k, v = line.split("=", 1)
+            out[k.strip()] = v.strip()
+    return out
+
+
+def _recon(orc, r, G):
+    """float64 reconstruction (q - z) * s from the oracle's outputs."""
+    q = r["q"].astype(np.float64)
+    N, K = q.shape
+    s = orc.f16_bits_to_f32(r["scale"]).astype(np.float64)
+    z = orc.f16_bits_to_f32(r["zero"]).astype(np.float64) if r["zero"] is not None else np.zeros_like(s)
+    return ((q.reshape(N, K // G, G) - z[..., None]) * s[..., None]).reshape(N, K), s, z
+
+
+# --------------------------------------------------------- worked examples
+
+def test_worked_block_minus02_to_1(orc):
+    """gowda.ai "LLM fast inference", "The naive symmetric baseline" and
+    "Achievement 1": a block spanning [-0.2, 1.0]; symmetric step ~ 1/7 = 0.143,
+    affine step 1.2/15 = 0.08 before zero-point rounding."""
+    g = _golden("worked_blocks.txt")
+    blk = np.array([[float(g["block_lo"]), 0.0, 0.5, float(g["block_hi"])]], dtype=np.float32)
+    ra = orc.quantize(blk, 4, "asym")
+    sa = float(orc.f16_bits_to_f32(ra["scale"])[0, 0])
+    assert abs(sa - float(g["asym_step"])) <= float(g["asym_step"]) * 2.0 ** -11
+    # by hand with s = fp16(1.2/15) = 0.0800171: -(-0.2)/s = 2.4995 -> z = 2;
+    # codes: -2.4995 -> -2 (+2 = 0), 0 -> 2, 6.2487 -> 6 (+2 = 8), 12.497 -> 12 (+2 = 14)
+    assert float(orc.f16_bits_to_f32(ra["zero"])[0, 0]) == 2.0
+    assert ra["q"].tolist() == [[0, 2, 8, 14]]
+    rs = orc.quantize(blk, 4, "sym")
+    ss = float(orc.f16_bits_to_f32(rs["scale"])[0, 0])
+    assert abs(ss - float(g["sym_step"])) < 5e-4
+    # by hand with s = fp16(1/7) = 0.142822: -1.40 -> -1, 0, 3.5009 -> 4, 7.0017 -> 7
+    assert rs["q"].tolist() == [[-1, 0, 4, 7]]
+    assert rs["q"].min() >= -7                       # -8 unreachable under amax/7
+    # the affine step is finer on the occupied interval
+    assert sa < ss
+
+
+def test_worked_outlier_collapse(orc):
+    """nebelwolfi.xyz "The outlier problem ...", "Emergent Outliers at 6.7B
+    Parameters": small weights around 0.01 plus one 8.5; per-tensor symmetric
+    INT8 scale 8.5/127 ~ 0.067, and the small weights collapse."""
+    g = _golden("worked_blocks.txt")
+    bulk = float(g["outlier_bulk_magnitude"])
+    w = synth.uniform_block(0, 127, -bulk, bulk)
+    w = np.concatenate([w, np.array([float(g["outlier_value"])], dtype=np.float32)])[None, :]
+    r = orc.quantize(w, w.shape[1], "sym", bits=8)
+    s = float(orc.f16_bits_to_f32(r["scale"])[0, 0])
+    assert abs(s - float(g["outlier_int8_scale"])) < 5e-4
+    assert np.all(r["q"][0, :-1] == 0)               # every small weight collapses to 0
+    assert r["q"][0, -1] == 127
+    # INT4 analogue: 8.5/7
+    r4 = orc.quantize(w, w.shape[1], "sym", bits=4)
+    assert abs(float(orc.f16_bits_to_f32(r4["scale"])[0, 0]) - 8.5 / 7) < 1e-3
+    # the error grows by orders of magnitude against the same block without the
+    # outlier (the page says roughly three; the exact ratio depends on the bulk)
+    wq, _, _ = _recon(orc, r, w.shape[1])
+    clean = w[:, :-1]
+    rc = orc.quantize(clean, clean.shape[1], "sym", bits=8)
+    cq, _, _ = _recon(orc, rc, clean.shape[1])
+    mse_out = np.mean((w[0, :-1] - wq[0, :-1]) ** 2)
+    mse_clean = np.mean((clean[0] - cq[0]) ** 2)
+    assert mse_out / mse_clean > 100
+
+
+def test_per_tensor_int4_step(orc):
+    """gsantana.dev, "One real weight matrix": |w| max 5.812 gives a per-tensor
+    INT4 step of 5.8/7 = 0.83, so almost every ordinary weight rounds to 0."""
+    g = _golden("worked_blocks.txt")
+    w = synth.normal_matrix(3, 64, 96, 0.2)
+    w[5, 7] = float(g["tensor_amax"])
+    flat = w.reshape(1, -1)
+    r = orc.quantize(flat, flat.shape[1], "sym")
+    s = float(orc.f16_bits_to_f32(r["scale"])[0, 0])
+    assert abs(s - float(g["tensor_int4_step"])) < 5e-3
+    assert np.mean(r["q"] == 0) > 0.9
+
+
+# ------------------------------------------------------------ closed forms
+
+def test_block_on_grid_is_exact(orc):
+    # 16 values exactly on the lattice (c - 5) * 2^-6: the plain quantizer
+    # recovers s = 2^-6, z = 5 and reconstructs every value exactly.
+    c = np.arange(16)
+    blk = ((c - 5) * 2.0 ** -6).astype(np.float32)
+    rng = np.random.default_rng(0)
+    blk = blk[rng.permutation(16)][None, :]
+    r = orc.quantize(blk, 16, "asym")
+    assert orc.f16_bits_to_f32(r["scale"])[0, 0] == 2.0 ** -6
+    assert orc.f16_bits_to_f32(r["zero"])[0, 0] == 5.0
+    wq, _, _ = _recon(orc, r, 16)
+    np.testing.assert_array_equal(wq, blk.astype(np.float64))
+    # same for symmetric: values k * 2^-4, k in -7..7 (amax = 7/16 -> s = 1/16)
+    k = np.arange(-7, 8)
+    sb = (k * 2.0 ** -4).astype(np.float32)
+    sb = np.concatenate([sb, [0.0]]).astype(np.float32)[None, :]
+    r = orc.quantize(sb, 16, "sym")
+    assert orc.f16_bits_to_f32(r["scale"])[0, 0] == 2.0 ** -4
+    np.testing.assert_array_equal(r["q"][0], np.concatenate([k, [0]]))
+
+
+def test_degenerate_groups(orc):
+    # all-zero group: zero scale is replaced by 1 (gsantana.dev fake-quant
+    # guard); everything reconstructs to exactly 0 and the zero point is +0.
+    z = np.zeros((1, 32), dtype=np.float32)
+    for mode in ("sym", "asym"):
+        r = orc.quantize(z, 32, mode, fracs=synth.FRACS_11)
+        assert r["scale"][0, 0] == 0x3C00
+        wq, _, _ = _recon(orc, r, 32)
+        assert np.all(wq == 0)
+        if mode == "asym":
+            assert r["zero"][0, 0] == 0x0000
+    # constant group c: s = 1, z = round(-c), codes 0, reconstruction round(c)
+    for c, zz in ((0.3, 0.0), (2.7, -3.0), (-4.5, 4.0)):
+        blk = np.full((1, 32), c, dtype=np.float32)
+        r = orc.quantize(blk, 32, "asym")
+        assert r["scale"][0, 0] == 0x3C00
+        assert float(orc.f16_bits_to_f32(r["zero"])[0, 0]) == zz
+        assert np.all(r["q"] == 0)
+
+
+def test_packing_nibble_order(orc):
+    # canonical packing: even k in the low nibble, odd k in the high nibble;
+    # symmetric codes as two's-complement nibbles
+    q = np.array([[1, 2, 3, 4], [-8, 7, -1, 0]], dtype=np.int16)
+    p = orc.pack(q)
+    assert p.tolist() == [[0x21, 0x43], [0x78, 0x0F]]
+
+
+# ------------------------------------------------------ bounds, invariants
+
+@pytest.mark.parametrize("mode", ["sym", "asym"])
+@pytest.mark.parametrize("G", [32, 128])
+def test_half_step_error_bound(orc, mode, G):
+    """gsantana.dev "Scale and zero point" and nebelwolfi.xyz "The Basic
+    Arithmetic": the error per value is at most half a step, scale/2, for
+    every value inside the range the grid covers."""
+    w = synth.weight(synth.WORKLOADS["llama8b_decode"], 0, rows=64)
+    r = orc.quantize(w, G, mode)
+    wq, s, z = _recon(orc, r, G)
+    N, K = w.shape
+    sg = np.repeat(s, G, axis=1)
+    zg = np.repeat(z, G, axis=1)
+    qlo, qhi = (0, 15) if mode == "asym" else (-8, 7)
+    lo = (qlo - zg) * sg - sg / 2
+    hi = (qhi - zg) * sg + sg / 2
+    inr = (w >= lo) & (w <= hi)
+    assert inr.mean() > 0.999
+    err = np.abs(w.astype(np.float64) - wq)
+    assert np.all(err[inr] <= sg[inr] / 2 * (1 + 1e-6) + 1e-30)
+
+
+def test_code_space_use(orc):
+    """gowda.ai "LLM fast inference": symmetric amax/7 never reaches -8;
+    the asymmetric quantizer uses the whole 0..15 code space."""
+    w = synth.weight(synth.WORKLOADS["llama8b_decode"], 0, rows=64)
+    ra = orc.quantize(w, 128, "asym")
+    blocks = w.reshape(64, -1, 128)
+    qa = ra["q"].reshape(64, -1, 128)
+    imin = blocks.argmin(axis=2)
+    imax = blocks.argmax(axis=2)
+    cmin = np.take_along_axis(qa, imin[..., None], axis=2)[..., 0]
+    cmax = np.take_along_axis(qa, imax[..., None], axis=2)[..., 0]
+    assert np.all(cmin == 0)                          # signed -8 used exactly
+    assert np.all((cmax == 14) | (cmax == 15))
+    assert set(np.unique(ra["q"])) == set(range(16))
+    rs = orc.quantize(w, 128, "sym")
+    assert rs["q"].min() >= -7 and rs["q"].max() <= 7
+    # with clipping, a strong negative outlier lands on -8
+    blk = synth.normal_matrix(11, 1, 128, 1.0)
+    blk[0, 3] = -9.0
+    r = orc.quantize(blk, 128, "sym", fracs=synth.FRACS_11)
+    assert r["clip"][0, 0] > 0
+    assert r["q"][0, 3] == -8
+
+
+def test_group_locality(orc):
+    """gsantana.dev "One real weight matrix": a planted weight at 10x the tensor
+    max changes only the scale it shares; with groups, only its own group."""
+    w = synth.normal_matrix(4, 32, 256, 0.2)
+    spiked = w.copy()
+    spiked[7, 100] = 10 * np.abs(w).max()
+    for G, fr in ((32, None), (128, synth.FRACS_11), (256, None)):
+        a = orc.quantize(w, G, "asym", fracs=fr)
+        b = orc.quantize(spiked, G, "asym", fracs=fr)
+        g = 100 // G
+        mask = np.ones(a["scale"].shape, dtype=bool)
+        mask[7, g] = False
+        np.testing.assert_array_equal(a["scale"][mask], b["scale"][mask])
+        np.testing.assert_array_equal(a["zero"][mask], b["zero"][mask])
+        np.testing.assert_array_equal(a["clip"][mask], b["clip"][mask])
+        qmask = np.repeat(mask, G, axis=1)
+        np.testing.assert_array_equal(a["q"][qmask], b["q"][qmask])
+        assert a["scale"][7, g] != b["scale"][7, g]
+
+
+def test_codes_are_nearest_grid_points_brute_force(orc):
+    # Given the scale and zero the oracle chose, every code is the grid point
+    # (out of all 16) closest to the weight, found here by exhaustive search
+    # in float64.  Ties (exact half steps) are skipped.
+    w = synth.weight(synth.WORKLOADS["gemma12b_w4a8"], 0, rows=16)
+    for mode in ("asym", "sym"):
+        r = orc.quantize(w, 128, mode, fracs=synth.FRACS_11)
+        N, K = w.shape
+        s = np.repeat(orc.f16_bits_to_f32(r["scale"]).astype(np.float64), 128, axis=1)
+        z = (np.repeat(orc.f16_bits_to_f32(r["zero"]).astype(np.float64), 128, axis=1)
+             if mode == "asym" else np.zeros_like(s))
+        codes = np.arange(16) if mode == "asym" else np.arange(-8, 8)
+        grid = (codes[None, None, :] - z[..., None]) * s[..., None]
+        d = np.abs(w.astype(np.float64)[..., None] - grid)
+        best = codes[d.argmin(axis=2)]
+        ds = np.sort(d, axis=2)
+        untied = (ds[..., 1] - ds[..., 0]) > 1e-6 * s
+        assert untied.mean() > 0.99
+        np.testing.assert_array_equal(r["q"][untied], best[untied])
+
+
+# ------------------------------------------------------------- clip search
+
+def test_clip_search_selection_and_sse(orc):
+    """gowda.ai "MSE clipping": per block, keep the plain quantizer unless a
+    contracted range is strictly better; the error counts clipped values."""
+    wl = synth.WORKLOADS["gemma12b_w4a8"]
+    w = synth.weight(wl, 0, rows=32)
+    fr = synth.FRACS_11
+    r = orc.quantize(w, 128, "asym", fracs=fr, want_sse=True)
+    sse = r["sse"]
+    # selection: first index attaining the minimum (strict < keeps earlier)
+    first_min = np.argmax(sse == sse.min(axis=2, keepdims=True), axis=2)
+    np.testing.assert_array_equal(r["clip"], first_min)
+    assert np.all(sse.min(axis=2) <= sse[..., 0])
+    # the reported SSE of the winner is the float64 error of what was emitted,
+    # clipped values included
+    wq, _, _ = _recon(orc, r, 128)
+    e64 = ((w.astype(np.float64) - wq) ** 2).reshape(32, -1, 128).sum(axis=2)
+    won = np.take_along_axis(sse, r["clip"][..., None].astype(np.int64), axis=2)[..., 0]
+    np.testing.assert_allclose(won, e64, rtol=2e-5)
+    # heavy-tailed weights: the search does pick contracted ranges somewhere,
+    # and never makes any group worse than the plain quantizer
+    assert (r["clip"] > 0).mean() > 0.05
+    r1 = orc.quantize(w, 128, "asym")
+    wq1, _, _ = _recon(orc, r1, 128)
+    e1 = ((w.astype(np.float64) - wq1) ** 2).reshape(32, -1, 128).sum(axis=2)
+    assert np.all(e64 <= e1 * (1 + 1e-5))
+    # groups that keep index 0 are bit-identical to the plain quantizer
+    keep = np.repeat(r["clip"] == 0, 128, axis=1)
+    np.testing.assert_array_equal(r["q"][keep], r1["q"][keep])
+
+
+def test_clip_search_brute_force_tiny_blocks(orc):
+    # Exhaustive check on tiny blocks: for each candidate fraction, every
+    # (scale, zero) pair it could produce is enumerated independently as the
+    # fp16 neighbours of the exact-arithmetic scale, and the float64 optimum of
+    # the block error over candidates is compared with the oracle's choice.
+    # Where two candidates are within 1e-6 relative the case is a near-tie and
+    # is only counted, not failed.
+    rng = np.random.default_rng(21)
+    fr = synth.FRACS_11
+    n_cases, agree, ties = 300, 0, 0
+    for _ in range(n_cases):
+        G = int(rng.choice([4, 8]))
+        blk = (rng.standard_t(2.5, size=G) * 0.1).astype(np.float32)
+        r = orc.quantize(blk[None, :], G, "asym", fracs=fr, want_sse=True)
+        errs = []
+        lo0, hi0 = float(blk.min()), float(blk.max())
+        mid, h = (lo0 + hi0) / 2, (hi0 - lo0) / 2
+        for f in fr.astype(np.float64):
+            lo, hi = (lo0, hi0) if f == 1.0 else (mid - f * h, mid + f * h)
+            s = np.float64(np.float16((hi - lo) / 15))
+            if s == 0:
+                s = 1.0
+            z = np.round(-lo / s)
+            q = np.clip(np.round(blk.astype(np.float64) / s) + z, 0, 15)
+            errs.append(float(np.sum((blk - (q - z) * s) ** 2)))
+        errs = np.array(errs)
+        best = int(np.argmin(errs))
+        srt = np.sort(errs)
+        if len(srt) > 1 and (srt[1] - srt[0]) <= 1e-6 * max(srt[0], 1e-30):
+            ties += 1
+            continue
+        agree += int(r["clip"][0, 0] == best)
+    assert agree >= (n_cases - ties) * 0.98, (agree, ties)
+
+
+def test_sym_clip_candidates(orc):
+    # symmetric clip search: the candidate range is [-f amax, f amax]; a block
+    # with one extreme value picks a contracted range and clips it
+    blk = synth.normal_matrix(2, 1, 32, 1.0)
+    blk[0, 0] = 12.0
+    r = orc.quantize(blk, 32, "sym", fracs=synth.FRACS_11, want_sse=True)
+    assert r["clip"][0, 0] > 0
+    f = synth.FRACS_11[r["clip"][0, 0]]
+    s = float(orc.f16_bits_to_f32(r["scale"])[0, 0])
+    assert abs(s - f * 12.0 / 7) <= f * 12.0 / 7 * 2.0 ** -10
+    assert r["q"][0, 0] == 7                          # the outlier is clipped at the top code
+
+
+def test_plain_quantizer_textbook_reduction(orc):
+    # with one candidate the quantizer is the textbook min/max (asym) or
+    # amax (sym) quantizer; per-channel is the special case G = K.
+    w = synth.normal_matrix(8, 8, 64, 0.05)
+    r = orc.quantize(w, 64, "asym")
+    s = orc.f16_bits_to_f32(r["scale"])[:, 0].astype(np.float64)
+    want = (w.max(axis=1).astype(np.float64) - w.min(axis=1)) / 15
+    np.testing.assert_allclose(s, want, rtol=2.0 ** -11)
+    r = orc.quantize(w, 64, "sym")
+    s = orc.f16_bits_to_f32(r["scale"])[:, 0].astype(np.float64)
+    np.testing.assert_allclose(s, np.abs(w).max(axis=1) / 7, rtol=2.0 ** -11)
+
+
+# --------------------------------------------------- accounting and quality
+
+def test_bits_per_weight_table(orc):
+    g = _golden("bits_per_weight.txt")
+    shape = (576, 1536)
+    for key, val in g.items():
+        bits, kind, gran = key.split(",")
+        if bits == "tahoma":
+            got = orc.bits_per_weight(4, False, int(gran), zero_bits=16)
+            assert abs(got - float(val)) < 1e-12
+            continue
+        block = shape[0] * shape[1] if gran == "tensor" else shape[1] if gran == "row" else int(gran)
+        got = orc.bits_per_weight(int(bits), kind == "sym", block)
+        assert f"{got:.2f}" == val, (key, got)
+
+
+def test_rel_error_metric(orc):
+    a = synth.normal_matrix(1, 16, 16)
+    assert orc.rel_error(a, a) == 0.0
+    assert orc.rel_error(a, np.zeros_like(a)) == pytest.approx(1.0)
+    assert orc.rel_error(a, 2 * a) == pytest.approx(1.0)
+    assert orc.rel_error(3 * a, 3 * a + 3e-3 * a) == pytest.approx(1e-3)
+
+
+def test_granularity_ordering_on_synthetic_layer(orc):
+    """gsantana.dev "One real weight matrix": per-tensor INT4 is destroyed,
+    groups beat per-channel, smaller groups beat larger, asymmetric groups beat
+    symmetric ones.  Shown here on a synthetic stand-in for the page's layer
+    (N(0, 0.2) with a few outlier input channels), as an ordering."""
+    w = synth.normal_matrix(9, 576, 1536, 0.2)
+    w[:, [17, 901]] *= 20
+    err = {}
+    for mode in ("sym", "asym"):
+        for G in (32, 128, 1536):
+            err[(mode, G)] = orc.rel_error(w, orc.fake_quant(w, G, mode))
+    flat = w.reshape(1, -1)
+    err[("sym", "tensor")] = orc.rel_error(flat, orc.fake_quant(flat, flat.shape[1], "sym"))
+    assert err[("sym", "tensor")] > 0.5
+    assert err[("sym", 32)] < err[("sym", 128)] < err[("sym", 1536)] < err[("sym", "tensor")]
+    assert err[("asym", 32)] < err[("sym", 32)]
+    assert err[("asym", 128)] < err[("sym", 128)]
