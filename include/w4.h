@@ -1,0 +1,180 @@
+/*
+ * w4.h -- C ABI of the MI355X (gfx950) library for blockwise 4-bit weight
+ * quantization and the fused dequantize-and-multiply that consumes it.
+ *
+ * What the operations compute (the pages this follows):
+ *  - gsantana.dev, "Quantizing LLMs Without Guesswork: What 4 Bits Really
+ *    Cost": "Scale and zero point" (the symmetric and asymmetric formulas),
+ *    "Granularity: who shares a scale" (a group is a run of G consecutive
+ *    weights inside one output row), "Quantize, then dequantize" (half-to-even
+ *    rounding, a zero scale replaced by 1), "Weight-only methods" (W4A16:
+ *    dequantize inside the matmul, compute in 16-bit).
+ *  - gowda.ai, "LLM fast inference" (Tahoma): "Achievement 1" (unsigned codes
+ *    0..15, integer zero point, 16-bit scale and zero per group along K),
+ *    "MSE clipping" (a data-free search over contracted ranges about the
+ *    observed midpoint; a candidate replaces the plain quantizer only if its
+ *    block error is strictly lower; clipped values count in the error; the
+ *    portable packed form is rearranged into a GPU layout without requantizing),
+ *    "Achievement 2" (each activation row quantized to FP8 E4M3 with a scale
+ *    from its maximum over 448, floored at 1e-8; FP32 accumulation; the row
+ *    scale applied in the epilogue; BF16 output).
+ *
+ * Conventions shared by every entry point:
+ *  - Matrices are row-major and contiguous.  A weight W is [N, K]: row n is
+ *    output channel n, K is the reduction (input) dimension.  Products are
+ *    Y[M, N] = X[M, K] . W'^T.
+ *  - Every pointer argument is a DEVICE pointer on the current HIP device,
+ *    owned by the caller, except where a parameter says "host".  The library
+ *    allocates no memory and keeps no state besides a thread-local message for
+ *    the last failed call.
+ *  - Device pointers must be 16-byte aligned.
+ *  - Every call is asynchronous on `stream` (0 = the null stream).  Arguments
+ *    are checked on the host before any launch: a violated precondition
+ *    returns W4_EINVAL (or W4_EUNSUPPORTED for a valid but unsupported
+ *    configuration) and launches nothing.  There is no fallback path: an
+ *    unsupported shape is an error, never a slow or dense substitute.
+ *    W4_EHIP reports a launch failure; faults during execution surface at the
+ *    caller's next synchronization.
+ *  - Weights must be finite with |w| <= 65504; activations must be finite.
+ *  - fp16 values are passed as uint16_t bit patterns, bf16 as uint16_t bit
+ *    patterns, FP8 E4M3 (OCP "fn" variant: max 448, no infinities) as bytes.
+ */
+#ifndef W4_H
+#define W4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+#define W4_OK 0
+#define W4_EINVAL 1        /* a precondition on the arguments is violated */
+#define W4_EUNSUPPORTED 2  /* well-formed, but not a configuration the library runs */
+#define W4_EHIP 3          /* the HIP runtime reported an error at launch */
+
+/* Quantizer modes. */
+#define W4_SYM 0   /* codes -8..7, scale = f * amax / 7, no zero point */
+#define W4_ASYM 1  /* codes 0..15, scale = (hi - lo) / 15, integer zero point */
+
+/* Largest number of clip fractions one call accepts. */
+#define W4_MAX_FRACS 32
+
+/*
+ * w4_quantize_blockwise -- quantize W[N, K] (fp32) in groups of G consecutive
+ * weights along K, with an optional MSE clip search.
+ *
+ * For every group the candidate ranges are, for each fraction f in `fracs`:
+ *   asym: f == 1 -> [min, max]; f < 1 -> [mid - f*h, mid + f*h] with
+ *         mid = (max + min) * 0.5, h = (max - min) * 0.5;
+ *   sym : [-f*amax, f*amax].
+ * Each candidate's scale is rounded to fp16 (a zero scale becomes 1.0), the
+ * asymmetric zero point is round_half_even(-lo / s) (an integer, not clamped),
+ * codes are clamp(round_half_even(w / s) + z, 0, 15) or
+ * clamp(round_half_even(w / s), -8, 7), and the candidate's error is the sum
+ * over the group of (w - (q - z) * s)^2, added by a fixed pairwise halving
+ * tree.  The first candidate is kept unless a later one has a strictly lower
+ * error.  All arithmetic is IEEE fp32 with round-to-nearest-even, so the
+ * result is bit-for-bit reproducible.
+ *
+ *   W        [N, K] fp32, device.
+ *   N, K     N >= 0, K > 0, K % G == 0.
+ *   G        32, 64 or 128.
+ *   mode     W4_SYM or W4_ASYM.
+ *   fracs    HOST pointer to n_fracs fp32 fractions, 1 <= n_fracs <= 32,
+ *            fracs[0] == 1.0f, every fraction in (0, 1].  n_fracs == 1 is the
+ *            plain quantizer (no search).
+ *   packed   [N, K/2] bytes out, the portable ("canonical") packing: byte
+ *            [n, k/2] holds code k (k even) in its low nibble and code k+1 in
+ *            its high nibble; symmetric codes as two's-complement nibbles.
+ *   scale    [N, K/G] fp16 out.
+ *   zero     [N, K/G] fp16 out: the integer zero point (exact for |z| <= 2048,
+ *            which holds for every group whose range contains 0).  Required
+ *            for W4_ASYM; must be NULL for W4_SYM.
+ *   clip_idx [N, K/G] bytes out, index of the chosen fraction; may be NULL.
+ */
+int w4_quantize_blockwise(const float* W, int64_t N, int64_t K, int G, int mode,
+                          const float* fracs, int n_fracs, uint8_t* packed, uint16_t* scale,
+                          uint16_t* zero, uint8_t* clip_idx, hipStream_t stream);
+
+/*
+ * w4_mse_clip_search -- the search of w4_quantize_blockwise alone: for every
+ * group, the index of the chosen fraction and optionally every candidate's
+ * error.  Arguments as for w4_quantize_blockwise, plus:
+ *   clip_idx [N, K/G] bytes out (required).
+ *   sse      [N, K/G, n_fracs] fp32 out, the candidates' squared-error sums
+ *            exactly as compared by the search; may be NULL.
+ */
+int w4_mse_clip_search(const float* W, int64_t N, int64_t K, int G, int mode,
+                       const float* fracs, int n_fracs, uint8_t* clip_idx, float* sse,
+                       hipStream_t stream);
+
+/*
+ * w4_prepack -- rearrange the portable packing into the layout the multiply
+ * kernels read ("GPU layout"), once per weight, without requantizing.
+ *   packed  [N, K/2] canonical bytes in (as written by w4_quantize_blockwise).
+ *   scale   [N, K/G] fp16 in;  zero [N, K/G] fp16 in (W4_ASYM), NULL (W4_SYM).
+ *   wq      [N, K/8] uint32 out.  Word [n, j] holds the 8 codes of k = 8j..8j+7
+ *           as unsigned 4-bit values u, with u = q (asym) or u = q + 8 (sym);
+ *           code k = 8j + 2i sits in bits 4i..4i+3 and code k = 8j + 2i + 1 in
+ *           bits 16+4i..16+4i+3 (i = 0..3).
+ *   sz      [N, K/G] uint32 out: low half the fp16 scale, high half the fp16
+ *           zero (8.0 for W4_SYM), so that W'[n, k] = (u - zero) * scale.
+ *   N >= 0, K > 0, K % G == 0, G in {32, 64, 128}.
+ */
+int w4_prepack(const uint8_t* packed, const uint16_t* scale, const uint16_t* zero, int64_t N,
+               int64_t K, int G, int mode, uint32_t* wq, uint32_t* sz, hipStream_t stream);
+
+/*
+ * w4_quantize_rows_e4m3 -- dynamic per-row FP8 quantization of activations:
+ *   xscale[m] = max(max_k |x[m, k]| / 448, 1e-8)   (fp32)
+ *   xq[m, k]  = e4m3(fl32(x[m, k] / xscale[m]))      (round to nearest even,
+ *                                                     saturating to +-448)
+ *   X [M, K] bf16 in;  xq [M, K] bytes out;  xscale [M] fp32 out.
+ *   M >= 0, K > 0, K % 8 == 0.  An all-zero row gives xscale = 1e-8 and codes 0.
+ */
+int w4_quantize_rows_e4m3(const uint16_t* X, int64_t M, int64_t K, uint8_t* xq, float* xscale,
+                          hipStream_t stream);
+
+/*
+ * w4a16_gemm -- W4A16: Y = bf16(X . W'^T) with W'[n, k] = (u - zero) * scale
+ * from the GPU layout, fp32 accumulation, bf16 output (round to nearest
+ * even).  One entry point for every M: M <= 16 runs a bandwidth-bound GEMV
+ * kernel, larger M a bf16-MFMA GEMM kernel.
+ *   X  [M, K] bf16 in;  wq, sz as written by w4_prepack;  Y [M, N] bf16 out.
+ *   M >= 0, N >= 0, K > 0, K % G == 0, G in {32, 64, 128}.
+ */
+int w4a16_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const uint32_t* sz,
+               int64_t N, int G, uint16_t* Y, hipStream_t stream);
+
+/*
+ * w4a8_gemm -- W4A8: each activation row is quantized to E4M3 exactly as by
+ * w4_quantize_rows_e4m3, then Y = bf16(xscale[m] * sum_k e4m3(xq[m, k]) *
+ * W'[n, k]) with fp32 accumulation.
+ *   X  [M, K] bf16 in.
+ *   xq [M, K] bytes and xscale [M] fp32: device buffers the call fills (they
+ *      are the operands of the multiply and are left for the caller to read).
+ *   Other arguments as for w4a16_gemm.
+ */
+int w4a8_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const uint32_t* sz,
+              int64_t N, int G, uint16_t* Y, uint8_t* xq, float* xscale, hipStream_t stream);
+
+/* Short text for a status code (static storage). */
+const char* w4_status_string(int status);
+
+/* Message of the last call on this thread that did not return W4_OK
+ * (thread-local storage, valid until the next failing call). */
+const char* w4_last_error(void);
+
+/* Version of this ABI, currently 1. */
+int w4_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4_H */

@@ -1,0 +1,119 @@
+"""The C ABI without a GPU: the library loads, exports every entry point
+``include/w4.h`` declares, and rejects bad arguments on the host before any
+launch (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?(?:int|char\s*\*|size_t|void)\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import w4_dequant_gemm_amd as w4
+    if not os.path.exists(w4.library_path):
+        from w4_dequant_gemm_amd import build
+        build.build()
+    return w4.lib()
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("w4_quantize_blockwise", "w4_mse_clip_search", "w4_prepack", "w4_quantize_rows_e4m3",
+              "w4a16_gemm", "w4a8_gemm", "w4_status_string", "w4_last_error", "w4_abi_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), f"{name} declared in w4.h but not exported"
+
+
+def test_status_strings(lib):
+    import w4_dequant_gemm_amd as w4
+    assert w4.w4_abi_version() == 1
+    assert w4.w4_status_string(0) == "ok"
+    assert w4.w4_status_string(1) == "invalid argument"
+    assert w4.w4_status_string(2) == "unsupported configuration"
+    assert w4.w4_status_string(3) == "HIP runtime error"
+
+
+def _fr(*v):
+    return (ctypes.c_float * len(v))(*v)
+
+
+def test_host_validation(lib):
+    import w4_dequant_gemm_amd as w4
+    fake = ctypes.c_void_p(0x1000)          # never dereferenced: every call below fails validation
+    one = _fr(1.0)
+    # unsupported group size
+    assert lib.w4_quantize_blockwise(fake, 4, 96, 48, 1, one, 1, fake, fake, fake, None, None) == 2
+    assert "group size 48" in w4.w4_last_error()
+    # K not a multiple of G
+    assert lib.w4_quantize_blockwise(fake, 4, 100, 32, 1, one, 1, fake, fake, fake, None, None) == 1
+    # bad mode, bad fracs
+    assert lib.w4_quantize_blockwise(fake, 4, 96, 32, 7, one, 1, fake, fake, fake, None, None) == 1
+    assert lib.w4_quantize_blockwise(fake, 4, 96, 32, 1, _fr(0.9), 1, fake, fake, fake, None, None) == 1
+    assert lib.w4_quantize_blockwise(fake, 4, 96, 32, 1, _fr(1.0, 1.5), 2, fake, fake, fake, None, None) == 1
+    assert lib.w4_quantize_blockwise(fake, 4, 96, 32, 1, _fr(1.0), 0, fake, fake, fake, None, None) == 1
+    assert lib.w4_quantize_blockwise(fake, 4, 96, 32, 1, _fr(*([1.0] * 33)), 33, fake, fake, fake, None, None) == 1
+    # asym needs a zero buffer; sym must not get one
+    assert lib.w4_quantize_blockwise(fake, 4, 96, 32, 1, one, 1, fake, fake, None, None, None) == 1
+    assert lib.w4_quantize_blockwise(fake, 4, 96, 32, 0, one, 1, fake, fake, fake, None, None) == 1
+    # misaligned pointer
+    assert lib.w4_quantize_blockwise(ctypes.c_void_p(0x1004), 4, 96, 32, 1, one, 1, fake, fake, fake, None,
+                                     None) == 1
+    assert "aligned" in w4.w4_last_error()
+    # null pointers and negative sizes in the products
+    assert lib.w4a16_gemm(None, 2, 96, fake, fake, 8, 32, fake, None) == 1
+    assert lib.w4a16_gemm(fake, -1, 96, fake, fake, 8, 32, fake, None) == 1
+    assert lib.w4a8_gemm(fake, 2, 96, fake, fake, 8, 32, fake, None, fake, None) == 1
+    assert lib.w4a16_gemm(fake, 2, 96, fake, fake, 8, 16, fake, None) == 2
+    assert lib.w4_quantize_rows_e4m3(fake, 2, 12, fake, fake, None) == 1
+    assert lib.w4_prepack(fake, fake, None, 4, 96, 32, 1, fake, fake, None) == 1
+    # clip search needs its output
+    assert lib.w4_mse_clip_search(fake, 4, 96, 32, 1, one, 1, None, None, None) == 1
+
+
+def test_empty_shapes_are_no_ops(lib):
+    # nothing to do: OK without touching any pointer (and without a device)
+    one = _fr(1.0)
+    assert lib.w4_quantize_blockwise(None, 0, 96, 32, 1, one, 1, None, None, None, None, None) == 0
+    assert lib.w4a16_gemm(None, 0, 96, None, None, 8, 32, None, None) == 0
+    assert lib.w4a16_gemm(None, 4, 96, None, None, 0, 32, None, None) == 0
+    assert lib.w4_quantize_rows_e4m3(None, 0, 96, None, None, None) == 0
+    assert lib.w4_prepack(None, None, None, 0, 96, 32, 1, None, None, None) == 0
+
+
+def test_product_path_has_no_fallback():
+    # the binding raises when the library is missing instead of computing anything
+    import importlib
+
+    import w4_dequant_gemm_amd as w4
+    saved_path, saved_lib = w4.library_path, w4._lib
+    try:
+        w4.library_path = os.path.join(ROOT, "does-not-exist", "libw4.so")
+        w4._lib = None
+        with pytest.raises(RuntimeError, match="not built"):
+            w4.lib()
+    finally:
+        w4.library_path, w4._lib = saved_path, saved_lib
+    importlib.reload  # noqa: B018 (module kept loaded)
+
+
+def test_binding_never_imports_the_oracle():
+    src = open(os.path.join(ROOT, "w4_dequant_gemm_amd", "__init__.py")).read()
+    assert "oracle" not in src.replace("no CPU or PyTorch fallback", "")
+    for f in os.listdir(os.path.join(ROOT, "w4_dequant_gemm_amd", "csrc")):
+        text = open(os.path.join(ROOT, "w4_dequant_gemm_amd", "csrc", f)).read()
+        assert "w4_oracle" not in text and "w4o_" not in text

@@ -1,0 +1,240 @@
+"""Parity of the HIP row quantizer (bit-exact) and of the W4A16 / W4A8
+GEMV and GEMM (relative Frobenius error <= 5e-3 against the float64 oracle
+over the oracle's own quantized weights)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import (REL_TOL, assert_bits_equal, bf16_dev, bits16, host, oracle_quant, prepack_dev,
+                     require_gpu, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _rows_cols(M, N, max_rows, max_cols, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = np.arange(M) if M <= max_rows else np.sort(rng.choice(M, max_rows, replace=False))
+    cols = np.arange(N) if N <= max_cols else np.sort(rng.choice(N, max_cols, replace=False))
+    return rows.astype(np.int64), cols.astype(np.int64)
+
+
+# ------------------------------------------------------------ row quantizer
+
+def test_rowquant_bit_exact_workloads():
+    require_gpu()
+    import torch
+    import w4_dequant_gemm_amd as w4
+    for name, K, Ms in (("gemma12b_w4a8", 3840, (1, 16, 64, 256)), ("gemma12b_w4a8", 15360, (16,)),
+                        ("llama70b_prefill", 8192, (2048,))):
+        wl = synth.WORKLOADS[name]
+        for M in Ms:
+            Xb = synth.activations_bf16_bits(wl, M, K)
+            Xb[M // 2] = 0                                    # an all-zero row
+            xq, xs = w4.w4_quantize_rows_e4m3(bf16_dev(Xb))
+            torch.cuda.synchronize()
+            rq, rs = oracle.row_quant_e4m3(Xb)
+            assert_bits_equal(host(xq), rq, f"E4M3 codes {name} M={M} K={K}")
+            assert_bits_equal(host(xs).view(np.uint32), rs.view(np.uint32), f"row scales {name} M={M}")
+            assert np.all(host(xq)[M // 2] == 0)
+
+
+def test_rowquant_every_bf16_value():
+    # every finite bf16 magnitude pattern, in rows whose max fixes the scale at a
+    # power of two (x / s is then exact), plus rows with arbitrary scales
+    require_gpu()
+    import torch
+    import w4_dequant_gemm_amd as w4
+    u = np.arange(0, 0x10000, dtype=np.uint32)
+    x = (u << 16).view(np.float32)
+    rows = []
+    for e in (-10, 0, 6):
+        lim = np.float32(448.0 * 2.0 ** e)
+        v = x[np.isfinite(x) & (np.abs(x) <= lim)]
+        v = np.concatenate([v, [lim]])
+        pad = (-len(v)) % 8
+        v = np.concatenate([v, np.zeros(pad, np.float32)])
+        rows.append(v)
+    rng = np.random.default_rng(4)
+    for _ in range(4):
+        v = (rng.standard_normal(4096) * np.exp2(rng.uniform(-12, 12, 4096))).astype(np.float32)
+        rows.append(v)
+    K = max(len(r) for r in rows)
+    K += (-K) % 8
+    X = np.zeros((len(rows), K), np.float32)
+    for i, r in enumerate(rows):
+        X[i, :len(r)] = r
+    Xb = synth.to_bf16_bits(X)
+    xq, xs = w4.w4_quantize_rows_e4m3(bf16_dev(Xb))
+    torch.cuda.synchronize()
+    rq, rs = oracle.row_quant_e4m3(Xb)
+    assert_bits_equal(host(xs).view(np.uint32), rs.view(np.uint32), "row scales")
+    assert_bits_equal(host(xq), rq, "E4M3 codes")
+
+
+# ------------------------------------------------------------------ products
+
+MUL_CASES = [
+    # (workload, matrix, rows of W or None, mode, G, n_fracs, M values)
+    ("tiny", 0, None, "asym", 32, 20, (1, 2, 3, 16, 17, 40)),
+    ("tiny", 0, None, "sym", 32, 20, (1, 5, 33)),
+    ("smollm2_135m_mlp", 0, None, "asym", 32, 1, (1, 4, 16)),
+    ("smollm2_135m_mlp", 1, None, "asym", 32, 1, (1, 4, 16, 64)),
+    ("llama8b_decode", 0, None, "asym", 128, 1, (1, 4, 16)),
+    ("llama8b_decode", 1, None, "asym", 128, 1, (1, 4, 16)),
+    ("gemma12b_w4a8", 0, None, "asym", 128, 11, (1, 16, 64, 256)),
+    ("gemma12b_w4a8", 1, None, "asym", 128, 11, (1, 16, 64, 256)),
+]
+
+
+def _x(name, M, K):
+    return synth.activations_bf16_bits(synth.WORKLOADS[name], M, K)
+
+
+@pytest.mark.parametrize("case", MUL_CASES, ids=lambda c: f"{c[0]}-{c[1]}-{c[3]}-g{c[4]}")
+@pytest.mark.parametrize("kind", ["w4a16", "w4a8"])
+def test_products_match_oracle(case, kind):
+    require_gpu()
+    import torch
+    import w4_dequant_gemm_amd as w4
+    name, idx, rows, mode, G, nf, Ms = case
+    q = oracle_quant(name, idx, rows, mode, G, nf)
+    pk, G = prepack_dev(q)
+    N, K = q["q"].shape
+    for M in Ms:
+        print(f"[{kind}] {name}[{idx}] {mode} G={G} M={M} N={N} K={K}", flush=True)
+        Xb = _x(name, M, K)
+        r, c = _rows_cols(M, N, 64, 1024, seed=M)
+        if kind == "w4a16":
+            Y = w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G)
+            torch.cuda.synchronize()
+            want = oracle.gemm_ref(oracle.bf16_bits_to_f64(Xb), q["packed"], q["scale"], q["zero"], G, mode,
+                                   rows=r, cols=c)
+        else:
+            Y, xq, xs = w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G)
+            torch.cuda.synchronize()
+            want, rq, rs = oracle.w4a8_ref(Xb, q["packed"], q["scale"], q["zero"], G, mode, rows=r, cols=c)
+            assert_bits_equal(host(xq), rq, "E4M3 activations")
+            assert_bits_equal(host(xs).view(np.uint32), rs.view(np.uint32), "row scales")
+        got = Y.float().cpu().numpy()[np.ix_(r, c)]
+        err = oracle.rel_error(want, got)
+        print(f"    rel err {err:.3e}", flush=True)
+        assert err <= REL_TOL, f"{kind} {name} M={M}: relative error {err:.3e} > {REL_TOL}"
+
+
+@pytest.mark.parametrize("kind", ["w4a16", "w4a8"])
+def test_70b_prefill_gemm_sampled(kind):
+    # full 2048 x 28672 x 8192 launch; outputs checked on sampled rows and columns
+    require_gpu()
+    import torch
+    import w4_dequant_gemm_amd as w4
+    from helpers import weight
+    W = weight("llama70b_prefill", 0, None)
+    fr = synth.FRACS_11
+    print(f"[{kind}] 70B prefill: quantizing on the GPU", flush=True)
+    quant = w4.w4_quantize_blockwise(to_dev(W), 128, "asym", fr)
+    # the oracle's codes for the sampled weight rows must agree bit for bit
+    rng = np.random.default_rng(11)
+    cols = np.sort(rng.choice(W.shape[0], 192, replace=False)).astype(np.int64)
+    qs = oracle.quantize(np.ascontiguousarray(W[cols]), 128, "asym", fracs=fr)
+    torch.cuda.synchronize()
+    assert_bits_equal(host(quant["packed"])[cols], qs["packed"], "packed codes (sampled rows)")
+    pk = w4.w4_prepack(quant["packed"], quant["scale"], quant["zero"], 128, "asym")
+    M = 2048
+    Xb = _x("llama70b_prefill", M, W.shape[1])
+    rows = np.sort(rng.choice(M, 48, replace=False)).astype(np.int64)
+    if kind == "w4a16":
+        Y = w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], 128)
+        torch.cuda.synchronize()
+        want = oracle.gemm_ref(oracle.bf16_bits_to_f64(Xb[rows]), qs["packed"], qs["scale"], qs["zero"], 128, "asym")
+    else:
+        Y, xq, xs = w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], 128)
+        torch.cuda.synchronize()
+        want, rq, rs = oracle.w4a8_ref(Xb[rows], qs["packed"], qs["scale"], qs["zero"], 128, "asym")
+        assert_bits_equal(host(xq)[rows], rq, "E4M3 activations (sampled rows)")
+    got = Y.float().cpu().numpy()[np.ix_(rows, cols)]
+    err = oracle.rel_error(want, got)
+    print(f"    rel err {err:.3e}", flush=True)
+    assert err <= REL_TOL
+
+
+@pytest.mark.parametrize("kind", ["w4a16", "w4a8"])
+def test_one_hot_rows_recover_dequantized_weights(kind):
+    # X = e_k: W4A16 output column k is bf16(W'[n, k]) exactly, since a single
+    # product of exact values is accumulated; W4A8 equals it after removing the
+    # row scale (one-hot rows quantize to a single 448 code)
+    require_gpu()
+    import torch
+    import w4_dequant_gemm_amd as w4
+    q = oracle_quant("smollm2_135m_mlp", 1, None, "asym", 32, 1)
+    pk, G = prepack_dev(q)
+    N, K = q["q"].shape
+    Wd = oracle.dequant(q["packed"], q["scale"], q["zero"], G, "asym")
+    for M in (1, 8, 16, 48):
+        ks = np.linspace(0, K - 1, M).astype(np.int64)
+        X = np.zeros((M, K), np.float32)
+        X[np.arange(M), ks] = 1.0
+        Xb = synth.to_bf16_bits(X)
+        want = synth.to_bf16_bits(Wd[:, ks].T.astype(np.float32))   # exact W' rounded once to bf16
+        if kind == "w4a16":
+            Y = w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G)
+            torch.cuda.synchronize()
+            assert_bits_equal(bits16(Y), want, f"one-hot W4A16 M={M}")
+        else:
+            Y, xq, xs = w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G)
+            torch.cuda.synchronize()
+            # xscale = 1/448, code 448: the product is W' * 448 * (1/448) in fp32
+            got = Y.float().cpu().numpy()
+            np.testing.assert_allclose(got, Wd[:, ks].T, rtol=2 ** -8, atol=0)
+
+
+def test_zero_rows_and_ragged_shapes():
+    require_gpu()
+    import torch
+    import w4_dequant_gemm_amd as w4
+    # K = 96 (3 groups of 32, less than one lane chunk), N = 200 (ragged tile)
+    W = synth.normal_matrix(31, 200, 96, 0.05)
+    for mode, G in (("asym", 32), ("sym", 32)):
+        q = oracle.quantize(W, G, mode, fracs=synth.FRACS_11)
+        pk, G2 = prepack_dev(q)
+        for M in (1, 3, 7, 17, 130):
+            Xb = synth.to_bf16_bits(synth.normal_matrix(M, M, 96))
+            Xb[0] = 0
+            Y = w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G2)
+            Y8, _, _ = w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G2)
+            torch.cuda.synchronize()
+            want = oracle.gemm_ref(oracle.bf16_bits_to_f64(Xb), q["packed"], q["scale"], q["zero"], G2, mode)
+            want8, _, _ = oracle.w4a8_ref(Xb, q["packed"], q["scale"], q["zero"], G2, mode)
+            assert np.all(bits16(Y)[0] & 0x7FFF == 0)           # a zero row gives zeros
+            assert np.all(bits16(Y8)[0] & 0x7FFF == 0)
+            if M > 1:
+                assert oracle.rel_error(want[1:], Y.float().cpu().numpy()[1:]) <= REL_TOL
+                assert oracle.rel_error(want8[1:], Y8.float().cpu().numpy()[1:]) <= REL_TOL
+
+
+def test_group_size_64():
+    require_gpu()
+    import torch
+    import w4_dequant_gemm_amd as w4
+    q = oracle_quant("smollm2_135m_mlp", 1, None, "sym", 64, 11)
+    pk, G = prepack_dev(q)
+    N, K = q["q"].shape
+    for M in (1, 16, 64):
+        Xb = _x("smollm2_135m_mlp", M, K)
+        Y = w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G)
+        torch.cuda.synchronize()
+        want = oracle.gemm_ref(oracle.bf16_bits_to_f64(Xb), q["packed"], q["scale"], q["zero"], G, "sym")
+        assert oracle.rel_error(want, Y.float().cpu().numpy()) <= REL_TOL
+
+
+def test_invalid_arguments_raise():
+    require_gpu()
+    import torch
+    import w4_dequant_gemm_amd as w4
+    W = torch.zeros((4, 96), device="cuda:0")
+    with pytest.raises(w4.W4Error):
+        w4.w4_quantize_blockwise(W, 48, "asym")            # unsupported group size
+    with pytest.raises(w4.W4Error):
+        w4.w4_quantize_blockwise(W, 32, "asym", (0.9, 0.8))  # fracs[0] must be 1
+    with pytest.raises(w4.W4Error):
+        w4.w4_quantize_blockwise(torch.zeros((4, 100), device="cuda:0"), 32, "asym")  # K % G

@@ -1,0 +1,225 @@
+"""Python binding of the W4 C ABI (``include/w4.h``) for MI355X (gfx950).
+
+Each function has the name of the C entry point it calls and only marshals
+arguments: torch tensors supply device memory and the current HIP stream,
+every step of the computation runs in the HIP library ``libw4.so``.  There is
+no CPU or PyTorch fallback: if the library is not built, or a call returns a
+non-zero status, the function raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+__all__ = [
+    "W4Error", "SYM", "ASYM", "MAX_FRACS", "lib", "library_path",
+    "w4_quantize_blockwise", "w4_mse_clip_search", "w4_prepack", "w4_quantize_rows_e4m3",
+    "w4a16_gemm", "w4a8_gemm", "w4_status_string", "w4_last_error", "w4_abi_version",
+    "FRACS_PLAIN", "FRACS_11",
+]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(HERE, "libw4.so")
+
+SYM = 0
+ASYM = 1
+MAX_FRACS = 32
+FRACS_PLAIN = (1.0,)
+# 1.00 down to 0.50 in steps of 0.05 (gowda.ai "LLM fast inference", "MSE clipping")
+FRACS_11 = (1.00, 0.95, 0.90, 0.85, 0.80, 0.75, 0.70, 0.65, 0.60, 0.55, 0.50)
+
+_MODES = {"sym": SYM, "asym": ASYM, SYM: SYM, ASYM: ASYM}
+
+
+class W4Error(RuntimeError):
+    """A W4 call returned a non-zero status."""
+
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn} failed with status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded ``libw4.so`` (raises if it was never built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise RuntimeError(f"W4 HIP library not built: {library_path} is missing "
+                           "(run __graft_entry__.build() or python w4_dequant_gemm_amd/build.py)")
+    L = ctypes.CDLL(library_path)
+    P, i64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.w4_quantize_blockwise.argtypes = [P, i64, i64, I, I, P, I, P, P, P, P, P]
+    L.w4_mse_clip_search.argtypes = [P, i64, i64, I, I, P, I, P, P, P]
+    L.w4_prepack.argtypes = [P, P, P, i64, i64, I, I, P, P, P]
+    L.w4_quantize_rows_e4m3.argtypes = [P, i64, i64, P, P, P]
+    L.w4a16_gemm.argtypes = [P, i64, i64, P, P, i64, I, P, P]
+    L.w4a8_gemm.argtypes = [P, i64, i64, P, P, i64, I, P, P, P, P]
+    for name in ("w4_quantize_blockwise", "w4_mse_clip_search", "w4_prepack", "w4_quantize_rows_e4m3",
+                 "w4a16_gemm", "w4a8_gemm"):
+        getattr(L, name).restype = I
+    L.w4_status_string.argtypes = [I]
+    L.w4_status_string.restype = ctypes.c_char_p
+    L.w4_last_error.argtypes = []
+    L.w4_last_error.restype = ctypes.c_char_p
+    L.w4_abi_version.argtypes = []
+    L.w4_abi_version.restype = I
+    _lib = L
+    return L
+
+
+def w4_status_string(status: int) -> str:
+    return lib().w4_status_string(status).decode()
+
+
+def w4_last_error() -> str:
+    return lib().w4_last_error().decode()
+
+
+def w4_abi_version() -> int:
+    return int(lib().w4_abi_version())
+
+
+# ------------------------------------------------------------------ helpers
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise W4Error(fn, status, w4_last_error())
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device, stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _fracs(fracs: Sequence[float]):
+    arr = (ctypes.c_float * len(fracs))(*[float(f) for f in fracs])
+    return arr, len(fracs)
+
+
+def _empty(shape, dtype, device):
+    return torch.empty(shape, dtype=dtype, device=device)
+
+
+# ---------------------------------------------------------------- quantizer
+
+def w4_quantize_blockwise(W: torch.Tensor, G: int, mode, fracs: Sequence[float] = FRACS_PLAIN, *,
+                          packed=None, scale=None, zero=None, clip_idx=None, want_clip: bool = True,
+                          stream=None) -> dict:
+    """Quantize fp32 ``W[N, K]`` in groups of ``G`` (see ``w4.h``).
+
+    Returns ``packed`` (uint8 [N, K/2], canonical nibbles), ``scale`` and
+    ``zero`` (float16 [N, K/G]; zero is None for symmetric) and
+    ``clip_idx`` (uint8 [N, K/G] or None).
+    """
+    m = _MODES[mode]
+    N, K = W.shape
+    dev = W.device
+    ng = K // G if G else 0
+    packed = _empty((N, K // 2), torch.uint8, dev) if packed is None else packed
+    scale = _empty((N, ng), torch.float16, dev) if scale is None else scale
+    if m == ASYM and zero is None:
+        zero = _empty((N, ng), torch.float16, dev)
+    if m == SYM:
+        zero = None
+    if want_clip and clip_idx is None:
+        clip_idx = _empty((N, ng), torch.uint8, dev)
+    fr, nf = _fracs(fracs)
+    rc = lib().w4_quantize_blockwise(_dev(W, "W", torch.float32), N, K, G, m, fr, nf,
+                                     _dev(packed, "packed"), _dev(scale, "scale"), _dev(zero, "zero"),
+                                     _dev(clip_idx, "clip_idx"), _stream(dev, stream))
+    _check("w4_quantize_blockwise", rc)
+    return {"packed": packed, "scale": scale, "zero": zero, "clip_idx": clip_idx}
+
+
+def w4_mse_clip_search(W: torch.Tensor, G: int, mode, fracs: Sequence[float], *, clip_idx=None,
+                       sse=None, want_sse: bool = False, stream=None) -> dict:
+    """Per-group index of the chosen clip fraction (and every candidate's error)."""
+    m = _MODES[mode]
+    N, K = W.shape
+    dev = W.device
+    ng = K // G if G else 0
+    clip_idx = _empty((N, ng), torch.uint8, dev) if clip_idx is None else clip_idx
+    if want_sse and sse is None:
+        sse = _empty((N, ng, len(fracs)), torch.float32, dev)
+    fr, nf = _fracs(fracs)
+    rc = lib().w4_mse_clip_search(_dev(W, "W", torch.float32), N, K, G, m, fr, nf,
+                                  _dev(clip_idx, "clip_idx"), _dev(sse, "sse"), _stream(dev, stream))
+    _check("w4_mse_clip_search", rc)
+    return {"clip_idx": clip_idx, "sse": sse}
+
+
+def w4_prepack(packed: torch.Tensor, scale: torch.Tensor, zero: Optional[torch.Tensor], G: int, mode, *,
+               wq=None, sz=None, stream=None) -> dict:
+    """Portable packing -> GPU layout: ``wq`` (int32 [N, K/8]) and ``sz`` (int32 [N, K/G])."""
+    m = _MODES[mode]
+    N, K2 = packed.shape
+    K = 2 * K2
+    dev = packed.device
+    wq = _empty((N, K // 8), torch.int32, dev) if wq is None else wq
+    sz = _empty((N, K // G if G else 0), torch.int32, dev) if sz is None else sz
+    rc = lib().w4_prepack(_dev(packed, "packed"), _dev(scale, "scale"), _dev(zero if m == ASYM else None, "zero"),
+                          N, K, G, m, _dev(wq, "wq"), _dev(sz, "sz"), _stream(dev, stream))
+    _check("w4_prepack", rc)
+    return {"wq": wq, "sz": sz}
+
+
+# --------------------------------------------------------------- multiplies
+
+def w4_quantize_rows_e4m3(X: torch.Tensor, *, xq=None, xscale=None, stream=None):
+    """Per-row dynamic E4M3 of bf16 ``X[M, K]``: returns (xq uint8 [M, K], xscale fp32 [M])."""
+    M, K = X.shape
+    dev = X.device
+    xq = _empty((M, K), torch.uint8, dev) if xq is None else xq
+    xscale = _empty((M,), torch.float32, dev) if xscale is None else xscale
+    rc = lib().w4_quantize_rows_e4m3(_dev(X, "X", torch.bfloat16), M, K, _dev(xq, "xq"),
+                                     _dev(xscale, "xscale", torch.float32), _stream(dev, stream))
+    _check("w4_quantize_rows_e4m3", rc)
+    return xq, xscale
+
+
+def w4a16_gemm(X: torch.Tensor, wq: torch.Tensor, sz: torch.Tensor, G: int, *, Y=None, stream=None):
+    """``Y[M, N] = bf16(X . W'^T)`` from bf16 ``X[M, K]`` and the GPU-layout weights."""
+    M, K = X.shape
+    N = wq.shape[0]
+    dev = X.device
+    Y = _empty((M, N), torch.bfloat16, dev) if Y is None else Y
+    rc = lib().w4a16_gemm(_dev(X, "X", torch.bfloat16), M, K, _dev(wq, "wq"), _dev(sz, "sz"), N, G,
+                          _dev(Y, "Y", torch.bfloat16), _stream(dev, stream))
+    _check("w4a16_gemm", rc)
+    return Y
+
+
+def w4a8_gemm(X: torch.Tensor, wq: torch.Tensor, sz: torch.Tensor, G: int, *, Y=None, xq=None, xscale=None,
+              stream=None):
+    """W4A8: per-row E4M3 of ``X`` then ``Y = bf16(xscale * Xq . W'^T)``; returns (Y, xq, xscale)."""
+    M, K = X.shape
+    N = wq.shape[0]
+    dev = X.device
+    Y = _empty((M, N), torch.bfloat16, dev) if Y is None else Y
+    xq = _empty((M, K), torch.uint8, dev) if xq is None else xq
+    xscale = _empty((M,), torch.float32, dev) if xscale is None else xscale
+    rc = lib().w4a8_gemm(_dev(X, "X", torch.bfloat16), M, K, _dev(wq, "wq"), _dev(sz, "sz"), N, G,
+                         _dev(Y, "Y", torch.bfloat16), _dev(xq, "xq"), _dev(xscale, "xscale", torch.float32),
+                         _stream(dev, stream))
+    _check("w4a8_gemm", rc)
+    return Y, xq, xscale

@@ -1,0 +1,200 @@
+// C ABI of the W4 library: argument checks, then one launch on the caller's
+// stream.  No allocation, no state beyond a thread-local error message, no
+// fallback: anything the kernels do not run is rejected before launch.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/w4.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return W4_OK;
+    return fail(W4_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int check_group(const char* fn, int64_t N, int64_t K, int G) {
+    if (N < 0) return fail(W4_EINVAL, "%s: N = %lld must be >= 0", fn, static_cast<long long>(N));
+    if (K <= 0) return fail(W4_EINVAL, "%s: K = %lld must be > 0", fn, static_cast<long long>(K));
+    if (G != 32 && G != 64 && G != 128)
+        return fail(W4_EUNSUPPORTED, "%s: group size %d is not one of 32, 64, 128", fn, G);
+    if (K % G != 0)
+        return fail(W4_EINVAL, "%s: K = %lld is not a multiple of the group size %d", fn,
+                    static_cast<long long>(K), G);
+    return W4_OK;
+}
+
+int check_fracs(const char* fn, const float* fracs, int n_fracs) {
+    if (!fracs) return fail(W4_EINVAL, "%s: fracs is NULL", fn);
+    if (n_fracs < 1 || n_fracs > W4_MAX_FRACS)
+        return fail(W4_EINVAL, "%s: n_fracs = %d outside 1..%d", fn, n_fracs, W4_MAX_FRACS);
+    if (fracs[0] != 1.0f) return fail(W4_EINVAL, "%s: fracs[0] must be 1.0 (the plain quantizer)", fn);
+    for (int i = 0; i < n_fracs; ++i)
+        if (!(fracs[i] > 0.0f && fracs[i] <= 1.0f))
+            return fail(W4_EINVAL, "%s: fracs[%d] = %g outside (0, 1]", fn, i, static_cast<double>(fracs[i]));
+    return W4_OK;
+}
+
+int check_mode(const char* fn, int mode) {
+    if (mode != W4_SYM && mode != W4_ASYM) return fail(W4_EINVAL, "%s: mode %d is neither W4_SYM nor W4_ASYM", fn, mode);
+    return W4_OK;
+}
+
+#define W4_REQUIRE_PTR(fn, p)                                                        \
+    do {                                                                             \
+        if (!(p)) return fail(W4_EINVAL, "%s: %s is NULL", fn, #p);                  \
+        if (!aligned16(p)) return fail(W4_EINVAL, "%s: %s is not 16-byte aligned", fn, #p); \
+    } while (0)
+
+#define W4_TRY(expr)            \
+    do {                        \
+        int _rc = (expr);       \
+        if (_rc != W4_OK) return _rc; \
+    } while (0)
+
+int quantize_common(const char* fn, const float* W, int64_t N, int64_t K, int G, int mode,
+                    const float* fracs, int n_fracs, bool encode, uint8_t* packed, uint16_t* scale,
+                    uint16_t* zero, uint8_t* clip, float* sse, hipStream_t stream) {
+    W4_TRY(check_group(fn, N, K, G));
+    W4_TRY(check_mode(fn, mode));
+    W4_TRY(check_fracs(fn, fracs, n_fracs));
+    if (N == 0) return W4_OK;
+    W4_REQUIRE_PTR(fn, W);
+    if (encode) {
+        W4_REQUIRE_PTR(fn, packed);
+        if (!scale) return fail(W4_EINVAL, "%s: scale is NULL", fn);
+        if (mode == W4_ASYM && !zero) return fail(W4_EINVAL, "%s: zero is NULL for W4_ASYM", fn);
+        if (mode == W4_SYM && zero) return fail(W4_EINVAL, "%s: zero must be NULL for W4_SYM", fn);
+    } else if (!clip) {
+        return fail(W4_EINVAL, "%s: clip_idx is NULL", fn);
+    }
+    w4::QuantizeParams p{};
+    p.W = W;
+    p.n_groups = N * (K / G);
+    p.G = G;
+    p.asym = mode == W4_ASYM;
+    p.n_fracs = n_fracs;
+    for (int i = 0; i < n_fracs; ++i) p.fracs[i] = fracs[i];
+    p.encode = encode;
+    p.packed = packed;
+    p.scale = scale;
+    p.zero = zero;
+    p.clip = clip;
+    p.sse = sse;
+    return hip_status(w4::launch_quantize(p, stream), fn);
+}
+
+int mul_common(const char* fn, const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq,
+               const uint32_t* sz, int64_t N, int G, uint16_t* Y) {
+    W4_TRY(check_group(fn, N, K, G));
+    if (M < 0) return fail(W4_EINVAL, "%s: M = %lld must be >= 0", fn, static_cast<long long>(M));
+    if (M == 0 || N == 0) return W4_OK;
+    W4_REQUIRE_PTR(fn, X);
+    W4_REQUIRE_PTR(fn, wq);
+    W4_REQUIRE_PTR(fn, sz);
+    W4_REQUIRE_PTR(fn, Y);
+    return W4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4_quantize_blockwise(const float* W, int64_t N, int64_t K, int G, int mode, const float* fracs,
+                          int n_fracs, uint8_t* packed, uint16_t* scale, uint16_t* zero,
+                          uint8_t* clip_idx, hipStream_t stream) {
+    return quantize_common("w4_quantize_blockwise", W, N, K, G, mode, fracs, n_fracs, true, packed, scale,
+                           zero, clip_idx, nullptr, stream);
+}
+
+int w4_mse_clip_search(const float* W, int64_t N, int64_t K, int G, int mode, const float* fracs,
+                       int n_fracs, uint8_t* clip_idx, float* sse, hipStream_t stream) {
+    return quantize_common("w4_mse_clip_search", W, N, K, G, mode, fracs, n_fracs, false, nullptr, nullptr,
+                           nullptr, clip_idx, sse, stream);
+}
+
+int w4_prepack(const uint8_t* packed, const uint16_t* scale, const uint16_t* zero, int64_t N, int64_t K,
+               int G, int mode, uint32_t* wq, uint32_t* sz, hipStream_t stream) {
+    const char* fn = "w4_prepack";
+    W4_TRY(check_group(fn, N, K, G));
+    W4_TRY(check_mode(fn, mode));
+    if (N == 0) return W4_OK;
+    W4_REQUIRE_PTR(fn, packed);
+    if (!scale) return fail(W4_EINVAL, "%s: scale is NULL", fn);
+    if (mode == W4_ASYM && !zero) return fail(W4_EINVAL, "%s: zero is NULL for W4_ASYM", fn);
+    W4_REQUIRE_PTR(fn, wq);
+    W4_REQUIRE_PTR(fn, sz);
+    w4::PrepackParams p{packed, scale, zero, N, K, G, mode == W4_ASYM, wq, sz};
+    return hip_status(w4::launch_prepack(p, stream), fn);
+}
+
+int w4_quantize_rows_e4m3(const uint16_t* X, int64_t M, int64_t K, uint8_t* xq, float* xscale,
+                          hipStream_t stream) {
+    const char* fn = "w4_quantize_rows_e4m3";
+    if (M < 0) return fail(W4_EINVAL, "%s: M = %lld must be >= 0", fn, static_cast<long long>(M));
+    if (K <= 0 || K % 8 != 0)
+        return fail(W4_EINVAL, "%s: K = %lld must be a positive multiple of 8", fn, static_cast<long long>(K));
+    if (M == 0) return W4_OK;
+    W4_REQUIRE_PTR(fn, X);
+    W4_REQUIRE_PTR(fn, xq);
+    if (!xscale) return fail(W4_EINVAL, "%s: xscale is NULL", fn);
+    w4::RowQuantParams p{X, M, K, xq, xscale};
+    return hip_status(w4::launch_rowquant(p, stream), fn);
+}
+
+int w4a16_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const uint32_t* sz, int64_t N,
+               int G, uint16_t* Y, hipStream_t stream) {
+    const char* fn = "w4a16_gemm";
+    W4_TRY(mul_common(fn, X, M, K, wq, sz, N, G, Y));
+    if (M == 0 || N == 0) return W4_OK;
+    w4::MulParams p{X, nullptr, M, K, N, G, wq, sz, Y, false};
+    if (M <= w4::kGemvMaxM) return hip_status(w4::launch_gemv(p, stream), fn);
+    return hip_status(w4::launch_gemm(p, stream), fn);
+}
+
+int w4a8_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const uint32_t* sz, int64_t N,
+              int G, uint16_t* Y, uint8_t* xq, float* xscale, hipStream_t stream) {
+    const char* fn = "w4a8_gemm";
+    W4_TRY(mul_common(fn, X, M, K, wq, sz, N, G, Y));
+    if (M == 0 || N == 0) return W4_OK;
+    W4_REQUIRE_PTR(fn, xq);
+    if (!xscale) return fail(W4_EINVAL, "%s: xscale is NULL", fn);
+    w4::RowQuantParams rq{X, M, K, xq, xscale};
+    W4_TRY(hip_status(w4::launch_rowquant(rq, stream), fn));
+    w4::MulParams p{xq, xscale, M, K, N, G, wq, sz, Y, true};
+    if (M <= w4::kGemvMaxM) return hip_status(w4::launch_gemv(p, stream), fn);
+    return hip_status(w4::launch_gemm(p, stream), fn);
+}
+
+const char* w4_status_string(int status) {
+    switch (status) {
+        case W4_OK: return "ok";
+        case W4_EINVAL: return "invalid argument";
+        case W4_EUNSUPPORTED: return "unsupported configuration";
+        case W4_EHIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* w4_last_error(void) { return g_last_error; }
+
+int w4_abi_version(void) { return 1; }
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// Device-side helpers shared by the gfx950 kernels of the W4 library.
+#pragma once
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4 {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef int int8x_t __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+// fp16 bits <-> float
+__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
+    return __half2float(__ushort_as_half(static_cast<unsigned short>(h & 0xFFFFu)));
+}
+__device__ __forceinline__ uint32_t float_to_half_bits(float f) {
+    return __half_as_ushort(__float2half_rn(f));
+}
+
+// bf16 halves of a 32-bit word -> float (exact)
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    float2_t v = {lo, hi};
+    bf16x2_t r = __builtin_convertvector(v, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
+    return static_cast<uint16_t>(pack_bf16x2(f, 0.0f) & 0xFFFFu);
+}
+
+// sum_i a.bf16[i] * b.bf16[i] + c  (v_dot2_f32_bf16)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Nibble pair i (0..3) of a GPU-layout code word as two bf16 values 128 + u:
+// the nibbles at bits 4i and 16 + 4i land in the low mantissa bits of the
+// bf16 constant 128.0 (0x4300), whose unit in the last place is exactly 1.
+__device__ __forceinline__ uint32_t nibble_pair_bf16(uint32_t w, int i) {
+    return ((w >> (4 * i)) & 0x000F000Fu) | 0x43004300u;
+}
+
+// Butterfly sum over the 64 lanes of a wavefront; every lane gets the total.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
+}  // namespace w4

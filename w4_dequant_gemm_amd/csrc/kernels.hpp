@@ -1,0 +1,62 @@
+// Host-side launch interface of the gfx950 kernels (used by api.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4 {
+
+constexpr int kMaxFracs = 32;
+
+struct QuantizeParams {
+    const float* W;          // [n_groups * G] fp32: groups are consecutive runs of G weights
+    int64_t n_groups;
+    int G;                   // 32, 64, 128
+    int asym;                // 0 symmetric, 1 asymmetric
+    int n_fracs;
+    float fracs[kMaxFracs];
+    bool encode;             // false: search only (clip index and errors)
+    uint8_t* packed;         // [n_groups * G / 2] canonical nibbles (encode)
+    uint16_t* scale;         // [n_groups] fp16 (encode)
+    uint16_t* zero;          // [n_groups] fp16 (encode, asym)
+    uint8_t* clip;           // [n_groups] or null
+    float* sse;              // [n_groups * n_fracs] or null
+};
+hipError_t launch_quantize(const QuantizeParams& p, hipStream_t stream);
+
+struct PrepackParams {
+    const uint8_t* packed;   // [N, K/2]
+    const uint16_t* scale;   // [N, K/G]
+    const uint16_t* zero;    // [N, K/G] or null (sym)
+    int64_t N, K;
+    int G;
+    int asym;
+    uint32_t* wq;            // [N, K/8]
+    uint32_t* sz;            // [N, K/G]
+};
+hipError_t launch_prepack(const PrepackParams& p, hipStream_t stream);
+
+struct RowQuantParams {
+    const uint16_t* X;       // [M, K] bf16
+    int64_t M, K;
+    uint8_t* xq;             // [M, K] e4m3
+    float* xscale;           // [M]
+};
+hipError_t launch_rowquant(const RowQuantParams& p, hipStream_t stream);
+
+struct MulParams {
+    const void* X;           // [M, K]: bf16 bits (W4A16) or e4m3 bytes (W4A8)
+    const float* xscale;     // [M] row scales (W4A8) or null
+    int64_t M, K, N;
+    int G;
+    const uint32_t* wq;      // [N, K/8] GPU-layout codes
+    const uint32_t* sz;      // [N, K/G] fp16 scale | fp16 zero << 16
+    uint16_t* Y;             // [M, N] bf16
+    bool x_fp8;
+};
+// M <= 16: wavefront-reduction GEMV (VALU); larger M: MFMA GEMM.
+constexpr int64_t kGemvMaxM = 16;
+hipError_t launch_gemv(const MulParams& p, hipStream_t stream);
+hipError_t launch_gemm(const MulParams& p, hipStream_t stream);
+
+}  // namespace w4
