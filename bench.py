@@ -1,0 +1,312 @@
+"""Benchmark of the W4 path on one MI355X.
+
+Headline (``value``): W4A16 decode GEMV at M = 1 on the 8B-class MLP shapes
+(up 14336 x 4096, down 4096 x 14336, asymmetric INT4, G = 128, fp16
+scale/zero).  One step is a decode pass through ``--layers`` distinct up/down
+weight pairs (default 16, about 1 GB of packed weights, four times the 256 MB
+Infinity Cache, so every step streams its weights from HBM).  ``value`` is the
+algorithmic bytes of the step (codes + scale/zero + activations + outputs)
+divided by its time, in GB/s.
+
+Also reported, in the same JSON line: the W4A16 and W4A8 GEMM at the 70B
+prefill shape (M = 2048, N = 28672, K = 8192) in TFLOP/s, the W4A8 GEMV on the
+12B-class shapes, the GEMV at M = 4 / 16, and the quantizer with the 11-way
+MSE clip search on the 70B weight.  Times come from HIP events on the stream
+the kernels are launched on.
+
+``cpu_baseline``: the CPU oracle (plain C, OpenMP over the host's cores)
+computing the same 8B up + down products at M = 1 in float64, repeated for a
+bounded time; same unit as ``value``.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def mul_bytes(M, N, K, G, x_bytes=2):
+    """Algorithmic HBM bytes of one product: codes, scale+zero, X, Y."""
+    return N * K // 2 + N * (K // G) * 4 + M * K * x_bytes + M * N * 2
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--layers", type=int, default=16)
+    ap.add_argument("--only", default="all", help="all | decode | gemm | quant | extra")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+class Timer:
+    """HIP-event timing on the current (launch) stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def time(self, fn, reps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps     # ms per call of fn
+
+
+def quantize_to_gpu_layout(w4, torch, W, G, fracs):
+    q = w4.w4_quantize_blockwise(torch.from_numpy(W).to("cuda:0"), G, "asym", fracs, want_clip=False)
+    pk = w4.w4_prepack(q["packed"], q["scale"], q["zero"], G, "asym")
+    del q
+    return pk
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build runs the path on a single MI355X; "
+              f"--gpus {args.gpus} is not supported (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import synth
+    import w4_dequant_gemm_amd as w4
+
+    dev = torch.device("cuda:0")
+    timer = Timer(torch)
+    extra = {}
+    result = {}
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    # ------------------------------------------------------- headline: decode
+    wl8 = synth.WORKLOADS["llama8b_decode"]
+    (Nu, Ku), (Nd, Kd) = wl8.shapes
+    G = wl8.group
+    if args.only in ("all", "decode", "extra"):
+        log("[bench] 8B decode: drawing and quantizing the up/down weights on the GPU")
+        up = quantize_to_gpu_layout(w4, torch, synth.weight(wl8, 0), G, (1.0,))
+        down = quantize_to_gpu_layout(w4, torch, synth.weight(wl8, 1), G, (1.0,))
+        L = args.layers
+        ups = [up] + [{k: v.clone() for k, v in up.items()} for _ in range(L - 1)]
+        downs = [down] + [{k: v.clone() for k, v in down.items()} for _ in range(L - 1)]
+        x_up = bf16(synth.activations_bf16_bits(wl8, 1, Ku))
+        x_dn = bf16(synth.activations_bf16_bits(wl8, 1, Kd))
+        y_up = torch.empty((1, Nu), dtype=torch.bfloat16, device=dev)
+        y_dn = torch.empty((1, Nd), dtype=torch.bfloat16, device=dev)
+
+        def step():
+            for i in range(L):
+                w4.w4a16_gemm(x_up, ups[i]["wq"], ups[i]["sz"], G, Y=y_up)
+                w4.w4a16_gemm(x_dn, downs[i]["wq"], downs[i]["sz"], G, Y=y_dn)
+
+    if args.only in ("all", "decode"):
+        log(f"[bench] decode step = {L} x (up + down) GEMV, M=1; warmup {args.warmup}, steps {args.steps}")
+        ms = timer.time(step, args.steps, args.warmup)
+        b_up = mul_bytes(1, Nu, Ku, G)
+        b_dn = mul_bytes(1, Nd, Kd, G)
+        step_bytes = L * (b_up + b_dn)
+        value = step_bytes / (ms * 1e-3) / 1e9
+        per_launch_ms = ms / (2 * L)
+        achieved = (b_up + b_dn) / 2 / (per_launch_ms * 1e-3) / 1e9
+        result.update(ms_per_step=ms, value=value, step_bytes=step_bytes)
+        result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                              "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                              "kernel": "gemv_kernel<1,32,4|2,false> (W4A16 GEMV, M=1)",
+                              "bytes_per_launch": (b_up + b_dn) // 2,
+                              "avg_launch_us": round(per_launch_ms * 1e3, 3)}
+        log(f"[bench] decode: {ms:.4f} ms/step, {value:.1f} GB/s, per launch {per_launch_ms*1e3:.2f} us")
+
+    if args.only in ("all", "extra"):
+        # per-shape GEMV times at M = 1, 4, 16 (same rotation of weight copies)
+        for M in (1, 4, 16):
+            xu = bf16(synth.activations_bf16_bits(wl8, M, Ku))
+            xd = bf16(synth.activations_bf16_bits(wl8, M, Kd))
+            yu = torch.empty((M, Nu), dtype=torch.bfloat16, device=dev)
+            yd = torch.empty((M, Nd), dtype=torch.bfloat16, device=dev)
+            for name, x, y, ws, N, K in (("up", xu, yu, ups, Nu, Ku), ("down", xd, yd, downs, Nd, Kd)):
+                def run(x=x, y=y, ws=ws):
+                    for i in range(L):
+                        w4.w4a16_gemm(x, ws[i]["wq"], ws[i]["sz"], G, Y=y)
+                ms = timer.time(run, 20, 3) / L
+                gbs = mul_bytes(M, N, K, G) / (ms * 1e-3) / 1e9
+                extra[f"w4a16_gemv_8b_{name}_m{M}"] = {"us": round(ms * 1e3, 3), "GB/s": round(gbs, 1),
+                                                        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+                log(f"[bench] W4A16 8B {name} M={M}: {ms*1e3:.2f} us, {gbs:.1f} GB/s")
+        del ups, downs
+        torch.cuda.empty_cache()
+
+        # W4A8 GEMV / small GEMM on the 12B shapes (weights with the 11-way clip search)
+        wl12 = synth.WORKLOADS["gemma12b_w4a8"]
+        for idx, (N, K) in enumerate(wl12.shapes):
+            base = quantize_to_gpu_layout(w4, torch, synth.weight(wl12, idx), 128, synth.FRACS_11)
+            copies = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(15)]
+            for M in wl12.ms:
+                x = bf16(synth.activations_bf16_bits(wl12, M, K))
+                y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+                xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+                xs = torch.empty((M,), dtype=torch.float32, device=dev)
+
+                def run(x=x, y=y, xq=xq, xs=xs, copies=copies):
+                    for c in copies:
+                        w4.w4a8_gemm(x, c["wq"], c["sz"], 128, Y=y, xq=xq, xscale=xs)
+                ms = timer.time(run, 10, 2) / len(copies)
+                by = mul_bytes(M, N, K, 128)
+                fl = 2.0 * M * N * K
+                extra[f"w4a8_12b_{idx}_m{M}"] = {"us": round(ms * 1e3, 3),
+                                                 "GB/s": round(by / (ms * 1e-3) / 1e9, 1),
+                                                 "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 2)}
+                log(f"[bench] W4A8 12B[{idx}] M={M}: {ms*1e3:.2f} us, {by/(ms*1e-3)/1e9:.1f} GB/s, "
+                    f"{fl/(ms*1e-3)/1e12:.2f} TFLOP/s (incl. row quant)")
+            del copies, base
+            torch.cuda.empty_cache()
+
+    # ------------------------------------------------ 70B prefill GEMM + quantizer
+    if args.only in ("all", "gemm", "quant"):
+        wl70 = synth.WORKLOADS["llama70b_prefill"]
+        (N, K), = wl70.shapes
+        M = wl70.ms[0]
+        log("[bench] 70B prefill: drawing W and X")
+        W = torch.from_numpy(synth.weight(wl70, 0)).to(dev)
+        fr = tuple(float(f) for f in synth.FRACS_11)
+        if args.only in ("all", "quant"):
+            packed = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+            scale = torch.empty((N, K // 128), dtype=torch.float16, device=dev)
+            zero = torch.empty((N, K // 128), dtype=torch.float16, device=dev)
+            clip = torch.empty((N, K // 128), dtype=torch.uint8, device=dev)
+
+            def quant():
+                w4.w4_quantize_blockwise(W, 128, "asym", fr, packed=packed, scale=scale, zero=zero, clip_idx=clip)
+            ms = timer.time(quant, 5, 1)
+            qbytes = N * K * 4 + N * K // 2 + N * (K // 128) * 5
+            extra["quantize_70b_clip11"] = {"ms": round(ms, 3), "GB/s": round(qbytes / (ms * 1e-3) / 1e9, 1),
+                                            "weights_per_s": round(N * K / (ms * 1e-3), 0)}
+            log(f"[bench] quantize 70B (11 candidates): {ms:.3f} ms, {qbytes/(ms*1e-3)/1e9:.1f} GB/s")
+            for nf in (1,):
+                def quant1():
+                    w4.w4_quantize_blockwise(W, 128, "asym", (1.0,), packed=packed, scale=scale, zero=zero,
+                                             clip_idx=clip)
+                ms1 = timer.time(quant1, 5, 1)
+                extra["quantize_70b_plain"] = {"ms": round(ms1, 3), "GB/s": round(qbytes / (ms1 * 1e-3) / 1e9, 1)}
+                log(f"[bench] quantize 70B (plain): {ms1:.3f} ms")
+            pk = w4.w4_prepack(packed, scale, zero, 128, "asym")
+
+            def prep():
+                w4.w4_prepack(packed, scale, zero, 128, "asym", wq=pk["wq"], sz=pk["sz"])
+            msp = timer.time(prep, 10, 2)
+            pbytes = 2 * (N * K // 2 + N * (K // 128) * 4)
+            extra["prepack_70b"] = {"us": round(msp * 1e3, 2), "GB/s": round(pbytes / (msp * 1e-3) / 1e9, 1)}
+            del packed, scale, zero, clip
+        else:
+            pk = quantize_to_gpu_layout(w4, torch, W.cpu().numpy(), 128, fr)
+        del W
+        torch.cuda.empty_cache()
+        if args.only in ("all", "gemm"):
+            X = bf16(synth.activations_bf16_bits(wl70, M, K))
+            Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+            xs = torch.empty((M,), dtype=torch.float32, device=dev)
+            flops = 2.0 * M * N * K
+            ms16 = timer.time(lambda: w4.w4a16_gemm(X, pk["wq"], pk["sz"], 128, Y=Y), 10, 2)
+            ms8 = timer.time(lambda: w4.w4a8_gemm(X, pk["wq"], pk["sz"], 128, Y=Y, xq=xq, xscale=xs), 10, 2)
+            t16 = flops / (ms16 * 1e-3) / 1e12
+            t8 = flops / (ms8 * 1e-3) / 1e12
+            extra["w4a16_gemm_70b_m2048"] = {"ms": round(ms16, 4), "TFLOP/s": round(t16, 1)}
+            extra["w4a8_gemm_70b_m2048"] = {"ms": round(ms8, 4), "TFLOP/s": round(t8, 1)}
+            result["roofline_gemm"] = {"bound": "mfma", "achieved": round(t16, 1), "peak": BF16_PEAK_TFLOPS,
+                                       "unit": "TFLOP/s", "frac": round(t16 / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                                       "kernel": "gemm_kernel<false> (W4A16 GEMM, M=2048)",
+                                       "flops_per_launch": flops, "avg_launch_us": round(ms16 * 1e3, 1)}
+            log(f"[bench] 70B GEMM M=2048: W4A16 {ms16:.3f} ms = {t16:.1f} TFLOP/s; "
+                f"W4A8 {ms8:.3f} ms = {t8:.1f} TFLOP/s")
+
+    # ------------------------------------------------------------ CPU oracle
+    cpu = None
+    if not args.no_cpu and args.only in ("all", "decode"):
+        cpu = cpu_baseline(args.cpu_seconds)
+
+    out = {
+        "metric": "W4A16 GEMV HBM GB/s (% peak) at M=1, 8B shapes; W4 GEMM TFLOP/s at M=2048",
+        "value": round(result.get("value", 0.0), 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(result.get("ms_per_step", 0.0), 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"llama8b_decode: W4A16 GEMV M=1 through {args.layers} distinct "
+                               "up[14336x4096] + down[4096x14336] INT4 asym G=128 weight pairs",
+                   "global_batch": 1, "group": 128, "layers": args.layers,
+                   "step_bytes": result.get("step_bytes")},
+        "roofline": result.get("roofline"),
+        "roofline_gemm": result.get("roofline_gemm"),
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(seconds: float):
+    """The oracle's float64 W4A16 product on the same 8B up + down layers, M = 1."""
+    import numpy as np
+
+    import oracle
+    import synth
+    wl = synth.WORKLOADS["llama8b_decode"]
+    log("[bench] CPU oracle baseline: quantizing the 8B layers on the host")
+    layers = []
+    for idx, (N, K) in enumerate(wl.shapes):
+        W = synth.weight(wl, idx)
+        q = oracle.quantize(W, wl.group, "asym")
+        del W
+        x = oracle.bf16_bits_to_f64(synth.activations_bf16_bits(wl, 1, K))
+        layers.append((q, x, N, K))
+    total_bytes = 0
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        for q, x, N, K in layers:
+            oracle.gemm_ref(x, q["packed"], q["scale"], q["zero"], wl.group, "asym")
+            total_bytes += mul_bytes(1, N, K, wl.group)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 50:
+            break
+    gbs = total_bytes / el / 1e9
+    log(f"[bench] CPU oracle: {reps} x (up + down) in {el:.2f} s = {gbs:.3f} GB/s on {oracle.num_threads()} threads")
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{reps} decode passes (M=1) through one 8B up+down layer pair, float64 oracle product "
+                      f"({el:.1f} s)"}
+
+
+if __name__ == "__main__":
+    main()

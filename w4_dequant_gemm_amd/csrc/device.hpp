@@ -45,11 +45,32 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                            __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load marked non-temporal: streamed weights are read exactly once, so
+// they should not displace reused data (activations, scales) in the caches.
+__device__ __forceinline__ uint4 load_nt_16(const uint32_t* p) {
+    const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(t[0], t[1], t[2], t[3]);
+}
+
+// A value the optimizer cannot see through, held in a VGPR.  Used for the
+// bf16 bias constant below: with it in a register, (x & mask) | bias becomes
+// one v_and_or_b32 (gfx9 VOP3 encodings take no literal, so two literal
+// operands would split it into an AND and an OR).
+__device__ __forceinline__ uint32_t opaque_vgpr(uint32_t v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+constexpr uint32_t kBf16Bias128x2 = 0x43004300u;   // two bf16 128.0
+
 // Nibble pair i (0..3) of a GPU-layout code word as two bf16 values 128 + u:
 // the nibbles at bits 4i and 16 + 4i land in the low mantissa bits of the
 // bf16 constant 128.0 (0x4300), whose unit in the last place is exactly 1.
-__device__ __forceinline__ uint32_t nibble_pair_bf16(uint32_t w, int i) {
-    return ((w >> (4 * i)) & 0x000F000Fu) | 0x43004300u;
+// `bias` is kBf16Bias128x2, passed in a register (see opaque_vgpr).
+__device__ __forceinline__ uint32_t nibble_pair_bf16(uint32_t w, int i, uint32_t bias) {
+    return ((w >> (4 * i)) & 0x000F000Fu) | bias;
 }
 
 // Butterfly sum over the 64 lanes of a wavefront; every lane gets the total.

@@ -38,6 +38,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(MulParams p) {
     const int64_t n_base = static_cast<int64_t>(blockIdx.x) * BN;
     const int64_t M = p.M, N = p.N, K = p.K;
     const int64_t words_row = K / 8, groups_row = K / p.G;
+    const uint32_t bias = opaque_vgpr(kBf16Bias128x2);
 
     float16_t acc[2][2];
 #pragma unroll
@@ -98,7 +99,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(MulParams p) {
                 for (int j = 0; j < 2; ++j)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const uint32_t pr = nibble_pair_bf16(ws[j], i);
+                        const uint32_t pr = nibble_pair_bf16(ws[j], i, bias);
                         out[4 * j + i] = pack_bf16x2(fmaf(bf16_lo(pr), s, -cs), fmaf(bf16_hi(pr), s, -cs));
                     }
             } else {
