@@ -158,27 +158,25 @@ __global__ void __launch_bounds__(256) gemm_kernel(MulParams p) {
 
 // ------------------------------------------------------------------ 256 x 256
 //
-// Large-M kernel.  A 256-thread workgroup (2 x 2 waves of 128 x 128 outputs,
-// 4 x 4 MFMA 32x32x16 tiles each) owns a 256 x 256 output tile and walks K in
-// steps of 64 with two LDS stages (128 KB):
-//   * activations go from global memory straight into LDS
-//     (global_load_lds_dwordx4: lane l's 16 bytes land at the instruction's
-//     LDS base + 16 l), so they never occupy registers;
-//   * each thread owns one weight row of the tile: 32 code bytes and its
-//     scale/zero word per K step, dequantized to bf16 and stored to LDS;
-//   * the next step's loads are in flight while the current step's 64 MFMAs
-//     per wave run, and its dequantization follows them.
+// Large-M kernel.  A 512-thread workgroup (4 x 2 waves of 64 x 128 outputs,
+// 2 x 4 MFMA 32x32x16 tiles each) owns a 256 x 256 output tile and walks K in
+// steps of 64 through two LDS stages of bf16 operands (2 x 64 KB).  Global
+// loads run two steps ahead of the MFMAs, which hides their latency (about
+// one step of MFMA work):
+//   * each thread owns half a row of the activation tile (32 values) and
+//     half a row of the weight tile (32 codes plus the group's scale/zero
+//     word), loaded into one of two register buffers;
+//   * a step issues the loads of step k + 2, runs the 64 MFMAs of step k per
+//     wave, converts step k + 1 (activations copied or widened from E4M3,
+//     weights dequantized to bf16) into the idle LDS stage, waits until only
+//     step k + 2's loads are outstanding, and synchronizes the workgroup.
 // LDS rows are 128 bytes (64 bf16); the 16-byte chunk c of row r is stored at
-// position c ^ ((r >> 1) & 7), which spreads the 32 rows an MFMA operand read
-// touches over all banks.
+// position c ^ ((r >> 1) & 7), spreading an MFMA operand read over the banks.
 namespace big {
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int STAGE = 256 * BK;          // bf16 elements per operand and stage
 
 __device__ __forceinline__ int lds_off(int row, int c) { return row * BK + ((c ^ ((row >> 1) & 7)) << 3); }
-
-typedef uint32_t __attribute__((address_space(1))) global_u32;
-typedef uint32_t __attribute__((address_space(3))) lds_u32;
 }  // namespace big
 
 template <int WM, int WN, bool XF8>
@@ -187,9 +185,11 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm256_kernel(MulParams p) {
     constexpr int NT = 64 * WM * WN;         // threads
     constexpr int TM = BM / WM, TN = BN / WN; // wave tile
     constexpr int FI = TM / 32, FJ = TN / 32; // 32 x 32 MFMA tiles per wave
-    constexpr int TPR = NT / 256;             // threads per weight row
-    constexpr int WPT = (BK / 8) / TPR;       // code words per thread and K step
-    constexpr int AINS = 32 / (NT / 64);      // direct-to-LDS instructions per wave and K step
+    constexpr int TPR = NT / 256;             // threads per operand row
+    constexpr int CPT = (BK / 8) / TPR;       // 16-byte bf16 chunks (8 k) per thread and row
+    constexpr int XB = XF8 ? 1 : 2;           // activation bytes per element in global memory
+    constexpr int ALD = CPT * 8 * XB / 16;    // 16-byte activation loads per thread and step
+    static_assert(CPT % 4 == 0 && ALD >= 1, "operand split");
     __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * STAGE];   // [stage][A, B][256 x 64]
 
     const int tid = threadIdx.x;
@@ -201,6 +201,7 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm256_kernel(MulParams p) {
     const int64_t M = p.M, N = p.N, K = p.K;
     const int64_t words_row = K / 8, groups_row = K / p.G;
     const int KT = static_cast<int>(K / BK);
+    const int g_shift = __builtin_ctz(static_cast<unsigned>(p.G));   // G is a power of two
     const uint32_t bias = opaque_vgpr(kBf16Bias128x2);
 
     float16_t acc[FI][FJ];
@@ -211,76 +212,66 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm256_kernel(MulParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // weight row of this thread and its first code word within a K step
-    const int b_row = tid / TPR;
-    const int b_w0 = (tid % TPR) * WPT;
-    int64_t bn = n_base + b_row;
-    bn = bn < N ? bn : N - 1;              // rows past N compute garbage that is never stored
-    const uint32_t* brow = p.wq + bn * words_row + b_w0;
-    const uint32_t* bsz = p.sz + bn * groups_row;
-    // activation row of this thread (W4A8 path: bytes converted through registers)
-    constexpr int A8_CH = (BK / 16) / TPR;  // 16-byte chunks of E4M3 activations per thread and K step
-    static_assert(A8_CH >= 1 && A8_CH * TPR * 16 == BK, "E4M3 row split");
-    int64_t am = m_base + b_row;
+    // operand row of this thread and its first 8-k chunk within a K step
+    const int o_row = tid / TPR;
+    const int o_c0 = (tid % TPR) * CPT;
+    int64_t bn = n_base + o_row;
+    bn = bn < N ? bn : N - 1;              // rows past N or M compute garbage that is never stored
+    int64_t am = m_base + o_row;
     am = am < M ? am : M - 1;
+    const uint32_t* brow = p.wq + bn * words_row + o_c0;
+    const uint32_t* bsz = p.sz + bn * groups_row;
+    // Activation row address with its provenance hidden (an empty asm): loads
+    // through it are then not known to be invariant, so the register
+    // allocator cannot re-issue them at their use a step later instead of
+    // keeping the prefetched values.  Re-cast to the global address space so
+    // that they stay global (not flat) loads.
+    uint64_t arow_addr = reinterpret_cast<uint64_t>(static_cast<const uint8_t*>(p.X) + (am * K + o_c0 * 8) * XB);
+    asm volatile("" : "+v"(arow_addr));
+    typedef const u32x4_t __attribute__((address_space(1))) global_u4;
+    const global_u4* arow = (const global_u4*)arow_addr;
 
-    uint32_t bq[WPT];
-    uint32_t bs;
-    uint4 aq[A8_CH];
+    struct Regs {
+        uint4 a[ALD];
+        uint32_t q[CPT];
+        uint32_t s;
+    };
+    Regs r0, r1;
 
-    auto issue_loads = [&](int kt, int stage) {
-        if constexpr (!XF8) {
-            // activations: instruction i of wave w fills LDS slots (w * AINS + i) *
-            // 64 + lane, slot s = row * 8 + position, position = chunk ^ ((row >> 1) & 7)
-            const uint16_t* X = static_cast<const uint16_t*>(p.X);
+    auto issue_loads = [&](int kt, Regs& r) {
+        kt = kt < KT ? kt : KT - 1;         // past the end: reload the last step (never used)
+        const global_u4* ga = arow + static_cast<int64_t>(kt) * (BK * XB / 16);
 #pragma unroll
-            for (int i = 0; i < AINS; ++i) {
-                const int slot0 = (wave * AINS + i) * 64;
-                const int s = slot0 + lane;
-                const int row = s >> 3;
-                const int c = (s & 7) ^ ((row >> 1) & 7);
-                int64_t m = m_base + row;
-                m = m < M ? m : M - 1;
-                const uint16_t* g = X + m * K + static_cast<int64_t>(kt) * BK + c * 8;
-                __builtin_amdgcn_global_load_lds((const global_u32*)(const void*)g,
-                                                 (lds_u32*)(void*)(lds + stage * 2 * STAGE + slot0 * 8), 16, 0, 0);
-            }
-        } else {
-            // E4M3 activations: each thread A8_CH 16-byte chunks (64 / TPR bytes) of its row
-            const uint4* g = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(p.X) + am * K +
-                                                            static_cast<int64_t>(kt) * BK) + (tid % TPR) * A8_CH;
-#pragma unroll
-            for (int i = 0; i < A8_CH; ++i) aq[i] = g[i];
+        for (int i = 0; i < ALD; ++i) {
+            const u32x4_t t = ga[i];
+            r.a[i] = make_uint4(t[0], t[1], t[2], t[3]);
         }
         const uint32_t* w = brow + static_cast<int64_t>(kt) * (BK / 8);
 #pragma unroll
-        for (int i = 0; i < WPT; i += 4) {
+        for (int i = 0; i < CPT; i += 4) {
             const uint4 t = *reinterpret_cast<const uint4*>(w + i);
-            bq[i] = t.x; bq[i + 1] = t.y; bq[i + 2] = t.z; bq[i + 3] = t.w;
+            r.q[i] = t.x; r.q[i + 1] = t.y; r.q[i + 2] = t.z; r.q[i + 3] = t.w;
         }
-        // the thread's WPT words (8 * WPT k) lie in one group when G >= 8 * WPT
-        bs = bsz[(static_cast<int64_t>(kt) * BK + b_w0 * 8) / p.G];
+        // the thread's CPT words (8 * CPT k) lie in one group when G >= 8 * CPT
+        r.s = bsz[(kt * BK + o_c0 * 8) >> g_shift];
     };
 
-    auto store_operands = [&](int stage) {
-        uint16_t* B = lds + stage * 2 * STAGE + STAGE;
-        const float sc = half_bits_to_float(bs);
-        const float cs = (128.0f + half_bits_to_float(bs >> 16)) * sc;
+    auto store_operands = [&](int stage, const Regs& r) {
+        uint16_t* A = lds + stage * 2 * STAGE;
+        uint16_t* B = A + STAGE;
+        if constexpr (!XF8) {
 #pragma unroll
-        for (int j = 0; j < WPT; ++j) {
-            uint32_t o[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t pr = nibble_pair_bf16(bq[j], i, bias);
-                o[i] = pack_bf16x2(fmaf(bf16_lo(pr), sc, -cs), fmaf(bf16_hi(pr), sc, -cs));
+            for (int i = 0; i < ALD; ++i) {
+                // pass through an empty asm at this point, so the copy (and the
+                // wait for its load) is not scheduled ahead of the MFMA phase
+                uint4 v = r.a[i];
+                asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+                *reinterpret_cast<uint4*>(A + lds_off(o_row, o_c0 + i)) = v;
             }
-            *reinterpret_cast<uint4*>(B + lds_off(b_row, b_w0 + j)) = make_uint4(o[0], o[1], o[2], o[3]);
-        }
-        if constexpr (XF8) {
-            uint16_t* A = lds + stage * 2 * STAGE;
+        } else {
 #pragma unroll
-            for (int i = 0; i < A8_CH; ++i) {
-                const uint32_t bw[4] = {aq[i].x, aq[i].y, aq[i].z, aq[i].w};
+            for (int i = 0; i < ALD; ++i) {
+                const uint32_t bw[4] = {r.a[i].x, r.a[i].y, r.a[i].z, r.a[i].w};
                 uint32_t o[8];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -289,10 +280,21 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm256_kernel(MulParams p) {
                     o[2 * j] = pack_bf16x2(lo[0], lo[1]);
                     o[2 * j + 1] = pack_bf16x2(hi[0], hi[1]);
                 }
-                const int c0 = ((tid % TPR) * A8_CH + i) * 2;
-                *reinterpret_cast<uint4*>(A + lds_off(b_row, c0)) = make_uint4(o[0], o[1], o[2], o[3]);
-                *reinterpret_cast<uint4*>(A + lds_off(b_row, c0 + 1)) = make_uint4(o[4], o[5], o[6], o[7]);
+                *reinterpret_cast<uint4*>(A + lds_off(o_row, o_c0 + 2 * i)) = make_uint4(o[0], o[1], o[2], o[3]);
+                *reinterpret_cast<uint4*>(A + lds_off(o_row, o_c0 + 2 * i + 1)) = make_uint4(o[4], o[5], o[6], o[7]);
             }
+        }
+        const float sc = half_bits_to_float(r.s);
+        const float cs = (128.0f + half_bits_to_float(r.s >> 16)) * sc;
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            uint32_t o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t pr = nibble_pair_bf16(r.q[j], i, bias);
+                o[i] = pack_bf16x2(fmaf(bf16_lo(pr), sc, -cs), fmaf(bf16_hi(pr), sc, -cs));
+            }
+            *reinterpret_cast<uint4*>(B + lds_off(o_row, o_c0 + j)) = make_uint4(o[0], o[1], o[2], o[3]);
         }
     };
 
@@ -301,14 +303,14 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm256_kernel(MulParams p) {
         const uint16_t* B = A + STAGE;
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
-            const int c = 2 * kk + (lane >> 5);
+            const int ch = 2 * kk + (lane >> 5);
             bf16x8_t a[FI], b[FJ];
 #pragma unroll
             for (int i = 0; i < FI; ++i)
-                a[i] = *reinterpret_cast<const bf16x8_t*>(A + lds_off(wm * TM + i * 32 + (lane & 31), c));
+                a[i] = *reinterpret_cast<const bf16x8_t*>(A + lds_off(wm * TM + i * 32 + (lane & 31), ch));
 #pragma unroll
             for (int j = 0; j < FJ; ++j)
-                b[j] = *reinterpret_cast<const bf16x8_t*>(B + lds_off(wn * TN + j * 32 + (lane & 31), c));
+                b[j] = *reinterpret_cast<const bf16x8_t*>(B + lds_off(wn * TN + j * 32 + (lane & 31), ch));
 #pragma unroll
             for (int i = 0; i < FI; ++i)
 #pragma unroll
@@ -317,20 +319,34 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm256_kernel(MulParams p) {
         }
     };
 
-    issue_loads(0, 0);
-    store_operands(0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-        const int stage = kt & 1;
-        // branch free: the last step reloads its own data into the idle stage
-        const int kn = kt + 1 < KT ? kt + 1 : kt;
-        issue_loads(kn, stage ^ 1);
-        compute(stage);
-        store_operands(stage ^ 1);
-        __builtin_amdgcn_s_waitcnt(0);     // direct-to-LDS loads and LDS stores of the next stage
+    // One K step: loads for kt + 2 into `next` (its previous contents, step
+    // kt, were converted during step kt - 1), MFMAs of kt, convert kt + 1
+    // from `ready` into the idle stage, then synchronize.
+    // The loads must stay in flight across the MFMAs.  An activation load
+    // whose value is only copied to LDS a step later would otherwise be sunk
+    // next to that copy by the optimizer (nothing in between writes global
+    // memory); the empty asm with a memory clobber pins the loads here without
+    // emitting code, and the scheduling barriers keep the phases in order.
+    auto step = [&](int kt, Regs& next, const Regs& ready) {
+        issue_loads(kt + 2, next);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        compute(kt & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        store_operands((kt + 1) & 1, ready);   // past the end this refills an idle stage
         __syncthreads();
+    };
+
+    issue_loads(0, r0);
+    issue_loads(1, r1);
+    store_operands(0, r0);
+    __syncthreads();
+    int kt = 0;
+    for (; kt + 2 <= KT; kt += 2) {
+        step(kt, r0, r1);
+        step(kt + 1, r1, r0);
     }
+    if (kt < KT) step(kt, r0, r1);
 
     // epilogue: register r of lane l holds row (r%4) + 4(l/32) + 8(r/4), column l%32
 #pragma unroll
