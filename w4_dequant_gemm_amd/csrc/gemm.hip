@@ -190,6 +190,9 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm256_kernel(MulParams p) {
     constexpr int XB = XF8 ? 1 : 2;           // activation bytes per element in global memory
     constexpr int ALD = CPT * 8 * XB / 16;    // 16-byte activation loads per thread and step
     static_assert(CPT % 4 == 0 && ALD >= 1, "operand split");
+    // dequantization VALU work per MFMA in one step (about 6 instructions per
+    // bf16 pair, 4 pairs per chunk; E4M3 widening adds 3 per pair)
+    constexpr int VALU_PER_MFMA = XF8 ? 5 : 3;
     __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * STAGE];   // [stage][A, B][256 x 64]
 
     const int tid = threadIdx.x;
@@ -326,14 +329,21 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm256_kernel(MulParams p) {
     // whose value is only copied to LDS a step later would otherwise be sunk
     // next to that copy by the optimizer (nothing in between writes global
     // memory); the empty asm with a memory clobber pins the loads here without
-    // emitting code, and the scheduling barriers keep the phases in order.
+    // emitting code, and the scheduling barrier keeps them ahead of the rest.
+    // The MFMAs of step kt and the conversion of step kt + 1 (different LDS
+    // stages) are then interleaved: one MFMA, then a few VALU instructions,
+    // so the matrix cores keep running while the dequantization executes.
     auto step = [&](int kt, Regs& next, const Regs& ready) {
         issue_loads(kt + 2, next);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         compute(kt & 1);
-        __builtin_amdgcn_sched_barrier(0);
         store_operands((kt + 1) & 1, ready);   // past the end this refills an idle stage
+#pragma unroll
+        for (int i = 0; i < FI * FJ * (BK / 16); ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, VALU_PER_MFMA, 0);   // VALU
+        }
         __syncthreads();
     };
 
