@@ -53,7 +53,48 @@ def parse():
     ap.add_argument("--only", default="all", help="all | decode | gemm | quant | extra")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the work, run a plain device copy of this many MiB three times "
+                         "(the known-size kernel that scales the HBM byte counters)")
     return ap.parse_args()
+
+
+# Source files that define the GEMV and GEMM kernels; a measured traffic figure
+# is used only while these files are unchanged since it was taken.
+KERNEL_SOURCES = ("w4_dequant_gemm_amd/csrc/gemv.hip", "w4_dequant_gemm_amd/csrc/gemm.hip",
+                  "w4_dequant_gemm_amd/csrc/device.hpp", "w4_dequant_gemm_amd/csrc/kernels.hpp")
+
+
+def kernel_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name):
+    """Per-launch HBM bytes of a kernel from its committed counter summary.
+
+    The summary (profiles/<name>.txt) holds ``key: value`` lines, among them
+    ``traffic_bytes_per_launch`` and ``kernel_source_digest``; the figure is
+    returned only when the digest matches the current kernel sources, else
+    None (the counters no longer describe this code).
+    """
+    path = os.path.join(ROOT, "profiles", name + ".txt")
+    try:
+        kv = {}
+        with open(path) as f:
+            for line in f:
+                if ":" in line and not line.startswith((" ", "#", "|")):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("kernel_source_digest") != kernel_source_digest():
+            return None
+        return int(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 class Timer:
@@ -136,8 +177,9 @@ def main():
         achieved = (b_up + b_dn) / 2 / (per_launch_ms * 1e-3) / 1e9
         result.update(ms_per_step=ms, value=value, step_bytes=step_bytes)
         result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                              "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                              "kernel": "gemv_kernel<1,32,4|2,false> (W4A16 GEMV, M=1)",
+                              "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                              "traffic": measured_traffic("traffic_gemv_w4a16_8b_m1"),
+                              "kernel": "gemv_split_kernel<1, 4, 128, false, 1> (W4A16 GEMV, M=1)",
                               "bytes_per_launch": (b_up + b_dn) // 2,
                               "avg_launch_us": round(per_launch_ms * 1e3, 3)}
         log(f"[bench] decode: {ms:.4f} ms/step, {value:.1f} GB/s, per launch {per_launch_ms*1e3:.2f} us")
@@ -239,11 +281,22 @@ def main():
             extra["w4a16_gemm_70b_m2048"] = {"ms": round(ms16, 4), "TFLOP/s": round(t16, 1)}
             extra["w4a8_gemm_70b_m2048"] = {"ms": round(ms8, 4), "TFLOP/s": round(t8, 1)}
             result["roofline_gemm"] = {"bound": "mfma", "achieved": round(t16, 1), "peak": BF16_PEAK_TFLOPS,
-                                       "unit": "TFLOP/s", "frac": round(t16 / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                                       "kernel": "gemm_kernel<false> (W4A16 GEMM, M=2048)",
+                                       "unit": "TFLOP/s", "frac": round(t16 / BF16_PEAK_TFLOPS, 4),
+                                       "traffic": measured_traffic("traffic_gemm_w4a16_70b_m2048"),
+                                       "kernel": "big::gemm256_kernel<4, 2, false> (W4A16 GEMM, M=2048)",
                                        "flops_per_launch": flops, "avg_launch_us": round(ms16 * 1e3, 1)}
             log(f"[bench] 70B GEMM M=2048: W4A16 {ms16:.3f} ms = {t16:.1f} TFLOP/s; "
                 f"W4A8 {ms8:.3f} ms = {t8:.1f} TFLOP/s")
+
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.arange(n, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)       # elementwise: reads and writes n * 4 bytes
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: {args.calib_copy_mib} MiB read + {args.calib_copy_mib} MiB written, 3 times")
+        del src, dst
 
     # ------------------------------------------------------------ CPU oracle
     cpu = None
