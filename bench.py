@@ -178,7 +178,7 @@ def main():
         result.update(ms_per_step=ms, value=value, step_bytes=step_bytes)
         result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                               "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                              "traffic": measured_traffic("traffic_gemv_w4a16_8b_m1"),
+                              "traffic": measured_traffic("gemv_split_w4a16_8b_m1"),
                               "kernel": "gemv_split_kernel<1, 4, 128, false, 1> (W4A16 GEMV, M=1)",
                               "bytes_per_launch": (b_up + b_dn) // 2,
                               "avg_launch_us": round(per_launch_ms * 1e3, 3)}
@@ -202,6 +202,28 @@ def main():
                 log(f"[bench] W4A16 8B {name} M={M}: {ms*1e3:.2f} us, {gbs:.1f} GB/s")
         del ups, downs
         torch.cuda.empty_cache()
+
+        # Context for the decode figure: torch's own kernels streaming the same
+        # 31.2 MB per launch through 17 rotating buffers (a read-only sum, and a
+        # copy of half the size that reads and writes 15.6 MB each).
+        nbytes = mul_bytes(1, Nu, Ku, G)
+        bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device=dev) for _ in range(17)]
+        halves = [torch.ones(nbytes // 4, dtype=torch.int16, device=dev) for _ in range(17)]
+        outs = [torch.empty_like(h) for h in halves]
+        acc = torch.empty((), dtype=torch.int64, device=dev)
+
+        def read_all():
+            for b in bufs:
+                torch.sum(b, dim=0, out=acc)
+
+        def copy_all():
+            for h, o in zip(halves, outs):
+                o.copy_(h)
+        for name, fn in (("torch_sum_read_31mb", read_all), ("torch_copy_31mb", copy_all)):
+            ms = timer.time(fn, 20, 3) / len(bufs)
+            extra[name] = {"us": round(ms * 1e3, 3), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+            log(f"[bench] {name}: {ms*1e3:.2f} us per 31.2 MB, {nbytes/(ms*1e-3)/1e9:.1f} GB/s")
+        del bufs, halves, outs
 
         # W4A8 GEMV / small GEMM on the 12B shapes (weights with the 11-way clip search)
         wl12 = synth.WORKLOADS["gemma12b_w4a8"]
@@ -282,7 +304,7 @@ def main():
             extra["w4a8_gemm_70b_m2048"] = {"ms": round(ms8, 4), "TFLOP/s": round(t8, 1)}
             result["roofline_gemm"] = {"bound": "mfma", "achieved": round(t16, 1), "peak": BF16_PEAK_TFLOPS,
                                        "unit": "TFLOP/s", "frac": round(t16 / BF16_PEAK_TFLOPS, 4),
-                                       "traffic": measured_traffic("traffic_gemm_w4a16_70b_m2048"),
+                                       "traffic": measured_traffic("gemm256_w4a16_70b_m2048"),
                                        "kernel": "big::gemm256_kernel<4, 2, false> (W4A16 GEMM, M=2048)",
                                        "flops_per_launch": flops, "avg_launch_us": round(ms16 * 1e3, 1)}
             log(f"[bench] 70B GEMM M=2048: W4A16 {ms16:.3f} ms = {t16:.1f} TFLOP/s; "
@@ -352,7 +374,7 @@ def cpu_baseline(seconds: float):
             total_bytes += mul_bytes(1, N, K, wl.group)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= seconds or reps >= 50:
+        if el >= seconds or reps >= 2000:
             break
     gbs = total_bytes / el / 1e9
     log(f"[bench] CPU oracle: {reps} x (up + down) in {el:.2f} s = {gbs:.3f} GB/s on {oracle.num_threads()} threads")
