@@ -16,6 +16,8 @@
 // Tile: 128 x 128 outputs per 256-thread workgroup (2 x 2 waves of 64 x 64),
 // K step 32.  Rows of X beyond M and rows of W beyond N read as zero; the
 // epilogue stores only in-range outputs.
+#include <type_traits>
+
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -176,7 +178,15 @@ namespace big {
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int STAGE = 256 * BK;          // bf16 elements per operand and stage
 
-__device__ __forceinline__ int lds_off(int row, int c) { return row * BK + ((c ^ ((row >> 1) & 7)) << 3); }
+#ifndef W4_SWZ
+#define W4_SWZ 1
+#endif
+// bf16 offset of 16-byte chunk c (8 k) of operand row `row` in one 256 x 64
+// stage: rows are 128 bytes; the chunk index is XORed with row bits so that
+// both the row-wise stores and the MFMA fragment reads spread over the banks
+__device__ __forceinline__ int lds_off(int row, int c) {
+    return row * BK + ((c ^ (W4_SWZ ? (row & 7) : ((row >> 1) & 7))) << 3);
+}
 }  // namespace big
 
 template <int WM, int WN, bool XF8>
@@ -190,9 +200,6 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm256_kernel(MulParams p) {
     constexpr int XB = XF8 ? 1 : 2;           // activation bytes per element in global memory
     constexpr int ALD = CPT * 8 * XB / 16;    // 16-byte activation loads per thread and step
     static_assert(CPT % 4 == 0 && ALD >= 1, "operand split");
-    // dequantization VALU work per MFMA in one step (about 6 instructions per
-    // bf16 pair, 4 pairs per chunk; E4M3 widening adds 3 per pair)
-    constexpr int VALU_PER_MFMA = XF8 ? 5 : 3;
     __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * STAGE];   // [stage][A, B][256 x 64]
 
     const int tid = threadIdx.x;
@@ -234,115 +241,155 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm256_kernel(MulParams p) {
     typedef const u32x4_t __attribute__((address_space(1))) global_u4;
     const global_u4* arow = (const global_u4*)arow_addr;
 
+    // scale/zero words per thread and step: one per 32 k (the smallest group)
+    constexpr int SZN = CPT / 4;
     struct Regs {
         uint4 a[ALD];
-        uint32_t q[CPT];
-        uint32_t s;
+        u32x4_t q[CPT / 4];   // code words, kept as 16-byte vectors (no register copies)
+        uint32_t s[SZN];
     };
     Regs r0, r1;
 
-    auto issue_loads = [&](int kt, Regs& r) {
+    // The global loads of one step: ALD activation loads, CPT / 4 code loads
+    // and SZN scale/zero loads, issued one item at a time.
+    constexpr int NLOAD = ALD + CPT / 4 + SZN;
+    auto issue_load_item = [&](int kt, Regs& r, int it) {
         kt = kt < KT ? kt : KT - 1;         // past the end: reload the last step (never used)
-        const global_u4* ga = arow + static_cast<int64_t>(kt) * (BK * XB / 16);
-#pragma unroll
-        for (int i = 0; i < ALD; ++i) {
-            const u32x4_t t = ga[i];
-            r.a[i] = make_uint4(t[0], t[1], t[2], t[3]);
+        if (it < ALD) {
+            const u32x4_t t = arow[static_cast<int64_t>(kt) * (BK * XB / 16) + it];
+            r.a[it] = make_uint4(t[0], t[1], t[2], t[3]);
+        } else if (it < ALD + CPT / 4) {
+            const int i = 4 * (it - ALD);
+            r.q[it - ALD] = *reinterpret_cast<const u32x4_t*>(brow + static_cast<int64_t>(kt) * (BK / 8) + i);
+        } else {
+            // words 4t .. 4t + 3 (32 k) of the thread lie in one group for every G
+            const int t = it - ALD - CPT / 4;
+            r.s[t] = bsz[(kt * BK + o_c0 * 8 + 32 * t) >> g_shift];
         }
-        const uint32_t* w = brow + static_cast<int64_t>(kt) * (BK / 8);
+    };
+    auto issue_loads = [&](int kt, Regs& r) {
 #pragma unroll
-        for (int i = 0; i < CPT; i += 4) {
-            const uint4 t = *reinterpret_cast<const uint4*>(w + i);
-            r.q[i] = t.x; r.q[i + 1] = t.y; r.q[i + 2] = t.z; r.q[i + 3] = t.w;
-        }
-        // the thread's CPT words (8 * CPT k) lie in one group when G >= 8 * CPT
-        r.s = bsz[(kt * BK + o_c0 * 8) >> g_shift];
+        for (int it = 0; it < NLOAD; ++it) issue_load_item(kt, r, it);
     };
 
+    // ---- operand conversion, split into small work items -------------------
+    // B: code word j (8 k) of the thread's row holds four pairs of codes; pair
+    // i becomes two fp16 values 1024 + u with one AND-OR (the nibbles land in
+    // the low mantissa bits of fp16 1024, whose unit in the last place is 1),
+    // then W' = (1024 + u) s - (1024 + z) s by two mixed-precision FMAs (fp16
+    // operands, fp32 result; exact: every term has at most 23 significant
+    // bits) and one rounding to a bf16 pair.  The fourth pair of a word
+    // completes a 16-byte LDS row chunk.
+    const uint32_t bias16 = opaque_vgpr(0x64006400u);   // two fp16 1024.0
+    float b_sc = 0.0f, b_cs = 0.0f;
+    uint32_t b_out[4];
+    auto b_pair = [&](int pr, const Regs& r, uint16_t* B) {
+        const int j = pr / 4, i = pr % 4;
+        if (i == 0 && j % 4 == 0) {
+            b_sc = half_bits_to_float(r.s[j / 4]);
+            b_cs = -(1024.0f + half_bits_to_float(r.s[j / 4] >> 16)) * b_sc;
+        }
+        const uint32_t h = ((r.q[j / 4][j % 4] >> (4 * i)) & 0x000F000Fu) | bias16;
+        const _Float16 lo = __builtin_bit_cast(_Float16, static_cast<uint16_t>(h & 0xFFFFu));
+        const _Float16 hi = __builtin_bit_cast(_Float16, static_cast<uint16_t>(h >> 16));
+        b_out[i] = pack_bf16x2(fmaf(static_cast<float>(lo), b_sc, b_cs), fmaf(static_cast<float>(hi), b_sc, b_cs));
+        if (i == 3)
+            *reinterpret_cast<uint4*>(B + lds_off(o_row, o_c0 + j)) = make_uint4(b_out[0], b_out[1], b_out[2], b_out[3]);
+    };
+    // A: bf16 activations are copied (ALD items of 16 bytes); E4M3 ones are
+    // widened exactly to bf16, each 16-byte load in two halves of 8 values.
+    constexpr int A_ITEMS = XF8 ? 2 * ALD : ALD;
+    auto a_item = [&](int it, const Regs& r, uint16_t* A) {
+        if constexpr (!XF8) {
+            // the empty asm keeps the wait for this load here, not earlier
+            uint4 v = r.a[it];
+            asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+            *reinterpret_cast<uint4*>(A + lds_off(o_row, o_c0 + it)) = v;
+        } else {
+            const uint4 src = r.a[it / 2];
+            const uint32_t w0 = (it & 1) ? src.z : src.x;
+            const uint32_t w1 = (it & 1) ? src.w : src.y;
+            uint32_t o[4];
+            const uint32_t bw[2] = {w0, w1};
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                float2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(bw[jj]), false);
+                float2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(bw[jj]), true);
+                o[2 * jj] = pack_bf16x2(lo[0], lo[1]);
+                o[2 * jj + 1] = pack_bf16x2(hi[0], hi[1]);
+            }
+            *reinterpret_cast<uint4*>(A + lds_off(o_row, o_c0 + it)) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+    };
+    // all conversion of one step at once (prologue)
     auto store_operands = [&](int stage, const Regs& r) {
         uint16_t* A = lds + stage * 2 * STAGE;
-        uint16_t* B = A + STAGE;
-        if constexpr (!XF8) {
 #pragma unroll
-            for (int i = 0; i < ALD; ++i) {
-                // pass through an empty asm at this point, so the copy (and the
-                // wait for its load) is not scheduled ahead of the MFMA phase
-                uint4 v = r.a[i];
-                asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
-                *reinterpret_cast<uint4*>(A + lds_off(o_row, o_c0 + i)) = v;
-            }
-        } else {
+        for (int it = 0; it < A_ITEMS; ++it) a_item(it, r, A);
 #pragma unroll
-            for (int i = 0; i < ALD; ++i) {
-                const uint32_t bw[4] = {r.a[i].x, r.a[i].y, r.a[i].z, r.a[i].w};
-                uint32_t o[8];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    float2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(bw[j]), false);
-                    float2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(bw[j]), true);
-                    o[2 * j] = pack_bf16x2(lo[0], lo[1]);
-                    o[2 * j + 1] = pack_bf16x2(hi[0], hi[1]);
-                }
-                *reinterpret_cast<uint4*>(A + lds_off(o_row, o_c0 + 2 * i)) = make_uint4(o[0], o[1], o[2], o[3]);
-                *reinterpret_cast<uint4*>(A + lds_off(o_row, o_c0 + 2 * i + 1)) = make_uint4(o[4], o[5], o[6], o[7]);
-            }
-        }
-        const float sc = half_bits_to_float(r.s);
-        const float cs = (128.0f + half_bits_to_float(r.s >> 16)) * sc;
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-            uint32_t o[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t pr = nibble_pair_bf16(r.q[j], i, bias);
-                o[i] = pack_bf16x2(fmaf(bf16_lo(pr), sc, -cs), fmaf(bf16_hi(pr), sc, -cs));
-            }
-            *reinterpret_cast<uint4*>(B + lds_off(o_row, o_c0 + j)) = make_uint4(o[0], o[1], o[2], o[3]);
-        }
+        for (int pr = 0; pr < 4 * CPT; ++pr) b_pair(pr, r, A + STAGE);
     };
 
-    auto compute = [&](int stage) {
-        const uint16_t* A = lds + stage * 2 * STAGE;
-        const uint16_t* B = A + STAGE;
+    auto load_frags = [&](const uint16_t* A, const uint16_t* B, int kk, bf16x8_t (&a)[FI], bf16x8_t (&b)[FJ]) {
+        const int ch = 2 * kk + (lane >> 5);
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            const int ch = 2 * kk + (lane >> 5);
-            bf16x8_t a[FI], b[FJ];
+        for (int i = 0; i < FI; ++i)
+            a[i] = *reinterpret_cast<const bf16x8_t*>(A + lds_off(wm * TM + i * 32 + (lane & 31), ch));
 #pragma unroll
-            for (int i = 0; i < FI; ++i)
-                a[i] = *reinterpret_cast<const bf16x8_t*>(A + lds_off(wm * TM + i * 32 + (lane & 31), ch));
-#pragma unroll
-            for (int j = 0; j < FJ; ++j)
-                b[j] = *reinterpret_cast<const bf16x8_t*>(B + lds_off(wn * TN + j * 32 + (lane & 31), ch));
-#pragma unroll
-            for (int i = 0; i < FI; ++i)
-#pragma unroll
-                for (int j = 0; j < FJ; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-        }
+        for (int j = 0; j < FJ; ++j)
+            b[j] = *reinterpret_cast<const bf16x8_t*>(B + lds_off(wn * TN + j * 32 + (lane & 31), ch));
     };
 
-    // One K step: loads for kt + 2 into `next` (its previous contents, step
-    // kt, were converted during step kt - 1), MFMAs of kt, convert kt + 1
-    // from `ready` into the idle stage, then synchronize.
+    // One K step: global loads for kt + 2 into `next` (its previous contents,
+    // step kt, were converted during step kt - 1); the MFMAs of step kt from
+    // one LDS stage; the conversion of step kt + 1 from `ready` into the other
+    // stage; then a barrier.
     // The loads must stay in flight across the MFMAs.  An activation load
     // whose value is only copied to LDS a step later would otherwise be sunk
     // next to that copy by the optimizer (nothing in between writes global
     // memory); the empty asm with a memory clobber pins the loads here without
     // emitting code, and the scheduling barrier keeps them ahead of the rest.
-    // The MFMAs of step kt and the conversion of step kt + 1 (different LDS
-    // stages) are then interleaved: one MFMA, then a few VALU instructions,
-    // so the matrix cores keep running while the dequantization executes.
+    // The MFMAs and the conversion work are laid out by hand: MFMA slot u
+    // (of FI * FJ * BK / 16 per step) is followed by B pair (u - 1) / 2 when
+    // u is odd and by A item u / 4 when u is a multiple of 4, and a
+    // scheduling barrier after every slot keeps that order, so the matrix
+    // cores run while the VALU converts.  Fragments for the next 16 k are
+    // read from LDS at the start of each 16-k sub-step.
+    constexpr int NSLOT = FI * FJ * (BK / 16);
+    static_assert(NSLOT >= 2 * 4 * CPT && NSLOT >= 4 * A_ITEMS, "conversion work must fit the MFMA slots");
+#ifndef W4_SPREAD
+#define W4_SPREAD 1
+#endif
+    constexpr int LOAD_EVERY = NSLOT / NLOAD;
     auto step = [&](int kt, Regs& next, const Regs& ready) {
-        issue_loads(kt + 2, next);
-        asm volatile("" ::: "memory");
+        if (!W4_SPREAD) {
+            issue_loads(kt + 2, next);
+            asm volatile("" ::: "memory");
+        }
         __builtin_amdgcn_sched_barrier(0);
-        compute(kt & 1);
-        store_operands((kt + 1) & 1, ready);   // past the end this refills an idle stage
+        const uint16_t* As = lds + (kt & 1) * 2 * STAGE;
+        const uint16_t* Bs = As + STAGE;
+        uint16_t* Ad = lds + ((kt + 1) & 1) * 2 * STAGE;   // past the end this refills an idle stage
+        uint16_t* Bd = Ad + STAGE;
+        bf16x8_t fa[2][FI], fb[2][FJ];
+        load_frags(As, Bs, 0, fa[0], fb[0]);
 #pragma unroll
-        for (int i = 0; i < FI * FJ * (BK / 16); ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, VALU_PER_MFMA, 0);   // VALU
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            if (kk + 1 < BK / 16) load_frags(As, Bs, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < FI * FJ; ++t) {
+                const int u = kk * FI * FJ + t;
+                const int i = t / FJ, j = t % FJ;
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j], acc[i][j], 0, 0, 0);
+                if (u % 2 == 1 && u / 2 < 4 * CPT) b_pair(u / 2, ready, Bd);
+                if (u % 4 == 0 && u / 4 < A_ITEMS) a_item(u / 4, ready, Ad);
+                if (W4_SPREAD && u % LOAD_EVERY == 0 && u / LOAD_EVERY < NLOAD) {
+                    issue_load_item(kt + 2, next, u / LOAD_EVERY);
+                    asm volatile("" ::: "memory");
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         __syncthreads();
     };
@@ -376,17 +423,234 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm256_kernel(MulParams p) {
         }
 }
 
+
+// ---------------------------------------------------------------------------
+// W4A16, M >= 128: activations straight from global memory into LDS.
+//
+// Same 256 x 256 tile, K step 64 and 2 x 2 waves of 128 x 128 outputs as
+// above, but the bf16 activations never pass through registers: each wave
+// issues global_load_lds_dwordx4 (lane l's 16 bytes land at the
+// instruction's LDS base + 16 l) one K step ahead, at the start of the step,
+// into the idle one of two activation stages.  The weight codes still come
+// through registers two steps ahead and are dequantized into two bf16
+// weight stages.  LDS: 2 x 32 KB + 2 x 32 KB, four separate arrays, so that
+// with the loop unrolled by two every access names its stage statically
+// and the compiler can tell the direct-to-LDS writes from the reads of the
+// other stage.
+//
+// The compiler does not order direct-to-LDS writes against the LDS reads of
+// later steps, so every step ends with an explicit wait for all global loads
+// and LDS stores, then the workgroup barrier.  Loads past the last
+// step are clamped to it (same count every step), and the loop ends with a
+// full wait so that nothing writes LDS after the workgroup has finished.
+namespace dma {
+constexpr int BM = 256, BN = 256, BK = 64, NW = 4, NT = 64 * NW;
+constexpr int STAGE = 256 * BK;                       // bf16 elements per stage
+constexpr int ADMA = BM * BK * 2 / (1024 * NW);       // direct-to-LDS loads per wave and step (8)
+constexpr int CPT = BK / 8;                           // code words per thread and step (8)
+constexpr int SZN = CPT / 4;                          // scale/zero words per thread and step
+constexpr int BLOAD = CPT / 4 + SZN;                  // weight loads per thread and step (4)
+constexpr int NSLOT = 4 * 4 * (BK / 16);              // MFMAs per wave and step (64)
+typedef uint32_t __attribute__((address_space(1))) global_u32;
+typedef uint32_t __attribute__((address_space(3))) lds_u32;
+__device__ __forceinline__ int lds_off(int row, int c) { return row * BK + ((c ^ (row & 7)) << 3); }
+}  // namespace dma
+
+__global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
+    using namespace dma;
+    constexpr int FI = 4, FJ = 4;
+    __shared__ __attribute__((aligned(16))) uint16_t lds_a0[STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_a1[STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_b0[STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_b1[STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t m_base = static_cast<int64_t>(blockIdx.y) * BM;
+    const int64_t n_base = static_cast<int64_t>(blockIdx.x) * BN;
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const int64_t words_row = K / 8, groups_row = K / p.G;
+    const int KT = static_cast<int>(K / BK);
+    const int g_shift = __builtin_ctz(static_cast<unsigned>(p.G));
+
+    float16_t acc[FI][FJ];
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // Activations: load i of this wave fills LDS rows 8 (wave * ADMA + i) ..
+    // + 7 of a stage; lane l writes row + l / 8 at chunk position l % 8,
+    // which holds chunk (l % 8) ^ (l / 8) of the row (the row index is a
+    // multiple of 8 plus l / 8, so this is the swizzle of lds_off).  Rows
+    // past M read row M - 1 and compute outputs that are never stored.
+    const int a_row0 = 8 * wave * ADMA + (lane >> 3);
+    int64_t a_m = m_base + a_row0;
+    const int64_t a_last = M - 1;
+    const uint16_t* a_src = static_cast<const uint16_t*>(p.X) + (((lane & 7) ^ (lane >> 3)) * 8);
+    auto dma_item = [&](int kt, uint16_t* stage, int it) {
+        kt = kt < KT ? kt : KT - 1;
+        int64_t m = a_m + 8 * it;
+        m = m < a_last ? m : a_last;
+        __builtin_amdgcn_global_load_lds((const global_u32*)(const void*)(a_src + m * K + static_cast<int64_t>(kt) * BK),
+                                         (lds_u32*)(void*)(stage + (wave * ADMA + it) * 512), 16, 0, 0);
+    };
+
+    // Weights: thread tid owns row tid of the tile (8 code words per step)
+    int64_t bn = n_base + tid;
+    bn = bn < N ? bn : N - 1;
+    const uint32_t* brow = p.wq + bn * words_row;
+    const uint32_t* bsz = p.sz + bn * groups_row;
+    struct Regs {
+        u32x4_t q[CPT / 4];
+        uint32_t s[SZN];
+    };
+    auto load_item = [&](int kt, Regs& r, int it) {
+        kt = kt < KT ? kt : KT - 1;
+        if (it < CPT / 4) r.q[it] = *reinterpret_cast<const u32x4_t*>(brow + static_cast<int64_t>(kt) * (BK / 8) + 4 * it);
+        else r.s[it - CPT / 4] = bsz[(kt * BK + 32 * (it - CPT / 4)) >> g_shift];
+    };
+
+    // dequantization of one pair of codes (see gemm256_kernel)
+    const uint32_t bias16 = opaque_vgpr(0x64006400u);
+    float b_sc = 0.0f, b_cs = 0.0f;
+    uint32_t b_out[4];
+    auto b_pair = [&](int pr, const Regs& r, uint16_t* B) {
+        const int j = pr / 4, i = pr % 4;
+        if (i == 0 && j % 4 == 0) {
+            b_sc = half_bits_to_float(r.s[j / 4]);
+            b_cs = -(1024.0f + half_bits_to_float(r.s[j / 4] >> 16)) * b_sc;
+        }
+        const uint32_t h = ((r.q[j / 4][j % 4] >> (4 * i)) & 0x000F000Fu) | bias16;
+        const _Float16 lo = __builtin_bit_cast(_Float16, static_cast<uint16_t>(h & 0xFFFFu));
+        const _Float16 hi = __builtin_bit_cast(_Float16, static_cast<uint16_t>(h >> 16));
+        b_out[i] = pack_bf16x2(fmaf(static_cast<float>(lo), b_sc, b_cs), fmaf(static_cast<float>(hi), b_sc, b_cs));
+        if (i == 3) *reinterpret_cast<uint4*>(B + lds_off(tid, j)) = make_uint4(b_out[0], b_out[1], b_out[2], b_out[3]);
+    };
+
+    auto load_frags = [&](const uint16_t* A, const uint16_t* B, int kk, bf16x8_t (&a)[FI], bf16x8_t (&b)[FJ]) {
+        const int ch = 2 * kk + (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < FI; ++i)
+            a[i] = *reinterpret_cast<const bf16x8_t*>(A + lds_off(wm * 128 + i * 32 + (lane & 31), ch));
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
+            b[j] = *reinterpret_cast<const bf16x8_t*>(B + lds_off(wn * 128 + j * 32 + (lane & 31), ch));
+    };
+
+    // All global loads (the next step's activations and the weights of the
+    // step after) and all LDS stores done, then the barrier.  The wait is the
+    // builtin, which the compiler's own wait insertion takes into account, so
+    // that the next step starts with nothing outstanding (with direct-to-LDS
+    // loads in flight the compiler would otherwise wait for every load before
+    // the first use of a weight register); the empty asm statements keep
+    // memory accesses on their side of the barrier.
+    auto step_end = [&]() {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0);        // vmcnt, expcnt and lgkmcnt all 0
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+
+    // One K step from stage S: MFMA slot u is followed by the direct-to-LDS
+    // load u of the next step (u < ADMA), B pair u / 2 of the next step (odd
+    // u) and, after all activation loads, weight load (u - 8) / 4 of the step
+    // after next (u = 8, 12, ...); a scheduling barrier after every slot
+    // keeps that order.  The fragments of the next 16 k are read at the start
+    // of each 16-k sub-step.
+    auto step = [&](int kt, auto S, Regs& next, const Regs& ready) {
+        constexpr int s = decltype(S)::value;
+        const uint16_t* As = s ? lds_a1 : lds_a0;
+        const uint16_t* Bs = s ? lds_b1 : lds_b0;
+        uint16_t* Ad = s ? lds_a0 : lds_a1;
+        uint16_t* Bd = s ? lds_b0 : lds_b1;
+        bf16x8_t fa[2][FI], fb[2][FJ];
+        load_frags(As, Bs, 0, fa[0], fb[0]);
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            if (kk + 1 < BK / 16) load_frags(As, Bs, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < FI * FJ; ++t) {
+                const int u = kk * FI * FJ + t;
+                const int i = t / FJ, j = t % FJ;
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j], acc[i][j], 0, 0, 0);
+                if (u < ADMA) dma_item(kt + 1, Ad, u);
+                if (u % 2 == 1) b_pair(u / 2, ready, Bd);
+                if (u >= ADMA && u % 4 == 0 && (u - ADMA) / 4 < BLOAD) {
+                    load_item(kt + 2, next, (u - ADMA) / 4);
+                    asm volatile("" ::: "memory");
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        step_end();
+    };
+    static_assert(NSLOT == 2 * 4 * CPT && ADMA + 4 * BLOAD <= NSLOT, "slot plan");
+
+    // prologue: activations of step 0, weights of steps 0 and 1, dequantize step 0
+    Regs r0, r1;
+#pragma unroll
+    for (int it = 0; it < ADMA; ++it) dma_item(0, lds_a0, it);
+#pragma unroll
+    for (int it = 0; it < BLOAD; ++it) load_item(0, r0, it);
+#pragma unroll
+    for (int it = 0; it < BLOAD; ++it) load_item(1, r1, it);
+#pragma unroll
+    for (int pr = 0; pr < 4 * CPT; ++pr) b_pair(pr, r0, lds_b0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);           // vmcnt, expcnt and lgkmcnt all 0
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    int kt = 0;
+    for (; kt + 2 <= KT; kt += 2) {
+        step(kt, std::integral_constant<int, 0>{}, r0, r1);
+        step(kt + 1, std::integral_constant<int, 1>{}, r1, r0);
+    }
+    if (kt < KT) step(kt, std::integral_constant<int, 0>{}, r0, r1);
+    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("" ::: "memory");
+
+    // epilogue: register r of lane l holds row (r%4) + 4(l/32) + 8(r/4), column l%32
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) {
+            const int64_t col = n_base + wn * 128 + j * 32 + (lane & 31);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = m_base + wm * 128 + i * 32 + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
+                if (row < M && col < N) p.Y[row * N + col] = float_to_bf16_bits(acc[i][j][r]);
+            }
+        }
+}
+
 }  // namespace
+
+#ifndef W4_BIG_WM
+#define W4_BIG_WM 2
+#define W4_BIG_WN 2
+#endif
+constexpr int kBigWM = W4_BIG_WM, kBigWN = W4_BIG_WN;
 
 hipError_t launch_gemm(const MulParams& p, hipStream_t stream) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
     if (p.M >= 128 && p.K % big::BK == 0) {
         const dim3 grid(static_cast<unsigned>((p.N + big::BN - 1) / big::BN),
                         static_cast<unsigned>((p.M + big::BM - 1) / big::BM));
+#ifndef W4_DMA
+#define W4_DMA 1
+#endif
         if (p.x_fp8)
-            hipLaunchKernelGGL((gemm256_kernel<4, 2, true>), grid, dim3(512), 0, stream, p);
+            hipLaunchKernelGGL((gemm256_kernel<kBigWM, kBigWN, true>), grid, dim3(64 * kBigWM * kBigWN), 0, stream, p);
+        else if (W4_DMA)
+            hipLaunchKernelGGL(gemm256_dma_kernel, grid, dim3(dma::NT), 0, stream, p);
         else
-            hipLaunchKernelGGL((gemm256_kernel<4, 2, false>), grid, dim3(512), 0, stream, p);
+            hipLaunchKernelGGL((gemm256_kernel<kBigWM, kBigWN, false>), grid, dim3(64 * kBigWM * kBigWN), 0, stream, p);
         return hipGetLastError();
     }
     const dim3 grid(static_cast<unsigned>((p.N + small::BN - 1) / small::BN),
