@@ -61,7 +61,7 @@ def parse():
 
 # Source files that define the GEMV and GEMM kernels; a measured traffic figure
 # is used only while these files are unchanged since it was taken.
-KERNEL_SOURCES = ("w4_dequant_gemm_amd/csrc/gemv.hip", "w4_dequant_gemm_amd/csrc/gemm.hip",
+KERNEL_SOURCES = ("w4_dequant_gemm_amd/csrc/skinny.hip", "w4_dequant_gemm_amd/csrc/gemm.hip",
                   "w4_dequant_gemm_amd/csrc/device.hpp", "w4_dequant_gemm_amd/csrc/kernels.hpp")
 
 
@@ -178,8 +178,9 @@ def main():
         result.update(ms_per_step=ms, value=value, step_bytes=step_bytes)
         result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                               "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                              "traffic": measured_traffic("gemv_split_w4a16_8b_m1"),
-                              "kernel": "gemv_split_kernel<1, 4, 128, false, 1> (W4A16 GEMV, M=1)",
+                              "traffic": measured_traffic("skinny_dot_w4a16_8b_m1"),
+                              "kernel": "gemm_skinny_kernel<1, FJ, false, 3> (W4A16, M=1: v_dot2, "
+                                        "activations staged in LDS; FJ = 2 up, 1 down)",
                               "bytes_per_launch": (b_up + b_dn) // 2,
                               "avg_launch_us": round(per_launch_ms * 1e3, 3)}
         log(f"[bench] decode: {ms:.4f} ms/step, {value:.1f} GB/s, per launch {per_launch_ms*1e3:.2f} us")
@@ -304,8 +305,8 @@ def main():
             extra["w4a8_gemm_70b_m2048"] = {"ms": round(ms8, 4), "TFLOP/s": round(t8, 1)}
             result["roofline_gemm"] = {"bound": "mfma", "achieved": round(t16, 1), "peak": BF16_PEAK_TFLOPS,
                                        "unit": "TFLOP/s", "frac": round(t16 / BF16_PEAK_TFLOPS, 4),
-                                       "traffic": measured_traffic("gemm256_w4a16_70b_m2048"),
-                                       "kernel": "big::gemm256_kernel<4, 2, false> (W4A16 GEMM, M=2048)",
+                                       "traffic": measured_traffic("gemm256_dma_w4a16_70b_m2048"),
+                                       "kernel": "gemm256_dma_kernel (W4A16 GEMM, M=2048)",
                                        "flops_per_launch": flops, "avg_launch_us": round(ms16 * 1e3, 1)}
             log(f"[bench] 70B GEMM M=2048: W4A16 {ms16:.3f} ms = {t16:.1f} TFLOP/s; "
                 f"W4A8 {ms8:.3f} ms = {t8:.1f} TFLOP/s")

@@ -118,12 +118,18 @@ int w4_mse_clip_search(const float* W, int64_t N, int64_t K, int G, int mode,
  * kernels read ("GPU layout"), once per weight, without requantizing.
  *   packed  [N, K/2] canonical bytes in (as written by w4_quantize_blockwise).
  *   scale   [N, K/G] fp16 in;  zero [N, K/G] fp16 in (W4_ASYM), NULL (W4_SYM).
- *   wq      [N, K/8] uint32 out.  Word [n, j] holds the 8 codes of k = 8j..8j+7
- *           as unsigned 4-bit values u, with u = q (asym) or u = q + 8 (sym);
- *           code k = 8j + 2i sits in bits 4i..4i+3 and code k = 8j + 2i + 1 in
- *           bits 16+4i..16+4i+3 (i = 0..3).
- *   sz      [N, K/G] uint32 out: low half the fp16 scale, high half the fp16
- *           zero (8.0 for W4_SYM), so that W'[n, k] = (u - zero) * scale.
+ *   wq      N*K/8 uint32 out.  The 8 codes of row n, k = 8j..8j+7, form one
+ *           word as unsigned 4-bit values u, with u = q (asym) or u = q + 8
+ *           (sym); code k = 8j + 2i sits in bits 4i..4i+3 and code
+ *           k = 8j + 2i + 1 in bits 16+4i..16+4i+3 (i = 0..3).  Words are
+ *           stored in blocks of 16 rows and tiles of 32 k: with r0 = n - n % 16
+ *           and nr = min(16, N - r0), word j of row n is at
+ *             r0*K/8 + (j/4)*4*nr + 4*(n - r0) + j%4,
+ *           so one 1 KB read holds a 16-row by 128-k fragment.
+ *   sz      N*K/G uint32 out: per (row, group) the fp16 scale in the low half
+ *           and the fp16 zero (8.0 for W4_SYM) in the high half, so that
+ *           W'[n, k] = (u - zero) * scale; group g of row n is at
+ *             r0*K/G + g*nr + (n - r0).
  *   N >= 0, K > 0, K % G == 0, G in {32, 64, 128}.
  */
 int w4_prepack(const uint8_t* packed, const uint16_t* scale, const uint16_t* zero, int64_t N,
@@ -143,8 +149,9 @@ int w4_quantize_rows_e4m3(const uint16_t* X, int64_t M, int64_t K, uint8_t* xq, 
 /*
  * w4a16_gemm -- W4A16: Y = bf16(X . W'^T) with W'[n, k] = (u - zero) * scale
  * from the GPU layout, fp32 accumulation, bf16 output (round to nearest
- * even).  One entry point for every M: M <= 16 runs a bandwidth-bound GEMV
- * kernel, larger M a bf16-MFMA GEMM kernel.
+ * even).  One entry point for every M: up to 64 rows run a kernel that
+ * streams the weights once (bandwidth bound), larger M a tiled bf16-MFMA
+ * GEMM.
  *   X  [M, K] bf16 in;  wq, sz as written by w4_prepack;  Y [M, N] bf16 out.
  *   M >= 0, N >= 0, K > 0, K % G == 0, G in {32, 64, 128}.
  */

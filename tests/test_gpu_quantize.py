@@ -126,15 +126,29 @@ def test_quantize_empty_and_ragged():
         assert_bits_equal(bits16(out["scale"]), ref["scale"], "scales")
 
 
+def _blocked(a: np.ndarray, per_tile: int) -> np.ndarray:
+    """Host model of the header's blocked order: rows in blocks of 16 (the
+    last may be shorter), items of a row in tiles of `per_tile`, each tile
+    holding that many items of every row of the block in turn."""
+    N, per_row = a.shape
+    out = np.empty(N * per_row, a.dtype)
+    for r0 in range(0, N, 16):
+        nr = min(16, N - r0)
+        blk = a[r0:r0 + nr].reshape(nr, per_row // per_tile, per_tile)      # [row, tile, item]
+        out[r0 * per_row:(r0 + nr) * per_row] = blk.transpose(1, 0, 2).reshape(-1)
+    return out
+
+
 def test_prepack_layout():
     # the GPU layout is a permutation of the canonical nibbles (plus the sym
-    # offset), with scale and zero interleaved -- checked against the layout
-    # the header defines, from the oracle's codes
+    # offset), with scale and zero interleaved, in 16-row blocks of 32-k tiles
+    # -- checked against the layout the header defines, from the oracle's
+    # codes; 37 rows leave a last block of 5
     require_gpu()
     import torch
     from helpers import prepack_dev
-    for mode in ("asym", "sym"):
-        q = oracle_quant("smollm2_135m_mlp", 0, None, mode, 32, 1)
+    for mode, rows in (("asym", None), ("sym", None), ("asym", 37)):
+        q = oracle_quant("smollm2_135m_mlp", 0, rows, mode, 32, 1)
         pk, G = prepack_dev(q)
         torch.cuda.synchronize()
         codes = q["q"].astype(np.int64)
@@ -145,7 +159,9 @@ def test_prepack_layout():
         for i in range(4):
             want |= (u8[:, :, 2 * i].astype(np.uint64) << np.uint64(4 * i))
             want |= (u8[:, :, 2 * i + 1].astype(np.uint64) << np.uint64(16 + 4 * i))
-        assert_bits_equal(host(pk["wq"]).view(np.uint32), want.astype(np.uint32), f"GPU-layout words ({mode})")
+        assert_bits_equal(host(pk["wq"]).view(np.uint32).reshape(-1), _blocked(want.astype(np.uint32), 4),
+                          f"GPU-layout words ({mode}, N={N})")
         zero = q["zero"] if mode == "asym" else np.full_like(q["scale"], 0x4800)
         want_sz = q["scale"].astype(np.uint32) | (zero.astype(np.uint32) << np.uint32(16))
-        assert_bits_equal(host(pk["sz"]).view(np.uint32), want_sz, f"scale|zero words ({mode})")
+        assert_bits_equal(host(pk["sz"]).view(np.uint32).reshape(-1), _blocked(want_sz, 1),
+                          f"scale|zero words ({mode}, N={N})")

@@ -19,7 +19,7 @@ OUT = os.path.join(HERE, "libw4.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-KERNELS = ["quantize.hip", "prepack.hip", "rowquant.hip", "gemv.hip", "gemm.hip"]
+KERNELS = ["quantize.hip", "prepack.hip", "rowquant.hip", "skinny.hip", "gemm.hip"]
 NO_CONTRACT = {"quantize.hip", "rowquant.hip"}
 
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -165,7 +165,7 @@ int w4a16_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, cons
     W4_TRY(mul_common(fn, X, M, K, wq, sz, N, G, Y));
     if (M == 0 || N == 0) return W4_OK;
     w4::MulParams p{X, nullptr, M, K, N, G, wq, sz, Y, false};
-    if (M <= w4::kGemvMaxM) return hip_status(w4::launch_gemv(p, stream), fn);
+    if (M <= w4::kSkinnyMaxM) return hip_status(w4::launch_skinny(p, stream), fn);
     return hip_status(w4::launch_gemm(p, stream), fn);
 }
 
@@ -179,7 +179,7 @@ int w4a8_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const
     w4::RowQuantParams rq{X, M, K, xq, xscale};
     W4_TRY(hip_status(w4::launch_rowquant(rq, stream), fn));
     w4::MulParams p{xq, xscale, M, K, N, G, wq, sz, Y, true};
-    if (M <= w4::kGemvMaxM) return hip_status(w4::launch_gemv(p, stream), fn);
+    if (M <= w4::kSkinnyMaxM) return hip_status(w4::launch_skinny(p, stream), fn);
     return hip_status(w4::launch_gemm(p, stream), fn);
 }
 

@@ -73,6 +73,30 @@ __device__ __forceinline__ uint32_t nibble_pair_bf16(uint32_t w, int i, uint32_t
     return ((w >> (4 * i)) & 0x000F000Fu) | bias;
 }
 
+// Row n of a weight in the blocked GPU layout (16-row blocks of 32-k tiles,
+// as written by the prepack kernel): code word j of the row is
+// words[(j / 4) * tile + j % 4] and its scale/zero word of group g is
+// sz[g * nr], where nr is the number of rows in the row's block.
+struct TiledRow {
+    const uint32_t* words;
+    const uint32_t* sz;
+    int64_t nr;
+    int64_t tile;            // words between consecutive tiles of the row (4 nr)
+    __device__ __forceinline__ const uint32_t* tile_ptr(int64_t t) const { return words + t * tile; }
+    __device__ __forceinline__ uint32_t group(int64_t g) const { return sz[g * nr]; }
+};
+__device__ __forceinline__ TiledRow tiled_row(const uint32_t* wq, const uint32_t* sz, int64_t n, int64_t N,
+                                              int64_t K, int G) {
+    const int64_t r0 = n & ~static_cast<int64_t>(15);
+    const int64_t nr = N - r0 < 16 ? N - r0 : 16;
+    TiledRow r;
+    r.words = wq + r0 * (K / 8) + 4 * (n - r0);
+    r.sz = sz + r0 * (K / G) + (n - r0);
+    r.nr = nr;
+    r.tile = 4 * nr;
+    return r;
+}
+
 // Butterfly sum over the 64 lanes of a wavefront; every lane gets the total.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

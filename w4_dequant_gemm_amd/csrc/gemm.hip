@@ -42,7 +42,6 @@ __global__ void __launch_bounds__(256) gemm_kernel(MulParams p) {
     const int64_t m_base = static_cast<int64_t>(blockIdx.y) * BM;
     const int64_t n_base = static_cast<int64_t>(blockIdx.x) * BN;
     const int64_t M = p.M, N = p.N, K = p.K;
-    const int64_t words_row = K / 8, groups_row = K / p.G;
     const uint32_t bias = opaque_vgpr(kBf16Bias128x2);
 
     float16_t acc[2][2];
@@ -95,8 +94,9 @@ __global__ void __launch_bounds__(256) gemm_kernel(MulParams p) {
             const int64_t n = n_base + b_row;
             uint32_t out[8];
             if (n < N) {
-                const uint2 w = *reinterpret_cast<const uint2*>(p.wq + n * words_row + k0 / 8 + b_w);
-                const uint32_t szw = p.sz[n * groups_row + (k0 + 8 * b_w) / p.G];
+                const TiledRow tr = tiled_row(p.wq, p.sz, n, N, K, p.G);
+                const uint2 w = *reinterpret_cast<const uint2*>(tr.tile_ptr(k0 / 32) + b_w);
+                const uint32_t szw = tr.group((k0 + 8 * b_w) / p.G);
                 const float s = half_bits_to_float(szw);
                 const float cs = (128.0f + half_bits_to_float(szw >> 16)) * s;
                 const uint32_t ws[2] = {w.x, w.y};
@@ -209,7 +209,6 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm256_kernel(MulParams p) {
     const int64_t m_base = static_cast<int64_t>(blockIdx.y) * BM;
     const int64_t n_base = static_cast<int64_t>(blockIdx.x) * BN;
     const int64_t M = p.M, N = p.N, K = p.K;
-    const int64_t words_row = K / 8, groups_row = K / p.G;
     const int KT = static_cast<int>(K / BK);
     const int g_shift = __builtin_ctz(static_cast<unsigned>(p.G));   // G is a power of two
     const uint32_t bias = opaque_vgpr(kBf16Bias128x2);
@@ -229,8 +228,7 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm256_kernel(MulParams p) {
     bn = bn < N ? bn : N - 1;              // rows past N or M compute garbage that is never stored
     int64_t am = m_base + o_row;
     am = am < M ? am : M - 1;
-    const uint32_t* brow = p.wq + bn * words_row + o_c0;
-    const uint32_t* bsz = p.sz + bn * groups_row;
+    const TiledRow brow = tiled_row(p.wq, p.sz, bn, N, K, p.G);
     // Activation row address with its provenance hidden (an empty asm): loads
     // through it are then not known to be invariant, so the register
     // allocator cannot re-issue them at their use a step later instead of
@@ -259,12 +257,13 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm256_kernel(MulParams p) {
             const u32x4_t t = arow[static_cast<int64_t>(kt) * (BK * XB / 16) + it];
             r.a[it] = make_uint4(t[0], t[1], t[2], t[3]);
         } else if (it < ALD + CPT / 4) {
-            const int i = 4 * (it - ALD);
-            r.q[it - ALD] = *reinterpret_cast<const u32x4_t*>(brow + static_cast<int64_t>(kt) * (BK / 8) + i);
+            // words o_c0 + 4i .. + 3 of the step: one 32-k tile of the row
+            const int i = it - ALD;
+            r.q[i] = *reinterpret_cast<const u32x4_t*>(brow.tile_ptr(static_cast<int64_t>(kt) * (BK / 32) + o_c0 / 4 + i));
         } else {
             // words 4t .. 4t + 3 (32 k) of the thread lie in one group for every G
             const int t = it - ALD - CPT / 4;
-            r.s[t] = bsz[(kt * BK + o_c0 * 8 + 32 * t) >> g_shift];
+            r.s[t] = brow.group((kt * BK + o_c0 * 8 + 32 * t) >> g_shift);
         }
     };
     auto issue_loads = [&](int kt, Regs& r) {
@@ -471,7 +470,6 @@ __global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
     const int64_t m_base = static_cast<int64_t>(blockIdx.y) * BM;
     const int64_t n_base = static_cast<int64_t>(blockIdx.x) * BN;
     const int64_t M = p.M, N = p.N, K = p.K;
-    const int64_t words_row = K / 8, groups_row = K / p.G;
     const int KT = static_cast<int>(K / BK);
     const int g_shift = __builtin_ctz(static_cast<unsigned>(p.G));
 
@@ -503,16 +501,15 @@ __global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
     // Weights: thread tid owns row tid of the tile (8 code words per step)
     int64_t bn = n_base + tid;
     bn = bn < N ? bn : N - 1;
-    const uint32_t* brow = p.wq + bn * words_row;
-    const uint32_t* bsz = p.sz + bn * groups_row;
+    const TiledRow brow = tiled_row(p.wq, p.sz, bn, N, K, p.G);
     struct Regs {
         u32x4_t q[CPT / 4];
         uint32_t s[SZN];
     };
     auto load_item = [&](int kt, Regs& r, int it) {
         kt = kt < KT ? kt : KT - 1;
-        if (it < CPT / 4) r.q[it] = *reinterpret_cast<const u32x4_t*>(brow + static_cast<int64_t>(kt) * (BK / 8) + 4 * it);
-        else r.s[it - CPT / 4] = bsz[(kt * BK + 32 * (it - CPT / 4)) >> g_shift];
+        if (it < CPT / 4) r.q[it] = *reinterpret_cast<const u32x4_t*>(brow.tile_ptr(static_cast<int64_t>(kt) * (BK / 32) + it));
+        else r.s[it - CPT / 4] = brow.group((kt * BK + 32 * (it - CPT / 4)) >> g_shift);
     };
 
     // dequantization of one pair of codes (see gemm256_kernel)

@@ -54,9 +54,14 @@ struct MulParams {
     uint16_t* Y;             // [M, N] bf16
     bool x_fp8;
 };
-// M <= 16: wavefront-reduction GEMV (VALU); larger M: MFMA GEMM.
-constexpr int64_t kGemvMaxM = 16;
-hipError_t launch_gemv(const MulParams& p, hipStream_t stream);
+// Which kernel runs a product: M <= kSkinnyMaxM: the weight-streaming
+// kernels (dot form for one or two rows, MFMA form above); larger M: the
+// tiled MFMA GEMM.
+#ifndef W4_SKINNY_MAX
+#define W4_SKINNY_MAX 64
+#endif
+constexpr int64_t kSkinnyMaxM = W4_SKINNY_MAX;
+hipError_t launch_skinny(const MulParams& p, hipStream_t stream);
 hipError_t launch_gemm(const MulParams& p, hipStream_t stream);
 
 }  // namespace w4

@@ -1,0 +1,582 @@
+// W4A16 / W4A8 products for small M (1 to 64 activation rows) on gfx950.
+//
+// With few activation rows the product is bound by streaming the packed
+// weights from HBM (gsantana.dev "Quantizing LLMs Without Guesswork",
+// "Production reality": small batches are memory-bound; decode reads every
+// weight once).  One kernel family covers the range; it differs only in how a
+// step is multiplied.
+//
+// Work decomposition.  A workgroup owns 16 * FJ output columns (FJ 16-row
+// blocks of the blocked weight layout) and all M rows; its wk waves split K:
+// wave w takes the 128-wide K steps w, w + wk, ...  No weight is shared
+// between waves, so the weights go from global memory straight into
+// registers: in a step, lane l (column c = l % 16 of a block, quarter
+// h = l / 16) loads the 16 bytes holding k = 32h .. 32h + 31 of its column --
+// in the blocked layout the 64 lanes' pieces are one contiguous 1 KB.  A wave
+// issues the loads of kDepth steps together, then multiplies them; the other
+// waves on the compute unit cover the latency.  At the end the wk partial
+// sums are added through LDS in a fixed order.
+//
+// Multiplying a step:
+//  * one or two rows (v_dot2_f32_bf16): the lane's codes become bf16 pairs
+//    128 + u with one AND-OR and are dotted with its 32 activations; the
+//    group's scale and zero are applied per lane (its 32 k lie in one group)
+//    as s (sum x (128 + u) - (128 + z) sum x).  The activations and their
+//    32-k sums are staged in LDS once per workgroup when they fit, else every
+//    lane loads its own.
+//  * more rows, groups of 128 (v_mfma_f32_16x16x32_bf16): the same exact
+//    values 128 + u times the activations, plus an MFMA of the activations
+//    against ones for sum x over the group, then the same correction per
+//    output.  MFMA b of a step multiplies, from every quarter h, the 8 k at
+//    32h + 8b, and the activation fragments use the same order.
+//  * more rows, groups of 32 or 64: every weight dequantized, W' = (1024 + u)
+//    s - (1024 + z) s (fp16 1024 + u by one AND-OR, two mixed-precision FMAs,
+//    exact before one rounding to bf16), then the MFMA.
+//
+// W4A8 reads the E4M3 activation codes, widens them exactly to bf16 and
+// applies the row scale at the end (gowda.ai "LLM fast inference",
+// "Achievement 2").
+#include <type_traits>
+
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace w4 {
+namespace {
+
+typedef float float4_v __attribute__((ext_vector_type(4)));
+
+constexpr int kStepK = 128;   // k per wave and step (4 quarters of 32)
+
+// weight steps in flight per wave (fewer with more activation rows, whose
+// fragments take the registers)
+#ifndef W4_SK_DEPTH
+#define W4_SK_DEPTH 2
+#endif
+#ifndef W4_DOT_DEPTH
+#define W4_DOT_DEPTH 4
+#endif
+template <int MB, int MODE>
+constexpr int skinny_depth() { return MODE == 2 ? W4_DOT_DEPTH : (MB == 1 ? W4_SK_DEPTH : 2); }
+
+// weights of one step: the lane's 16 bytes of codes and its scale/zero word,
+// per 16-column block
+template <int FJ>
+struct SkinnyB {
+    u32x4_t q[FJ];          // codes of k = 32h .. 32h + 31 of the lane's column
+    uint32_t s[FJ];         // scale | zero << 16
+};
+// activations of one step: k = 32h .. 32h + 31 of the lane's row, per 16-row block
+template <int MB, bool XF8>
+struct SkinnyA {
+    static constexpr int AL = XF8 ? 2 : 4;   // 16-byte loads per block
+    u32x4_t a[MB][AL];
+    bool valid;             // the lane's quarter lies inside K (else its products are dropped)
+};
+
+// how a step is multiplied
+constexpr int kDeq = 0;    // dequantize every weight to bf16, MFMA (groups of 32 or 64)
+constexpr int kCorr = 1;   // MFMA on 128 + u, per-group correction (groups of 128)
+constexpr int kDot = 2;    // v_dot2 on 128 + u, per-group correction (one or two rows)
+constexpr int kDotLds = 3; // the same, activations and their 32-k sums staged in LDS once
+constexpr int kDotMaxM = 2;
+
+// up to 16 waves per workgroup for the one-row dot form (few registers), 8 otherwise
+template <int MB, int MODE>
+constexpr int skinny_max_threads() { return (MODE == 2 || MODE == 3) && MB == 1 ? 1024 : 512; }
+
+template <int MB, int FJ, bool XF8, int MODE>
+__global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_kernel(MulParams p, int wk) {
+    constexpr bool CORR = MODE == kCorr, DOTL = MODE == kDotLds, DOT = MODE == kDot || DOTL;
+    using BStage = SkinnyB<FJ>;
+    using AStage = SkinnyA<MB, XF8>;
+    constexpr int AL = AStage::AL;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c = lane & 15, h = lane >> 4;
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * (16 * FJ);
+    const int64_t words_row = K / 8, groups_row = K / p.G;
+    const int g_shift = __builtin_ctz(static_cast<unsigned>(p.G));
+    const int KS = static_cast<int>((K + kStepK - 1) / kStepK);
+
+    // lane's column in each block and row in each 16-row block (clamped:
+    // columns past N and rows past M compute values that are never stored)
+    // the lane's row c in each 16-row block of the blocked GPU layout: its
+    // 16-byte piece of tile t is at word 4 c + 4 nr t of the block, its
+    // scale/zero word of group g at c + nr g (nr = rows in the block; rows
+    // past N read the block's last row and give values never stored)
+    const uint32_t* bcol[FJ];
+    const uint32_t* bsz[FJ];
+    int64_t bnr[FJ];
+#pragma unroll
+    for (int j = 0; j < FJ; ++j) {
+        int64_t r0 = n0 + 16 * j;
+        r0 = r0 < N ? r0 : ((N - 1) / 16) * 16;
+        const int64_t nr = N - r0 < 16 ? N - r0 : 16;
+        const int64_t cc = c < nr ? c : nr - 1;
+        bcol[j] = p.wq + r0 * words_row + 4 * cc;
+        bsz[j] = p.sz + r0 * groups_row + cc;
+        bnr[j] = nr;
+    }
+    // activation rows: the MFMA forms give lane (c, h) row c of every 16-row
+    // block; the dot form gives every lane all MB rows
+    const uint8_t* arow[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+        int64_t m = DOT ? i : 16 * i + c;
+        m = m < M ? m : M - 1;
+        arow[i] = static_cast<const uint8_t*>(p.X) + m * K * (XF8 ? 1 : 2);
+    }
+
+    auto load_b = [&](int step, BStage& st) {
+        const int64_t kb = static_cast<int64_t>(step) * kStepK + 32 * h;
+        const int64_t k = kb < K ? kb : 0;          // K is a multiple of 32
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) {
+            st.q[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(bcol[j] + (k / 32) * 4 * bnr[j]));
+            st.s[j] = bsz[j][(k >> g_shift) * bnr[j]];
+        }
+    };
+    auto load_a = [&](int step, AStage& st) {
+        const int64_t kb = static_cast<int64_t>(step) * kStepK + 32 * h;
+        const bool valid = kb < K;
+        const int64_t k = valid ? kb : 0;
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+            const u32x4_t* ap = reinterpret_cast<const u32x4_t*>(arow[i] + k * (XF8 ? 1 : 2));
+#pragma unroll
+            for (int t = 0; t < AL; ++t) st.a[i][t] = ap[t];
+        }
+        // applied when the step is multiplied: touching the loaded values
+        // here would make the wave wait for the loads at once
+        st.valid = valid;
+    };
+
+    float4_v acc[MB][FJ];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) acc[i][j] = float4_v{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // Activation fragment b (8 k) of 16-row block i as bf16 (E4M3 codes are
+    // widened exactly; a quarter outside K contributes zeros).
+    auto a_frag = [&](const AStage& sa, int i, int b) -> bf16x8_t {
+        if constexpr (!XF8) {
+            return __builtin_bit_cast(bf16x8_t, sa.valid ? sa.a[i][b] : u32x4_t{0u, 0u, 0u, 0u});
+        } else {
+            const u32x4_t v = sa.valid ? sa.a[i][b / 2] : u32x4_t{0u, 0u, 0u, 0u};
+            const uint32_t w0 = (b & 1) ? v[2] : v[0];
+            const uint32_t w1 = (b & 1) ? v[3] : v[1];
+            const float2_t f0 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w0), false);
+            const float2_t f1 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w0), true);
+            const float2_t f2 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w1), false);
+            const float2_t f3 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w1), true);
+            return __builtin_bit_cast(bf16x8_t, u32x4_t{pack_bf16x2(f0[0], f0[1]), pack_bf16x2(f1[0], f1[1]),
+                                                        pack_bf16x2(f2[0], f2[1]), pack_bf16x2(f3[0], f3[1])});
+        }
+    };
+
+    const uint32_t bias16 = opaque_vgpr(0x64006400u);   // two fp16 1024.0
+    const uint32_t bias128 = opaque_vgpr(kBf16Bias128x2);
+    // dot form with staged activations: LDS holds, per row, the activations
+    // as bf16 pairs ([MB][K / 2] words) and the sum of every 32-k quarter
+    // ([MB][K / 32] floats); the partial sums of the final reduction follow
+    extern __shared__ float red[];
+    uint32_t* const lds_x = reinterpret_cast<uint32_t*>(red);
+    float* const lds_xs = red + (DOTL ? MB * (K / 2) : 0);
+    float* const red_base = DOTL ? lds_xs + MB * (K / 32) : red;
+
+    auto compute = [&](const BStage& st, const AStage& sa, int step) {
+        if constexpr (DOT) {
+            // the lane's 32 activations of every row as bf16 pairs in k order
+            uint32_t xw[MB][16];
+            float xs[MB];
+            if constexpr (DOTL) {
+                const int64_t kq = static_cast<int64_t>(step) * (kStepK / 32) + h;   // the lane's 32-k quarter
+                const bool valid = kq < K / 32;
+#pragma unroll
+                for (int m = 0; m < MB; ++m) {
+                    const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(lds_x + m * (K / 2) + (valid ? kq : 0) * 16);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const u32x4_t v = valid ? xp[t] : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) xw[m][4 * t + e] = v[e];
+                    }
+                    xs[m] = valid ? lds_xs[m * (K / 32) + kq] : 0.0f;
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < MB && !DOTL; ++m) {
+                if constexpr (!XF8) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const u32x4_t v = sa.valid ? sa.a[m][t] : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) xw[m][4 * t + e] = v[e];
+                    }
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        const u32x4_t v = sa.valid ? sa.a[m][t] : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float2_t f0 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v[e]), false);
+                            const float2_t f1 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v[e]), true);
+                            xw[m][8 * t + 2 * e] = pack_bf16x2(f0[0], f0[1]);
+                            xw[m][8 * t + 2 * e + 1] = pack_bf16x2(f1[0], f1[1]);
+                        }
+                    }
+                }
+            }
+            // sum of the 32 activations of every row (the lane's 32 k lie in
+            // one group); four partial sums per chain keep the dependent
+            // dot products apart
+#pragma unroll
+            for (int m = 0; m < MB && !DOTL; ++m) {
+                float t[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int w = 0; w < 16; ++w) t[w & 3] = dot2_bf16(xw[m][w], 0x3F803F80u, t[w & 3]);
+                xs[m] = (t[0] + t[1]) + (t[2] + t[3]);
+            }
+#pragma unroll
+            for (int j = 0; j < FJ; ++j) {
+                float d[MB][4];
+#pragma unroll
+                for (int m = 0; m < MB; ++m)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) d[m][b] = 0.0f;
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t pr = nibble_pair_bf16(st.q[j][b], i, bias128);
+#pragma unroll
+                        for (int m = 0; m < MB; ++m) d[m][b] = dot2_bf16(pr, xw[m][4 * b + i], d[m][b]);
+                    }
+                const float sc = half_bits_to_float(st.s[j]);
+                const float zc = 128.0f + half_bits_to_float(st.s[j] >> 16);
+#pragma unroll
+                for (int m = 0; m < MB; ++m) {
+                    const float dm = (d[m][0] + d[m][1]) + (d[m][2] + d[m][3]);
+                    acc[m][j][0] = fmaf(sc, fmaf(-zc, xs[m], dm), acc[m][j][0]);
+                }
+            }
+        } else if constexpr (CORR) {
+            // One group per step (G = 128): multiply the exact bf16 values
+            // 128 + u, and the row sums of x over the group (an MFMA against
+            // ones), then acc += s (P - (128 + z) sum x) for every output.
+            const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+            float4_v ps[MB][FJ], xs[MB];
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+                xs[i] = float4_v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int j = 0; j < FJ; ++j) ps[i][j] = float4_v{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                bf16x8_t bp[FJ];
+#pragma unroll
+                for (int j = 0; j < FJ; ++j) {
+                    const uint32_t w = st.q[j][b];
+                    bp[j] = __builtin_bit_cast(bf16x8_t, u32x4_t{nibble_pair_bf16(w, 0, bias128), nibble_pair_bf16(w, 1, bias128),
+                                                                 nibble_pair_bf16(w, 2, bias128), nibble_pair_bf16(w, 3, bias128)});
+                }
+#pragma unroll
+                for (int i = 0; i < MB; ++i) {
+                    const bf16x8_t ap = a_frag(sa, i, b);
+                    xs[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, ones, xs[i], 0, 0, 0);
+#pragma unroll
+                    for (int j = 0; j < FJ; ++j)
+                        ps[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, bp[j], ps[i][j], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < FJ; ++j) {
+                const float sc = half_bits_to_float(st.s[j]);
+                const float zc = 128.0f + half_bits_to_float(st.s[j] >> 16);
+#pragma unroll
+                for (int i = 0; i < MB; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf(sc, fmaf(-zc, xs[i][e], ps[i][j][e]), acc[i][j][e]);
+            }
+        } else {
+            // Groups smaller than a step: dequantize every weight, W' =
+            // (1024 + u) s - (1024 + z) s rounded once to bf16.
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                bf16x8_t bp[FJ];
+#pragma unroll
+                for (int j = 0; j < FJ; ++j) {
+                    const float sc = half_bits_to_float(st.s[j]);
+                    const float cs = -(1024.0f + half_bits_to_float(st.s[j] >> 16)) * sc;
+                    const uint32_t w = st.q[j][b];
+                    uint32_t o[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t hw = ((w >> (4 * i)) & 0x000F000Fu) | bias16;
+                        const _Float16 lo = __builtin_bit_cast(_Float16, static_cast<uint16_t>(hw & 0xFFFFu));
+                        const _Float16 hi = __builtin_bit_cast(_Float16, static_cast<uint16_t>(hw >> 16));
+                        o[i] = pack_bf16x2(fmaf(static_cast<float>(lo), sc, cs), fmaf(static_cast<float>(hi), sc, cs));
+                    }
+                    bp[j] = __builtin_bit_cast(bf16x8_t, u32x4_t{o[0], o[1], o[2], o[3]});
+                }
+#pragma unroll
+                for (int i = 0; i < MB; ++i) {
+                    const bf16x8_t ap = a_frag(sa, i, b);
+#pragma unroll
+                    for (int j = 0; j < FJ; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, bp[j], acc[i][j], 0, 0, 0);
+                }
+            }
+        }
+    };
+
+    // Steps wave, wave + wk, ... in rounds of kDepth: a round issues the
+    // loads of its steps together (weights, and activations unless they are
+    // staged in LDS), then multiplies them in order.  Nothing is loaded that
+    // is not used, and the latency of one round is covered by the other waves
+    // on the compute unit.  The empty asm with a memory clobber after the
+    // loads keeps the optimizer from sinking them down to their use, and the
+    // scheduling barrier keeps the multiplications after them.
+    constexpr int kDepth = skinny_depth<MB, MODE>();
+    BStage bq[kDepth];
+    AStage aq[kDepth];
+    auto issue = [&](int step) {
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) {
+            const int st = step + d * wk;
+            if (st < KS) {
+                load_b(st, bq[d]);
+                if constexpr (!DOTL) load_a(st, aq[d]);
+            }
+        }
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    int step = wave;                     // every wave has at least one step
+    issue(step);
+    if constexpr (DOTL) {
+        // stage the activations while the first weights are in flight:
+        // unit u = one 32-k quarter of one row (64 bytes of bf16 or 32 of
+        // E4M3, widened exactly), stored as 16 bf16 pairs with its sum
+        const int64_t units = MB * (K / 32);
+        for (int64_t u = threadIdx.x; u < units; u += blockDim.x) {
+            const int64_t m = u / (K / 32), q = u % (K / 32);
+            const int64_t row = m < M ? m : M - 1;
+            uint32_t w[16];
+            if constexpr (!XF8) {
+                const u32x4_t* src = reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(p.X) + row * K + 32 * q);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const u32x4_t v = src[t];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) w[4 * t + e] = v[e];
+                }
+            } else {
+                const u32x4_t* src = reinterpret_cast<const u32x4_t*>(static_cast<const uint8_t*>(p.X) + row * K + 32 * q);
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const u32x4_t v = src[t];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float2_t f0 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v[e]), false);
+                        const float2_t f1 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v[e]), true);
+                        w[8 * t + 2 * e] = pack_bf16x2(f0[0], f0[1]);
+                        w[8 * t + 2 * e + 1] = pack_bf16x2(f1[0], f1[1]);
+                    }
+                }
+            }
+            float t4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int i = 0; i < 16; ++i) t4[i & 3] = dot2_bf16(w[i], 0x3F803F80u, t4[i & 3]);
+            u32x4_t* dst = reinterpret_cast<u32x4_t*>(lds_x + m * (K / 2) + 16 * q);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) dst[t] = u32x4_t{w[4 * t], w[4 * t + 1], w[4 * t + 2], w[4 * t + 3]};
+            lds_xs[m * (K / 32) + q] = (t4[0] + t4[1]) + (t4[2] + t4[3]);
+        }
+        __syncthreads();
+    }
+    while (true) {
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d)
+            if (step + d * wk < KS) compute(bq[d], aq[d], step + d * wk);
+        step += kDepth * wk;
+        if (step >= KS) break;
+        issue(step);
+    }
+
+    if constexpr (DOT) {
+        // sum the four quarters of every column (lanes c, c + 16, c + 32,
+        // c + 48), then the wk waves through LDS ([wk][MB][16 FJ]) in wave order
+        constexpr int TILE = 16 * MB * FJ;
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int j = 0; j < FJ; ++j) {
+                float v = acc[m][j][0];
+                v += __shfl_xor(v, 16, kWave);
+                v += __shfl_xor(v, 32, kWave);
+                if (h == 0) red_base[wave * TILE + m * 16 * FJ + 16 * j + c] = v;
+            }
+        __syncthreads();
+        for (int o = threadIdx.x; o < TILE; o += blockDim.x) {
+            const int row = o / (16 * FJ), col = o % (16 * FJ);
+            float y = 0.0f;
+            for (int w = 0; w < wk; ++w) y += red_base[w * TILE + o];
+            const int64_t n = n0 + col;
+            if (row < M && n < N) {
+                if constexpr (XF8) y *= p.xscale[row];
+                p.Y[static_cast<int64_t>(row) * N + n] = float_to_bf16_bits(y);
+            }
+        }
+        return;
+    }
+    // Sum the wk partial tiles in LDS: wave w stores its [16 MB][16 FJ] tile
+    // (register e of lane l holds row 4 (l / 16) + e of its 16-row block and
+    // column l % 16 of its 16-column block), then each thread adds the wk
+    // values of some outputs in wave order.
+    constexpr int TILE = 256 * MB * FJ;
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                red[wave * TILE + (16 * i + 4 * h + e) * (16 * FJ) + 16 * j + c] = acc[i][j][e];
+    __syncthreads();
+    for (int o = threadIdx.x; o < TILE; o += blockDim.x) {
+        const int row = o / (16 * FJ), col = o % (16 * FJ);
+        float y = 0.0f;
+        for (int w = 0; w < wk; ++w) y += red[w * TILE + o];
+        const int64_t n = n0 + col;
+        if (row < M && n < N) {
+            if constexpr (XF8) y *= p.xscale[row];
+            p.Y[static_cast<int64_t>(row) * N + n] = float_to_bf16_bits(y);
+        }
+    }
+}
+
+template <int MB, int FJ, bool XF8, int MODE>
+hipError_t launch_skinny_c(const MulParams& p, int wk, hipStream_t stream) {
+    const int64_t blocks = (p.N + 16 * FJ - 1) / (16 * FJ);
+    size_t lds = static_cast<size_t>(wk) * (MODE == kDot || MODE == kDotLds ? 16 : 256) * MB * FJ * sizeof(float);
+    if (MODE == kDotLds) lds += static_cast<size_t>(MB) * (p.K / 2 + p.K / 32) * sizeof(uint32_t);
+    hipLaunchKernelGGL((gemm_skinny_kernel<MB, FJ, XF8, MODE>), dim3(static_cast<unsigned>(blocks)), dim3(64 * wk), lds,
+                       stream, p, wk);
+    return hipGetLastError();
+}
+
+// groups of 128 (one per K step) use the exact correction form, smaller
+// groups dequantize every weight
+template <int MB, int FJ, bool XF8>
+hipError_t launch_skinny_t(const MulParams& p, int wk, hipStream_t stream) {
+    if (p.G == kStepK) {
+        // four bf16 row blocks with two column blocks would not fit the registers
+        if constexpr (MB == 4 && FJ > 1 && !XF8) return launch_skinny_c<MB, 1, XF8, kCorr>(p, wk, stream);
+        else return launch_skinny_c<MB, FJ, XF8, kCorr>(p, wk, stream);
+    }
+    return launch_skinny_c<MB, FJ, XF8, kDeq>(p, wk, stream);
+}
+
+template <int MB, bool XF8>
+hipError_t launch_skinny_m(const MulParams& p, int fj, int wk, hipStream_t stream) {
+    // four 16-row blocks by four 16-column blocks would not fit the registers
+    if constexpr (MB < 4) {
+        if (fj == 4) return launch_skinny_t<MB, 4, XF8>(p, wk, stream);
+    }
+    if (fj >= 2) return launch_skinny_t<MB, 2, XF8>(p, wk, stream);
+    return launch_skinny_t<MB, 1, XF8>(p, wk, stream);
+}
+
+}  // namespace
+
+// Launch shape: the widest column tile (16, 32 or 64 columns; 32 at most for
+// 64 rows) that still gives at least 240 workgroups (one per compute unit,
+// nearly), then enough K-splitting waves per workgroup (at most 8) for about
+// 16 waves per compute unit, each wave keeping at least two 128-wide K steps.
+hipError_t launch_skinny(const MulParams& p, hipStream_t stream) {
+    if (p.M == 0 || p.N == 0) return hipSuccess;
+#ifndef W4_SK_FJMAX
+#define W4_SK_FJMAX 4
+#endif
+#ifndef W4_SK_MINBLK
+#define W4_SK_MINBLK 240
+#endif
+#ifndef W4_SK_WKMAX
+#define W4_SK_WKMAX 8
+#endif
+#ifndef W4_SK_MINSTEPS
+#define W4_SK_MINSTEPS 8
+#endif
+#ifndef W4_DOT_FJMAX
+#define W4_DOT_FJMAX 4
+#endif
+#ifndef W4_DOT_MINBLK
+#define W4_DOT_MINBLK 240
+#endif
+#ifndef W4_DOT_MINSTEPS
+#define W4_DOT_MINSTEPS 4
+#endif
+#ifndef W4_DOT_WAVES
+#define W4_DOT_WAVES 8192
+#endif
+    const bool dotm = p.M <= kDotMaxM;
+    const int mb = p.M <= 16 ? 1 : (p.M <= 32 ? 2 : 4);
+    int fj = dotm ? W4_DOT_FJMAX : (mb == 4 ? 2 : W4_SK_FJMAX);
+    const int minblk = dotm ? W4_DOT_MINBLK : W4_SK_MINBLK;
+    while (fj > 1 && (p.N + 16 * fj - 1) / (16 * fj) < minblk) fj /= 2;
+    const int64_t blocks = (p.N + 16 * fj - 1) / (16 * fj);
+    const int64_t ks = (p.K + kStepK - 1) / kStepK;
+    const int64_t minsteps = dotm ? W4_DOT_MINSTEPS : W4_SK_MINSTEPS;
+    int64_t wk = ((dotm ? W4_DOT_WAVES : 4096) + blocks - 1) / blocks;
+    if (wk > ks / minsteps) wk = ks / minsteps;
+#ifndef W4_DOT_WKMAX
+#define W4_DOT_WKMAX 16
+#endif
+    const int64_t wk_max = dotm && p.M == 1 ? W4_DOT_WKMAX : W4_SK_WKMAX;
+    if (wk > wk_max) wk = wk_max;
+    if (wk < 1) wk = 1;
+    // the LDS for the final sum: wk x 1 KB per 16 x 16 block of the tile
+    while (wk > 1 && wk * mb * fj > 128) --wk;
+    const int w = static_cast<int>(wk);
+    if (p.M <= kDotMaxM) {
+#ifndef W4_DOT_LDS_MAX
+#define W4_DOT_LDS_MAX 65536
+#endif
+        // activations staged in LDS when they fit (up to 64 KB per workgroup)
+        const bool lds_x = static_cast<int64_t>(p.M) * (p.K * 2 + p.K / 8) <= W4_DOT_LDS_MAX;
+        auto dot = [&](auto mt, auto xf8) -> hipError_t {
+            constexpr int MT = decltype(mt)::value;
+            constexpr bool X8 = decltype(xf8)::value;
+            if (lds_x) {
+                if (fj == 4) return launch_skinny_c<MT, 4, X8, kDotLds>(p, w, stream);
+                if (fj == 2) return launch_skinny_c<MT, 2, X8, kDotLds>(p, w, stream);
+                return launch_skinny_c<MT, 1, X8, kDotLds>(p, w, stream);
+            }
+            if (fj == 4) return launch_skinny_c<MT, 4, X8, kDot>(p, w, stream);
+            if (fj == 2) return launch_skinny_c<MT, 2, X8, kDot>(p, w, stream);
+            return launch_skinny_c<MT, 1, X8, kDot>(p, w, stream);
+        };
+        using one = std::integral_constant<int, 1>;
+        using two = std::integral_constant<int, 2>;
+        if (p.x_fp8) return p.M == 1 ? dot(one{}, std::true_type{}) : dot(two{}, std::true_type{});
+        return p.M == 1 ? dot(one{}, std::false_type{}) : dot(two{}, std::false_type{});
+    }
+    if (p.x_fp8) {
+        switch (mb) {
+            case 1: return launch_skinny_m<1, true>(p, fj, w, stream);
+            case 2: return launch_skinny_m<2, true>(p, fj, w, stream);
+            default: return launch_skinny_m<4, true>(p, fj, w, stream);
+        }
+    }
+    switch (mb) {
+        case 1: return launch_skinny_m<1, false>(p, fj, w, stream);
+        case 2: return launch_skinny_m<2, false>(p, fj, w, stream);
+        default: return launch_skinny_m<4, false>(p, fj, w, stream);
+    }
+}
+
+}  // namespace w4
