@@ -106,19 +106,22 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
     // 16-byte piece of tile t is at word 4 c + 4 nr t of the block, its
     // scale/zero word of group g at c + nr g (nr = rows in the block; rows
     // past N read the block's last row and give values never stored)
+    // (offsets within a block fit 32 bits; the per-step parts are uniform)
     const uint32_t* bcol[FJ];
     const uint32_t* bsz[FJ];
-    int64_t bnr[FJ];
+    int bnr[FJ];
 #pragma unroll
     for (int j = 0; j < FJ; ++j) {
         int64_t r0 = n0 + 16 * j;
         r0 = r0 < N ? r0 : ((N - 1) / 16) * 16;
-        const int64_t nr = N - r0 < 16 ? N - r0 : 16;
-        const int64_t cc = c < nr ? c : nr - 1;
+        const int nr = static_cast<int>(N - r0 < 16 ? N - r0 : 16);
+        const int cc = c < nr ? c : nr - 1;
         bcol[j] = p.wq + r0 * words_row + 4 * cc;
         bsz[j] = p.sz + r0 * groups_row + cc;
-        bnr[j] = nr;
+        bnr[j] = __builtin_amdgcn_readfirstlane(nr);
     }
+    const int KQ = static_cast<int>(K / 32);          // 32-k quarters (tiles) per row
+    const int q_shift = g_shift - 5;                  // tile -> group
     // activation rows: the MFMA forms give lane (c, h) row c of every 16-row
     // block; the dot form gives every lane all MB rows
     const uint8_t* arow[MB];
@@ -130,21 +133,21 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
     }
 
     auto load_b = [&](int step, BStage& st) {
-        const int64_t kb = static_cast<int64_t>(step) * kStepK + 32 * h;
-        const int64_t k = kb < K ? kb : 0;          // K is a multiple of 32
+        int tq = 4 * step + h;                        // the lane's tile
+        tq = tq < KQ ? tq : 0;                        // past K (K a multiple of 32): a valid tile, unused
 #pragma unroll
         for (int j = 0; j < FJ; ++j) {
-            st.q[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(bcol[j] + (k / 32) * 4 * bnr[j]));
-            st.s[j] = bsz[j][(k >> g_shift) * bnr[j]];
+            st.q[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(bcol[j] + tq * (4 * bnr[j])));
+            st.s[j] = bsz[j][(tq >> q_shift) * bnr[j]];
         }
     };
     auto load_a = [&](int step, AStage& st) {
-        const int64_t kb = static_cast<int64_t>(step) * kStepK + 32 * h;
-        const bool valid = kb < K;
-        const int64_t k = valid ? kb : 0;
+        const int tq0 = 4 * step + h;
+        const bool valid = tq0 < KQ;
+        const int tq = valid ? tq0 : 0;
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
-            const u32x4_t* ap = reinterpret_cast<const u32x4_t*>(arow[i] + k * (XF8 ? 1 : 2));
+            const u32x4_t* ap = reinterpret_cast<const u32x4_t*>(arow[i] + tq * (XF8 ? 32 : 64));
 #pragma unroll
             for (int t = 0; t < AL; ++t) st.a[i][t] = ap[t];
         }
@@ -193,18 +196,18 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
             uint32_t xw[MB][16];
             float xs[MB];
             if constexpr (DOTL) {
-                const int64_t kq = static_cast<int64_t>(step) * (kStepK / 32) + h;   // the lane's 32-k quarter
-                const bool valid = kq < K / 32;
+                const int kq = 4 * step + h;          // the lane's 32-k quarter
+                const bool valid = kq < KQ;
 #pragma unroll
                 for (int m = 0; m < MB; ++m) {
-                    const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(lds_x + m * (K / 2) + (valid ? kq : 0) * 16);
+                    const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(lds_x + m * (16 * KQ) + (valid ? kq : 0) * 16);
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
                         const u32x4_t v = valid ? xp[t] : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
                         for (int e = 0; e < 4; ++e) xw[m][4 * t + e] = v[e];
                     }
-                    xs[m] = valid ? lds_xs[m * (K / 32) + kq] : 0.0f;
+                    xs[m] = valid ? lds_xs[m * KQ + kq] : 0.0f;
                 }
             }
 #pragma unroll
@@ -362,9 +365,9 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
         // stage the activations while the first weights are in flight:
         // unit u = one 32-k quarter of one row (64 bytes of bf16 or 32 of
         // E4M3, widened exactly), stored as 16 bf16 pairs with its sum
-        const int64_t units = MB * (K / 32);
-        for (int64_t u = threadIdx.x; u < units; u += blockDim.x) {
-            const int64_t m = u / (K / 32), q = u % (K / 32);
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+        for (int q = threadIdx.x; q < KQ; q += blockDim.x) {
             const int64_t row = m < M ? m : M - 1;
             uint32_t w[16];
             if constexpr (!XF8) {
@@ -392,10 +395,10 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
             float t4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int i = 0; i < 16; ++i) t4[i & 3] = dot2_bf16(w[i], 0x3F803F80u, t4[i & 3]);
-            u32x4_t* dst = reinterpret_cast<u32x4_t*>(lds_x + m * (K / 2) + 16 * q);
+            u32x4_t* dst = reinterpret_cast<u32x4_t*>(lds_x + m * (16 * KQ) + 16 * q);
 #pragma unroll
             for (int t = 0; t < 4; ++t) dst[t] = u32x4_t{w[4 * t], w[4 * t + 1], w[4 * t + 2], w[4 * t + 3]};
-            lds_xs[m * (K / 32) + q] = (t4[0] + t4[1]) + (t4[2] + t4[3]);
+            lds_xs[m * KQ + q] = (t4[0] + t4[1]) + (t4[2] + t4[3]);
         }
         __syncthreads();
     }
