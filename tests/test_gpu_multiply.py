@@ -212,6 +212,44 @@ def test_zero_rows_and_ragged_shapes():
                 assert oracle.rel_error(want8[1:], Y8.float().cpu().numpy()[1:]) <= REL_TOL
 
 
+def test_w4a8_decode_row_quant_in_product():
+    # one or two rows: the product kernel quantizes the bf16 rows itself; its
+    # codes and scales must still be the row quantizer's, bit for bit, over
+    # wide dynamic ranges, bf16 values at the clamp, and an all-zero row.
+    # K = 32768 does not fit the in-kernel staging and takes the separate path.
+    require_gpu()
+    import torch
+    import w4_dequant_gemm_amd as w4
+    rng = np.random.default_rng(11)
+    for K, N in ((8192, 96), (3840, 40), (32768, 48)):
+        W = synth.normal_matrix(41, N, K, 0.05)
+        q = oracle.quantize(W, 128, "asym")
+        pk, G = prepack_dev(q)
+        allv = (np.arange(0, 0x10000, dtype=np.uint32) << 16).view(np.float32)
+        lim = np.float32(448.0 * 2.0 ** -3)
+        pool = allv[np.isfinite(allv) & (np.abs(allv) <= lim)]
+        rows = [
+            (rng.standard_normal(K) * np.exp2(rng.uniform(-14, 14, K))).astype(np.float32),
+            np.concatenate([[lim], rng.choice(pool, K - 1)]).astype(np.float32),
+            np.zeros(K, np.float32),
+        ]
+        for M, pick in ((1, (0,)), (1, (1,)), (2, (0, 1)), (2, (2, 0)), (1, (2,))):
+            print(f"[w4a8 decode] K={K} N={N} M={M} rows={pick}", flush=True)
+            Xb = synth.to_bf16_bits(np.stack([rows[i] for i in pick]))
+            Y, xq, xs = w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G)
+            torch.cuda.synchronize()
+            want, rq, rs = oracle.w4a8_ref(Xb, q["packed"], q["scale"], q["zero"], G, "asym")
+            assert_bits_equal(host(xq), rq, f"E4M3 activations K={K} M={M}")
+            assert_bits_equal(host(xs).view(np.uint32), rs.view(np.uint32), f"row scales K={K} M={M}")
+            got = Y.float().cpu().numpy()
+            for i, r in enumerate(pick):
+                if r == 2:
+                    assert np.all(bits16(Y)[i] & 0x7FFF == 0)
+                else:
+                    err = oracle.rel_error(want[i], got[i])
+                    assert err <= REL_TOL, f"K={K} M={M} row {i}: relative error {err:.3e}"
+
+
 def test_group_size_64():
     require_gpu()
     import torch

@@ -176,6 +176,11 @@ int w4a8_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const
     if (M == 0 || N == 0) return W4_OK;
     W4_REQUIRE_PTR(fn, xq);
     if (!xscale) return fail(W4_EINVAL, "%s: xscale is NULL", fn);
+    if (w4::skinny_quantizes_rows(M, K)) {
+        // one kernel: row quantization (same arithmetic) and product
+        w4::MulParams p{X, nullptr, M, K, N, G, wq, sz, Y, true, xq, xscale};
+        return hip_status(w4::launch_skinny(p, stream), fn);
+    }
     w4::RowQuantParams rq{X, M, K, xq, xscale};
     W4_TRY(hip_status(w4::launch_rowquant(rq, stream), fn));
     w4::MulParams p{xq, xscale, M, K, N, G, wq, sz, Y, true};

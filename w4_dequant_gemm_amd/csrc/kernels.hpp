@@ -53,6 +53,11 @@ struct MulParams {
     const uint32_t* sz;      // [N, K/G] fp16 scale | fp16 zero << 16
     uint16_t* Y;             // [M, N] bf16
     bool x_fp8;
+    // W4A8 with the row quantization done inside the product (see
+    // skinny_quantizes_rows): X is then the bf16 input, and the kernel also
+    // writes the E4M3 codes and row scales here
+    uint8_t* xq_out = nullptr;
+    float* xscale_out = nullptr;
 };
 // Which kernel runs a product: M <= kSkinnyMaxM: the weight-streaming
 // kernels (dot form for one or two rows, MFMA form above); larger M: the
@@ -62,6 +67,9 @@ struct MulParams {
 #endif
 constexpr int64_t kSkinnyMaxM = W4_SKINNY_MAX;
 hipError_t launch_skinny(const MulParams& p, hipStream_t stream);
+// true when a W4A8 product of M rows quantizes its activation rows itself
+// (one or two rows whose bf16 activations fit the kernel's LDS staging)
+bool skinny_quantizes_rows(int64_t M, int64_t K);
 hipError_t launch_gemm(const MulParams& p, hipStream_t stream);
 
 }  // namespace w4

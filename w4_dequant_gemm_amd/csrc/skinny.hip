@@ -56,8 +56,13 @@ constexpr int kStepK = 128;   // k per wave and step (4 quarters of 32)
 #ifndef W4_DOT_DEPTH
 #define W4_DOT_DEPTH 4
 #endif
+#ifndef W4_DOTL_DEPTH
+#define W4_DOTL_DEPTH 2
+#endif
 template <int MB, int MODE>
-constexpr int skinny_depth() { return MODE == 2 ? W4_DOT_DEPTH : (MB == 1 ? W4_SK_DEPTH : 2); }
+constexpr int skinny_depth() {
+    return MODE >= 3 ? W4_DOTL_DEPTH : (MODE == 2 ? W4_DOT_DEPTH : (MB == 1 ? W4_SK_DEPTH : 2));
+}
 
 // weights of one step: the lane's 16 bytes of codes and its scale/zero word,
 // per 16-column block
@@ -79,15 +84,18 @@ constexpr int kDeq = 0;    // dequantize every weight to bf16, MFMA (groups of 3
 constexpr int kCorr = 1;   // MFMA on 128 + u, per-group correction (groups of 128)
 constexpr int kDot = 2;    // v_dot2 on 128 + u, per-group correction (one or two rows)
 constexpr int kDotLds = 3; // the same, activations and their 32-k sums staged in LDS once
+constexpr int kDotLdsQ = 4; // the same for W4A8, quantizing the bf16 rows to E4M3 while staging
 constexpr int kDotMaxM = 2;
 
 // up to 16 waves per workgroup for the one-row dot form (few registers), 8 otherwise
 template <int MB, int MODE>
-constexpr int skinny_max_threads() { return (MODE == 2 || MODE == 3) && MB == 1 ? 1024 : 512; }
+constexpr int skinny_max_threads() { return MODE == kDotLds || MODE == kDotLdsQ ? 1024 : 512; }
 
 template <int MB, int FJ, bool XF8, int MODE>
 __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_kernel(MulParams p, int wk) {
-    constexpr bool CORR = MODE == kCorr, DOTL = MODE == kDotLds, DOT = MODE == kDot || DOTL;
+    constexpr bool CORR = MODE == kCorr, QX = MODE == kDotLdsQ, DOTL = MODE == kDotLds || QX,
+                   DOT = MODE == kDot || DOTL;
+    static_assert(!QX || XF8, "in-kernel row quantization is the W4A8 product");
     using BStage = SkinnyB<FJ>;
     using AStage = SkinnyA<MB, XF8>;
     constexpr int AL = AStage::AL;
@@ -107,8 +115,9 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
     // scale/zero word of group g at c + nr g (nr = rows in the block; rows
     // past N read the block's last row and give values never stored)
     // (offsets within a block fit 32 bits; the per-step parts are uniform)
-    const uint32_t* bcol[FJ];
-    const uint32_t* bsz[FJ];
+    const uint8_t* bblk[FJ];                           // block bases (uniform)
+    const uint8_t* sblk[FJ];
+    uint32_t qlane[FJ], slane[FJ];                     // the lane's byte offsets in a tile
     int bnr[FJ];
 #pragma unroll
     for (int j = 0; j < FJ; ++j) {
@@ -116,11 +125,14 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
         r0 = r0 < N ? r0 : ((N - 1) / 16) * 16;
         const int nr = static_cast<int>(N - r0 < 16 ? N - r0 : 16);
         const int cc = c < nr ? c : nr - 1;
-        bcol[j] = p.wq + r0 * words_row + 4 * cc;
-        bsz[j] = p.sz + r0 * groups_row + cc;
+        bblk[j] = reinterpret_cast<const uint8_t*>(p.wq + r0 * words_row);
+        sblk[j] = reinterpret_cast<const uint8_t*>(p.sz + r0 * groups_row);
+        qlane[j] = 16 * cc;
+        slane[j] = 4 * cc;
         bnr[j] = __builtin_amdgcn_readfirstlane(nr);
     }
     const int KQ = static_cast<int>(K / 32);          // 32-k quarters (tiles) per row
+    const int KQ4 = (KQ + 3) & ~3;                    // padded to whole steps (LDS staging)
     const int q_shift = g_shift - 5;                  // tile -> group
     // activation rows: the MFMA forms give lane (c, h) row c of every 16-row
     // block; the dot form gives every lane all MB rows
@@ -133,12 +145,17 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
     }
 
     auto load_b = [&](int step, BStage& st) {
-        int tq = 4 * step + h;                        // the lane's tile
-        tq = tq < KQ ? tq : 0;                        // past K (K a multiple of 32): a valid tile, unused
+        // the lane's tile; past K (a multiple of 32 but not of 128) the lane
+        // reads the last tile, whose products meet zero activations
+        const int t = 4 * step + h;
+        const uint32_t tq = static_cast<uint32_t>(t < KQ ? t : KQ - 1);
+        const uint32_t g = tq >> q_shift;
 #pragma unroll
         for (int j = 0; j < FJ; ++j) {
-            st.q[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(bcol[j] + tq * (4 * bnr[j])));
-            st.s[j] = bsz[j][(tq >> q_shift) * bnr[j]];
+            // 32-bit byte offsets from uniform bases (a block spans K nr / 2 bytes)
+            st.q[j] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4_t*>(bblk[j] + (__umul24(tq, 16 * bnr[j]) + qlane[j])));
+            st.s[j] = *reinterpret_cast<const uint32_t*>(sblk[j] + (__umul24(g, 4 * bnr[j]) + slane[j]));
         }
     };
     auto load_a = [&](int step, AStage& st) {
@@ -183,12 +200,14 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
     const uint32_t bias16 = opaque_vgpr(0x64006400u);   // two fp16 1024.0
     const uint32_t bias128 = opaque_vgpr(kBf16Bias128x2);
     // dot form with staged activations: LDS holds, per row, the activations
-    // as bf16 pairs ([MB][K / 2] words) and the sum of every 32-k quarter
-    // ([MB][K / 32] floats); the partial sums of the final reduction follow
+    // as bf16 pairs ([MB][16 KQ4] words) and the sum of every 32-k quarter
+    // ([MB][KQ4] floats), both zero past K up to a whole step; the partial
+    // sums of the final reduction follow
     extern __shared__ float red[];
     uint32_t* const lds_x = reinterpret_cast<uint32_t*>(red);
-    float* const lds_xs = red + (DOTL ? MB * (K / 2) : 0);
-    float* const red_base = DOTL ? lds_xs + MB * (K / 32) : red;
+    float* const lds_xs = red + (DOTL ? MB * 16 * KQ4 : 0);
+    float* const red_base = DOTL ? lds_xs + MB * KQ4 : red;
+    float row_scale[MB];                    // in-kernel W4A8 row scales (QX)
 
     auto compute = [&](const BStage& st, const AStage& sa, int step) {
         if constexpr (DOT) {
@@ -196,18 +215,17 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
             uint32_t xw[MB][16];
             float xs[MB];
             if constexpr (DOTL) {
-                const int kq = 4 * step + h;          // the lane's 32-k quarter
-                const bool valid = kq < KQ;
+                const int kq = 4 * step + h;          // the lane's 32-k quarter (zeros past K)
 #pragma unroll
                 for (int m = 0; m < MB; ++m) {
-                    const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(lds_x + m * (16 * KQ) + (valid ? kq : 0) * 16);
+                    const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(lds_x + m * (16 * KQ4) + kq * 16);
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
-                        const u32x4_t v = valid ? xp[t] : u32x4_t{0u, 0u, 0u, 0u};
+                        const u32x4_t v = xp[t];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) xw[m][4 * t + e] = v[e];
                     }
-                    xs[m] = valid ? lds_xs[m * KQ + kq] : 0.0f;
+                    xs[m] = lds_xs[m * KQ4 + kq];
                 }
             }
 #pragma unroll
@@ -243,28 +261,25 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
                 for (int w = 0; w < 16; ++w) t[w & 3] = dot2_bf16(xw[m][w], 0x3F803F80u, t[w & 3]);
                 xs[m] = (t[0] + t[1]) + (t[2] + t[3]);
             }
+            // one chain per output: it starts at -(128 + z) sum x and adds
+            // the products of the 32 exact values 128 + u
 #pragma unroll
             for (int j = 0; j < FJ; ++j) {
-                float d[MB][4];
+                const float sc = half_bits_to_float(st.s[j]);
+                const float zc = 128.0f + half_bits_to_float(st.s[j] >> 16);
+                float d[MB];
 #pragma unroll
-                for (int m = 0; m < MB; ++m)
-#pragma unroll
-                    for (int b = 0; b < 4; ++b) d[m][b] = 0.0f;
+                for (int m = 0; m < MB; ++m) d[m] = -zc * xs[m];
 #pragma unroll
                 for (int b = 0; b < 4; ++b)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const uint32_t pr = nibble_pair_bf16(st.q[j][b], i, bias128);
 #pragma unroll
-                        for (int m = 0; m < MB; ++m) d[m][b] = dot2_bf16(pr, xw[m][4 * b + i], d[m][b]);
+                        for (int m = 0; m < MB; ++m) d[m] = dot2_bf16(pr, xw[m][4 * b + i], d[m]);
                     }
-                const float sc = half_bits_to_float(st.s[j]);
-                const float zc = 128.0f + half_bits_to_float(st.s[j] >> 16);
 #pragma unroll
-                for (int m = 0; m < MB; ++m) {
-                    const float dm = (d[m][0] + d[m][1]) + (d[m][2] + d[m][3]);
-                    acc[m][j][0] = fmaf(sc, fmaf(-zc, xs[m], dm), acc[m][j][0]);
-                }
+                for (int m = 0; m < MB; ++m) acc[m][j][0] = fmaf(sc, d[m], acc[m][j][0]);
             }
         } else if constexpr (CORR) {
             // One group per step (G = 128): multiply the exact bf16 values
@@ -351,9 +366,14 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
 #pragma unroll
         for (int d = 0; d < kDepth; ++d) {
             const int st = step + d * wk;
-            if (st < KS) {
+            if constexpr (DOTL) {
+                // unconditional, so that each multiplication waits only for
+                // its own step: a step past K reloads the last one (a cache
+                // hit) and is not multiplied
+                load_b(st < KS ? st : KS - 1, bq[d]);
+            } else if (st < KS) {
                 load_b(st, bq[d]);
-                if constexpr (!DOTL) load_a(st, aq[d]);
+                load_a(st, aq[d]);
             }
         }
         asm volatile("" ::: "memory");
@@ -365,6 +385,77 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
         // stage the activations while the first weights are in flight:
         // unit u = one 32-k quarter of one row (64 bytes of bf16 or 32 of
         // E4M3, widened exactly), stored as 16 bf16 pairs with its sum
+        if constexpr (QX) {
+            // W4A8 rows quantized here, with the arithmetic of the row
+            // quantizer: scale = max(max |x| / 448, 1e-8), codes =
+            // e4m3(clamp(x / scale, +-448)) (correctly rounded division,
+            // round to nearest even); the codes, widened exactly to bf16,
+            // are what the products use.  Workgroup 0 also writes the codes
+            // and scales out.
+            __shared__ float wave_amax[kDotMaxM][16];
+            float amax[MB];
+#pragma unroll
+            for (int m = 0; m < MB; ++m) {
+                amax[m] = 0.0f;
+                for (int q = threadIdx.x; q < KQ; q += blockDim.x) {
+                    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(p.X) + static_cast<int64_t>(m) * K + 32 * q);
+                    u32x4_t* dst = reinterpret_cast<u32x4_t*>(lds_x + m * (16 * KQ4) + 16 * q);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const u32x4_t v = src[t];
+                        dst[t] = v;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            amax[m] = fmaxf(fmaxf(amax[m], fabsf(bf16_lo(v[e]))), fabsf(bf16_hi(v[e])));
+                    }
+                }
+                amax[m] = wave_max(amax[m]);
+                if (lane == 0) wave_amax[m][wave] = amax[m];
+            }
+            __syncthreads();
+#pragma unroll
+            for (int m = 0; m < MB; ++m) {
+                float a = 0.0f;
+                for (int w = 0; w < wk; ++w) a = fmaxf(a, wave_amax[m][w]);
+                float sc = a / 448.0f;
+                sc = fmaxf(sc, 1e-8f);
+                row_scale[m] = sc;
+                if (blockIdx.x == 0 && threadIdx.x == 0) p.xscale_out[m] = sc;
+                for (int q = threadIdx.x; q < KQ; q += blockDim.x) {
+                    u32x4_t* buf = reinterpret_cast<u32x4_t*>(lds_x + m * (16 * KQ4) + 16 * q);
+                    uint32_t codes[8];
+                    float t4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const u32x4_t v = buf[t];
+                        u32x4_t wv;
+#pragma unroll
+                        for (int e = 0; e < 4; e += 2) {
+                            const float f0 = fminf(fmaxf(bf16_lo(v[e]) / sc, -448.0f), 448.0f);
+                            const float f1 = fminf(fmaxf(bf16_hi(v[e]) / sc, -448.0f), 448.0f);
+                            const float f2 = fminf(fmaxf(bf16_lo(v[e + 1]) / sc, -448.0f), 448.0f);
+                            const float f3 = fminf(fmaxf(bf16_hi(v[e + 1]) / sc, -448.0f), 448.0f);
+                            int c4 = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
+                            c4 = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, c4, true);
+                            codes[2 * t + e / 2] = static_cast<uint32_t>(c4);
+                            const float2_t g0 = __builtin_amdgcn_cvt_pk_f32_fp8(c4, false);
+                            const float2_t g1 = __builtin_amdgcn_cvt_pk_f32_fp8(c4, true);
+                            wv[e] = pack_bf16x2(g0[0], g0[1]);
+                            wv[e + 1] = pack_bf16x2(g1[0], g1[1]);
+                            t4[e] = dot2_bf16(wv[e], 0x3F803F80u, t4[e]);
+                            t4[e + 1] = dot2_bf16(wv[e + 1], 0x3F803F80u, t4[e + 1]);
+                        }
+                        buf[t] = wv;
+                    }
+                    lds_xs[m * KQ4 + q] = (t4[0] + t4[1]) + (t4[2] + t4[3]);
+                    if (blockIdx.x == 0) {
+                        u32x4_t* out = reinterpret_cast<u32x4_t*>(p.xq_out + static_cast<int64_t>(m) * K + 32 * q);
+                        out[0] = u32x4_t{codes[0], codes[1], codes[2], codes[3]};
+                        out[1] = u32x4_t{codes[4], codes[5], codes[6], codes[7]};
+                    }
+                }
+            }
+        } else
 #pragma unroll
         for (int m = 0; m < MB; ++m)
         for (int q = threadIdx.x; q < KQ; q += blockDim.x) {
@@ -395,11 +486,20 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
             float t4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int i = 0; i < 16; ++i) t4[i & 3] = dot2_bf16(w[i], 0x3F803F80u, t4[i & 3]);
-            u32x4_t* dst = reinterpret_cast<u32x4_t*>(lds_x + m * (16 * KQ) + 16 * q);
+            u32x4_t* dst = reinterpret_cast<u32x4_t*>(lds_x + m * (16 * KQ4) + 16 * q);
 #pragma unroll
             for (int t = 0; t < 4; ++t) dst[t] = u32x4_t{w[4 * t], w[4 * t + 1], w[4 * t + 2], w[4 * t + 3]};
-            lds_xs[m * KQ + q] = (t4[0] + t4[1]) + (t4[2] + t4[3]);
+            lds_xs[m * KQ4 + q] = (t4[0] + t4[1]) + (t4[2] + t4[3]);
         }
+        // zero quarters past K up to a whole step
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+            for (int q = KQ + static_cast<int>(threadIdx.x); q < KQ4; q += blockDim.x) {
+                u32x4_t* dst = reinterpret_cast<u32x4_t*>(lds_x + m * (16 * KQ4) + 16 * q);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) dst[t] = u32x4_t{0u, 0u, 0u, 0u};
+                lds_xs[m * KQ4 + q] = 0.0f;
+            }
         __syncthreads();
     }
     while (true) {
@@ -431,7 +531,8 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
             for (int w = 0; w < wk; ++w) y += red_base[w * TILE + o];
             const int64_t n = n0 + col;
             if (row < M && n < N) {
-                if constexpr (XF8) y *= p.xscale[row];
+                if constexpr (QX) y *= row == 0 ? row_scale[0] : row_scale[MB - 1];
+                else if constexpr (XF8) y *= p.xscale[row];
                 p.Y[static_cast<int64_t>(row) * N + n] = float_to_bf16_bits(y);
             }
         }
@@ -462,11 +563,15 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
     }
 }
 
+// LDS words of one staged activation row: 16 bf16 pairs and one sum per
+// 32-k quarter, quarters padded to a whole 128-k step
+int64_t staged_words_row(int64_t K) { return 17 * (((K / 32) + 3) & ~int64_t{3}); }
+
 template <int MB, int FJ, bool XF8, int MODE>
 hipError_t launch_skinny_c(const MulParams& p, int wk, hipStream_t stream) {
     const int64_t blocks = (p.N + 16 * FJ - 1) / (16 * FJ);
-    size_t lds = static_cast<size_t>(wk) * (MODE == kDot || MODE == kDotLds ? 16 : 256) * MB * FJ * sizeof(float);
-    if (MODE == kDotLds) lds += static_cast<size_t>(MB) * (p.K / 2 + p.K / 32) * sizeof(uint32_t);
+    size_t lds = static_cast<size_t>(wk) * (MODE >= kDot ? 16 : 256) * MB * FJ * sizeof(float);
+    if (MODE == kDotLds || MODE == kDotLdsQ) lds += static_cast<size_t>(MB) * staged_words_row(p.K) * sizeof(uint32_t);
     hipLaunchKernelGGL((gemm_skinny_kernel<MB, FJ, XF8, MODE>), dim3(static_cast<unsigned>(blocks)), dim3(64 * wk), lds,
                        stream, p, wk);
     return hipGetLastError();
@@ -496,10 +601,20 @@ hipError_t launch_skinny_m(const MulParams& p, int fj, int wk, hipStream_t strea
 
 }  // namespace
 
+bool skinny_quantizes_rows(int64_t M, int64_t K) {
+#ifndef W4_DOT_LDS_MAX
+#define W4_DOT_LDS_MAX 65536
+#endif
+    return M >= 1 && M <= kDotMaxM && M * staged_words_row(K) * 4 <= W4_DOT_LDS_MAX;
+}
+
 // Launch shape: the widest column tile (16, 32 or 64 columns; 32 at most for
 // 64 rows) that still gives at least 240 workgroups (one per compute unit,
-// nearly), then enough K-splitting waves per workgroup (at most 8) for about
-// 16 waves per compute unit, each wave keeping at least two 128-wide K steps.
+// nearly), then K-splitting waves per workgroup: with one or two rows, about
+// 32 waves per compute unit in all, at most 16 per workgroup (8 unless the
+// rows are staged in LDS) with at least four 128-wide K steps each; with more
+// rows about 16 waves per compute unit, at most 8 per workgroup, with at
+// least eight steps each.
 hipError_t launch_skinny(const MulParams& p, hipStream_t stream) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
 #ifndef W4_SK_FJMAX
@@ -539,21 +654,25 @@ hipError_t launch_skinny(const MulParams& p, hipStream_t stream) {
 #ifndef W4_DOT_WKMAX
 #define W4_DOT_WKMAX 16
 #endif
-    const int64_t wk_max = dotm && p.M == 1 ? W4_DOT_WKMAX : W4_SK_WKMAX;
+    // up to 16 waves where the activations are staged in LDS (1024-thread
+    // workgroups, 128 registers a lane), else up to 8
+    const bool lds_x = dotm && skinny_quantizes_rows(p.M, p.K);
+    const int64_t wk_max = lds_x ? W4_DOT_WKMAX : W4_SK_WKMAX;
     if (wk > wk_max) wk = wk_max;
     if (wk < 1) wk = 1;
     // the LDS for the final sum: wk x 1 KB per 16 x 16 block of the tile
     while (wk > 1 && wk * mb * fj > 128) --wk;
     const int w = static_cast<int>(wk);
     if (p.M <= kDotMaxM) {
-#ifndef W4_DOT_LDS_MAX
-#define W4_DOT_LDS_MAX 65536
-#endif
         // activations staged in LDS when they fit (up to 64 KB per workgroup)
-        const bool lds_x = static_cast<int64_t>(p.M) * (p.K * 2 + p.K / 8) <= W4_DOT_LDS_MAX;
         auto dot = [&](auto mt, auto xf8) -> hipError_t {
             constexpr int MT = decltype(mt)::value;
             constexpr bool X8 = decltype(xf8)::value;
+            if (X8 && p.xq_out) {
+                if (fj == 4) return launch_skinny_c<MT, 4, true, kDotLdsQ>(p, w, stream);
+                if (fj == 2) return launch_skinny_c<MT, 2, true, kDotLdsQ>(p, w, stream);
+                return launch_skinny_c<MT, 1, true, kDotLdsQ>(p, w, stream);
+            }
             if (lds_x) {
                 if (fj == 4) return launch_skinny_c<MT, 4, X8, kDotLds>(p, w, stream);
                 if (fj == 2) return launch_skinny_c<MT, 2, X8, kDotLds>(p, w, stream);
