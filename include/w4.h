@@ -26,7 +26,8 @@
  *  - Every pointer argument is a DEVICE pointer on the current HIP device,
  *    owned by the caller, except where a parameter says "host".  The library
  *    allocates no memory and keeps no state besides a thread-local message for
- *    the last failed call.
+ *    the last failed call; the products take their scratch memory from the
+ *    caller (w4_gemm_workspace_bytes).
  *  - Device pointers must be 16-byte aligned.
  *  - Every call is asynchronous on `stream` (0 = the null stream).  Arguments
  *    are checked on the host before any launch: a violated precondition
@@ -147,16 +148,32 @@ int w4_quantize_rows_e4m3(const uint16_t* X, int64_t M, int64_t K, uint8_t* xq, 
                           hipStream_t stream);
 
 /*
+ * w4_gemm_workspace_bytes -- bytes of device workspace that w4a16_gemm and
+ * w4a8_gemm need for a product of M rows, reduction K and N outputs.  It is 0
+ * for most shapes (64 rows or fewer, or enough output tiles to fill the GPU);
+ * a product with more rows but few 256 x 256 output tiles splits K across
+ * workgroups and needs splits * M * N * 4 bytes for the fp32 partial sums.
+ * Depends on the shape only; 0 for shapes the products reject.
+ */
+size_t w4_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
+
+/*
  * w4a16_gemm -- W4A16: Y = bf16(X . W'^T) with W'[n, k] = (u - zero) * scale
  * from the GPU layout, fp32 accumulation, bf16 output (round to nearest
  * even).  One entry point for every M: up to 64 rows run a kernel that
  * streams the weights once (bandwidth bound), larger M a tiled bf16-MFMA
  * GEMM.
  *   X  [M, K] bf16 in;  wq, sz as written by w4_prepack;  Y [M, N] bf16 out.
- *   M >= 0, N >= 0, K > 0, K % G == 0, G in {32, 64, 128}.
+ *   workspace: device memory of workspace_bytes >= w4_gemm_workspace_bytes(M,
+ *      K, N) bytes, 16-byte aligned, owned by the caller; its contents on
+ *      entry do not matter and are overwritten.  May be NULL when that size
+ *      is 0.  Calls in flight at the same time need separate workspaces.
+ *      Too small or NULL when needed: W4_EINVAL.
+ *   With a split K the partial sums are added in a fixed order: results do
+ *   not depend on timing.
  */
 int w4a16_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const uint32_t* sz,
-               int64_t N, int G, uint16_t* Y, hipStream_t stream);
+               int64_t N, int G, uint16_t* Y, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * w4a8_gemm -- W4A8: each activation row is quantized to E4M3 exactly as by
@@ -168,7 +185,8 @@ int w4a16_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, cons
  *   Other arguments as for w4a16_gemm.
  */
 int w4a8_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const uint32_t* sz,
-              int64_t N, int G, uint16_t* Y, uint8_t* xq, float* xscale, hipStream_t stream);
+              int64_t N, int G, uint16_t* Y, uint8_t* xq, float* xscale, void* workspace,
+              size_t workspace_bytes, hipStream_t stream);
 
 /* Short text for a status code (static storage). */
 const char* w4_status_string(int status);
@@ -177,7 +195,7 @@ const char* w4_status_string(int status);
  * (thread-local storage, valid until the next failing call). */
 const char* w4_last_error(void);
 
-/* Version of this ABI, currently 1. */
+/* Version of this ABI, currently 2. */
 int w4_abi_version(void);
 
 #ifdef __cplusplus

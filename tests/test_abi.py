@@ -30,7 +30,8 @@ def lib():
 def test_header_declares_the_boundary():
     names = _declared()
     for n in ("w4_quantize_blockwise", "w4_mse_clip_search", "w4_prepack", "w4_quantize_rows_e4m3",
-              "w4a16_gemm", "w4a8_gemm", "w4_status_string", "w4_last_error", "w4_abi_version"):
+              "w4a16_gemm", "w4a8_gemm", "w4_gemm_workspace_bytes", "w4_status_string", "w4_last_error",
+              "w4_abi_version"):
         assert n in names
 
 
@@ -41,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_status_strings(lib):
     import w4_dequant_gemm_amd as w4
-    assert w4.w4_abi_version() == 1
+    assert w4.w4_abi_version() == 2
     assert w4.w4_status_string(0) == "ok"
     assert w4.w4_status_string(1) == "invalid argument"
     assert w4.w4_status_string(2) == "unsupported configuration"
@@ -75,22 +76,46 @@ def test_host_validation(lib):
                                      None) == 1
     assert "aligned" in w4.w4_last_error()
     # null pointers and negative sizes in the products
-    assert lib.w4a16_gemm(None, 2, 96, fake, fake, 8, 32, fake, None) == 1
-    assert lib.w4a16_gemm(fake, -1, 96, fake, fake, 8, 32, fake, None) == 1
-    assert lib.w4a8_gemm(fake, 2, 96, fake, fake, 8, 32, fake, None, fake, None) == 1
-    assert lib.w4a16_gemm(fake, 2, 96, fake, fake, 8, 16, fake, None) == 2
+    assert lib.w4a16_gemm(None, 2, 96, fake, fake, 8, 32, fake, None, 0, None) == 1
+    assert lib.w4a16_gemm(fake, -1, 96, fake, fake, 8, 32, fake, None, 0, None) == 1
+    assert lib.w4a8_gemm(fake, 2, 96, fake, fake, 8, 32, fake, None, fake, None, 0, None) == 1
+    assert lib.w4a16_gemm(fake, 2, 96, fake, fake, 8, 16, fake, None, 0, None) == 2
     assert lib.w4_quantize_rows_e4m3(fake, 2, 12, fake, fake, None) == 1
     assert lib.w4_prepack(fake, fake, None, 4, 96, 32, 1, fake, fake, None) == 1
     # clip search needs its output
     assert lib.w4_mse_clip_search(fake, 4, 96, 32, 1, one, 1, None, None, None) == 1
 
 
+def test_gemm_workspace_sizes_and_checks(lib):
+    # few 256 x 256 output tiles: K is split across workgroups, the fp32
+    # partial sums need splits * M * N * 4 bytes; otherwise nothing
+    import w4_dequant_gemm_amd as w4
+    ws = lib.w4_gemm_workspace_bytes
+    assert ws(256, 15360, 3840) == 16 * 256 * 3840 * 4      # 15 tiles: 16 splits of 15 K steps
+    assert ws(256, 3840, 15360) == 4 * 256 * 15360 * 4      # 60 tiles: 4 splits
+    assert ws(2048, 8192, 28672) == 0                        # 896 tiles fill the GPU
+    assert ws(64, 15360, 3840) == 0                          # weight-streaming kernel
+    assert ws(256, 96, 3840) == 0                            # K not a multiple of 64: 128 x 128 tiles
+    assert ws(256, 512, 256) == 0                            # too few K steps to split
+    assert ws(-1, 512, 256) == 0 and ws(256, 0, 256) == 0
+    # a shape that needs one: NULL or too small is rejected before any launch
+    fake = ctypes.c_void_p(0x1000)
+    need = ws(256, 15360, 3840)
+    assert lib.w4a16_gemm(fake, 256, 15360, fake, fake, 3840, 128, fake, None, 0, None) == 1
+    assert "workspace" in w4.w4_last_error()
+    assert lib.w4a16_gemm(fake, 256, 15360, fake, fake, 3840, 128, fake, fake, need - 16, None) == 1
+    assert lib.w4a8_gemm(fake, 256, 15360, fake, fake, 3840, 128, fake, fake, fake, None, 0, None) == 1
+    assert lib.w4a16_gemm(fake, 256, 15360, fake, fake, 3840, 128, fake, ctypes.c_void_p(0x1004), need,
+                          None) == 1
+    assert "aligned" in w4.w4_last_error()
+
+
 def test_empty_shapes_are_no_ops(lib):
     # nothing to do: OK without touching any pointer (and without a device)
     one = _fr(1.0)
     assert lib.w4_quantize_blockwise(None, 0, 96, 32, 1, one, 1, None, None, None, None, None) == 0
-    assert lib.w4a16_gemm(None, 0, 96, None, None, 8, 32, None, None) == 0
-    assert lib.w4a16_gemm(None, 4, 96, None, None, 0, 32, None, None) == 0
+    assert lib.w4a16_gemm(None, 0, 96, None, None, 8, 32, None, None, 0, None) == 0
+    assert lib.w4a16_gemm(None, 4, 96, None, None, 0, 32, None, None, 0, None) == 0
     assert lib.w4_quantize_rows_e4m3(None, 0, 96, None, None, None) == 0
     assert lib.w4_prepack(None, None, None, 0, 96, 32, 1, None, None, None) == 0
 

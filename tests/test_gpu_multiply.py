@@ -250,6 +250,44 @@ def test_w4a8_decode_row_quant_in_product():
                     assert err <= REL_TOL, f"K={K} M={M} row {i}: relative error {err:.3e}"
 
 
+def test_split_k_products():
+    # few output tiles: the K split (fp32 partials in the workspace, summed in
+    # a second kernel) on a ragged shape, with a caller workspace that holds
+    # NaNs on entry, and on the 12B down shape at M = 256 (16 splits)
+    require_gpu()
+    import torch
+    import w4_dequant_gemm_amd as w4
+    W = synth.normal_matrix(52, 200, 4096, 0.02)
+    q = oracle.quantize(W, 128, "asym")
+    pk, G = prepack_dev(q)
+    M, K, N = 300, 4096, 200
+    need = w4.w4_gemm_workspace_bytes(M, K, N)
+    assert need == 8 * M * N * 4
+    Xb = synth.to_bf16_bits(synth.normal_matrix(53, M, K))
+    ws = torch.full((need // 4 + 16,), float("nan"), dtype=torch.float32, device="cuda")
+    for kind in ("w4a16", "w4a8"):
+        print(f"[split-K] {kind} M={M} K={K} N={N}", flush=True)
+        if kind == "w4a16":
+            Y = w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G, workspace=ws)
+            want = oracle.gemm_ref(oracle.bf16_bits_to_f64(Xb), q["packed"], q["scale"], q["zero"], G, "asym")
+        else:
+            Y, xq, xs = w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G, workspace=ws)
+            want, rq, rs = oracle.w4a8_ref(Xb, q["packed"], q["scale"], q["zero"], G, "asym")
+            torch.cuda.synchronize()
+            assert_bits_equal(host(xq), rq, "E4M3 activations")
+        torch.cuda.synchronize()
+        err = oracle.rel_error(want, Y.float().cpu().numpy())
+        assert err <= REL_TOL, f"{kind}: relative error {err:.3e}"
+        # the same call again gives the same bits (fixed summation order)
+        Y2 = (w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G, workspace=ws) if kind == "w4a16" else
+              w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G, workspace=ws)[0])
+        torch.cuda.synchronize()
+        assert np.array_equal(bits16(Y), bits16(Y2))
+    # too small a workspace is an error, not a slower path
+    with pytest.raises(w4.W4Error):
+        w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G, workspace=ws[:16])
+
+
 def test_group_size_64():
     require_gpu()
     import torch

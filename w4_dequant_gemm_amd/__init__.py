@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "W4Error", "SYM", "ASYM", "MAX_FRACS", "lib", "library_path",
     "w4_quantize_blockwise", "w4_mse_clip_search", "w4_prepack", "w4_quantize_rows_e4m3",
-    "w4a16_gemm", "w4a8_gemm", "w4_status_string", "w4_last_error", "w4_abi_version",
+    "w4a16_gemm", "w4a8_gemm", "w4_gemm_workspace_bytes", "w4_status_string", "w4_last_error",
+    "w4_abi_version",
     "FRACS_PLAIN", "FRACS_11",
 ]
 
@@ -59,8 +60,11 @@ def lib():
     L.w4_mse_clip_search.argtypes = [P, i64, i64, I, I, P, I, P, P, P]
     L.w4_prepack.argtypes = [P, P, P, i64, i64, I, I, P, P, P]
     L.w4_quantize_rows_e4m3.argtypes = [P, i64, i64, P, P, P]
-    L.w4a16_gemm.argtypes = [P, i64, i64, P, P, i64, I, P, P]
-    L.w4a8_gemm.argtypes = [P, i64, i64, P, P, i64, I, P, P, P, P]
+    sz_t = ctypes.c_size_t
+    L.w4a16_gemm.argtypes = [P, i64, i64, P, P, i64, I, P, P, sz_t, P]
+    L.w4a8_gemm.argtypes = [P, i64, i64, P, P, i64, I, P, P, P, P, sz_t, P]
+    L.w4_gemm_workspace_bytes.argtypes = [i64, i64, i64]
+    L.w4_gemm_workspace_bytes.restype = sz_t
     for name in ("w4_quantize_blockwise", "w4_mse_clip_search", "w4_prepack", "w4_quantize_rows_e4m3",
                  "w4a16_gemm", "w4a8_gemm"):
         getattr(L, name).restype = I
@@ -118,6 +122,19 @@ def _fracs(fracs: Sequence[float]):
 
 def _empty(shape, dtype, device):
     return torch.empty(shape, dtype=dtype, device=device)
+
+
+def _workspace(M: int, K: int, N: int, device, workspace, stream):
+    """(pointer, bytes) of the product's workspace: the caller's tensor, or a
+    new byte tensor when the shape needs one (kept alive on ``stream``)."""
+    need = w4_gemm_workspace_bytes(M, K, N)
+    if workspace is None:
+        if need == 0:
+            return None, 0
+        workspace = torch.empty((need,), dtype=torch.uint8, device=device)
+        if stream is not None:
+            workspace.record_stream(stream)
+    return _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
 
 
 # ---------------------------------------------------------------- quantizer
@@ -197,20 +214,30 @@ def w4_quantize_rows_e4m3(X: torch.Tensor, *, xq=None, xscale=None, stream=None)
     return xq, xscale
 
 
-def w4a16_gemm(X: torch.Tensor, wq: torch.Tensor, sz: torch.Tensor, G: int, *, Y=None, stream=None):
-    """``Y[M, N] = bf16(X . W'^T)`` from bf16 ``X[M, K]`` and the GPU-layout weights."""
+def w4_gemm_workspace_bytes(M: int, K: int, N: int) -> int:
+    """Device workspace bytes a product of this shape needs (0 for most)."""
+    return int(lib().w4_gemm_workspace_bytes(M, K, N))
+
+
+def w4a16_gemm(X: torch.Tensor, wq: torch.Tensor, sz: torch.Tensor, G: int, *, Y=None, workspace=None,
+               stream=None):
+    """``Y[M, N] = bf16(X . W'^T)`` from bf16 ``X[M, K]`` and the GPU-layout weights.
+
+    ``workspace``: a device tensor of at least ``w4_gemm_workspace_bytes(M, K, N)``
+    bytes; allocated here when omitted and the shape needs one."""
     M, K = X.shape
     N = wq.shape[0]
     dev = X.device
     Y = _empty((M, N), torch.bfloat16, dev) if Y is None else Y
+    ws, ws_bytes = _workspace(M, K, N, dev, workspace, stream)
     rc = lib().w4a16_gemm(_dev(X, "X", torch.bfloat16), M, K, _dev(wq, "wq"), _dev(sz, "sz"), N, G,
-                          _dev(Y, "Y", torch.bfloat16), _stream(dev, stream))
+                          _dev(Y, "Y", torch.bfloat16), ws, ws_bytes, _stream(dev, stream))
     _check("w4a16_gemm", rc)
     return Y
 
 
 def w4a8_gemm(X: torch.Tensor, wq: torch.Tensor, sz: torch.Tensor, G: int, *, Y=None, xq=None, xscale=None,
-              stream=None):
+              workspace=None, stream=None):
     """W4A8: per-row E4M3 of ``X`` then ``Y = bf16(xscale * Xq . W'^T)``; returns (Y, xq, xscale)."""
     M, K = X.shape
     N = wq.shape[0]
@@ -218,8 +245,9 @@ def w4a8_gemm(X: torch.Tensor, wq: torch.Tensor, sz: torch.Tensor, G: int, *, Y=
     Y = _empty((M, N), torch.bfloat16, dev) if Y is None else Y
     xq = _empty((M, K), torch.uint8, dev) if xq is None else xq
     xscale = _empty((M,), torch.float32, dev) if xscale is None else xscale
+    ws, ws_bytes = _workspace(M, K, N, dev, workspace, stream)
     rc = lib().w4a8_gemm(_dev(X, "X", torch.bfloat16), M, K, _dev(wq, "wq"), _dev(sz, "sz"), N, G,
                          _dev(Y, "Y", torch.bfloat16), _dev(xq, "xq"), _dev(xscale, "xscale", torch.float32),
-                         _stream(dev, stream))
+                         ws, ws_bytes, _stream(dev, stream))
     _check("w4a8_gemm", rc)
     return Y, xq, xscale

@@ -102,7 +102,7 @@ int quantize_common(const char* fn, const float* W, int64_t N, int64_t K, int G,
 }
 
 int mul_common(const char* fn, const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq,
-               const uint32_t* sz, int64_t N, int G, uint16_t* Y) {
+               const uint32_t* sz, int64_t N, int G, uint16_t* Y, void* workspace, size_t workspace_bytes) {
     W4_TRY(check_group(fn, N, K, G));
     if (M < 0) return fail(W4_EINVAL, "%s: M = %lld must be >= 0", fn, static_cast<long long>(M));
     if (M == 0 || N == 0) return W4_OK;
@@ -110,7 +110,23 @@ int mul_common(const char* fn, const uint16_t* X, int64_t M, int64_t K, const ui
     W4_REQUIRE_PTR(fn, wq);
     W4_REQUIRE_PTR(fn, sz);
     W4_REQUIRE_PTR(fn, Y);
+    const size_t need = M <= w4::kSkinnyMaxM ? 0 : w4::gemm_workspace_bytes(M, K, N);
+    if (need > 0) {
+        if (!workspace)
+            return fail(W4_EINVAL, "%s: this shape needs a workspace of %zu bytes (w4_gemm_workspace_bytes)", fn, need);
+        if (workspace_bytes < need)
+            return fail(W4_EINVAL, "%s: workspace of %zu bytes, this shape needs %zu", fn, workspace_bytes, need);
+        if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+            return fail(W4_EINVAL, "%s: workspace is not 16-byte aligned", fn);
+    }
     return W4_OK;
+}
+
+// the tiled-GEMM launch of a product, with the K split that its workspace was sized for
+w4::MulParams with_split(w4::MulParams p, void* workspace) {
+    p.splits = w4::gemm_split_k(p.M, p.K, p.N);
+    p.ws = p.splits > 1 ? static_cast<float*>(workspace) : nullptr;
+    return p;
 }
 
 }  // namespace
@@ -159,20 +175,26 @@ int w4_quantize_rows_e4m3(const uint16_t* X, int64_t M, int64_t K, uint8_t* xq, 
     return hip_status(w4::launch_rowquant(p, stream), fn);
 }
 
+size_t w4_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+    if (M <= w4::kSkinnyMaxM || K <= 0 || N <= 0) return 0;
+    return w4::gemm_workspace_bytes(M, K, N);
+}
+
 int w4a16_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const uint32_t* sz, int64_t N,
-               int G, uint16_t* Y, hipStream_t stream) {
+               int G, uint16_t* Y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     const char* fn = "w4a16_gemm";
-    W4_TRY(mul_common(fn, X, M, K, wq, sz, N, G, Y));
+    W4_TRY(mul_common(fn, X, M, K, wq, sz, N, G, Y, workspace, workspace_bytes));
     if (M == 0 || N == 0) return W4_OK;
     w4::MulParams p{X, nullptr, M, K, N, G, wq, sz, Y, false};
     if (M <= w4::kSkinnyMaxM) return hip_status(w4::launch_skinny(p, stream), fn);
-    return hip_status(w4::launch_gemm(p, stream), fn);
+    return hip_status(w4::launch_gemm(with_split(p, workspace), stream), fn);
 }
 
 int w4a8_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const uint32_t* sz, int64_t N,
-              int G, uint16_t* Y, uint8_t* xq, float* xscale, hipStream_t stream) {
+              int G, uint16_t* Y, uint8_t* xq, float* xscale, void* workspace, size_t workspace_bytes,
+              hipStream_t stream) {
     const char* fn = "w4a8_gemm";
-    W4_TRY(mul_common(fn, X, M, K, wq, sz, N, G, Y));
+    W4_TRY(mul_common(fn, X, M, K, wq, sz, N, G, Y, workspace, workspace_bytes));
     if (M == 0 || N == 0) return W4_OK;
     W4_REQUIRE_PTR(fn, xq);
     if (!xscale) return fail(W4_EINVAL, "%s: xscale is NULL", fn);
@@ -185,7 +207,7 @@ int w4a8_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const
     W4_TRY(hip_status(w4::launch_rowquant(rq, stream), fn));
     w4::MulParams p{xq, xscale, M, K, N, G, wq, sz, Y, true};
     if (M <= w4::kSkinnyMaxM) return hip_status(w4::launch_skinny(p, stream), fn);
-    return hip_status(w4::launch_gemm(p, stream), fn);
+    return hip_status(w4::launch_gemm(with_split(p, workspace), stream), fn);
 }
 
 const char* w4_status_string(int status) {
@@ -200,6 +222,6 @@ const char* w4_status_string(int status) {
 
 const char* w4_last_error(void) { return g_last_error; }
 
-int w4_abi_version(void) { return 1; }
+int w4_abi_version(void) { return 2; }
 
 }  // extern "C"

@@ -209,7 +209,10 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm256_kernel(MulParams p) {
     const int64_t m_base = static_cast<int64_t>(blockIdx.y) * BM;
     const int64_t n_base = static_cast<int64_t>(blockIdx.x) * BN;
     const int64_t M = p.M, N = p.N, K = p.K;
-    const int KT = static_cast<int>(K / BK);
+    // this workgroup's K steps: split blockIdx.z of p.splits (all when 1)
+    const int KT_all = static_cast<int>(K / BK);
+    const int kb = static_cast<int>(blockIdx.z) * KT_all / p.splits;
+    const int KT = (static_cast<int>(blockIdx.z) + 1) * KT_all / p.splits - kb;
     const int g_shift = __builtin_ctz(static_cast<unsigned>(p.G));   // G is a power of two
     const uint32_t bias = opaque_vgpr(kBf16Bias128x2);
 
@@ -252,7 +255,7 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm256_kernel(MulParams p) {
     // and SZN scale/zero loads, issued one item at a time.
     constexpr int NLOAD = ALD + CPT / 4 + SZN;
     auto issue_load_item = [&](int kt, Regs& r, int it) {
-        kt = kt < KT ? kt : KT - 1;         // past the end: reload the last step (never used)
+        kt = (kt < KT ? kt : KT - 1) + kb;  // past the end: reload the last step (never used)
         if (it < ALD) {
             const u32x4_t t = arow[static_cast<int64_t>(kt) * (BK * XB / 16) + it];
             r.a[it] = make_uint4(t[0], t[1], t[2], t[3]);
@@ -415,8 +418,12 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm256_kernel(MulParams p) {
                 const int64_t row = m_base + wm * TM + i * 32 + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
                 if (row < M && col < N) {
                     float y = acc[i][j][r];
-                    if constexpr (XF8) y *= p.xscale[row];
-                    p.Y[row * N + col] = float_to_bf16_bits(y);
+                    if (p.ws) {
+                        p.ws[(blockIdx.z * M + row) * N + col] = y;   // partial sum of a K split
+                    } else {
+                        if constexpr (XF8) y *= p.xscale[row];
+                        p.Y[row * N + col] = float_to_bf16_bits(y);
+                    }
                 }
             }
         }
@@ -470,7 +477,10 @@ __global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
     const int64_t m_base = static_cast<int64_t>(blockIdx.y) * BM;
     const int64_t n_base = static_cast<int64_t>(blockIdx.x) * BN;
     const int64_t M = p.M, N = p.N, K = p.K;
-    const int KT = static_cast<int>(K / BK);
+    // this workgroup's K steps: split blockIdx.z of p.splits (all when 1)
+    const int KT_all = static_cast<int>(K / BK);
+    const int kb = static_cast<int>(blockIdx.z) * KT_all / p.splits;
+    const int KT = (static_cast<int>(blockIdx.z) + 1) * KT_all / p.splits - kb;
     const int g_shift = __builtin_ctz(static_cast<unsigned>(p.G));
 
     float16_t acc[FI][FJ];
@@ -491,7 +501,7 @@ __global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
     const int64_t a_last = M - 1;
     const uint16_t* a_src = static_cast<const uint16_t*>(p.X) + (((lane & 7) ^ (lane >> 3)) * 8);
     auto dma_item = [&](int kt, uint16_t* stage, int it) {
-        kt = kt < KT ? kt : KT - 1;
+        kt = (kt < KT ? kt : KT - 1) + kb;
         int64_t m = a_m + 8 * it;
         m = m < a_last ? m : a_last;
         __builtin_amdgcn_global_load_lds((const global_u32*)(const void*)(a_src + m * K + static_cast<int64_t>(kt) * BK),
@@ -507,7 +517,7 @@ __global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
         uint32_t s[SZN];
     };
     auto load_item = [&](int kt, Regs& r, int it) {
-        kt = kt < KT ? kt : KT - 1;
+        kt = (kt < KT ? kt : KT - 1) + kb;
         if (it < CPT / 4) r.q[it] = *reinterpret_cast<const u32x4_t*>(brow.tile_ptr(static_cast<int64_t>(kt) * (BK / 32) + it));
         else r.s[it - CPT / 4] = brow.group((kt * BK + 32 * (it - CPT / 4)) >> g_shift);
     };
@@ -621,12 +631,50 @@ __global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t row = m_base + wm * 128 + i * 32 + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
-                if (row < M && col < N) p.Y[row * N + col] = float_to_bf16_bits(acc[i][j][r]);
+                if (row < M && col < N) {
+                    if (p.ws) p.ws[(blockIdx.z * M + row) * N + col] = acc[i][j][r];   // partial sum of a K split
+                    else p.Y[row * N + col] = float_to_bf16_bits(acc[i][j][r]);
+                }
             }
         }
 }
 
+// Sum of the K-split partials: element i of Y is the fp32 sum of ws[z][i]
+// in split order z = 0, 1, ..., times the row scale (W4A8), rounded to bf16.
+// Each thread takes four elements 256 apart, so every load is coalesced.
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(MulParams p) {
+    const int64_t MN = p.M * p.N;
+    const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 1024 + threadIdx.x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int64_t i = i0 + 256 * e;
+        if (i >= MN) break;
+        float y = 0.0f;
+        for (int z = 0; z < p.splits; ++z) y += p.ws[z * MN + i];
+        if (p.x_fp8) y *= p.xscale[i / p.N];
+        p.Y[i] = float_to_bf16_bits(y);
+    }
+}
+
 }  // namespace
+
+// A product with fewer 256 x 256 output tiles than half the compute units
+// splits K across workgroups: as many splits as keep about one workgroup per
+// compute unit, at most 16, each with at least 8 K steps of 64.
+int gemm_split_k(int64_t M, int64_t K, int64_t N) {
+    if (M < 128 || K % big::BK != 0 || N <= 0) return 1;
+    const int64_t tiles = ((N + big::BN - 1) / big::BN) * ((M + big::BM - 1) / big::BM);
+    if (tiles >= 128) return 1;
+    int64_t s = 256 / tiles;
+    if (s > (K / big::BK) / 8) s = (K / big::BK) / 8;
+    if (s > 16) s = 16;
+    return s > 1 ? static_cast<int>(s) : 1;
+}
+
+size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+    const int s = gemm_split_k(M, K, N);
+    return s > 1 ? static_cast<size_t>(s) * static_cast<size_t>(M) * static_cast<size_t>(N) * sizeof(float) : 0;
+}
 
 // wave grid of the register-path kernel (used for E4M3 activations): 4 x 2
 // waves of 64 x 128 outputs measured faster than 2 x 2 of 128 x 128
@@ -639,17 +687,28 @@ constexpr int kBigWM = W4_BIG_WM, kBigWN = W4_BIG_WN;
 hipError_t launch_gemm(const MulParams& p, hipStream_t stream) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
     if (p.M >= 128 && p.K % big::BK == 0) {
+        // the split count (1 or the one the workspace was sized for) must
+        // leave every split at least one K step
+        if (p.splits < 1 || p.splits > p.K / big::BK || (p.splits > 1 && !p.ws)) return hipErrorInvalidValue;
         const dim3 grid(static_cast<unsigned>((p.N + big::BN - 1) / big::BN),
-                        static_cast<unsigned>((p.M + big::BM - 1) / big::BM));
+                        static_cast<unsigned>((p.M + big::BM - 1) / big::BM), static_cast<unsigned>(p.splits));
+        MulParams q = p;
+        if (q.splits == 1) q.ws = nullptr;
 #ifndef W4_DMA
 #define W4_DMA 1
 #endif
-        if (p.x_fp8)
-            hipLaunchKernelGGL((gemm256_kernel<kBigWM, kBigWN, true>), grid, dim3(64 * kBigWM * kBigWN), 0, stream, p);
+        if (q.x_fp8)
+            hipLaunchKernelGGL((gemm256_kernel<kBigWM, kBigWN, true>), grid, dim3(64 * kBigWM * kBigWN), 0, stream, q);
         else if (W4_DMA)
-            hipLaunchKernelGGL(gemm256_dma_kernel, grid, dim3(dma::NT), 0, stream, p);
+            hipLaunchKernelGGL(gemm256_dma_kernel, grid, dim3(dma::NT), 0, stream, q);
         else
-            hipLaunchKernelGGL((gemm256_kernel<kBigWM, kBigWN, false>), grid, dim3(64 * kBigWM * kBigWN), 0, stream, p);
+            hipLaunchKernelGGL((gemm256_kernel<kBigWM, kBigWN, false>), grid, dim3(64 * kBigWM * kBigWN), 0, stream, q);
+        if (q.splits > 1) {
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            const int64_t blocks = (q.M * q.N + 1023) / 1024;
+            hipLaunchKernelGGL(splitk_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, q);
+        }
         return hipGetLastError();
     }
     const dim3 grid(static_cast<unsigned>((p.N + small::BN - 1) / small::BN),

@@ -58,6 +58,11 @@ struct MulParams {
     // writes the E4M3 codes and row scales here
     uint8_t* xq_out = nullptr;
     float* xscale_out = nullptr;
+    // K split across workgroups (tiled GEMM only): splits > 1 writes fp32
+    // partial sums to ws [splits][M][N] and a second kernel adds them in
+    // split order, applies the row scale and rounds to bf16
+    int splits = 1;
+    float* ws = nullptr;
 };
 // Which kernel runs a product: M <= kSkinnyMaxM: the weight-streaming
 // kernels (dot form for one or two rows, MFMA form above); larger M: the
@@ -71,5 +76,9 @@ hipError_t launch_skinny(const MulParams& p, hipStream_t stream);
 // (one or two rows whose bf16 activations fit the kernel's LDS staging)
 bool skinny_quantizes_rows(int64_t M, int64_t K);
 hipError_t launch_gemm(const MulParams& p, hipStream_t stream);
+// K splits the tiled GEMM uses for an [M, K] x [N, K] product (1: none) and
+// the fp32 workspace bytes they need
+int gemm_split_k(int64_t M, int64_t K, int64_t N);
+size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
 
 }  // namespace w4
