@@ -236,10 +236,12 @@ def main():
                 y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
                 xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
                 xs = torch.empty((M,), dtype=torch.float32, device=dev)
+                # split-K partial sums for shapes with few output tiles
+                ws = torch.empty((max(w4.w4_gemm_workspace_bytes(M, K, N), 16),), dtype=torch.uint8, device=dev)
 
-                def run(x=x, y=y, xq=xq, xs=xs, copies=copies):
+                def run(x=x, y=y, xq=xq, xs=xs, ws=ws, copies=copies):
                     for c in copies:
-                        w4.w4a8_gemm(x, c["wq"], c["sz"], 128, Y=y, xq=xq, xscale=xs)
+                        w4.w4a8_gemm(x, c["wq"], c["sz"], 128, Y=y, xq=xq, xscale=xs, workspace=ws)
                 ms = timer.time(run, 10, 2) / len(copies)
                 by = mul_bytes(M, N, K, 128)
                 fl = 2.0 * M * N * K
