@@ -641,16 +641,35 @@ __global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
 
 // Sum of the K-split partials: element i of Y is the fp32 sum of ws[z][i]
 // in split order z = 0, 1, ..., times the row scale (W4A8), rounded to bf16.
-// Each thread takes four elements 256 apart, so every load is coalesced.
+// With N a multiple of 4 a thread takes four consecutive elements of one row
+// (16-byte loads); otherwise four elements 256 apart (4-byte loads).  Either
+// way consecutive lanes read consecutive addresses.
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(MulParams p) {
     const int64_t MN = p.M * p.N;
+    if (p.N % 4 == 0) {
+        const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+        if (i >= MN) return;
+        float4 y = *reinterpret_cast<const float4*>(p.ws + i);
+        for (int z = 1; z < p.splits; ++z) {
+            const float4 v = *reinterpret_cast<const float4*>(p.ws + z * MN + i);
+            y.x += v.x; y.y += v.y; y.z += v.z; y.w += v.w;
+        }
+        if (p.x_fp8) {
+            const float r = p.xscale[i / p.N];
+            y.x *= r; y.y *= r; y.z *= r; y.w *= r;
+        }
+        *reinterpret_cast<uint2*>(p.Y + i) = make_uint2(
+            float_to_bf16_bits(y.x) | (static_cast<uint32_t>(float_to_bf16_bits(y.y)) << 16),
+            float_to_bf16_bits(y.z) | (static_cast<uint32_t>(float_to_bf16_bits(y.w)) << 16));
+        return;
+    }
     const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 1024 + threadIdx.x;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int64_t i = i0 + 256 * e;
         if (i >= MN) break;
-        float y = 0.0f;
-        for (int z = 0; z < p.splits; ++z) y += p.ws[z * MN + i];
+        float y = p.ws[i];
+        for (int z = 1; z < p.splits; ++z) y += p.ws[z * MN + i];
         if (p.x_fp8) y *= p.xscale[i / p.N];
         p.Y[i] = float_to_bf16_bits(y);
     }

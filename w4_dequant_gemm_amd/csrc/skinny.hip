@@ -502,13 +502,48 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
             }
         __syncthreads();
     }
-    while (true) {
+#ifndef W4_DOTL_PIPE
+#define W4_DOTL_PIPE 1
+#endif
+    if constexpr (DOTL && W4_DOTL_PIPE) {
+        // Rolling pipeline: each buffer is refilled with the step kDepth
+        // ahead as soon as it has been multiplied, so kDepth steps stay in
+        // flight.  While every refill is a real step the loads are
+        // unconditional (each multiplication waits only for its own step);
+        // the last two rounds guard them.
+        const int n = (KS - wave + wk - 1) / wk;      // steps of this wave
+        int i = 0;
+        for (; i + 2 * kDepth <= n; i += kDepth) {
+#pragma unroll
+            for (int d = 0; d < kDepth; ++d) {
+                compute(bq[d], aq[d], step + d * wk);
+                load_b(step + (kDepth + d) * wk, bq[d]);
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            step += kDepth * wk;
+        }
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) {
+            if (i + d < n) compute(bq[d], aq[d], step + d * wk);
+            if (i + kDepth + d < n) load_b(step + (kDepth + d) * wk, bq[d]);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        step += kDepth * wk;
+        i += kDepth;
 #pragma unroll
         for (int d = 0; d < kDepth; ++d)
-            if (step + d * wk < KS) compute(bq[d], aq[d], step + d * wk);
-        step += kDepth * wk;
-        if (step >= KS) break;
-        issue(step);
+            if (i + d < n) compute(bq[d], aq[d], step + d * wk);
+    } else {
+        while (true) {
+#pragma unroll
+            for (int d = 0; d < kDepth; ++d)
+                if (step + d * wk < KS) compute(bq[d], aq[d], step + d * wk);
+            step += kDepth * wk;
+            if (step >= KS) break;
+            issue(step);
+        }
     }
 
     if constexpr (DOT) {
@@ -643,7 +678,8 @@ hipError_t launch_skinny(const MulParams& p, hipStream_t stream) {
 #endif
     const bool dotm = p.M <= kDotMaxM;
     const int mb = p.M <= 16 ? 1 : (p.M <= 32 ? 2 : 4);
-    int fj = dotm ? W4_DOT_FJMAX : (mb == 4 ? 2 : W4_SK_FJMAX);
+    // two rows with four column blocks would not fit 128 registers a lane
+    int fj = dotm ? (p.M == 2 && W4_DOT_FJMAX > 2 ? 2 : W4_DOT_FJMAX) : (mb == 4 ? 2 : W4_SK_FJMAX);
     const int minblk = dotm ? W4_DOT_MINBLK : W4_SK_MINBLK;
     while (fj > 1 && (p.N + 16 * fj - 1) / (16 * fj) < minblk) fj /= 2;
     const int64_t blocks = (p.N + 16 * fj - 1) / (16 * fj);
@@ -669,13 +705,15 @@ hipError_t launch_skinny(const MulParams& p, hipStream_t stream) {
             constexpr int MT = decltype(mt)::value;
             constexpr bool X8 = decltype(xf8)::value;
             if (X8 && p.xq_out) {
-                if (fj == 4) return launch_skinny_c<MT, 4, true, kDotLdsQ>(p, w, stream);
-                if (fj == 2) return launch_skinny_c<MT, 2, true, kDotLdsQ>(p, w, stream);
+                if constexpr (MT == 1)
+                    if (fj == 4) return launch_skinny_c<MT, 4, true, kDotLdsQ>(p, w, stream);
+                if (fj >= 2) return launch_skinny_c<MT, 2, true, kDotLdsQ>(p, w, stream);
                 return launch_skinny_c<MT, 1, true, kDotLdsQ>(p, w, stream);
             }
             if (lds_x) {
-                if (fj == 4) return launch_skinny_c<MT, 4, X8, kDotLds>(p, w, stream);
-                if (fj == 2) return launch_skinny_c<MT, 2, X8, kDotLds>(p, w, stream);
+                if constexpr (MT == 1)
+                    if (fj == 4) return launch_skinny_c<MT, 4, X8, kDotLds>(p, w, stream);
+                if (fj >= 2) return launch_skinny_c<MT, 2, X8, kDotLds>(p, w, stream);
                 return launch_skinny_c<MT, 1, X8, kDotLds>(p, w, stream);
             }
             if (fj == 4) return launch_skinny_c<MT, 4, X8, kDot>(p, w, stream);
