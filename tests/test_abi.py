@@ -87,13 +87,17 @@ def test_host_validation(lib):
 
 
 def test_gemm_workspace_sizes_and_checks(lib):
-    # few 256 x 256 output tiles: K is split across workgroups, the fp32
-    # partial sums need splits * M * N * 4 bytes; otherwise nothing
+    # 256 x 256 output tiles whose K is split across workgroups need one
+    # fp32 partial tile (256 KB) per split: every tile when there are few,
+    # else the tiles of the last partial round over 256 compute units
     import w4_dequant_gemm_amd as w4
     ws = lib.w4_gemm_workspace_bytes
-    assert ws(256, 15360, 3840) == 16 * 256 * 3840 * 4      # 15 tiles: 16 splits of 15 K steps
-    assert ws(256, 3840, 15360) == 4 * 256 * 15360 * 4      # 60 tiles: 4 splits
-    assert ws(2048, 8192, 28672) == 0                        # 896 tiles fill the GPU
+    tile = 256 * 256 * 4
+    assert ws(256, 15360, 3840) == 15 * 16 * tile           # 15 tiles: 16 splits of 15 K steps
+    assert ws(256, 3840, 15360) == 60 * 4 * tile            # 60 tiles: 4 splits
+    assert ws(2048, 8192, 28672) == 128 * 2 * tile          # 896 tiles: the last 128 in halves
+    assert ws(2048, 8192, 32768) == 0                        # 1024 tiles: four full rounds
+    assert ws(300, 4096, 33000) == 2 * 8 * tile              # 258 tiles: the last 2 in eighths
     assert ws(64, 15360, 3840) == 0                          # weight-streaming kernel
     assert ws(256, 96, 3840) == 0                            # K not a multiple of 64: 128 x 128 tiles
     assert ws(256, 512, 256) == 0                            # too few K steps to split

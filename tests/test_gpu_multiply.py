@@ -262,7 +262,7 @@ def test_split_k_products():
     pk, G = prepack_dev(q)
     M, K, N = 300, 4096, 200
     need = w4.w4_gemm_workspace_bytes(M, K, N)
-    assert need == 8 * M * N * 4
+    assert need == 2 * 8 * 256 * 256 * 4             # 2 tiles, each in 8 K ranges
     Xb = synth.to_bf16_bits(synth.normal_matrix(53, M, K))
     ws = torch.full((need // 4 + 16,), float("nan"), dtype=torch.float32, device="cuda")
     for kind in ("w4a16", "w4a8"):
@@ -286,6 +286,40 @@ def test_split_k_products():
     # too small a workspace is an error, not a slower path
     with pytest.raises(w4.W4Error):
         w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G, workspace=ws[:16])
+
+
+def test_split_last_round_products():
+    # 258 output tiles over 256 compute units: the first 256 tiles whole, the
+    # last two (rows 256..299, columns 32512..32999, ragged in both) in eight
+    # K ranges each; sampled outputs cover both kinds of tile
+    require_gpu()
+    import torch
+    import w4_dequant_gemm_amd as w4
+    M, K, N = 300, 4096, 33000
+    W = synth.normal_matrix(54, N, K, 0.02)
+    q = oracle.quantize(W, 128, "asym")
+    del W
+    pk, G = prepack_dev(q)
+    Xb = synth.to_bf16_bits(synth.normal_matrix(55, M, K))
+    rng = np.random.default_rng(56)
+    rows = np.concatenate([np.arange(0, 8), np.arange(250, 300)]).astype(np.int64)
+    cols = np.unique(np.concatenate([rng.choice(32512, 256, replace=False), np.arange(32512, N, 2)])).astype(np.int64)
+    for kind in ("w4a16", "w4a8"):
+        print(f"[split last round] {kind} M={M} K={K} N={N}", flush=True)
+        if kind == "w4a16":
+            Y = w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G)
+            want = oracle.gemm_ref(oracle.bf16_bits_to_f64(Xb), q["packed"], q["scale"], q["zero"], G, "asym",
+                                   rows=rows, cols=cols)
+        else:
+            Y, _, _ = w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G)
+            want, _, _ = oracle.w4a8_ref(Xb, q["packed"], q["scale"], q["zero"], G, "asym", rows=rows, cols=cols)
+        torch.cuda.synchronize()
+        got = Y.float().cpu().numpy()[np.ix_(rows, cols)]
+        err = oracle.rel_error(want, got)
+        assert err <= REL_TOL, f"{kind}: relative error {err:.3e}"
+        tail = np.ix_(rows >= 256, cols >= 32512)
+        err_t = oracle.rel_error(want[tail], got[tail])
+        assert err_t <= REL_TOL, f"{kind} split tiles: relative error {err_t:.3e}"
 
 
 def test_group_size_64():

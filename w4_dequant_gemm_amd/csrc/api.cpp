@@ -124,8 +124,10 @@ int mul_common(const char* fn, const uint16_t* X, int64_t M, int64_t K, const ui
 
 // the tiled-GEMM launch of a product, with the K split that its workspace was sized for
 w4::MulParams with_split(w4::MulParams p, void* workspace) {
-    p.splits = w4::gemm_split_k(p.M, p.K, p.N);
-    p.ws = p.splits > 1 ? static_cast<float*>(workspace) : nullptr;
+    const w4::GemmSplit g = w4::gemm_split(p.M, p.K, p.N);
+    p.splits = g.splits;
+    p.split_t0 = g.t0;
+    p.ws = g.splits > 1 ? static_cast<float*>(workspace) : nullptr;
     return p;
 }
 

@@ -187,6 +187,40 @@ constexpr int STAGE = 256 * BK;          // bf16 elements per operand and stage
 __device__ __forceinline__ int lds_off(int row, int c) {
     return row * BK + ((c ^ (W4_SWZ ? (row & 7) : ((row >> 1) & 7))) << 3);
 }
+
+// The work of one workgroup of the 256 x 256 kernels (1-D grid): workgroup
+// b < split_t0 computes tile b whole; the rest compute K range z of tile
+// split_t0 + (b - split_t0) / splits, z = (b - split_t0) % splits.  Tiles are
+// row-major over the tile grid, so the 8 row tiles of a column tile land on
+// one XCD (workgroups go round-robin over the 8 XCDs; 112 column tiles).
+struct TileJob {
+    int64_t m_base, n_base;
+    int kb, KT;        // first K step and number of K steps
+    int64_t part;      // partial-tile index in ws, or -1: write Y
+};
+__device__ __forceinline__ TileJob tile_job(const MulParams& p) {
+    const int64_t b = blockIdx.x;
+    const int64_t nt = (p.N + BN - 1) / BN;
+    const int KT_all = static_cast<int>(p.K / BK);
+    TileJob t;
+    int64_t tile;
+    if (b < p.split_t0) {
+        tile = b;
+        t.kb = 0;
+        t.KT = KT_all;
+        t.part = -1;
+    } else {
+        const int64_t j = (b - p.split_t0) / p.splits;
+        const int z = static_cast<int>((b - p.split_t0) % p.splits);
+        tile = p.split_t0 + j;
+        t.kb = z * KT_all / p.splits;
+        t.KT = (z + 1) * KT_all / p.splits - t.kb;
+        t.part = j * p.splits + z;
+    }
+    t.m_base = (tile / nt) * BM;
+    t.n_base = (tile % nt) * BN;
+    return t;
+}
 }  // namespace big
 
 template <int WM, int WN, bool XF8>
@@ -206,13 +240,10 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm256_kernel(MulParams p) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
-    const int64_t m_base = static_cast<int64_t>(blockIdx.y) * BM;
-    const int64_t n_base = static_cast<int64_t>(blockIdx.x) * BN;
+    const TileJob job = tile_job(p);
+    const int64_t m_base = job.m_base, n_base = job.n_base;
     const int64_t M = p.M, N = p.N, K = p.K;
-    // this workgroup's K steps: split blockIdx.z of p.splits (all when 1)
-    const int KT_all = static_cast<int>(K / BK);
-    const int kb = static_cast<int>(blockIdx.z) * KT_all / p.splits;
-    const int KT = (static_cast<int>(blockIdx.z) + 1) * KT_all / p.splits - kb;
+    const int kb = job.kb, KT = job.KT;      // this workgroup's K steps
     const int g_shift = __builtin_ctz(static_cast<unsigned>(p.G));   // G is a power of two
     const uint32_t bias = opaque_vgpr(kBf16Bias128x2);
 
@@ -412,18 +443,18 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm256_kernel(MulParams p) {
     for (int i = 0; i < FI; ++i)
 #pragma unroll
         for (int j = 0; j < FJ; ++j) {
-            const int64_t col = n_base + wn * TN + j * 32 + (lane & 31);
+            const int lc = wn * TN + j * 32 + (lane & 31);
+            const int64_t col = n_base + lc;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int64_t row = m_base + wm * TM + i * 32 + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
-                if (row < M && col < N) {
+                const int lr = wm * TM + i * 32 + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
+                const int64_t row = m_base + lr;
+                if (job.part >= 0) {
+                    p.ws[job.part * (BM * BN) + lr * BN + lc] = acc[i][j][r];   // partial tile of a K split
+                } else if (row < M && col < N) {
                     float y = acc[i][j][r];
-                    if (p.ws) {
-                        p.ws[(blockIdx.z * M + row) * N + col] = y;   // partial sum of a K split
-                    } else {
-                        if constexpr (XF8) y *= p.xscale[row];
-                        p.Y[row * N + col] = float_to_bf16_bits(y);
-                    }
+                    if constexpr (XF8) y *= p.xscale[row];
+                    p.Y[row * N + col] = float_to_bf16_bits(y);
                 }
             }
         }
@@ -474,13 +505,10 @@ __global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
-    const int64_t m_base = static_cast<int64_t>(blockIdx.y) * BM;
-    const int64_t n_base = static_cast<int64_t>(blockIdx.x) * BN;
+    const big::TileJob job = big::tile_job(p);
+    const int64_t m_base = job.m_base, n_base = job.n_base;
     const int64_t M = p.M, N = p.N, K = p.K;
-    // this workgroup's K steps: split blockIdx.z of p.splits (all when 1)
-    const int KT_all = static_cast<int>(K / BK);
-    const int kb = static_cast<int>(blockIdx.z) * KT_all / p.splits;
-    const int KT = (static_cast<int>(blockIdx.z) + 1) * KT_all / p.splits - kb;
+    const int kb = job.kb, KT = job.KT;      // this workgroup's K steps
     const int g_shift = __builtin_ctz(static_cast<unsigned>(p.G));
 
     float16_t acc[FI][FJ];
@@ -627,72 +655,85 @@ __global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
     for (int i = 0; i < FI; ++i)
 #pragma unroll
         for (int j = 0; j < FJ; ++j) {
-            const int64_t col = n_base + wn * 128 + j * 32 + (lane & 31);
+            const int lc = wn * 128 + j * 32 + (lane & 31);
+            const int64_t col = n_base + lc;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int64_t row = m_base + wm * 128 + i * 32 + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
-                if (row < M && col < N) {
-                    if (p.ws) p.ws[(blockIdx.z * M + row) * N + col] = acc[i][j][r];   // partial sum of a K split
-                    else p.Y[row * N + col] = float_to_bf16_bits(acc[i][j][r]);
-                }
+                const int lr = wm * 128 + i * 32 + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
+                const int64_t row = m_base + lr;
+                if (job.part >= 0) p.ws[job.part * (BM * BN) + lr * BN + lc] = acc[i][j][r];   // partial tile of a K split
+                else if (row < M && col < N) p.Y[row * N + col] = float_to_bf16_bits(acc[i][j][r]);
             }
         }
 }
 
-// Sum of the K-split partials: element i of Y is the fp32 sum of ws[z][i]
-// in split order z = 0, 1, ..., times the row scale (W4A8), rounded to bf16.
-// With N a multiple of 4 a thread takes four consecutive elements of one row
-// (16-byte loads); otherwise four elements 256 apart (4-byte loads).  Either
-// way consecutive lanes read consecutive addresses.
+// Sum of the K-split partial tiles: output (r, c) of split tile j is the
+// fp32 sum of its `splits` partials in split order, times the row scale
+// (W4A8), rounded to bf16.  A thread takes four consecutive columns of one
+// tile row (16-byte loads; consecutive lanes read consecutive addresses).
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(MulParams p) {
-    const int64_t MN = p.M * p.N;
-    if (p.N % 4 == 0) {
-        const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
-        if (i >= MN) return;
-        float4 y = *reinterpret_cast<const float4*>(p.ws + i);
-        for (int z = 1; z < p.splits; ++z) {
-            const float4 v = *reinterpret_cast<const float4*>(p.ws + z * MN + i);
-            y.x += v.x; y.y += v.y; y.z += v.z; y.w += v.w;
-        }
-        if (p.x_fp8) {
-            const float r = p.xscale[i / p.N];
-            y.x *= r; y.y *= r; y.z *= r; y.w *= r;
-        }
-        *reinterpret_cast<uint2*>(p.Y + i) = make_uint2(
-            float_to_bf16_bits(y.x) | (static_cast<uint32_t>(float_to_bf16_bits(y.y)) << 16),
-            float_to_bf16_bits(y.z) | (static_cast<uint32_t>(float_to_bf16_bits(y.w)) << 16));
-        return;
+    using namespace big;
+    const int64_t e4 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;   // element of the split tiles
+    const int64_t j = e4 / (BM * BN);
+    const int lr = static_cast<int>((e4 % (BM * BN)) / BN), lc = static_cast<int>(e4 % BN);
+    const int64_t nt = (p.N + BN - 1) / BN;
+    const int64_t tile = p.split_t0 + j;
+    const int64_t row = (tile / nt) * BM + lr, col = (tile % nt) * BN + lc;
+    if (row >= p.M || col >= p.N) return;
+    const float* src = p.ws + j * p.splits * (BM * BN) + lr * BN + lc;
+    float4 y = *reinterpret_cast<const float4*>(src);
+    for (int z = 1; z < p.splits; ++z) {
+        const float4 v = *reinterpret_cast<const float4*>(src + z * (BM * BN));
+        y.x += v.x; y.y += v.y; y.z += v.z; y.w += v.w;
     }
-    const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 1024 + threadIdx.x;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int64_t i = i0 + 256 * e;
-        if (i >= MN) break;
-        float y = p.ws[i];
-        for (int z = 1; z < p.splits; ++z) y += p.ws[z * MN + i];
-        if (p.x_fp8) y *= p.xscale[i / p.N];
-        p.Y[i] = float_to_bf16_bits(y);
+    if (p.x_fp8) {
+        const float r = p.xscale[row];
+        y.x *= r; y.y *= r; y.z *= r; y.w *= r;
+    }
+    const float yv[4] = {y.x, y.y, y.z, y.w};
+    uint16_t* dst = p.Y + row * p.N + col;
+    if (col + 3 < p.N && p.N % 4 == 0) {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(
+            float_to_bf16_bits(yv[0]) | (static_cast<uint32_t>(float_to_bf16_bits(yv[1])) << 16),
+            float_to_bf16_bits(yv[2]) | (static_cast<uint32_t>(float_to_bf16_bits(yv[3])) << 16));
+    } else {
+        for (int e = 0; e < 4 && col + e < p.N; ++e) dst[e] = float_to_bf16_bits(yv[e]);
     }
 }
 
 }  // namespace
 
-// A product with fewer 256 x 256 output tiles than half the compute units
-// splits K across workgroups: as many splits as keep about one workgroup per
-// compute unit, at most 16, each with at least 8 K steps of 64.
-int gemm_split_k(int64_t M, int64_t K, int64_t N) {
-    if (M < 128 || K % big::BK != 0 || N <= 0) return 1;
-    const int64_t tiles = ((N + big::BN - 1) / big::BN) * ((M + big::BM - 1) / big::BM);
-    if (tiles >= 128) return 1;
-    int64_t s = 256 / tiles;
+// K-split schedule of the 256 x 256 GEMM (workgroups run about one per
+// compute unit at a time):
+//  * fewer tiles than half the compute units: every tile is split, into as
+//    many K ranges as keep about one workgroup per compute unit;
+//  * otherwise the tiles of the last, partial round are split, so that the
+//    round uses every compute unit and takes a fraction of a tile's time.
+// At most 16 splits, each of at least 8 K steps of 64.
+GemmSplit gemm_split(int64_t M, int64_t K, int64_t N) {
+    constexpr int64_t kCUs = 256;
+    GemmSplit g{1, 0, 0};
+    if (M < 128 || K % big::BK != 0 || N <= 0) return g;
+    g.tiles = ((N + big::BN - 1) / big::BN) * ((M + big::BM - 1) / big::BM);
+    g.t0 = g.tiles;
+#ifndef W4_TAIL_SPLIT
+#define W4_TAIL_SPLIT 1
+#endif
+    const int64_t rem = g.tiles < kCUs / 2 ? g.tiles : (W4_TAIL_SPLIT ? g.tiles % kCUs : 0);
+    if (rem == 0) return g;
+    int64_t s = kCUs / rem;
     if (s > (K / big::BK) / 8) s = (K / big::BK) / 8;
     if (s > 16) s = 16;
-    return s > 1 ? static_cast<int>(s) : 1;
+    if (s < 2) return g;
+    g.splits = static_cast<int>(s);
+    g.t0 = g.tiles - rem;
+    return g;
 }
 
 size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
-    const int s = gemm_split_k(M, K, N);
-    return s > 1 ? static_cast<size_t>(s) * static_cast<size_t>(M) * static_cast<size_t>(N) * sizeof(float) : 0;
+    const GemmSplit g = gemm_split(M, K, N);
+    if (g.splits == 1) return 0;
+    return static_cast<size_t>(g.tiles - g.t0) * g.splits * big::BM * big::BN * sizeof(float);
 }
 
 // wave grid of the register-path kernel (used for E4M3 activations): 4 x 2
@@ -706,13 +747,19 @@ constexpr int kBigWM = W4_BIG_WM, kBigWN = W4_BIG_WN;
 hipError_t launch_gemm(const MulParams& p, hipStream_t stream) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
     if (p.M >= 128 && p.K % big::BK == 0) {
-        // the split count (1 or the one the workspace was sized for) must
-        // leave every split at least one K step
-        if (p.splits < 1 || p.splits > p.K / big::BK || (p.splits > 1 && !p.ws)) return hipErrorInvalidValue;
-        const dim3 grid(static_cast<unsigned>((p.N + big::BN - 1) / big::BN),
-                        static_cast<unsigned>((p.M + big::BM - 1) / big::BM), static_cast<unsigned>(p.splits));
+        // the split schedule the workspace was sized for; every split keeps
+        // at least one K step
+        const int64_t tiles = ((p.N + big::BN - 1) / big::BN) * ((p.M + big::BM - 1) / big::BM);
         MulParams q = p;
-        if (q.splits == 1) q.ws = nullptr;
+        if (q.splits <= 1) {
+            q.splits = 1;
+            q.split_t0 = tiles;
+            q.ws = nullptr;
+        }
+        if (q.splits > q.K / big::BK || q.split_t0 < 0 || q.split_t0 > tiles || (q.splits > 1 && !q.ws))
+            return hipErrorInvalidValue;
+        const int64_t wgs = q.split_t0 + (tiles - q.split_t0) * q.splits;
+        const dim3 grid(static_cast<unsigned>(wgs));
 #ifndef W4_DMA
 #define W4_DMA 1
 #endif
@@ -722,10 +769,10 @@ hipError_t launch_gemm(const MulParams& p, hipStream_t stream) {
             hipLaunchKernelGGL(gemm256_dma_kernel, grid, dim3(dma::NT), 0, stream, q);
         else
             hipLaunchKernelGGL((gemm256_kernel<kBigWM, kBigWN, false>), grid, dim3(64 * kBigWM * kBigWN), 0, stream, q);
-        if (q.splits > 1) {
+        if (q.splits > 1 && q.split_t0 < tiles) {
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
-            const int64_t blocks = (q.M * q.N + 1023) / 1024;
+            const int64_t blocks = (tiles - q.split_t0) * (big::BM * big::BN / 1024);
             hipLaunchKernelGGL(splitk_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, q);
         }
         return hipGetLastError();

@@ -58,10 +58,14 @@ struct MulParams {
     // writes the E4M3 codes and row scales here
     uint8_t* xq_out = nullptr;
     float* xscale_out = nullptr;
-    // K split across workgroups (tiled GEMM only): splits > 1 writes fp32
-    // partial sums to ws [splits][M][N] and a second kernel adds them in
-    // split order, applies the row scale and rounds to bf16
+    // K split across workgroups (256 x 256 GEMM only): output tiles
+    // split_t0 .. tiles - 1 (row-major over the tile grid) are each computed
+    // by `splits` workgroups over consecutive K ranges, which write fp32
+    // partial tiles to ws [tile - split_t0][split][256 x 256]; a second
+    // kernel adds them in split order, applies the row scale and rounds to
+    // bf16.  Tiles before split_t0 are computed whole.
     int splits = 1;
+    int64_t split_t0 = 0;
     float* ws = nullptr;
 };
 // Which kernel runs a product: M <= kSkinnyMaxM: the weight-streaming
@@ -76,9 +80,14 @@ hipError_t launch_skinny(const MulParams& p, hipStream_t stream);
 // (one or two rows whose bf16 activations fit the kernel's LDS staging)
 bool skinny_quantizes_rows(int64_t M, int64_t K);
 hipError_t launch_gemm(const MulParams& p, hipStream_t stream);
-// K splits the tiled GEMM uses for an [M, K] x [N, K] product (1: none) and
-// the fp32 workspace bytes they need
-int gemm_split_k(int64_t M, int64_t K, int64_t N);
+// K-split schedule of the tiled GEMM for an [M, K] x [N, K] product
+// (splits = 1: none) and the fp32 workspace bytes it needs
+struct GemmSplit {
+    int splits;
+    int64_t t0;        // first split tile
+    int64_t tiles;     // all output tiles
+};
+GemmSplit gemm_split(int64_t M, int64_t K, int64_t N);
 size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
 
 }  // namespace w4
