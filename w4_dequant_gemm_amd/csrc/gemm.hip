@@ -173,20 +173,31 @@ __global__ void __launch_bounds__(256) gemm_kernel(MulParams p) {
 //     weights dequantized to bf16) into the idle LDS stage, waits until only
 //     step k + 2's loads are outstanding, and synchronizes the workgroup.
 // LDS rows are 128 bytes (64 bf16); the 16-byte chunk c of row r is stored at
-// position c ^ ((r >> 1) & 7), spreading an MFMA operand read over the banks.
+// position c ^ ((r >> 1) & 7), spreading the row stores and the MFMA operand
+// reads over the banks (the fastest of the XOR forms measured for this kernel).
 namespace big {
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int STAGE = 256 * BK;          // bf16 elements per operand and stage
 
-#ifndef W4_SWZ
-#define W4_SWZ 1
+// Chunk swizzles of 128-byte LDS operand rows: the 16-byte chunk c of row
+// `row` sits at position c ^ swizzle(row).  Variants (chosen by measurement):
+__device__ __forceinline__ int swizzle_fn(int f, int row) {
+    switch (f) {
+        case 1: return (row >> 1) & 7;
+        case 2: return (row >> 2) & 7;
+        case 3: return (row ^ (row >> 3)) & 7;
+        case 4: return ((row >> 1) ^ (row >> 4)) & 7;
+        case 5: return ((row >> 2) ^ (row << 2)) & 7;
+        default: return row & 7;
+    }
+}
+#ifndef W4_RSWZ
+#define W4_RSWZ 1
 #endif
 // bf16 offset of 16-byte chunk c (8 k) of operand row `row` in one 256 x 64
 // stage: rows are 128 bytes; the chunk index is XORed with row bits so that
 // both the row-wise stores and the MFMA fragment reads spread over the banks
-__device__ __forceinline__ int lds_off(int row, int c) {
-    return row * BK + ((c ^ (W4_SWZ ? (row & 7) : ((row >> 1) & 7))) << 3);
-}
+__device__ __forceinline__ int lds_off(int row, int c) { return row * BK + ((c ^ swizzle_fn(W4_RSWZ, row)) << 3); }
 
 // The work of one workgroup of the 256 x 256 kernels (1-D grid): workgroup
 // b < split_t0 computes tile b whole; the rest compute K range z of tile
@@ -490,7 +501,11 @@ constexpr int BLOAD = CPT / 4 + SZN;                  // weight loads per thread
 constexpr int NSLOT = 4 * 4 * (BK / 16);              // MFMAs per wave and step (64)
 typedef uint32_t __attribute__((address_space(1))) global_u32;
 typedef uint32_t __attribute__((address_space(3))) lds_u32;
-__device__ __forceinline__ int lds_off(int row, int c) { return row * BK + ((c ^ (row & 7)) << 3); }
+#ifndef W4_DSWZ
+#define W4_DSWZ 3
+#endif
+__device__ __forceinline__ int swz(int row) { return big::swizzle_fn(W4_DSWZ, row); }
+__device__ __forceinline__ int lds_off(int row, int c) { return row * BK + ((c ^ swz(row)) << 3); }
 }  // namespace dma
 
 __global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
@@ -520,19 +535,23 @@ __global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     // Activations: load i of this wave fills LDS rows 8 (wave * ADMA + i) ..
-    // + 7 of a stage; lane l writes row + l / 8 at chunk position l % 8,
-    // which holds chunk (l % 8) ^ (l / 8) of the row (the row index is a
-    // multiple of 8 plus l / 8, so this is the swizzle of lds_off).  Rows
-    // past M read row M - 1 and compute outputs that are never stored.
+    // + 7 of a stage; lane l writes row + l / 8 at chunk position l % 8, so
+    // it loads the chunk that the swizzle of lds_off puts there: (l % 8) ^
+    // swz(row), with swz(row) = (row ^ (row >> 3)) & 7 (the fastest of the
+    // XOR forms measured for this kernel).  Rows past M read row M - 1 and
+    // compute outputs that are never stored.
     const int a_row0 = 8 * wave * ADMA + (lane >> 3);
     int64_t a_m = m_base + a_row0;
     const int64_t a_last = M - 1;
-    const uint16_t* a_src = static_cast<const uint16_t*>(p.X) + (((lane & 7) ^ (lane >> 3)) * 8);
+    const uint16_t* a_src = static_cast<const uint16_t*>(p.X);
     auto dma_item = [&](int kt, uint16_t* stage, int it) {
         kt = (kt < KT ? kt : KT - 1) + kb;
         int64_t m = a_m + 8 * it;
         m = m < a_last ? m : a_last;
-        __builtin_amdgcn_global_load_lds((const global_u32*)(const void*)(a_src + m * K + static_cast<int64_t>(kt) * BK),
+        // lane l lands at chunk position l % 8 of its row, so it loads the
+        // chunk whose swizzled position that is
+        const int chunk = (lane & 7) ^ swz(a_row0 + 8 * it);
+        __builtin_amdgcn_global_load_lds((const global_u32*)(const void*)(a_src + chunk * 8 + m * K + static_cast<int64_t>(kt) * BK),
                                          (lds_u32*)(void*)(stage + (wave * ADMA + it) * 512), 16, 0, 0);
     };
 
