@@ -491,6 +491,9 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm256_kernel(MulParams p) {
 // and LDS stores, then the workgroup barrier.  Loads past the last
 // step are clamped to it (same count every step), and the loop ends with a
 // full wait so that nothing writes LDS after the workgroup has finished.
+#ifndef W4_A3
+#define W4_A3 1
+#endif
 namespace dma {
 constexpr int BM = 256, BN = 256, BK = 64, NW = 4, NT = 64 * NW;
 constexpr int STAGE = 256 * BK;                       // bf16 elements per stage
@@ -515,6 +518,9 @@ __global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
     __shared__ __attribute__((aligned(16))) uint16_t lds_a1[STAGE];
     __shared__ __attribute__((aligned(16))) uint16_t lds_b0[STAGE];
     __shared__ __attribute__((aligned(16))) uint16_t lds_b1[STAGE];
+#if W4_A3
+    __shared__ __attribute__((aligned(16))) uint16_t lds_a2[STAGE];   // 160 KB in all
+#endif
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -551,8 +557,21 @@ __global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
         // lane l lands at chunk position l % 8 of its row, so it loads the
         // chunk whose swizzled position that is
         const int chunk = (lane & 7) ^ swz(a_row0 + 8 * it);
-        __builtin_amdgcn_global_load_lds((const global_u32*)(const void*)(a_src + chunk * 8 + m * K + static_cast<int64_t>(kt) * BK),
+        const uint16_t* src = a_src + chunk * 8 + m * K + static_cast<int64_t>(kt) * BK;
+#if W4_A3
+        // Issued as plain instructions: the compiler cannot tell the three
+        // activation stages apart and would otherwise wait for every pending
+        // direct-to-LDS load before any LDS read.  There is no register
+        // result (the data goes to LDS at M0 + 16 lane), and completion is
+        // covered by the explicit wait at the end of each step.  Loads the
+        // compiler does not know of only make its own vmcnt waits stricter.
+        const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+            static_cast<uint32_t>(reinterpret_cast<uintptr_t>(stage + (wave * ADMA + it) * 512)));
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
+#else
+        __builtin_amdgcn_global_load_lds((const global_u32*)(const void*)src,
                                          (lds_u32*)(void*)(stage + (wave * ADMA + it) * 512), 16, 0, 0);
+#endif
     };
 
     // Weights: thread tid owns row tid of the tile (8 code words per step)
@@ -646,6 +665,85 @@ __global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
     };
     static_assert(NSLOT == 2 * 4 * CPT && ADMA + 4 * BLOAD <= NSLOT, "slot plan");
 
+#if W4_A3
+    // Three activation stages: step kt reads stage kt % 3 and sends the
+    // activations of step kt + 2 to stage (kt + 2) % 3, so a direct-to-LDS
+    // load has two steps to land.  A step ends waiting only for what was
+    // issued before it (the 12 global loads of the step itself stay in
+    // flight) and for its LDS stores, then the barrier.
+    constexpr int kStepLoads = ADMA + BLOAD;
+    static_assert(kStepLoads < 64, "vmcnt field");
+    auto step_end3 = [&]() {
+        asm volatile("" ::: "memory");
+        // vmcnt = kStepLoads (bits 3:0 and 15:14), expcnt 7 (no wait), lgkmcnt 0
+        __builtin_amdgcn_s_waitcnt((kStepLoads & 15) | (7 << 4) | ((kStepLoads >> 4) << 14));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    auto stage_a = [&](auto S) -> uint16_t* {
+        constexpr int s3 = decltype(S)::value;
+        return s3 == 0 ? lds_a0 : (s3 == 1 ? lds_a1 : lds_a2);
+    };
+    auto step3 = [&](int kt, auto SA, auto SB, Regs& next, const Regs& ready) {
+        constexpr int sa = decltype(SA)::value, sb = decltype(SB)::value;
+        const uint16_t* As = stage_a(std::integral_constant<int, sa>{});
+        uint16_t* Ad = stage_a(std::integral_constant<int, (sa + 2) % 3>{});
+        const uint16_t* Bs = sb ? lds_b1 : lds_b0;
+        uint16_t* Bd = sb ? lds_b0 : lds_b1;
+        bf16x8_t fa[2][FI], fb[2][FJ];
+        load_frags(As, Bs, 0, fa[0], fb[0]);
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            if (kk + 1 < BK / 16) load_frags(As, Bs, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < FI * FJ; ++t) {
+                const int u = kk * FI * FJ + t;
+                const int i = t / FJ, j = t % FJ;
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j], acc[i][j], 0, 0, 0);
+                // weight loads first (slots 0, 4, 8, 12), then the
+                // activation loads (slots 2, 6, ..., 30): the next step's
+                // first dequantization then waits only for the weights
+                if (u % 4 == 0 && u / 4 < BLOAD) {
+                    load_item(kt + 2, next, u / 4);
+                    asm volatile("" ::: "memory");
+                }
+                if (u % 4 == 2 && u / 4 < ADMA) dma_item(kt + 2, Ad, u / 4);
+                if (u % 2 == 1) b_pair(u / 2, ready, Bd);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        step_end3();
+    };
+    // prologue: activations of steps 0 and 1, weights of steps 0 and 1, dequantize step 0
+    Regs r0, r1;
+#pragma unroll
+    for (int it = 0; it < ADMA; ++it) dma_item(0, lds_a0, it);
+#pragma unroll
+    for (int it = 0; it < ADMA; ++it) dma_item(1, lds_a1, it);
+#pragma unroll
+    for (int it = 0; it < BLOAD; ++it) load_item(0, r0, it);
+#pragma unroll
+    for (int it = 0; it < BLOAD; ++it) load_item(1, r1, it);
+#pragma unroll
+    for (int pr = 0; pr < 4 * CPT; ++pr) b_pair(pr, r0, lds_b0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);           // vmcnt, expcnt and lgkmcnt all 0
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    // stage of A cycles with period 3, of B and the registers with period 2
+    for (int kt = 0; kt < KT; kt += 6) {
+        step3(kt, I0{}, I0{}, r0, r1);
+        if (kt + 1 < KT) step3(kt + 1, I1{}, I1{}, r1, r0);
+        if (kt + 2 < KT) step3(kt + 2, I2{}, I0{}, r0, r1);
+        if (kt + 3 < KT) step3(kt + 3, I0{}, I1{}, r1, r0);
+        if (kt + 4 < KT) step3(kt + 4, I1{}, I0{}, r0, r1);
+        if (kt + 5 < KT) step3(kt + 5, I2{}, I1{}, r1, r0);
+    }
+#else
     // prologue: activations of step 0, weights of steps 0 and 1, dequantize step 0
     Regs r0, r1;
 #pragma unroll
@@ -666,6 +764,7 @@ __global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
         step(kt + 1, std::integral_constant<int, 1>{}, r1, r0);
     }
     if (kt < KT) step(kt, std::integral_constant<int, 0>{}, r0, r1);
+#endif
     __builtin_amdgcn_s_waitcnt(0);
     asm volatile("" ::: "memory");
 
