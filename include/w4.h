@@ -188,6 +188,46 @@ int w4a8_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const
               int64_t N, int G, uint16_t* Y, uint8_t* xq, float* xscale, void* workspace,
               size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Portable on-disk form of a quantized weight (gowda.ai "LLM fast inference",
+ * "MSE clipping", last paragraph: the packed codes, scales and zero terms are
+ * exported once in a portable representation and rearranged into the GPU
+ * layout at load, without dequantizing and requantizing; "What the WMT26
+ * paper finds": portable int4 codes are specialized for the kernel once).
+ * The file holds exactly the canonical arrays of w4_quantize_blockwise, with
+ * a header (shape, group size, mode, the clip fractions) and a 64-bit FNV-1a
+ * hash of the payload.  Loading reads them into host memory; the caller
+ * uploads them and runs w4_prepack (the Python binding's w4_portable_load
+ * does both).  These three calls take HOST pointers, do file I/O only and
+ * never touch the GPU.  Errors (unopenable, short, corrupted or foreign
+ * files, inconsistent shapes) return W4_EINVAL, an unknown file version
+ * W4_EUNSUPPORTED; w4_last_error says which.
+ */
+#define W4_PORTABLE_MAX_FRACS 32
+typedef struct {
+    int64_t N, K;            /* weight shape [N, K] */
+    int32_t G;               /* group size (32, 64, 128) */
+    int32_t mode;            /* W4_SYM or W4_ASYM */
+    int32_t n_fracs;         /* clip fractions used by the quantizer (1 = plain) */
+    int32_t has_clip;        /* 1 if the file holds the clip index of every group */
+    uint64_t payload_bytes;  /* bytes after the header */
+    float fracs[W4_PORTABLE_MAX_FRACS];
+} w4_portable_info;
+
+/* Writes packed [N, K/2], scale [N, K/G], zero [N, K/G] (W4_ASYM only; NULL
+ * for W4_SYM) and clip_idx [N, K/G] (or NULL) to `path` (through a temporary
+ * file renamed into place).  fracs: the n_fracs clip fractions of the search. */
+int w4_portable_save(const char* path, int64_t N, int64_t K, int G, int mode, const float* fracs, int n_fracs,
+                     const uint8_t* packed, const uint16_t* scale, const uint16_t* zero, const uint8_t* clip_idx);
+
+/* Reads and checks the header of `path` into *info. */
+int w4_portable_info_read(const char* path, w4_portable_info* info);
+
+/* Reads the arrays of `path` into host buffers sized from its header (zero
+ * may be NULL for W4_SYM; clip_idx may be NULL, and is zero-filled when the
+ * file has none).  The payload hash is checked before anything is copied. */
+int w4_portable_load(const char* path, uint8_t* packed, uint16_t* scale, uint16_t* zero, uint8_t* clip_idx);
+
 /* Short text for a status code (static storage). */
 const char* w4_status_string(int status);
 

@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     for n in ("w4_quantize_blockwise", "w4_mse_clip_search", "w4_prepack", "w4_quantize_rows_e4m3",
               "w4a16_gemm", "w4a8_gemm", "w4_gemm_workspace_bytes", "w4_status_string", "w4_last_error",
-              "w4_abi_version"):
+              "w4_abi_version", "w4_portable_save", "w4_portable_info_read", "w4_portable_load"):
         assert n in names
 
 

@@ -18,7 +18,7 @@ __all__ = [
     "W4Error", "SYM", "ASYM", "MAX_FRACS", "lib", "library_path",
     "w4_quantize_blockwise", "w4_mse_clip_search", "w4_prepack", "w4_quantize_rows_e4m3",
     "w4a16_gemm", "w4a8_gemm", "w4_gemm_workspace_bytes", "w4_status_string", "w4_last_error",
-    "w4_abi_version",
+    "w4_abi_version", "w4_portable_save", "w4_portable_info_read", "w4_portable_load",
     "FRACS_PLAIN", "FRACS_11",
 ]
 
@@ -43,6 +43,13 @@ class W4Error(RuntimeError):
         self.status = status
 
 
+class _PortableInfo(ctypes.Structure):
+    """``w4_portable_info`` of ``include/w4.h``."""
+    _fields_ = [("N", ctypes.c_int64), ("K", ctypes.c_int64), ("G", ctypes.c_int32), ("mode", ctypes.c_int32),
+                ("n_fracs", ctypes.c_int32), ("has_clip", ctypes.c_int32), ("payload_bytes", ctypes.c_uint64),
+                ("fracs", ctypes.c_float * MAX_FRACS)]
+
+
 _lib = None
 
 
@@ -65,6 +72,12 @@ def lib():
     L.w4a8_gemm.argtypes = [P, i64, i64, P, P, i64, I, P, P, P, P, sz_t, P]
     L.w4_gemm_workspace_bytes.argtypes = [i64, i64, i64]
     L.w4_gemm_workspace_bytes.restype = sz_t
+    cp = ctypes.c_char_p
+    L.w4_portable_save.argtypes = [cp, i64, i64, I, I, P, I, P, P, P, P]
+    L.w4_portable_info_read.argtypes = [cp, ctypes.POINTER(_PortableInfo)]
+    L.w4_portable_load.argtypes = [cp, P, P, P, P]
+    for name in ("w4_portable_save", "w4_portable_info_read", "w4_portable_load"):
+        getattr(L, name).restype = I
     for name in ("w4_quantize_blockwise", "w4_mse_clip_search", "w4_prepack", "w4_quantize_rows_e4m3",
                  "w4a16_gemm", "w4a8_gemm"):
         getattr(L, name).restype = I
@@ -198,6 +211,81 @@ def w4_prepack(packed: torch.Tensor, scale: torch.Tensor, zero: Optional[torch.T
                           N, K, G, m, _dev(wq, "wq"), _dev(sz, "sz"), _stream(dev, stream))
     _check("w4_prepack", rc)
     return {"wq": wq, "sz": sz}
+
+
+# ------------------------------------------------------ portable file form
+
+def _host_bytes(t, name, dtype):
+    """A C-contiguous host numpy view of tensor/array ``t`` with element type ``dtype``."""
+    import numpy as np
+    if t is None:
+        return None
+    if isinstance(t, torch.Tensor):
+        t = t.detach()
+        if t.dtype == torch.float16:
+            t = t.view(torch.int16)
+        t = t.cpu().numpy()
+    a = np.ascontiguousarray(t)
+    if a.dtype.itemsize != np.dtype(dtype).itemsize:
+        raise ValueError(f"{name} must have {np.dtype(dtype).itemsize}-byte elements, got {a.dtype}")
+    return a.view(dtype)
+
+
+def _ptr_np(a):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def w4_portable_save(path: str, packed, scale, zero, G: int, mode, fracs: Sequence[float] = FRACS_PLAIN,
+                     clip_idx=None) -> None:
+    """Writes the canonical arrays (device or host tensors, or numpy arrays) to ``path``."""
+    import numpy as np
+    m = _MODES[mode]
+    pk = _host_bytes(packed, "packed", np.uint8)
+    sc = _host_bytes(scale, "scale", np.uint16)
+    ze = _host_bytes(zero, "zero", np.uint16) if m == ASYM else None
+    ci = _host_bytes(clip_idx, "clip_idx", np.uint8)
+    N, K2 = pk.shape
+    arr, n = _fracs(fracs)
+    rc = lib().w4_portable_save(os.fsencode(path), N, 2 * K2, G, m, arr, n, _ptr_np(pk), _ptr_np(sc), _ptr_np(ze),
+                                _ptr_np(ci))
+    _check("w4_portable_save", rc)
+
+
+def w4_portable_info_read(path: str) -> dict:
+    """Header of a portable file: N, K, G, mode, fracs, has_clip, payload_bytes."""
+    info = _PortableInfo()
+    _check("w4_portable_info_read", lib().w4_portable_info_read(os.fsencode(path), ctypes.byref(info)))
+    return {"N": info.N, "K": info.K, "G": info.G, "mode": info.mode, "has_clip": bool(info.has_clip),
+            "fracs": tuple(info.fracs[i] for i in range(info.n_fracs)), "payload_bytes": info.payload_bytes}
+
+
+def w4_portable_load(path: str, device=None, *, prepack: bool = True, stream=None) -> dict:
+    """Reads a portable file.  With ``device`` (a GPU) the canonical arrays are
+    uploaded there and, with ``prepack``, rearranged into the GPU layout
+    (``wq``, ``sz``) at once: the load-time prepack.  Without ``device`` the
+    arrays stay in host memory (numpy)."""
+    import numpy as np
+    info = w4_portable_info_read(path)
+    N, K, G = info["N"], info["K"], info["G"]
+    asym = info["mode"] == ASYM
+    packed = np.empty((N, K // 2), np.uint8)
+    scale = np.empty((N, K // G), np.uint16)
+    zero = np.empty((N, K // G), np.uint16) if asym else None
+    clip = np.empty((N, K // G), np.uint8) if info["has_clip"] else None
+    rc = lib().w4_portable_load(os.fsencode(path), _ptr_np(packed), _ptr_np(scale), _ptr_np(zero), _ptr_np(clip))
+    _check("w4_portable_load", rc)
+    out = dict(info)
+    if device is None:
+        out.update(packed=packed, scale=scale, zero=zero, clip_idx=clip)
+        return out
+    dev = torch.device(device)
+    out["packed"] = torch.from_numpy(packed).to(dev)
+    out["scale"] = torch.from_numpy(scale.view(np.float16)).to(dev)
+    out["zero"] = torch.from_numpy(zero.view(np.float16)).to(dev) if asym else None
+    out["clip_idx"] = torch.from_numpy(clip).to(dev) if clip is not None else None
+    if prepack:
+        out.update(w4_prepack(out["packed"], out["scale"], out["zero"], G, info["mode"], stream=stream))
+    return out
 
 
 # --------------------------------------------------------------- multiplies

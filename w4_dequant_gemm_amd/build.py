@@ -21,6 +21,7 @@ ARCH = "gfx950"
 
 KERNELS = ["quantize.hip", "prepack.hip", "rowquant.hip", "skinny.hip", "gemm.hip"]
 NO_CONTRACT = {"quantize.hip", "rowquant.hip"}
+HOST_SOURCES = ["api.cpp", "portable.cpp"]   # host C++ (argument checks, file I/O)
 
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
              "-fhip-fp32-correctly-rounded-divide-sqrt",
@@ -49,9 +50,11 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         if src in NO_CONTRACT:
             flags.append("-ffp-contract=off")
         jobs_list.append([HIPCC, *flags, "-c", os.path.join(CSRC, src), "-o", obj])
-    api_obj = os.path.join(BUILD, "api.o")
-    jobs_list.append([HIPCC, "-x", "c++", "-O2", "-std=c++17", "-fPIC", "-D__HIP_PLATFORM_AMD__",
-                      "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", "-c", os.path.join(CSRC, "api.cpp"), "-o", api_obj])
+    for host_src in HOST_SOURCES:
+        obj = os.path.join(BUILD, host_src.replace(".cpp", ".o"))
+        jobs_list.append([HIPCC, "-x", "c++", "-O2", "-std=c++17", "-fPIC", "-D__HIP_PLATFORM_AMD__",
+                          "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", "-c",
+                          os.path.join(CSRC, host_src), "-o", obj])
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         for f in [ex.submit(_run, cmd, verbose) for cmd in jobs_list]:
             f.result()

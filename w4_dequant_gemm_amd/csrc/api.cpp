@@ -10,18 +10,22 @@
 
 #include "../../include/w4.h"
 #include "kernels.hpp"
+#include "status.hpp"
 
 namespace {
-
 thread_local char g_last_error[512] = "";
+}  // namespace
 
-int fail(int status, const char* fmt, ...) {
+int w4::fail(int status, const char* fmt, ...) {
     va_list ap;
     va_start(ap, fmt);
     std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
     va_end(ap);
     return status;
 }
+
+namespace {
+using w4::fail;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -61,12 +65,6 @@ int check_mode(const char* fn, int mode) {
     do {                                                                             \
         if (!(p)) return fail(W4_EINVAL, "%s: %s is NULL", fn, #p);                  \
         if (!aligned16(p)) return fail(W4_EINVAL, "%s: %s is not 16-byte aligned", fn, #p); \
-    } while (0)
-
-#define W4_TRY(expr)            \
-    do {                        \
-        int _rc = (expr);       \
-        if (_rc != W4_OK) return _rc; \
     } while (0)
 
 int quantize_common(const char* fn, const float* W, int64_t N, int64_t K, int G, int mode,
