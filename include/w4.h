@@ -78,13 +78,17 @@ extern "C" {
  * codes are clamp(round_half_even(w / s) + z, 0, 15) or
  * clamp(round_half_even(w / s), -8, 7), and the candidate's error is the sum
  * over the group of (w - (q - z) * s)^2, added by a fixed pairwise halving
- * tree.  The first candidate is kept unless a later one has a strictly lower
+ * tree (a[j] += a[j + len], len = P/2 ... 1, over the errors padded with
+ * zeros to the next power of two P).  The first candidate is kept unless a later one has a strictly lower
  * error.  All arithmetic is IEEE fp32 with round-to-nearest-even, so the
  * result is bit-for-bit reproducible.
  *
  *   W        [N, K] fp32, device.
  *   N, K     N >= 0, K > 0, K % G == 0.
- *   G        32, 64 or 128.
+ *   G        32, 64 or 128; or G == K: one group per row, the per-channel
+ *            granularity (gsantana.dev "Granularity: who shares a scale"),
+ *            for K a multiple of 32 up to 32768.  Every other value is
+ *            W4_EUNSUPPORTED.  The products take the same G.
  *   mode     W4_SYM or W4_ASYM.
  *   fracs    HOST pointer to n_fracs fp32 fractions, 1 <= n_fracs <= 32,
  *            fracs[0] == 1.0f, every fraction in (0, 1].  n_fracs == 1 is the
@@ -131,7 +135,7 @@ int w4_mse_clip_search(const float* W, int64_t N, int64_t K, int G, int mode,
  *           and the fp16 zero (8.0 for W4_SYM) in the high half, so that
  *           W'[n, k] = (u - zero) * scale; group g of row n is at
  *             r0*K/G + g*nr + (n - r0).
- *   N >= 0, K > 0, K % G == 0, G in {32, 64, 128}.
+ *   N >= 0, K > 0, K % G == 0, G in {32, 64, 128} or G == K (per-channel).
  */
 int w4_prepack(const uint8_t* packed, const uint16_t* scale, const uint16_t* zero, int64_t N,
                int64_t K, int G, int mode, uint32_t* wq, uint32_t* sz, hipStream_t stream);
@@ -206,7 +210,7 @@ int w4a8_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const
 #define W4_PORTABLE_MAX_FRACS 32
 typedef struct {
     int64_t N, K;            /* weight shape [N, K] */
-    int32_t G;               /* group size (32, 64, 128) */
+    int32_t G;               /* group size (32, 64, 128, or K: per-channel) */
     int32_t mode;            /* W4_SYM or W4_ASYM */
     int32_t n_fracs;         /* clip fractions used by the quantizer (1 = plain) */
     int32_t has_clip;        /* 1 if the file holds the clip index of every group */

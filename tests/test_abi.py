@@ -114,6 +114,24 @@ def test_gemm_workspace_sizes_and_checks(lib):
     assert "aligned" in w4.w4_last_error()
 
 
+def test_per_channel_group_sizes(lib):
+    # G == K is the per-channel granularity: accepted for K a multiple of 32
+    # up to 32768 (checked before the empty-shape early return, so N = 0
+    # launches nothing); other sizes are unsupported
+    import w4_dequant_gemm_amd as w4
+    one = _fr(1.0)
+    q = lib.w4_quantize_blockwise
+    assert q(None, 0, 4096, 4096, 1, one, 1, None, None, None, None, None) == 0
+    assert q(None, 0, 14336, 14336, 1, one, 1, None, None, None, None, None) == 0
+    assert q(None, 0, 32768, 32768, 0, one, 1, None, None, None, None, None) == 0
+    assert q(None, 0, 4008, 4008, 1, one, 1, None, None, None, None, None) == 2
+    assert "per-channel" in w4.w4_last_error()
+    assert q(None, 0, 65536, 65536, 1, one, 1, None, None, None, None, None) == 2
+    assert q(None, 0, 192, 96, 1, one, 1, None, None, None, None, None) == 2
+    assert lib.w4a16_gemm(None, 0, 14336, None, None, 8, 14336, None, None, 0, None) == 0
+    assert lib.w4_prepack(None, None, None, 0, 4096, 4096, 1, None, None, None) == 0
+
+
 def test_empty_shapes_are_no_ops(lib):
     # nothing to do: OK without touching any pointer (and without a device)
     one = _fr(1.0)

@@ -348,3 +348,30 @@ def test_invalid_arguments_raise():
         w4.w4_quantize_blockwise(W, 32, "asym", (0.9, 0.8))  # fracs[0] must be 1
     with pytest.raises(w4.W4Error):
         w4.w4_quantize_blockwise(torch.zeros((4, 100), device="cuda:0"), 32, "asym")  # K % G
+
+
+def test_per_channel_products():
+    # per-channel weights (G = K) through every product kernel: one and two
+    # rows (dot form), 16 and 64 rows (MFMA with the exact correction), 256
+    # rows (tiled GEMM with a K split) and K = 14336, not a power of two
+    require_gpu()
+    import torch
+    import w4_dequant_gemm_amd as w4
+    for name, idx, rows in (("llama8b_decode", 0, 512), ("llama8b_decode", 1, 384)):
+        W = synth.weight(synth.WORKLOADS[name], idx, rows=rows)
+        N, K = W.shape
+        q = oracle.quantize(W, K, "asym", fracs=synth.FRACS_11)
+        pk, G = prepack_dev(q)
+        assert G == K
+        for M in (1, 2, 16, 64, 256):
+            print(f"[per-channel] {name}[{idx}] N={N} K={K} M={M}", flush=True)
+            Xb = _x(name, M, K)
+            Y = w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G)
+            Y8, xq, xs = w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G)
+            torch.cuda.synchronize()
+            want = oracle.gemm_ref(oracle.bf16_bits_to_f64(Xb), q["packed"], q["scale"], q["zero"], G, "asym")
+            want8, rq, rs = oracle.w4a8_ref(Xb, q["packed"], q["scale"], q["zero"], G, "asym")
+            assert_bits_equal(host(xq), rq, "E4M3 activations")
+            e16 = oracle.rel_error(want, Y.float().cpu().numpy())
+            e8 = oracle.rel_error(want8, Y8.float().cpu().numpy())
+            assert e16 <= REL_TOL and e8 <= REL_TOL, (M, e16, e8)

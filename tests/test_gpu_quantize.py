@@ -165,3 +165,59 @@ def test_prepack_layout():
         want_sz = q["scale"].astype(np.uint32) | (zero.astype(np.uint32) << np.uint32(16))
         assert_bits_equal(host(pk["sz"]).view(np.uint32).reshape(-1), _blocked(want_sz, 1),
                           f"scale|zero words ({mode}, N={N})")
+
+
+# ------------------------------------------------------------ per-channel
+
+PER_CHANNEL = [
+    # (workload, matrix index, rows, mode, n_fracs): G = K, one group per row
+    ("smollm2_135m_mlp", 0, None, "asym", 11),     # K = 576: tree padded to 1024
+    ("smollm2_135m_mlp", 1, None, "sym", 11),      # K = 1536: padded to 2048
+    ("llama8b_decode", 0, 512, "asym", 11),        # K = 4096
+    ("llama8b_decode", 1, 256, "asym", 11),        # K = 14336: padded to 16384
+    ("llama8b_decode", 1, 128, "sym", 1),
+    ("llama70b_prefill", 0, 64, "asym", 11),       # K = 8192
+]
+
+
+@pytest.mark.parametrize("case", PER_CHANNEL, ids=lambda c: f"{c[0]}-{c[1]}-{c[3]}-n{c[4]}")
+def test_per_channel_quantize_bit_exact(case):
+    # gsantana.dev "Granularity: who shares a scale": per-channel is the group
+    # G = K; codes, scales, zeros, clip indices and every candidate's error
+    # equal the oracle's bit for bit
+    require_gpu()
+    import torch
+    import w4_dequant_gemm_amd as w4
+    name, idx, rows, mode, nf = case
+    W = weight(name, idx, rows)
+    K = W.shape[1]
+    print(f"[per-channel quantize] {case} K={K}", flush=True)
+    fr = fracs_for(nf)
+    ref = oracle.quantize(W, K, mode, fracs=fr, want_sse=True)
+    out = _run_gpu_quant(W, mode, K, fr)
+    assert_bits_equal(host(out["packed"]), ref["packed"], "packed codes")
+    assert_bits_equal(bits16(out["scale"]), ref["scale"], "fp16 scales")
+    if mode == "asym":
+        assert_bits_equal(bits16(out["zero"]), ref["zero"], "fp16 zero points")
+    assert_bits_equal(host(out["clip_idx"]), ref["clip"], "clip indices")
+    srch = w4.w4_mse_clip_search(to_dev(W), K, mode, fr, want_sse=True)
+    torch.cuda.synchronize()
+    assert_bits_equal(host(srch["sse"]).view(np.uint32), ref["sse"].view(np.uint32), "candidate errors")
+
+
+def test_per_channel_largest_and_smallest_rows():
+    # K = 32768 (32 values per thread) and K = 96 (the tree mostly padding),
+    # heavy-tailed rows with an outlier, both modes
+    require_gpu()
+    rng = np.random.default_rng(31)
+    for K in (32768, 96, 32 * 37):
+        W = (rng.standard_t(3, size=(6, K)) * 0.02).astype(np.float32)
+        W[1, K // 3] = 0.9
+        for mode in ("asym", "sym"):
+            print(f"[per-channel quantize] K={K} {mode}", flush=True)
+            fr = fracs_for(11)
+            ref = oracle.quantize(W, K, mode, fracs=fr)
+            out = _run_gpu_quant(W, mode, K, fr)
+            assert_bits_equal(host(out["packed"]), ref["packed"], f"packed codes K={K}")
+            assert_bits_equal(bits16(out["scale"]), ref["scale"], f"fp16 scales K={K}")
+            assert_bits_equal(host(out["clip_idx"]), ref["clip"], f"clip indices K={K}")

@@ -306,6 +306,37 @@ def test_clip_search_brute_force_tiny_blocks(orc):
     assert agree >= (n_cases - ties) * 0.98, (agree, ties)
 
 
+def test_padded_tree_for_groups_that_are_not_powers_of_two(orc):
+    # A group whose size is not a power of two (per-channel rows, G = K) adds
+    # its errors by the halving tree over the errors padded with zeros to the
+    # next power of two.  Pinned two ways: the reported error of the winner
+    # is the float64 sum within fp32 rounding, and the padded tree written
+    # out here from its definition gives the same bits.
+    rng = np.random.default_rng(41)
+    fr = synth.FRACS_11
+    for G in (6, 12, 24, 96):
+        blk = (rng.standard_t(2.5, size=(4, G)) * 0.1).astype(np.float32)
+        r = orc.quantize(blk, G, "asym", fracs=fr, want_sse=True)
+        wq, _, _ = _recon(orc, r, G)
+        e64 = ((blk.astype(np.float64) - wq) ** 2).sum(axis=1)
+        won = np.take_along_axis(r["sse"], r["clip"][..., None].astype(np.int64), axis=2)[:, 0, 0]
+        np.testing.assert_allclose(won, e64, rtol=1e-5)
+        # the tree from its definition, over float32 squared errors of the
+        # emitted reconstruction (the winner's), padded with zeros
+        P = 1
+        while P < G:
+            P *= 2
+        for row in range(4):
+            e = (blk[row] - wq[row].astype(np.float32)).astype(np.float32)
+            a = np.zeros(P, np.float32)
+            a[:G] = e * e
+            n = P // 2
+            while n >= 1:
+                a[:n] = a[:n] + a[n:2 * n]
+                n //= 2
+            assert np.float32(a[0]).view(np.uint32) == np.float32(won[row]).view(np.uint32), (G, row)
+
+
 def test_sym_clip_candidates(orc):
     # symmetric clip search: the candidate range is [-f amax, f amax]; a block
     # with one extreme value picks a contracted range and clips it

@@ -37,12 +37,19 @@ int hip_status(hipError_t e, const char* what) {
 int check_group(const char* fn, int64_t N, int64_t K, int G) {
     if (N < 0) return fail(W4_EINVAL, "%s: N = %lld must be >= 0", fn, static_cast<long long>(N));
     if (K <= 0) return fail(W4_EINVAL, "%s: K = %lld must be > 0", fn, static_cast<long long>(K));
-    if (G != 32 && G != 64 && G != 128)
-        return fail(W4_EUNSUPPORTED, "%s: group size %d is not one of 32, 64, 128", fn, G);
-    if (K % G != 0)
-        return fail(W4_EINVAL, "%s: K = %lld is not a multiple of the group size %d", fn,
-                    static_cast<long long>(K), G);
-    return W4_OK;
+    if (G == 32 || G == 64 || G == 128) {
+        if (K % G != 0)
+            return fail(W4_EINVAL, "%s: K = %lld is not a multiple of the group size %d", fn,
+                        static_cast<long long>(K), G);
+        return W4_OK;
+    }
+    if (G == K) {   // per-channel: one group per row
+        if (K % 32 != 0 || K > w4::kMaxPerChannelK)
+            return fail(W4_EUNSUPPORTED, "%s: per-channel groups (G = K = %lld) need K a multiple of 32, at most %lld",
+                        fn, static_cast<long long>(K), static_cast<long long>(w4::kMaxPerChannelK));
+        return W4_OK;
+    }
+    return fail(W4_EUNSUPPORTED, "%s: group size %d is not one of 32, 64, 128, or K (per-channel)", fn, G);
 }
 
 int check_fracs(const char* fn, const float* fracs, int n_fracs) {

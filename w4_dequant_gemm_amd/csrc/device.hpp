@@ -77,6 +77,13 @@ __device__ __forceinline__ uint32_t nibble_pair_bf16(uint32_t w, int i, uint32_t
 // as written by the prepack kernel): code word j of the row is
 // words[(j / 4) * tile + j % 4] and its scale/zero word of group g is
 // sz[g * nr], where nr is the number of rows in the row's block.
+// Shift that maps a k index to its group: log2 G for the power-of-two group
+// sizes; a group that is not a power of two is a whole row (per-channel,
+// G = K), whose only group is 0 = k >> 31 for every k < K < 2^31.
+__device__ __forceinline__ int group_shift(int G) {
+    return (G & (G - 1)) == 0 ? __builtin_ctz(static_cast<unsigned>(G)) : 31;
+}
+
 struct TiledRow {
     const uint32_t* words;
     const uint32_t* sz;

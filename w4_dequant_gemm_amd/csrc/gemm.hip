@@ -255,7 +255,7 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm256_kernel(MulParams p) {
     const int64_t m_base = job.m_base, n_base = job.n_base;
     const int64_t M = p.M, N = p.N, K = p.K;
     const int kb = job.kb, KT = job.KT;      // this workgroup's K steps
-    const int g_shift = __builtin_ctz(static_cast<unsigned>(p.G));   // G is a power of two
+    const int g_shift = group_shift(p.G);
     const uint32_t bias = opaque_vgpr(kBf16Bias128x2);
 
     float16_t acc[FI][FJ];
@@ -530,7 +530,7 @@ __global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
     const int64_t m_base = job.m_base, n_base = job.n_base;
     const int64_t M = p.M, N = p.N, K = p.K;
     const int kb = job.kb, KT = job.KT;      // this workgroup's K steps
-    const int g_shift = __builtin_ctz(static_cast<unsigned>(p.G));
+    const int g_shift = group_shift(p.G);
 
     float16_t acc[FI][FJ];
 #pragma unroll

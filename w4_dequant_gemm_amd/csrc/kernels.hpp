@@ -7,11 +7,13 @@
 namespace w4 {
 
 constexpr int kMaxFracs = 32;
+// largest K of a per-channel weight (one group of G = K per row)
+constexpr int64_t kMaxPerChannelK = 32768;
 
 struct QuantizeParams {
     const float* W;          // [n_groups * G] fp32: groups are consecutive runs of G weights
     int64_t n_groups;
-    int G;                   // 32, 64, 128
+    int G;                   // 32, 64, 128, or K of the rows (per-channel)
     int asym;                // 0 symmetric, 1 asymmetric
     int n_fracs;
     float fracs[kMaxFracs];

@@ -93,8 +93,8 @@ uint64_t get_u64(const uint8_t* p) {
 
 int check_shape(const char* fn, int64_t N, int64_t K, int G, int mode, int n_fracs) {
     if (N < 0 || K <= 0) return fail(W4_EINVAL, "%s: bad shape N = %lld, K = %lld", fn, (long long)N, (long long)K);
-    if (G != 32 && G != 64 && G != 128)
-        return fail(W4_EUNSUPPORTED, "%s: group size %d is not one of 32, 64, 128", fn, G);
+    if (G != 32 && G != 64 && G != 128 && G != K)
+        return fail(W4_EUNSUPPORTED, "%s: group size %d is not one of 32, 64, 128, or K (per-channel)", fn, G);
     if (K % G != 0) return fail(W4_EINVAL, "%s: K = %lld is not a multiple of G = %d", fn, (long long)K, G);
     if (mode != W4_SYM && mode != W4_ASYM) return fail(W4_EINVAL, "%s: mode %d is not W4_SYM or W4_ASYM", fn, mode);
     if (n_fracs < 1 || n_fracs > W4_PORTABLE_MAX_FRACS)

@@ -153,6 +153,170 @@ __global__ void __launch_bounds__(256) quantize_kernel(QuantizeParams p) {
     }
 }
 
+// ------------------------------------------------------------ per-channel
+//
+// One group per row (G = K, the per-channel granularity of gsantana.dev
+// "Granularity: who shares a scale"): one 1024-thread workgroup per row.  The
+// halving tree of a group whose size is not a power of two runs over the
+// errors padded with zeros to the next power of two P (zeros change no sum),
+// and a tree over max(P, 1024) values gives the same sums (the extra first
+// levels add zeros).  Thread t holds elements t + 1024 i, i < RPT: the levels
+// with length >= 1024 pair elements of one thread, the rest go through LDS
+// (lengths 512 .. 64) and wave shuffles (32 .. 1), each level computing
+// a[j] = a[j] + a[j + len] exactly as the group kernel does in registers.
+constexpr int kRowThreads = 1024;
+
+template <int RPT, bool ASYM>
+__global__ void __launch_bounds__(kRowThreads) quantize_row_kernel(QuantizeParams p, int64_t K) {
+    __shared__ float red[kRowThreads];
+    __shared__ float wstat[3][kRowThreads / 64];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int64_t row = blockIdx.x;
+    const float* w_row = p.W + row * K;
+    // element t + 1024 i is in the row when i < n_in
+    const int n_in = static_cast<int>((K - t + kRowThreads - 1) / kRowThreads);
+    float v[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) v[i] = i < n_in ? w_row[t + static_cast<int64_t>(kRowThreads) * i] : 0.0f;
+    // statistics of the row (order-free: min, max, max |w|)
+    float wmin = INFINITY, wmax = -INFINITY, amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+        if (i < n_in) {
+            wmin = fminf(wmin, v[i]);
+            wmax = fmaxf(wmax, v[i]);
+            amax = fmaxf(amax, fabsf(v[i]));
+        }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        wmin = fminf(wmin, __shfl_xor(wmin, o, 64));
+        wmax = fmaxf(wmax, __shfl_xor(wmax, o, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    }
+    if (lane == 0) {
+        wstat[0][wave] = wmin;
+        wstat[1][wave] = wmax;
+        wstat[2][wave] = amax;
+    }
+    __syncthreads();
+    wmin = wstat[0][0];
+    wmax = wstat[1][0];
+    amax = wstat[2][0];
+    for (int w = 1; w < kRowThreads / 64; ++w) {
+        wmin = fminf(wmin, wstat[0][w]);
+        wmax = fmaxf(wmax, wstat[1][w]);
+        amax = fmaxf(amax, wstat[2][w]);
+    }
+
+    int best = 0;
+    float best_err = 0.0f, best_s = 1.0f, best_z = 0.0f;
+    uint32_t best_sb = 0x3C00u;
+    for (int c = 0; c < p.n_fracs; ++c) {
+        const float f = p.fracs[c];
+        float s32;
+        float lo = 0.0f;
+        if constexpr (ASYM) {
+            float hi;
+            if (f == 1.0f) {
+                lo = wmin;
+                hi = wmax;
+            } else {
+                float mid = (wmax + wmin) * 0.5f;
+                float h = (wmax - wmin) * 0.5f;
+                float fh = f * h;
+                lo = mid - fh;
+                hi = mid + fh;
+            }
+            s32 = (hi - lo) / 15.0f;
+        } else {
+            s32 = (f * amax) / 7.0f;
+        }
+        uint32_t sb = float_to_half_bits(s32);
+        float s = half_bits_to_float(sb);
+        if (s == 0.0f) {
+            s = 1.0f;
+            sb = 0x3C00u;
+        }
+        const float zf = ASYM ? rintf(-lo / s) : 0.0f;
+        // the tree: levels inside the thread, then LDS, then shuffles
+        float a[RPT];
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) a[i] = i < n_in ? err2<ASYM>(v[i], s, zf) : 0.0f;
+#pragma unroll
+        for (int len = RPT / 2; len >= 1; len /= 2)
+#pragma unroll
+            for (int i = 0; i < len; ++i) a[i] = a[i] + a[i + len];
+        __syncthreads();                     // the previous candidate's reads of red are done
+        red[t] = a[0];
+        __syncthreads();
+#pragma unroll
+        for (int len = kRowThreads / 2; len >= 64; len /= 2) {
+            if (t < len) red[t] = red[t] + red[t + len];
+            __syncthreads();
+        }
+        if (wave == 0) {
+            float x = red[t];
+#pragma unroll
+            for (int len = 32; len >= 1; len /= 2) {
+                const float y = __shfl_down(x, len, 64);
+                if (t < len) x = x + y;
+            }
+            if (t == 0) red[0] = x;
+        }
+        __syncthreads();
+        const float e = red[0];
+        if (p.sse && t == 0) p.sse[row * p.n_fracs + c] = e;
+        if (c == 0 || e < best_err) {
+            best = c;
+            best_err = e;
+            best_s = s;
+            best_z = zf;
+            best_sb = sb;
+        }
+    }
+
+    if (t == 0) {
+        if (p.clip) p.clip[row] = static_cast<uint8_t>(best);
+        if (p.encode) {
+            p.scale[row] = static_cast<uint16_t>(best_sb);
+            if constexpr (ASYM) p.zero[row] = static_cast<uint16_t>(float_to_half_bits(best_z + 0.0f));
+        }
+    }
+    if (!p.encode) return;
+    // canonical packing: element j = t + 1024 i pairs with j + 1 in lane t + 1
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const float q = fminf(fmaxf(rintf(v[i] / best_s) + best_z, Grid<ASYM>::lo), Grid<ASYM>::hi);
+        const uint32_t nib = static_cast<uint32_t>(static_cast<int>(q)) & 0xFu;
+        const uint32_t hi_nib = __shfl_down(nib, 1, 64);
+        const int64_t j = t + static_cast<int64_t>(kRowThreads) * i;
+        if ((t & 1) == 0 && i < n_in) p.packed[(row * K + j) / 2] = static_cast<uint8_t>(nib | (hi_nib << 4));
+    }
+}
+
+template <int RPT, bool ASYM>
+hipError_t launch_row(const QuantizeParams& p, int64_t K, hipStream_t stream) {
+    hipLaunchKernelGGL((quantize_row_kernel<RPT, ASYM>), dim3(static_cast<unsigned>(p.n_groups)), dim3(kRowThreads), 0,
+                       stream, p, K);
+    return hipGetLastError();
+}
+
+template <bool ASYM>
+hipError_t launch_per_channel(const QuantizeParams& p, hipStream_t stream) {
+    const int64_t K = p.G;
+    int64_t P = kRowThreads;
+    while (P < K) P *= 2;
+    switch (P / kRowThreads) {
+        case 1: return launch_row<1, ASYM>(p, K, stream);
+        case 2: return launch_row<2, ASYM>(p, K, stream);
+        case 4: return launch_row<4, ASYM>(p, K, stream);
+        case 8: return launch_row<8, ASYM>(p, K, stream);
+        case 16: return launch_row<16, ASYM>(p, K, stream);
+        case 32: return launch_row<32, ASYM>(p, K, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <int G, bool ASYM>
 hipError_t launch(const QuantizeParams& p, hipStream_t stream) {
     const int threads = 256;
@@ -170,7 +334,10 @@ hipError_t launch_quantize(const QuantizeParams& p, hipStream_t stream) {
         case 32: return p.asym ? launch<32, true>(p, stream) : launch<32, false>(p, stream);
         case 64: return p.asym ? launch<64, true>(p, stream) : launch<64, false>(p, stream);
         case 128: return p.asym ? launch<128, true>(p, stream) : launch<128, false>(p, stream);
-        default: return hipErrorInvalidValue;
+        default:
+            // any other size is one group per row (per-channel, G = K <= 32768)
+            if (p.G > kMaxPerChannelK || p.G % 32 != 0) return hipErrorInvalidValue;
+            return p.asym ? launch_per_channel<true>(p, stream) : launch_per_channel<false>(p, stream);
     }
 }
 

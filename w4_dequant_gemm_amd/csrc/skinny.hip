@@ -105,7 +105,7 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
     const int64_t M = p.M, N = p.N, K = p.K;
     const int64_t n0 = static_cast<int64_t>(blockIdx.x) * (16 * FJ);
     const int64_t words_row = K / 8, groups_row = K / p.G;
-    const int g_shift = __builtin_ctz(static_cast<unsigned>(p.G));
+    const int g_shift = group_shift(p.G);
     const int KS = static_cast<int>((K + kStepK - 1) / kStepK);
 
     // lane's column in each block and row in each 16-row block (clamped:
@@ -612,11 +612,11 @@ hipError_t launch_skinny_c(const MulParams& p, int wk, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// groups of 128 (one per K step) use the exact correction form, smaller
-// groups dequantize every weight
+// groups of 128 or more (a K step lies in one group; per-channel included)
+// use the exact correction form, smaller groups dequantize every weight
 template <int MB, int FJ, bool XF8>
 hipError_t launch_skinny_t(const MulParams& p, int wk, hipStream_t stream) {
-    if (p.G == kStepK) {
+    if (p.G % kStepK == 0) {
         // four bf16 row blocks with two column blocks would not fit the registers
         if constexpr (MB == 4 && FJ > 1 && !XF8) return launch_skinny_c<MB, 1, XF8, kCorr>(p, wk, stream);
         else return launch_skinny_c<MB, FJ, XF8, kCorr>(p, wk, stream);
