@@ -193,6 +193,35 @@ int w4a8_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const
               size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * w4a16_gate_up / w4a8_gate_up -- the gate and up projections of a gated MLP
+ * block in one pass, with the activation-and-multiply epilogue (gowda.ai "LLM
+ * fast inference", "Machete, with credit where it is due": the speed comes
+ * from a stack that includes model-specific fused paths):
+ *   H = bf16(act(X . Wg'^T) * (X . Wu'^T)),
+ * each product with fp32 accumulation (W4A8: the row-quantized E4M3
+ * activations and their row scale, exactly as w4a8_gemm), the activation and
+ * product in fp32, one rounding to bf16.  act: W4_ACT_SILU, x / (1 + e^-x)
+ * (SwiGLU blocks), or W4_ACT_GELU_TANH, 0.5 x (1 + tanh(sqrt(2/pi) (x +
+ * 0.044715 x^3))) (GeGLU blocks).  The weight-streaming kernel reads both
+ * matrices at the same 16 output columns per workgroup; H feeds the down
+ * projection (w4a8_gemm on one or two rows quantizes it to E4M3 inside its
+ * own kernel).
+ *   X            [M, K] bf16 in; 0 <= M <= 32 (larger M: W4_EUNSUPPORTED).
+ *   wq_gate, sz_gate, wq_up, sz_up: two [N, K] weights in the GPU layout of
+ *                w4_prepack, with the same G.
+ *   H            [M, N] bf16 out.
+ *   xq, xscale   (W4A8) as for w4a8_gemm.
+ */
+#define W4_ACT_SILU 1
+#define W4_ACT_GELU_TANH 2
+int w4a16_gate_up(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq_gate, const uint32_t* sz_gate,
+                  const uint32_t* wq_up, const uint32_t* sz_up, int64_t N, int G, int act, uint16_t* H,
+                  hipStream_t stream);
+int w4a8_gate_up(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq_gate, const uint32_t* sz_gate,
+                 const uint32_t* wq_up, const uint32_t* sz_up, int64_t N, int G, int act, uint16_t* H, uint8_t* xq,
+                 float* xscale, hipStream_t stream);
+
+/*
  * Portable on-disk form of a quantized weight (gowda.ai "LLM fast inference",
  * "MSE clipping", last paragraph: the packed codes, scales and zero terms are
  * exported once in a portable representation and rearranged into the GPU

@@ -232,6 +232,34 @@ def w4a8_ref(X_bits, packed, scale, zero, G: int, mode, rows=None, cols=None):
     return gemm_ref(X64, packed, scale, zero, G, mode, a_scale=s, rows=rows, cols=cols), xq, s
 
 
+def activation(act: str, x: np.ndarray) -> np.ndarray:
+    """Gate activation of a gated MLP block in float64: ``silu`` x / (1 + e^-x)
+    (SwiGLU) or ``gelu_tanh`` 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))
+    (GeGLU), written from their definitions."""
+    x = np.asarray(x, dtype=np.float64)
+    if act == "silu":
+        return x / (1.0 + np.exp(-x))
+    if act == "gelu_tanh":
+        return 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (x + 0.044715 * x ** 3)))
+    raise ValueError(act)
+
+
+def gate_up_ref(X_bits, gate, up, G: int, mode, act: str, kind: str = "w4a16", rows=None, cols=None):
+    """Gated MLP front half, ``act(X . Wg'^T) * (X . Wu'^T)`` in float64, with
+    bf16 activations (``w4a16``) or their per-row E4M3 quantization
+    (``w4a8``).  ``gate`` and ``up`` are oracle quantizations (packed, scale,
+    zero).  Returns the products' float64 result (and for ``w4a8`` the codes
+    and row scales)."""
+    if kind == "w4a16":
+        X64 = bf16_bits_to_f64(X_bits)
+        g = gemm_ref(X64, gate["packed"], gate["scale"], gate["zero"], G, mode, rows=rows, cols=cols)
+        u = gemm_ref(X64, up["packed"], up["scale"], up["zero"], G, mode, rows=rows, cols=cols)
+        return activation(act, g) * u
+    g, xq, s = w4a8_ref(X_bits, gate["packed"], gate["scale"], gate["zero"], G, mode, rows=rows, cols=cols)
+    u, _, _ = w4a8_ref(X_bits, up["packed"], up["scale"], up["zero"], G, mode, rows=rows, cols=cols)
+    return activation(act, g) * u, xq, s
+
+
 # ----------------------------------------------------------- host formulas
 
 def rel_error(reference: np.ndarray, approx: np.ndarray) -> float:

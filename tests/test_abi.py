@@ -31,7 +31,8 @@ def test_header_declares_the_boundary():
     names = _declared()
     for n in ("w4_quantize_blockwise", "w4_mse_clip_search", "w4_prepack", "w4_quantize_rows_e4m3",
               "w4a16_gemm", "w4a8_gemm", "w4_gemm_workspace_bytes", "w4_status_string", "w4_last_error",
-              "w4_abi_version", "w4_portable_save", "w4_portable_info_read", "w4_portable_load"):
+              "w4_abi_version", "w4_portable_save", "w4_portable_info_read", "w4_portable_load",
+              "w4a16_gate_up", "w4a8_gate_up"):
         assert n in names
 
 
@@ -130,6 +131,18 @@ def test_per_channel_group_sizes(lib):
     assert q(None, 0, 192, 96, 1, one, 1, None, None, None, None, None) == 2
     assert lib.w4a16_gemm(None, 0, 14336, None, None, 8, 14336, None, None, 0, None) == 0
     assert lib.w4_prepack(None, None, None, 0, 4096, 4096, 1, None, None, None) == 0
+
+
+def test_gate_up_validation(lib):
+    import w4_dequant_gemm_amd as w4
+    fake = ctypes.c_void_p(0x1000)
+    g = lib.w4a16_gate_up
+    assert g(fake, 33, 4096, fake, fake, fake, fake, 64, 128, 1, fake, None) == 2     # M > 32
+    assert "at most 32" in w4.w4_last_error()
+    assert g(fake, 1, 4096, fake, fake, fake, fake, 64, 128, 3, fake, None) == 1      # unknown activation
+    assert g(fake, 1, 4096, fake, fake, None, fake, 64, 128, 1, fake, None) == 1      # no up weights
+    assert g(None, 0, 4096, None, None, None, None, 64, 128, 1, None, None) == 0      # nothing to do
+    assert lib.w4a8_gate_up(fake, 1, 4096, fake, fake, fake, fake, 64, 128, 2, fake, None, fake, None) == 1
 
 
 def test_empty_shapes_are_no_ops(lib):

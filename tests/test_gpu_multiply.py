@@ -375,3 +375,43 @@ def test_per_channel_products():
             e16 = oracle.rel_error(want, Y.float().cpu().numpy())
             e8 = oracle.rel_error(want8, Y8.float().cpu().numpy())
             assert e16 <= REL_TOL and e8 <= REL_TOL, (M, e16, e8)
+
+
+@pytest.mark.parametrize("kind", ["w4a16", "w4a8"])
+def test_gate_up_products(kind):
+    # gate and up projections in one pass with the activation-and-multiply
+    # epilogue, against act(X Wg'^T) * (X Wu'^T) in float64: 8B-class rows
+    # (gate and up are disjoint row ranges of the 8B up weight), one to 32
+    # activation rows, both activations; and a ragged N with symmetric G = 32
+    # weights (the dequantizing form for more than two rows)
+    require_gpu()
+    import torch
+    import w4_dequant_gemm_amd as w4
+    wl = synth.WORKLOADS["llama8b_decode"]
+    W = synth.weight(wl, 0, rows=2048)
+    cases = [(W[:1024], W[1024:], 128, "asym", (1, 2, 3, 16, 32)),
+             (W[:1000, :1536], W[1000:2000, :1536], 32, "sym", (1, 2, 5))]
+    for Wg, Wu, G, mode, Ms in cases:
+        qg = oracle.quantize(np.ascontiguousarray(Wg), G, mode)
+        qu = oracle.quantize(np.ascontiguousarray(Wu), G, mode)
+        pg, _ = prepack_dev(qg)
+        pu, _ = prepack_dev(qu)
+        N, K = Wg.shape
+        for act in ("silu", "gelu_tanh"):
+            for M in Ms:
+                print(f"[gate_up] {kind} N={N} K={K} G={G} {mode} {act} M={M}", flush=True)
+                Xb = _x("llama8b_decode", M, K)
+                if kind == "w4a16":
+                    H = w4.w4a16_gate_up(bf16_dev(Xb), pg, pu, G, act)
+                    want = oracle.gate_up_ref(Xb, qg, qu, G, mode, act)
+                else:
+                    H, xq, xs = w4.w4a8_gate_up(bf16_dev(Xb), pg, pu, G, act)
+                    want, rq, rs = oracle.gate_up_ref(Xb, qg, qu, G, mode, act, kind="w4a8")
+                    torch.cuda.synchronize()
+                    assert_bits_equal(host(xq), rq, "E4M3 activations")
+                    assert_bits_equal(host(xs).view(np.uint32), rs.view(np.uint32), "row scales")
+                torch.cuda.synchronize()
+                err = oracle.rel_error(want, H.float().cpu().numpy())
+                assert err <= REL_TOL, f"{kind} {act} M={M}: relative error {err:.3e}"
+    with pytest.raises(w4.W4Error):
+        w4.w4a16_gate_up(bf16_dev(_x("llama8b_decode", 33, 4096)), pg, pu, 32, "silu")

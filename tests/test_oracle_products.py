@@ -94,3 +94,34 @@ def test_w4a8_reference_is_scaled_product(orc):
     # and it is close to the unquantized-activation product (FP8 error only)
     Y16 = orc.gemm_ref(orc.bf16_bits_to_f64(X), r["packed"], r["scale"], r["zero"], 128, "asym")
     assert orc.rel_error(Y16, Y) < 0.05
+
+
+def test_gate_activations_against_library_routines(orc):
+    # the oracle's gate activations pinned to torch's own (float64, CPU):
+    # SiLU and the tanh form of GELU, on a wide range and near zero; the tanh
+    # form stays within 1e-3 of the exact erf GELU
+    import torch
+    from scipy.special import erf
+    x = np.concatenate([np.linspace(-30, 30, 2001), np.geomspace(1e-8, 1e-1, 50), -np.geomspace(1e-8, 1e-1, 50)])
+    t = torch.from_numpy(x)
+    np.testing.assert_allclose(orc.activation("silu", x), torch.nn.functional.silu(t).numpy(), rtol=1e-14, atol=1e-300)
+    np.testing.assert_allclose(orc.activation("gelu_tanh", x),
+                               torch.nn.functional.gelu(t, approximate="tanh").numpy(), rtol=1e-13, atol=1e-14)
+    exact = 0.5 * x * (1 + erf(x / np.sqrt(2)))
+    assert np.max(np.abs(orc.activation("gelu_tanh", x) - exact)) < 1e-3
+    with pytest.raises(ValueError):
+        orc.activation("relu", x)
+
+
+def test_gate_up_reference_composes_the_products(orc):
+    # act(X Wg'^T) * (X Wu'^T): with the up weights equal to the gate weights
+    # the result is act(y) * y for the plain product y
+    W = synth.normal_matrix(60, 48, 128, 0.05)
+    q = orc.quantize(W, 32, "asym")
+    Xb = synth.to_bf16_bits(synth.normal_matrix(61, 3, 128))
+    y = orc.gemm_ref(orc.bf16_bits_to_f64(Xb), q["packed"], q["scale"], q["zero"], 32, "asym")
+    h = orc.gate_up_ref(Xb, q, q, 32, "asym", "silu")
+    np.testing.assert_array_equal(h, orc.activation("silu", y) * y)
+    h8, xq, s = orc.gate_up_ref(Xb, q, q, 32, "asym", "gelu_tanh", kind="w4a8")
+    y8, _, _ = orc.w4a8_ref(Xb, q["packed"], q["scale"], q["zero"], 32, "asym")
+    np.testing.assert_array_equal(h8, orc.activation("gelu_tanh", y8) * y8)

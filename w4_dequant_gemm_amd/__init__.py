@@ -19,6 +19,7 @@ __all__ = [
     "w4_quantize_blockwise", "w4_mse_clip_search", "w4_prepack", "w4_quantize_rows_e4m3",
     "w4a16_gemm", "w4a8_gemm", "w4_gemm_workspace_bytes", "w4_status_string", "w4_last_error",
     "w4_abi_version", "w4_portable_save", "w4_portable_info_read", "w4_portable_load",
+    "w4a16_gate_up", "w4a8_gate_up", "ACT_SILU", "ACT_GELU_TANH",
     "FRACS_PLAIN", "FRACS_11",
 ]
 
@@ -33,6 +34,9 @@ FRACS_PLAIN = (1.0,)
 FRACS_11 = (1.00, 0.95, 0.90, 0.85, 0.80, 0.75, 0.70, 0.65, 0.60, 0.55, 0.50)
 
 _MODES = {"sym": SYM, "asym": ASYM, SYM: SYM, ASYM: ASYM}
+ACT_SILU = 1
+ACT_GELU_TANH = 2
+_ACTS = {"silu": ACT_SILU, "gelu_tanh": ACT_GELU_TANH, ACT_SILU: ACT_SILU, ACT_GELU_TANH: ACT_GELU_TANH}
 
 
 class W4Error(RuntimeError):
@@ -72,6 +76,10 @@ def lib():
     L.w4a8_gemm.argtypes = [P, i64, i64, P, P, i64, I, P, P, P, P, sz_t, P]
     L.w4_gemm_workspace_bytes.argtypes = [i64, i64, i64]
     L.w4_gemm_workspace_bytes.restype = sz_t
+    L.w4a16_gate_up.argtypes = [P, i64, i64, P, P, P, P, i64, I, I, P, P]
+    L.w4a8_gate_up.argtypes = [P, i64, i64, P, P, P, P, i64, I, I, P, P, P, P]
+    L.w4a16_gate_up.restype = I
+    L.w4a8_gate_up.restype = I
     cp = ctypes.c_char_p
     L.w4_portable_save.argtypes = [cp, i64, i64, I, I, P, I, P, P, P, P]
     L.w4_portable_info_read.argtypes = [cp, ctypes.POINTER(_PortableInfo)]
@@ -339,3 +347,35 @@ def w4a8_gemm(X: torch.Tensor, wq: torch.Tensor, sz: torch.Tensor, G: int, *, Y=
                          ws, ws_bytes, _stream(dev, stream))
     _check("w4a8_gemm", rc)
     return Y, xq, xscale
+
+
+def w4a16_gate_up(X: torch.Tensor, gate: dict, up: dict, G: int, act="silu", *, H=None, stream=None):
+    """Gate and up projections in one pass: ``H = bf16(act(X . Wg'^T) * (X . Wu'^T))``
+    for bf16 ``X[M, K]`` (M <= 32); ``gate`` and ``up`` are GPU layouts from
+    ``w4_prepack`` (``wq``, ``sz``); ``act`` is ``"silu"`` or ``"gelu_tanh"``."""
+    M, K = X.shape
+    N = gate["wq"].shape[0]
+    dev = X.device
+    H = _empty((M, N), torch.bfloat16, dev) if H is None else H
+    rc = lib().w4a16_gate_up(_dev(X, "X", torch.bfloat16), M, K, _dev(gate["wq"], "gate wq"), _dev(gate["sz"], "gate sz"),
+                             _dev(up["wq"], "up wq"), _dev(up["sz"], "up sz"), N, G, _ACTS[act],
+                             _dev(H, "H", torch.bfloat16), _stream(dev, stream))
+    _check("w4a16_gate_up", rc)
+    return H
+
+
+def w4a8_gate_up(X: torch.Tensor, gate: dict, up: dict, G: int, act="silu", *, H=None, xq=None, xscale=None,
+                 stream=None):
+    """W4A8 form of ``w4a16_gate_up``: per-row E4M3 of ``X`` first; returns (H, xq, xscale)."""
+    M, K = X.shape
+    N = gate["wq"].shape[0]
+    dev = X.device
+    H = _empty((M, N), torch.bfloat16, dev) if H is None else H
+    xq = _empty((M, K), torch.uint8, dev) if xq is None else xq
+    xscale = _empty((M,), torch.float32, dev) if xscale is None else xscale
+    rc = lib().w4a8_gate_up(_dev(X, "X", torch.bfloat16), M, K, _dev(gate["wq"], "gate wq"), _dev(gate["sz"], "gate sz"),
+                            _dev(up["wq"], "up wq"), _dev(up["sz"], "up sz"), N, G, _ACTS[act],
+                            _dev(H, "H", torch.bfloat16), _dev(xq, "xq"), _dev(xscale, "xscale", torch.float32),
+                            _stream(dev, stream))
+    _check("w4a8_gate_up", rc)
+    return H, xq, xscale

@@ -26,7 +26,8 @@ HOST_SOURCES = ["api.cpp", "portable.cpp"]   # host C++ (argument checks, file I
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
              "-fhip-fp32-correctly-rounded-divide-sqrt",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             "-Wall", "-Wno-unused-function"]
+             "-Wall", "-Wno-unused-function",
+             "-fvisibility=hidden"]   # kernels and launchers stay internal; the C ABI is in api.cpp / portable.cpp
 
 
 def _run(cmd, verbose):

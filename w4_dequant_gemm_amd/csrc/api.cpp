@@ -138,6 +138,24 @@ w4::MulParams with_split(w4::MulParams p, void* workspace) {
 
 }  // namespace
 
+namespace {
+// shared checks of the gate and up product
+int gate_up_common(const char* fn, const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq_gate,
+                   const uint32_t* sz_gate, const uint32_t* wq_up, const uint32_t* sz_up, int64_t N, int G, int act,
+                   uint16_t* H) {
+    W4_TRY(mul_common(fn, X, M, K, wq_gate, sz_gate, N, G, H, nullptr, 0));
+    if (M > w4::kGateUpMaxM)
+        return fail(W4_EUNSUPPORTED, "%s: M = %lld rows; the fused gate and up product takes at most %lld", fn,
+                    static_cast<long long>(M), static_cast<long long>(w4::kGateUpMaxM));
+    if (act != W4_ACT_SILU && act != W4_ACT_GELU_TANH)
+        return fail(W4_EINVAL, "%s: act = %d is neither W4_ACT_SILU nor W4_ACT_GELU_TANH", fn, act);
+    if (M == 0 || N == 0) return W4_OK;
+    W4_REQUIRE_PTR(fn, wq_up);
+    W4_REQUIRE_PTR(fn, sz_up);
+    return W4_OK;
+}
+}  // namespace
+
 extern "C" {
 
 int w4_quantize_blockwise(const float* W, int64_t N, int64_t K, int G, int mode, const float* fracs,
@@ -215,6 +233,43 @@ int w4a8_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const
     w4::MulParams p{xq, xscale, M, K, N, G, wq, sz, Y, true};
     if (M <= w4::kSkinnyMaxM) return hip_status(w4::launch_skinny(p, stream), fn);
     return hip_status(w4::launch_gemm(with_split(p, workspace), stream), fn);
+}
+
+
+int w4a16_gate_up(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq_gate, const uint32_t* sz_gate,
+                  const uint32_t* wq_up, const uint32_t* sz_up, int64_t N, int G, int act, uint16_t* H,
+                  hipStream_t stream) {
+    const char* fn = "w4a16_gate_up";
+    W4_TRY(gate_up_common(fn, X, M, K, wq_gate, sz_gate, wq_up, sz_up, N, G, act, H));
+    if (M == 0 || N == 0) return W4_OK;
+    w4::MulParams p{X, nullptr, M, K, N, G, wq_gate, sz_gate, H, false};
+    p.wq2 = wq_up;
+    p.sz2 = sz_up;
+    p.act = act;
+    return hip_status(w4::launch_skinny(p, stream), fn);
+}
+
+int w4a8_gate_up(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq_gate, const uint32_t* sz_gate,
+                 const uint32_t* wq_up, const uint32_t* sz_up, int64_t N, int G, int act, uint16_t* H, uint8_t* xq,
+                 float* xscale, hipStream_t stream) {
+    const char* fn = "w4a8_gate_up";
+    W4_TRY(gate_up_common(fn, X, M, K, wq_gate, sz_gate, wq_up, sz_up, N, G, act, H));
+    if (M == 0 || N == 0) return W4_OK;
+    W4_REQUIRE_PTR(fn, xq);
+    if (!xscale) return fail(W4_EINVAL, "%s: xscale is NULL", fn);
+    w4::MulParams p{X, nullptr, M, K, N, G, wq_gate, sz_gate, H, true, xq, xscale};
+    p.wq2 = wq_up;
+    p.sz2 = sz_up;
+    p.act = act;
+    if (!w4::skinny_quantizes_rows(M, K)) {
+        w4::RowQuantParams rq{X, M, K, xq, xscale};
+        W4_TRY(hip_status(w4::launch_rowquant(rq, stream), fn));
+        p.X = xq;
+        p.xscale = xscale;
+        p.xq_out = nullptr;
+        p.xscale_out = nullptr;
+    }
+    return hip_status(w4::launch_skinny(p, stream), fn);
 }
 
 const char* w4_status_string(int status) {

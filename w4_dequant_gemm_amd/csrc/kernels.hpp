@@ -69,7 +69,16 @@ struct MulParams {
     int splits = 1;
     int64_t split_t0 = 0;
     float* ws = nullptr;
+    // gate and up projections in one pass (streaming kernel, two column
+    // blocks): block 0 reads wq/sz (gate), block 1 wq2/sz2 (up) at the same 16
+    // output columns, and Y = bf16(act(gate) * up); act 1 = SiLU, 2 = GELU
+    // (tanh form)
+    const uint32_t* wq2 = nullptr;
+    const uint32_t* sz2 = nullptr;
+    int act = 0;
 };
+// largest M of the fused gate and up product
+constexpr int64_t kGateUpMaxM = 32;
 // Which kernel runs a product: M <= kSkinnyMaxM: the weight-streaming
 // kernels (dot form for one or two rows, MFMA form above); larger M: the
 // tiled MFMA GEMM.

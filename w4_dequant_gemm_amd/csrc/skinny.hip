@@ -48,6 +48,15 @@ typedef float float4_v __attribute__((ext_vector_type(4)));
 
 constexpr int kStepK = 128;   // k per wave and step (4 quarters of 32)
 
+// Activation of the gate projection in a gated MLP: SiLU x / (1 + e^-x)
+// (SwiGLU) or the tanh form of GELU, 0.5 x (1 + tanh(sqrt(2/pi) (x +
+// 0.044715 x^3))) (GeGLU), in fp32.
+__device__ __forceinline__ float activation(int act, float x) {
+    if (act == 1) return x / (1.0f + expf(-x));
+    const float t = 0.7978845608028654f * (x + 0.044715f * x * x * x);
+    return 0.5f * x * (1.0f + tanhf(t));
+}
+
 // weight steps in flight per wave (fewer with more activation rows, whose
 // fragments take the registers)
 #ifndef W4_SK_DEPTH
@@ -103,7 +112,9 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c = lane & 15, h = lane >> 4;
     const int64_t M = p.M, N = p.N, K = p.K;
-    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * (16 * FJ);
+    // gate and up in one pass: both blocks cover the same 16 columns (FJ = 2)
+    const bool pair = p.wq2 != nullptr;
+    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * (pair ? 16 : 16 * FJ);
     const int64_t words_row = K / 8, groups_row = K / p.G;
     const int g_shift = group_shift(p.G);
     const int KS = static_cast<int>((K + kStepK - 1) / kStepK);
@@ -121,12 +132,14 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
     int bnr[FJ];
 #pragma unroll
     for (int j = 0; j < FJ; ++j) {
-        int64_t r0 = n0 + 16 * j;
+        int64_t r0 = pair ? n0 : n0 + 16 * j;
         r0 = r0 < N ? r0 : ((N - 1) / 16) * 16;
         const int nr = static_cast<int>(N - r0 < 16 ? N - r0 : 16);
         const int cc = c < nr ? c : nr - 1;
-        bblk[j] = reinterpret_cast<const uint8_t*>(p.wq + r0 * words_row);
-        sblk[j] = reinterpret_cast<const uint8_t*>(p.sz + r0 * groups_row);
+        const uint32_t* wq = pair && j == 1 ? p.wq2 : p.wq;
+        const uint32_t* szp = pair && j == 1 ? p.sz2 : p.sz;
+        bblk[j] = reinterpret_cast<const uint8_t*>(wq + r0 * words_row);
+        sblk[j] = reinterpret_cast<const uint8_t*>(szp + r0 * groups_row);
         qlane[j] = 16 * cc;
         slane[j] = 4 * cc;
         bnr[j] = __builtin_amdgcn_readfirstlane(nr);
@@ -560,14 +573,35 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
                 if (h == 0) red_base[wave * TILE + m * 16 * FJ + 16 * j + c] = v;
             }
         __syncthreads();
+        auto row_factor = [&](int row) -> float {
+            if constexpr (QX) return row == 0 ? row_scale[0] : row_scale[MB - 1];
+            else if constexpr (XF8) return p.xscale[row];
+            else return 1.0f;
+        };
+        if (pair) {
+            // output (row, c): act(gate) * up from blocks 0 and 1
+            for (int o = threadIdx.x; o < 16 * MB; o += blockDim.x) {
+                const int row = o / 16, cc = o % 16;
+                float g = 0.0f, u = 0.0f;
+                for (int w = 0; w < wk; ++w) {
+                    g += red_base[w * TILE + row * 16 * FJ + cc];
+                    u += red_base[w * TILE + row * 16 * FJ + 16 + cc];
+                }
+                const int64_t n = n0 + cc;
+                if (row < M && n < N) {
+                    const float r = row_factor(row);
+                    p.Y[static_cast<int64_t>(row) * N + n] = float_to_bf16_bits(activation(p.act, g * r) * (u * r));
+                }
+            }
+            return;
+        }
         for (int o = threadIdx.x; o < TILE; o += blockDim.x) {
             const int row = o / (16 * FJ), col = o % (16 * FJ);
             float y = 0.0f;
             for (int w = 0; w < wk; ++w) y += red_base[w * TILE + o];
             const int64_t n = n0 + col;
             if (row < M && n < N) {
-                if constexpr (QX) y *= row == 0 ? row_scale[0] : row_scale[MB - 1];
-                else if constexpr (XF8) y *= p.xscale[row];
+                if constexpr (QX || XF8) y *= row_factor(row);
                 p.Y[static_cast<int64_t>(row) * N + n] = float_to_bf16_bits(y);
             }
         }
@@ -586,6 +620,22 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
             for (int e = 0; e < 4; ++e)
                 red[wave * TILE + (16 * i + 4 * h + e) * (16 * FJ) + 16 * j + c] = acc[i][j][e];
     __syncthreads();
+    if (pair) {
+        for (int o = threadIdx.x; o < 256 * MB; o += blockDim.x) {
+            const int row = o / 16, cc = o % 16;
+            float g = 0.0f, u = 0.0f;
+            for (int w = 0; w < wk; ++w) {
+                g += red[w * TILE + row * 16 * FJ + cc];
+                u += red[w * TILE + row * 16 * FJ + 16 + cc];
+            }
+            const int64_t n = n0 + cc;
+            if (row < M && n < N) {
+                const float r = XF8 ? p.xscale[row] : 1.0f;
+                p.Y[static_cast<int64_t>(row) * N + n] = float_to_bf16_bits(activation(p.act, g * r) * (u * r));
+            }
+        }
+        return;
+    }
     for (int o = threadIdx.x; o < TILE; o += blockDim.x) {
         const int row = o / (16 * FJ), col = o % (16 * FJ);
         float y = 0.0f;
@@ -604,7 +654,9 @@ int64_t staged_words_row(int64_t K) { return 17 * (((K / 32) + 3) & ~int64_t{3})
 
 template <int MB, int FJ, bool XF8, int MODE>
 hipError_t launch_skinny_c(const MulParams& p, int wk, hipStream_t stream) {
-    const int64_t blocks = (p.N + 16 * FJ - 1) / (16 * FJ);
+    const int64_t cols = p.wq2 ? 16 : 16 * FJ;       // output columns per workgroup
+    if (p.wq2 && FJ != 2) return hipErrorInvalidValue;
+    const int64_t blocks = (p.N + cols - 1) / cols;
     size_t lds = static_cast<size_t>(wk) * (MODE >= kDot ? 16 : 256) * MB * FJ * sizeof(float);
     if (MODE == kDotLds || MODE == kDotLdsQ) lds += static_cast<size_t>(MB) * staged_words_row(p.K) * sizeof(uint32_t);
     hipLaunchKernelGGL((gemm_skinny_kernel<MB, FJ, XF8, MODE>), dim3(static_cast<unsigned>(blocks)), dim3(64 * wk), lds,
@@ -682,7 +734,12 @@ hipError_t launch_skinny(const MulParams& p, hipStream_t stream) {
     int fj = dotm ? (p.M == 2 && W4_DOT_FJMAX > 2 ? 2 : W4_DOT_FJMAX) : (mb == 4 ? 2 : W4_SK_FJMAX);
     const int minblk = dotm ? W4_DOT_MINBLK : W4_SK_MINBLK;
     while (fj > 1 && (p.N + 16 * fj - 1) / (16 * fj) < minblk) fj /= 2;
-    const int64_t blocks = (p.N + 16 * fj - 1) / (16 * fj);
+    if (p.wq2) {
+        // gate and up: two blocks over the same 16 columns (at most 32 rows)
+        if (mb > 2) return hipErrorInvalidValue;
+        fj = 2;
+    }
+    const int64_t blocks = p.wq2 ? (p.N + 15) / 16 : (p.N + 16 * fj - 1) / (16 * fj);
     const int64_t ks = (p.K + kStepK - 1) / kStepK;
     const int64_t minsteps = dotm ? W4_DOT_MINSTEPS : W4_SK_MINSTEPS;
     int64_t wk = ((dotm ? W4_DOT_WAVES : 4096) + blocks - 1) / blocks;
