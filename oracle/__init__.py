@@ -260,6 +260,87 @@ def gate_up_ref(X_bits, gate, up, G: int, mode, act: str, kind: str = "w4a16", r
     return activation(act, g) * u, xq, s
 
 
+# --------------------------------------------------------- NF4 comparator
+#
+# gsantana.dev "Quantizing LLMs Without Guesswork", "Weight-only methods" (the
+# NF4 paragraph): 16 levels that are quantiles of a normal distribution, in
+# blocks of 64 weights, with double quantization of the block scales
+# bringing their cost from 0.5 to 0.127 bits per weight.  The page names
+# QLoRA as the source; the steps below are QLoRA's construction and the
+# plainest reading of the rest (each listed with the other readings).
+
+NF4_BLOCK = 64          # weights per block (one absmax scale)
+NF4_DQ_GROUP = 256      # block scales per second-level fp32 constant
+
+
+def nf4_levels() -> np.ndarray:
+    """The 16 NF4 levels, ascending, as float32: the normal quantiles at 8
+    evenly spaced probabilities from delta down to 1/2 (exclusive) for the
+    positive side and 7 for the negative side, delta = (1 - 1/30 + 1 - 1/32) / 2,
+    plus an exact zero, scaled so that the largest is 1.  Computed in float64
+    with scipy's inverse normal CDF, then rounded once to float32."""
+    from scipy.special import ndtri
+    delta = 0.5 * (1 - 1 / (2 * 15)) + 0.5 * (1 - 1 / (2 * 16))
+    pos = ndtri(np.linspace(delta, 0.5, 9)[:-1])
+    neg = -ndtri(np.linspace(delta, 0.5, 8)[:-1])
+    v = np.sort(np.concatenate([pos, [0.0], neg]))
+    return (v / v.max()).astype(np.float32)
+
+
+def nf4_quantize(W: np.ndarray):
+    """NF4 of ``W[N, K]`` (fp32, K a multiple of 64): per block of 64 weights
+    along K, absmax = max |w|; every weight becomes the index of the level
+    nearest to fp32(w / absmax) (fp32 distances, the lower index on ties; a
+    zero block maps to the zero level).  The block absmax values, flattened
+    row-major, are quantized in groups of 256: c2 = fp32(max / 255) (1 if
+    the group is all zero), q = round_half_even(absmax / c2) as uint8.
+    Returns codes [N, K] (uint8 0..15), packed [N, K/2] (even k in the low
+    nibble), absmax_q [N*K/64] uint8, c2 [ceil(N*K/64/256)] float32 and the
+    unquantized absmax."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    N, K = W.shape
+    assert K % NF4_BLOCK == 0
+    L = nf4_levels()
+    blocks = W.reshape(-1, NF4_BLOCK)
+    amax = np.abs(blocks).max(axis=1).astype(np.float32)
+    safe = np.where(amax == 0, np.float32(1), amax).astype(np.float32)
+    x = (blocks / safe[:, None]).astype(np.float32)
+    d = np.abs(x[:, :, None] - L[None, None, :]).astype(np.float32)
+    codes = np.argmin(d, axis=2).astype(np.uint8).reshape(N, K)
+    nb = amax.size
+    ng = (nb + NF4_DQ_GROUP - 1) // NF4_DQ_GROUP
+    c2 = np.empty(ng, np.float32)
+    aq = np.empty(nb, np.uint8)
+    for g in range(ng):
+        a = amax[g * NF4_DQ_GROUP:(g + 1) * NF4_DQ_GROUP]
+        c = np.float32(a.max()) / np.float32(255)
+        c = np.float32(1) if c == 0 else np.float32(c)
+        c2[g] = c
+        aq[g * NF4_DQ_GROUP:(g + 1) * NF4_DQ_GROUP] = np.clip(np.rint(a / c), 0, 255).astype(np.uint8)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return {"codes": codes, "packed": packed, "absmax_q": aq, "c2": c2, "absmax": amax}
+
+
+def nf4_dequant(codes: np.ndarray, absmax_q: np.ndarray, c2: np.ndarray) -> np.ndarray:
+    """W'[n, k] = level[code] * (q * c2) of its block, in float64 from the fp32 values."""
+    N, K = codes.shape
+    L = nf4_levels().astype(np.float64)
+    nb = absmax_q.size
+    scale = (absmax_q.astype(np.float32) * np.repeat(c2, NF4_DQ_GROUP)[:nb]).astype(np.float32)
+    return L[codes] * np.repeat(scale.astype(np.float64), NF4_BLOCK).reshape(N, K)
+
+
+def nf4_gemv_ref(x_bits: np.ndarray, codes, absmax_q, c2) -> np.ndarray:
+    """float64 ``y = W' . x`` for one bf16 activation row."""
+    x = bf16_bits_to_f64(np.asarray(x_bits).reshape(1, -1))[0]
+    return nf4_dequant(codes, absmax_q, c2) @ x
+
+
+def nf4_bits_per_weight() -> float:
+    """4-bit codes + an 8-bit scale per 64 weights + an fp32 per 256 blocks."""
+    return 4 + 8 / NF4_BLOCK + 32 / (NF4_BLOCK * NF4_DQ_GROUP)
+
+
 # ----------------------------------------------------------- host formulas
 
 def rel_error(reference: np.ndarray, approx: np.ndarray) -> float:
