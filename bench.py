@@ -225,6 +225,28 @@ def main():
                                                "two_products_us": round(msa * 1e3, 3)}
             log(f"[bench] W4A16 8B gate+up M={M}: fused {msf*1e3:.2f} us ({by/(msf*1e-3)/1e9:.1f} GB/s), "
                 f"two products {msa*1e3:.2f} us")
+        # NF4 comparator at M = 1: the same up/down weights in NF4 (blocks of
+        # 64, double-quantized scales), same rotation of copies
+        for name, idx, x in (("up", 0, x_up), ("down", 1, x_dn)):
+            Wd = torch.from_numpy(synth.weight(wl8, idx)).to(dev)
+            base = w4.w4_nf4_quantize(Wd)
+            del Wd
+            copies = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(L - 1)]
+            N, K = base["packed"].shape[0], 2 * base["packed"].shape[1]
+            y = torch.empty((N,), dtype=torch.bfloat16, device=dev)
+
+            def run_nf4(x=x, y=y, copies=copies):
+                for c in copies:
+                    w4.w4_nf4_gemv(x, c, y=y)
+            ms = timer.time(run_nf4, 20, 3) / L
+            nb = N * K // 64
+            by = N * K // 2 + nb + 4 * ((nb + 255) // 256) + 2 * K + 2 * N
+            gbs = by / (ms * 1e-3) / 1e9
+            w4us = extra[f"w4a16_gemv_8b_{name}_m1"]["us"]
+            extra[f"nf4_gemv_8b_{name}_m1"] = {"us": round(ms * 1e3, 3), "GB/s": round(gbs, 1),
+                                              "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "w4a16_us": w4us}
+            log(f"[bench] NF4 8B {name} M=1: {ms*1e3:.2f} us, {gbs:.1f} GB/s (W4A16 G={G}: {w4us:.2f} us)")
+            del copies, base
         del ups, downs
         torch.cuda.empty_cache()
 

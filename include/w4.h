@@ -222,6 +222,37 @@ int w4a8_gate_up(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq_gat
                  float* xscale, hipStream_t stream);
 
 /*
+ * NF4 comparator (gsantana.dev "Quantizing LLMs Without Guesswork",
+ * "Weight-only methods: GPTQ, AWQ and the file formats", the NF4 paragraph):
+ * 16 levels that are normal quantiles (QLoRA's construction: 8 positive and 7
+ * negative quantiles at evenly spaced probabilities from delta = (1 - 1/30 +
+ * 1 - 1/32) / 2 down to 1/2, an exact zero, scaled to [-1, 1]), blocks of 64
+ * weights with an absmax scale, and double quantization of the scales: per
+ * group of 256 consecutive block scales (flattened row-major) an fp32
+ * constant c2 = max / 255 and 8-bit codes round_half_even(absmax / c2), 4.127
+ * bits per weight in all.  It is the pages' comparison point, multiplied here
+ * by the same kind of decode GEMV as W4A16.
+ *
+ * w4_nf4_levels: the 16 levels (fp32, ascending) into a HOST array.
+ * w4_nf4_quantize: W [N, K] fp32 (K a multiple of 64) -> packed [N, K/2]
+ *   (code of k even in the low nibble), absmax_q [N*K/64] bytes, absmax_c2
+ *   [ceil(N*K/64/256)] fp32.  A weight's code is the level nearest to
+ *   fp32(w / absmax) of its block (fp32 distances, the lower index on ties; a
+ *   zero block gets the zero level); the codes use the unquantized absmax.
+ *   Bit-reproducible (plain fp32 operations in a fixed order).
+ * w4_nf4_gemv: y [N] = bf16(W' . x) for one bf16 row x [K] (K <= 32768),
+ *   W'[n, k] = bf16(level[code]) * absmax_q * c2 of its block, fp32
+ *   accumulation.
+ * Device pointers, asynchronous on `stream`; W, packed, x and y 16-byte
+ * aligned.
+ */
+int w4_nf4_levels(float* levels);
+int w4_nf4_quantize(const float* W, int64_t N, int64_t K, uint8_t* packed, uint8_t* absmax_q, float* absmax_c2,
+                    hipStream_t stream);
+int w4_nf4_gemv(const uint16_t* x, int64_t K, const uint8_t* packed, const uint8_t* absmax_q, const float* absmax_c2,
+                int64_t N, uint16_t* y, hipStream_t stream);
+
+/*
  * Portable on-disk form of a quantized weight (gowda.ai "LLM fast inference",
  * "MSE clipping", last paragraph: the packed codes, scales and zero terms are
  * exported once in a portable representation and rearranged into the GPU

@@ -32,7 +32,7 @@ def test_header_declares_the_boundary():
     for n in ("w4_quantize_blockwise", "w4_mse_clip_search", "w4_prepack", "w4_quantize_rows_e4m3",
               "w4a16_gemm", "w4a8_gemm", "w4_gemm_workspace_bytes", "w4_status_string", "w4_last_error",
               "w4_abi_version", "w4_portable_save", "w4_portable_info_read", "w4_portable_load",
-              "w4a16_gate_up", "w4a8_gate_up"):
+              "w4a16_gate_up", "w4a8_gate_up", "w4_nf4_levels", "w4_nf4_quantize", "w4_nf4_gemv"):
         assert n in names
 
 
@@ -143,6 +143,23 @@ def test_gate_up_validation(lib):
     assert g(fake, 1, 4096, fake, fake, None, fake, 64, 128, 1, fake, None) == 1      # no up weights
     assert g(None, 0, 4096, None, None, None, None, 64, 128, 1, None, None) == 0      # nothing to do
     assert lib.w4a8_gate_up(fake, 1, 4096, fake, fake, fake, fake, 64, 128, 2, fake, None, fake, None) == 1
+
+
+def test_nf4_levels_match_the_oracle(lib):
+    # the library computes its NF4 table on the host (bisection on erfc); the
+    # oracle with scipy's inverse normal CDF: the same 16 fp32 values
+    import numpy as np
+    import oracle
+    import w4_dequant_gemm_amd as w4
+    np.testing.assert_array_equal(w4.w4_nf4_levels().view(np.uint32), oracle.nf4_levels().view(np.uint32))
+
+
+def test_nf4_validation(lib):
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.w4_nf4_quantize(fake, 4, 96, fake, fake, fake, None) == 1           # K not a multiple of 64
+    assert lib.w4_nf4_gemv(fake, 65536, fake, fake, fake, 8, fake, None) == 2       # K above the LDS staging
+    assert lib.w4_nf4_gemv(fake, 128, fake, None, fake, 8, fake, None) == 1         # no block scales
+    assert lib.w4_nf4_quantize(None, 0, 128, None, None, None, None) == 0           # nothing to do
 
 
 def test_empty_shapes_are_no_ops(lib):

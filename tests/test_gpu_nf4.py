@@ -1,0 +1,63 @@
+"""NF4 comparator on the GPU against the oracle: the quantizer bit-exact
+(codes, 8-bit block scales, second-level constants) and the decode GEMV
+within the product tolerance, on the 8B-class shapes and ragged ones
+(gsantana.dev "Quantizing LLMs Without Guesswork", "Weight-only methods:
+GPTQ, AWQ and the file formats", the NF4 paragraph)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import REL_TOL, assert_bits_equal, bf16_dev, host, require_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name,idx,rows", [("llama8b_decode", 0, 2048), ("llama8b_decode", 1, 512),
+                                           ("smollm2_135m_mlp", 0, None), ("tiny", 0, None)])
+def test_nf4_quantize_and_gemv(name, idx, rows):
+    require_gpu()
+    import torch
+    import w4_dequant_gemm_amd as w4
+    wl = synth.WORKLOADS[name]
+    W = synth.weight(wl, idx, rows=rows)
+    N, K = W.shape
+    print(f"[nf4] {name}[{idx}] N={N} K={K}", flush=True)
+    ref = oracle.nf4_quantize(W)
+    out = w4.w4_nf4_quantize(to_dev(W))
+    torch.cuda.synchronize()
+    assert_bits_equal(host(out["packed"]), ref["packed"], "NF4 codes")
+    assert_bits_equal(host(out["absmax_q"]), ref["absmax_q"], "8-bit block scales")
+    assert_bits_equal(host(out["absmax_c2"]).view(np.uint32), ref["c2"].view(np.uint32), "second-level constants")
+    xb = synth.activations_bf16_bits(wl, 1, K)[0]
+    y = w4.w4_nf4_gemv(bf16_dev(xb), out)
+    torch.cuda.synchronize()
+    want = oracle.nf4_gemv_ref(xb, ref["codes"], ref["absmax_q"], ref["c2"])
+    err = oracle.rel_error(want, y.float().cpu().numpy())
+    assert err <= REL_TOL, f"relative error {err:.3e}"
+
+
+def test_nf4_ragged_and_zero_blocks():
+    # blocks not a multiple of 256 (a partial last group), a zero row, an
+    # outlier, and K not a multiple of 2048 (lanes past the row's chunks)
+    require_gpu()
+    import torch
+    import w4_dequant_gemm_amd as w4
+    rng = np.random.default_rng(12)
+    for N, K in ((37, 576), (301, 1600), (5, 64)):
+        W = (rng.standard_normal((N, K)) * 0.03).astype(np.float32)
+        W[0] = 0.0
+        W[-1, K // 2] = 2.5
+        ref = oracle.nf4_quantize(W)
+        out = w4.w4_nf4_quantize(to_dev(W))
+        torch.cuda.synchronize()
+        assert_bits_equal(host(out["packed"]), ref["packed"], f"codes N={N} K={K}")
+        assert_bits_equal(host(out["absmax_q"]), ref["absmax_q"], f"block scales N={N} K={K}")
+        assert_bits_equal(host(out["absmax_c2"]).view(np.uint32), ref["c2"].view(np.uint32), f"c2 N={N} K={K}")
+        xb = synth.to_bf16_bits(rng.standard_normal((1, K)).astype(np.float32))[0]
+        y = w4.w4_nf4_gemv(bf16_dev(xb), out)
+        torch.cuda.synchronize()
+        want = oracle.nf4_gemv_ref(xb, ref["codes"], ref["absmax_q"], ref["c2"])
+        got = y.float().cpu().numpy()
+        assert got[0] == 0.0
+        assert oracle.rel_error(want[1:], got[1:]) <= REL_TOL

@@ -20,6 +20,7 @@ __all__ = [
     "w4a16_gemm", "w4a8_gemm", "w4_gemm_workspace_bytes", "w4_status_string", "w4_last_error",
     "w4_abi_version", "w4_portable_save", "w4_portable_info_read", "w4_portable_load",
     "w4a16_gate_up", "w4a8_gate_up", "ACT_SILU", "ACT_GELU_TANH",
+    "w4_nf4_levels", "w4_nf4_quantize", "w4_nf4_gemv",
     "FRACS_PLAIN", "FRACS_11",
 ]
 
@@ -79,6 +80,11 @@ def lib():
     L.w4a16_gate_up.argtypes = [P, i64, i64, P, P, P, P, i64, I, I, P, P]
     L.w4a8_gate_up.argtypes = [P, i64, i64, P, P, P, P, i64, I, I, P, P, P, P]
     L.w4a16_gate_up.restype = I
+    L.w4_nf4_levels.argtypes = [P]
+    L.w4_nf4_quantize.argtypes = [P, i64, i64, P, P, P, P]
+    L.w4_nf4_gemv.argtypes = [P, i64, P, P, P, i64, P, P]
+    for name in ("w4_nf4_levels", "w4_nf4_quantize", "w4_nf4_gemv"):
+        getattr(L, name).restype = I
     L.w4a8_gate_up.restype = I
     cp = ctypes.c_char_p
     L.w4_portable_save.argtypes = [cp, i64, i64, I, I, P, I, P, P, P, P]
@@ -379,3 +385,41 @@ def w4a8_gate_up(X: torch.Tensor, gate: dict, up: dict, G: int, act="silu", *, H
                             _stream(dev, stream))
     _check("w4a8_gate_up", rc)
     return H, xq, xscale
+
+
+# -------------------------------------------------------- NF4 comparator
+
+def w4_nf4_levels():
+    """The 16 NF4 levels (float32, ascending) the library's kernels use."""
+    import numpy as np
+    out = np.empty(16, np.float32)
+    _check("w4_nf4_levels", lib().w4_nf4_levels(_ptr_np(out)))
+    return out
+
+
+def w4_nf4_quantize(W: torch.Tensor, *, stream=None) -> dict:
+    """NF4 of fp32 ``W[N, K]`` (K a multiple of 64): ``packed`` (uint8 [N, K/2]),
+    ``absmax_q`` (uint8 [N*K/64]) and ``absmax_c2`` (float32 [ceil(N*K/64/256)])."""
+    N, K = W.shape
+    dev = W.device
+    nb = N * (K // 64)
+    packed = _empty((N, K // 2), torch.uint8, dev)
+    aq = _empty((nb,), torch.uint8, dev)
+    c2 = _empty(((nb + 255) // 256,), torch.float32, dev)
+    rc = lib().w4_nf4_quantize(_dev(W, "W", torch.float32), N, K, _dev(packed, "packed"), _dev(aq, "absmax_q"),
+                               _dev(c2, "absmax_c2", torch.float32), _stream(dev, stream))
+    _check("w4_nf4_quantize", rc)
+    return {"packed": packed, "absmax_q": aq, "absmax_c2": c2}
+
+
+def w4_nf4_gemv(x: torch.Tensor, nf4: dict, *, y=None, stream=None):
+    """``y[N] = bf16(W' . x)`` for one bf16 row ``x[K]`` and NF4 weights from ``w4_nf4_quantize``."""
+    K = x.numel()
+    N = nf4["packed"].shape[0]
+    dev = x.device
+    y = _empty((N,), torch.bfloat16, dev) if y is None else y
+    rc = lib().w4_nf4_gemv(_dev(x, "x", torch.bfloat16), K, _dev(nf4["packed"], "packed"), _dev(nf4["absmax_q"], "absmax_q"),
+                           _dev(nf4["absmax_c2"], "absmax_c2", torch.float32), N, _dev(y, "y", torch.bfloat16),
+                           _stream(dev, stream))
+    _check("w4_nf4_gemv", rc)
+    return y

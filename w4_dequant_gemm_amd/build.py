@@ -19,8 +19,8 @@ OUT = os.path.join(HERE, "libw4.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-KERNELS = ["quantize.hip", "prepack.hip", "rowquant.hip", "skinny.hip", "gemm.hip"]
-NO_CONTRACT = {"quantize.hip", "rowquant.hip"}
+KERNELS = ["quantize.hip", "prepack.hip", "rowquant.hip", "skinny.hip", "gemm.hip", "nf4.hip"]
+NO_CONTRACT = {"quantize.hip", "rowquant.hip", "nf4.hip"}
 HOST_SOURCES = ["api.cpp", "portable.cpp"]   # host C++ (argument checks, file I/O)
 
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

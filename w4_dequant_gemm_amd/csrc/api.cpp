@@ -139,6 +139,60 @@ w4::MulParams with_split(w4::MulParams p, void* workspace) {
 }  // namespace
 
 namespace {
+// The 16 NF4 levels (QLoRA's construction): normal quantiles at 8 evenly
+// spaced probabilities from delta down to 1/2 (exclusive) for the positive
+// side and 7 for the negative side, delta = (1 - 1/30 + 1 - 1/32) / 2, and
+// an exact zero, divided by the largest and rounded once to fp32.  The
+// inverse normal CDF is found by bisection on Phi(x) = erfc(-x / sqrt 2) / 2
+// in double precision (to the last bit of the bracket).
+double inv_normal_cdf(double p) {
+    double lo = -10.0, hi = 10.0;
+    for (int i = 0; i < 200; ++i) {
+        const double mid = 0.5 * (lo + hi);
+        if (mid == lo || mid == hi) break;
+        if (0.5 * std::erfc(-mid / std::sqrt(2.0)) < p) lo = mid;
+        else hi = mid;
+    }
+    return 0.5 * (lo + hi);
+}
+
+void nf4_levels_compute(float* out) {
+    const double delta = 0.5 * (1.0 - 1.0 / 30.0) + 0.5 * (1.0 - 1.0 / 32.0);
+    double v[16];
+    int n = 0;
+    for (int i = 0; i < 7; ++i) v[n++] = -inv_normal_cdf(delta + (0.5 - delta) * i / 7.0);
+    v[n++] = 0.0;
+    for (int i = 0; i < 8; ++i) v[n++] = inv_normal_cdf(delta + (0.5 - delta) * i / 8.0);
+    double vmax = 0.0;
+    for (int i = 0; i < 16; ++i) vmax = v[i] > vmax ? v[i] : vmax;
+    // ascending: the negative side from -1 up to 0, then the positive side from 0 up to 1
+    float sorted[16];
+    for (int i = 0; i < 7; ++i) sorted[i] = static_cast<float>(v[i] / vmax);
+    sorted[7] = 0.0f;
+    for (int i = 0; i < 8; ++i) sorted[15 - i] = static_cast<float>(v[8 + i] / vmax);
+    for (int i = 0; i < 16; ++i) out[i] = sorted[i];
+}
+
+// The table, computed once (the bisection costs tens of microseconds, more
+// than a decode product).
+struct Nf4Table {
+    float v[16];
+    Nf4Table() { nf4_levels_compute(v); }
+};
+
+void nf4_levels(float* out) {
+    static const Nf4Table table;
+    for (int i = 0; i < 16; ++i) out[i] = table.v[i];
+}
+
+int check_nf4_shape(const char* fn, int64_t N, int64_t K) {
+    if (N < 0) return fail(W4_EINVAL, "%s: N = %lld must be >= 0", fn, static_cast<long long>(N));
+    if (K <= 0 || K % 64 != 0)
+        return fail(W4_EINVAL, "%s: K = %lld must be a positive multiple of the NF4 block (64)", fn,
+                    static_cast<long long>(K));
+    return W4_OK;
+}
+
 // shared checks of the gate and up product
 int gate_up_common(const char* fn, const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq_gate,
                    const uint32_t* sz_gate, const uint32_t* wq_up, const uint32_t* sz_up, int64_t N, int G, int act,
@@ -270,6 +324,54 @@ int w4a8_gate_up(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq_gat
         p.xscale_out = nullptr;
     }
     return hip_status(w4::launch_skinny(p, stream), fn);
+}
+
+int w4_nf4_levels(float* levels) {
+    if (!levels) return fail(W4_EINVAL, "w4_nf4_levels: levels is NULL");
+    nf4_levels(levels);
+    return W4_OK;
+}
+
+int w4_nf4_quantize(const float* W, int64_t N, int64_t K, uint8_t* packed, uint8_t* absmax_q, float* absmax_c2,
+                    hipStream_t stream) {
+    const char* fn = "w4_nf4_quantize";
+    W4_TRY(check_nf4_shape(fn, N, K));
+    if (N == 0) return W4_OK;
+    W4_REQUIRE_PTR(fn, W);
+    W4_REQUIRE_PTR(fn, packed);
+    if (!absmax_q || !absmax_c2) return fail(W4_EINVAL, "%s: absmax_q or absmax_c2 is NULL", fn);
+    w4::Nf4QuantParams p{};
+    p.W = W;
+    p.n_blocks = N * (K / 64);
+    nf4_levels(p.levels);
+    p.packed = packed;
+    p.absmax_q = absmax_q;
+    p.c2 = absmax_c2;
+    return hip_status(w4::launch_nf4_quantize(p, stream), fn);
+}
+
+int w4_nf4_gemv(const uint16_t* x, int64_t K, const uint8_t* packed, const uint8_t* absmax_q, const float* absmax_c2,
+                int64_t N, uint16_t* y, hipStream_t stream) {
+    const char* fn = "w4_nf4_gemv";
+    W4_TRY(check_nf4_shape(fn, N, K));
+    if (K > w4::kNf4MaxK)
+        return fail(W4_EUNSUPPORTED, "%s: K = %lld above %lld (one 32-k chunk per lane of a 1024-lane workgroup)", fn,
+                    static_cast<long long>(K), static_cast<long long>(w4::kNf4MaxK));
+    if (N == 0) return W4_OK;
+    W4_REQUIRE_PTR(fn, x);
+    W4_REQUIRE_PTR(fn, packed);
+    W4_REQUIRE_PTR(fn, y);
+    if (!absmax_q || !absmax_c2) return fail(W4_EINVAL, "%s: absmax_q or absmax_c2 is NULL", fn);
+    w4::Nf4GemvParams p{};
+    p.x = x;
+    p.K = K;
+    p.N = N;
+    p.packed = packed;
+    p.absmax_q = absmax_q;
+    p.c2 = absmax_c2;
+    p.y = y;
+    nf4_levels(p.levels);
+    return hip_status(w4::launch_nf4_gemv(p, stream), fn);
 }
 
 const char* w4_status_string(int status) {

@@ -101,4 +101,26 @@ struct GemmSplit {
 GemmSplit gemm_split(int64_t M, int64_t K, int64_t N);
 size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
 
+// NF4 comparator (normal-quantile levels, blocks of 64, double-quantized scales)
+constexpr int64_t kNf4MaxK = 32768;             // one 32-k chunk per lane of a 1024-lane workgroup
+struct Nf4QuantParams {
+    const float* W;          // [n_blocks * 64] fp32
+    int64_t n_blocks;
+    float levels[16];
+    uint8_t* packed;         // [n_blocks * 32] codes, k even in the low nibble
+    uint8_t* absmax_q;       // [n_blocks] 8-bit block scales
+    float* c2;               // [ceil(n_blocks / 256)] second-level constants
+};
+hipError_t launch_nf4_quantize(const Nf4QuantParams& p, hipStream_t stream);
+struct Nf4GemvParams {
+    const uint16_t* x;       // [K] bf16
+    int64_t K, N;
+    const uint8_t* packed;   // [N, K/2]
+    const uint8_t* absmax_q; // [N * K / 64]
+    const float* c2;
+    uint16_t* y;             // [N] bf16
+    float levels[16];
+};
+hipError_t launch_nf4_gemv(const Nf4GemvParams& p, hipStream_t stream);
+
 }  // namespace w4
