@@ -277,7 +277,7 @@ def main():
         for idx, (N, K) in enumerate(wl12.shapes):
             base = quantize_to_gpu_layout(w4, torch, synth.weight(wl12, idx), 128, synth.FRACS_11)
             copies = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(15)]
-            for M in wl12.ms:
+            for M in sorted(set(wl12.ms) | {128}):
                 x = bf16(synth.activations_bf16_bits(wl12, M, K))
                 y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
                 xq = torch.empty((M, K), dtype=torch.uint8, device=dev)

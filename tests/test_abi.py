@@ -100,6 +100,13 @@ def test_gemm_workspace_sizes_and_checks(lib):
     assert ws(2048, 8192, 32768) == 0                        # 1024 tiles: four full rounds
     assert ws(300, 4096, 33000) == 2 * 8 * tile              # 258 tiles: the last 2 in eighths
     assert ws(64, 15360, 3840) == 0                          # weight-streaming kernel
+    # 64 < M <= 128: 64 x 128 tiles, split along K towards 512 workgroups,
+    # at most 16 ways and at least 4 K steps of 64 each
+    mid = 64 * 128 * 4
+    assert ws(128, 3840, 15360) == 240 * 3 * mid             # 240 tiles: 3 splits
+    assert ws(100, 15360, 3840) == 60 * 9 * mid              # 60 tiles: 9 splits
+    assert ws(128, 576, 130) == 4 * 2 * mid                  # 9 K steps: 2 splits
+    assert ws(65, 256, 128) == 0                             # 4 K steps: no split
     assert ws(256, 96, 3840) == 0                            # K not a multiple of 64: 128 x 128 tiles
     assert ws(256, 512, 256) == 0                            # too few K steps to split
     assert ws(-1, 512, 256) == 0 and ws(256, 0, 256) == 0

@@ -415,3 +415,58 @@ def test_gate_up_products(kind):
                 assert err <= REL_TOL, f"{kind} {act} M={M}: relative error {err:.3e}"
     with pytest.raises(w4.W4Error):
         w4.w4a16_gate_up(bf16_dev(_x("llama8b_decode", 33, 4096)), pg, pu, 32, "silu")
+
+
+def test_mid_size_products():
+    # 64 < M <= 128 with K a multiple of 64: 64 x 128 output tiles, split
+    # along K into fp32 partials (a caller workspace holding NaNs on entry)
+    # when the tiles are few; both kinds, every group size, per-channel
+    # groups, ragged M and N, a zero row, and the 12B shapes at M = 128 on
+    # sampled outputs
+    require_gpu()
+    import torch
+    import w4_dequant_gemm_amd as w4
+    cases = [(200, 1024, 32, "asym", (65, 100)), (333, 2048, 64, "sym", (128,)),
+             (130, 576, 576, "asym", (97,)), (256, 4096, 128, "asym", (128, 70))]
+    for N, K, G, mode, Ms in cases:
+        W = synth.normal_matrix(60 + N, N, K, 0.03)
+        q = oracle.quantize(W, G, mode)
+        pk, G2 = prepack_dev(q)
+        for M in Ms:
+            Xb = synth.to_bf16_bits(synth.normal_matrix(M + K, M, K))
+            Xb[M // 2] = 0
+            need = w4.w4_gemm_workspace_bytes(M, K, N)
+            ws = torch.full((need // 4 + 16,), float("nan"), dtype=torch.float32, device="cuda")
+            print(f"[mid] N={N} K={K} G={G} {mode} M={M} workspace={need}", flush=True)
+            Y = w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G2, workspace=ws)
+            Y8, xq, xs = w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G2, workspace=ws)
+            torch.cuda.synchronize()
+            want = oracle.gemm_ref(oracle.bf16_bits_to_f64(Xb), q["packed"], q["scale"], q["zero"], G2, mode)
+            want8, rq, rs = oracle.w4a8_ref(Xb, q["packed"], q["scale"], q["zero"], G2, mode)
+            assert_bits_equal(host(xq), rq, "E4M3 activations")
+            assert np.all(bits16(Y)[M // 2] & 0x7FFF == 0) and np.all(bits16(Y8)[M // 2] & 0x7FFF == 0)
+            e16 = oracle.rel_error(want, Y.float().cpu().numpy())
+            e8 = oracle.rel_error(want8, Y8.float().cpu().numpy())
+            assert e16 <= REL_TOL and e8 <= REL_TOL, (N, K, G, M, e16, e8)
+    # the 12B shapes at M = 128 (sampled rows and columns; K split 2 and 16 ways)
+    wl = synth.WORKLOADS["gemma12b_w4a8"]
+    rng = np.random.default_rng(61)
+    for idx in (0, 1):
+        q = oracle_quant("gemma12b_w4a8", idx, None, "asym", 128, 1)
+        pk, G = prepack_dev(q)
+        N, K = q["q"].shape
+        M = 128
+        Xb = synth.activations_bf16_bits(wl, M, K)
+        rows = np.sort(rng.choice(M, 24, replace=False))
+        cols = np.sort(rng.choice(N, 192, replace=False))
+        print(f"[mid] 12B[{idx}] N={N} K={K} M={M}", flush=True)
+        Y = w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G)
+        Y8, _, _ = w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G)
+        torch.cuda.synchronize()
+        want = oracle.gemm_ref(oracle.bf16_bits_to_f64(Xb), q["packed"], q["scale"], q["zero"], G, "asym",
+                               rows=rows, cols=cols)
+        want8, _, _ = oracle.w4a8_ref(Xb, q["packed"], q["scale"], q["zero"], G, "asym", rows=rows, cols=cols)
+        got = Y.float().cpu().numpy()[np.ix_(rows, cols)]
+        got8 = Y8.float().cpu().numpy()[np.ix_(rows, cols)]
+        assert oracle.rel_error(want, got) <= REL_TOL
+        assert oracle.rel_error(want8, got8) <= REL_TOL

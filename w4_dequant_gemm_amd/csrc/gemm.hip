@@ -473,6 +473,232 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm256_kernel(MulParams p) {
 
 
 // ---------------------------------------------------------------------------
+// Mid-size M (a few hundred rows at most): the register-path kernel above
+// with a smaller output tile, TBM x TBN = 64 x 128 or 128 x 128, so that the
+// 12B-class shapes give hundreds of tiles instead of 15-60 and the K split
+// (and its fp32 partial tiles) stays small.  About 48-64 KB of LDS and few
+// registers let two or three workgroups share a compute unit, so one
+// workgroup's conversion work runs while another's MFMAs do.  A and B have
+// their own thread-to-row maps (TBM and TBN rows); the conversion items of a
+// step are spread evenly over its MFMA slots.
+
+// The work of one workgroup of the TBM x TBN kernels (same scheme as
+// big::tile_job).
+template <int TBM, int TBN>
+__device__ __forceinline__ big::TileJob tile_job_t(const MulParams& p) {
+    const int64_t b = blockIdx.x;
+    const int64_t nt = (p.N + TBN - 1) / TBN;
+    const int KT_all = static_cast<int>(p.K / big::BK);
+    big::TileJob t;
+    int64_t tile;
+    if (b < p.split_t0) {
+        tile = b;
+        t.kb = 0;
+        t.KT = KT_all;
+        t.part = -1;
+    } else {
+        const int64_t j = (b - p.split_t0) / p.splits;
+        const int z = static_cast<int>((b - p.split_t0) % p.splits);
+        tile = p.split_t0 + j;
+        t.kb = z * KT_all / p.splits;
+        t.KT = (z + 1) * KT_all / p.splits - t.kb;
+        t.part = j * p.splits + z;
+    }
+    t.m_base = (tile / nt) * TBM;
+    t.n_base = (tile % nt) * TBN;
+    return t;
+}
+
+template <int TBM, int TBN, int WM, int WN, bool XF8>
+__global__ void __launch_bounds__(64 * WM * WN) gemm_mid_kernel(MulParams p) {
+    using big::BK;
+    using big::lds_off;
+    constexpr int NT = 64 * WM * WN;
+    constexpr int TM = TBM / WM, TN = TBN / WN;
+    constexpr int FI = TM / 32, FJ = TN / 32;
+    constexpr int TPRA = NT / TBM, CPTA = (BK / 8) / TPRA;   // A: threads per row, 8-k chunks per thread
+    constexpr int TPRB = NT / TBN, CPTB = (BK / 8) / TPRB;   // B: threads per row, code words per thread
+    constexpr int XB = XF8 ? 1 : 2;
+    constexpr int ALD = CPTA * 8 * XB / 16;                  // 16-byte activation loads per thread and step
+    constexpr int SZN = CPTB / 4;
+    static_assert(FI >= 1 && FJ >= 1 && TPRA >= 1 && TPRB >= 1 && ALD >= 1 && CPTB % 4 == 0, "tile split");
+    constexpr int SA = TBM * BK, SB = TBN * BK;               // bf16 elements per stage and operand
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (SA + SB)];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const big::TileJob job = tile_job_t<TBM, TBN>(p);
+    const int64_t m_base = job.m_base, n_base = job.n_base;
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const int kb = job.kb, KT = job.KT;
+    const int g_shift = group_shift(p.G);
+
+    float16_t acc[FI][FJ];
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int a_row = tid / TPRA, a_c0 = (tid % TPRA) * CPTA;
+    const int b_row = tid / TPRB, b_c0 = (tid % TPRB) * CPTB;
+    int64_t bn = n_base + b_row;
+    bn = bn < N ? bn : N - 1;               // rows past N or M compute values never stored
+    int64_t am = m_base + a_row;
+    am = am < M ? am : M - 1;
+    const TiledRow brow = tiled_row(p.wq, p.sz, bn, N, K, p.G);
+    // activation row address with its provenance hidden (see gemm256_kernel)
+    uint64_t arow_addr = reinterpret_cast<uint64_t>(static_cast<const uint8_t*>(p.X) + (am * K + a_c0 * 8) * XB);
+    asm volatile("" : "+v"(arow_addr));
+    typedef const u32x4_t __attribute__((address_space(1))) global_u4;
+    const global_u4* arow = (const global_u4*)arow_addr;
+
+    struct Regs {
+        uint4 a[ALD];
+        u32x4_t q[CPTB / 4];
+        uint32_t s[SZN];
+    };
+    Regs r0, r1;
+    constexpr int NLOAD = ALD + CPTB / 4 + SZN;
+    auto issue_load_item = [&](int kt, Regs& r, int it) {
+        kt = (kt < KT ? kt : KT - 1) + kb;
+        if (it < ALD) {
+            const u32x4_t t = arow[static_cast<int64_t>(kt) * (BK * XB / 16) + it];
+            r.a[it] = make_uint4(t[0], t[1], t[2], t[3]);
+        } else if (it < ALD + CPTB / 4) {
+            const int i = it - ALD;
+            r.q[i] = *reinterpret_cast<const u32x4_t*>(brow.tile_ptr(static_cast<int64_t>(kt) * (BK / 32) + b_c0 / 4 + i));
+        } else {
+            const int t = it - ALD - CPTB / 4;
+            r.s[t] = brow.group((kt * BK + b_c0 * 8 + 32 * t) >> g_shift);
+        }
+    };
+
+    // conversion items (as in gemm256_kernel)
+    const uint32_t bias16 = opaque_vgpr(0x64006400u);
+    float b_sc = 0.0f, b_cs = 0.0f;
+    uint32_t b_out[4];
+    auto b_pair = [&](int pr, const Regs& r, uint16_t* B) {
+        const int j = pr / 4, i = pr % 4;
+        if (i == 0 && j % 4 == 0) {
+            b_sc = half_bits_to_float(r.s[j / 4]);
+            b_cs = -(1024.0f + half_bits_to_float(r.s[j / 4] >> 16)) * b_sc;
+        }
+        const uint32_t h = ((r.q[j / 4][j % 4] >> (4 * i)) & 0x000F000Fu) | bias16;
+        const _Float16 lo = __builtin_bit_cast(_Float16, static_cast<uint16_t>(h & 0xFFFFu));
+        const _Float16 hi = __builtin_bit_cast(_Float16, static_cast<uint16_t>(h >> 16));
+        b_out[i] = pack_bf16x2(fmaf(static_cast<float>(lo), b_sc, b_cs), fmaf(static_cast<float>(hi), b_sc, b_cs));
+        if (i == 3)
+            *reinterpret_cast<uint4*>(B + lds_off(b_row, b_c0 + j)) = make_uint4(b_out[0], b_out[1], b_out[2], b_out[3]);
+    };
+    constexpr int A_ITEMS = XF8 ? 2 * ALD : ALD;
+    auto a_item = [&](int it, const Regs& r, uint16_t* A) {
+        if constexpr (!XF8) {
+            uint4 v = r.a[it];
+            asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+            *reinterpret_cast<uint4*>(A + lds_off(a_row, a_c0 + it)) = v;
+        } else {
+            const uint4 src = r.a[it / 2];
+            const uint32_t bw[2] = {(it & 1) ? src.z : src.x, (it & 1) ? src.w : src.y};
+            uint32_t o[4];
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                float2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(bw[jj]), false);
+                float2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(bw[jj]), true);
+                o[2 * jj] = pack_bf16x2(lo[0], lo[1]);
+                o[2 * jj + 1] = pack_bf16x2(hi[0], hi[1]);
+            }
+            *reinterpret_cast<uint4*>(A + lds_off(a_row, a_c0 + it)) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+    };
+    auto load_frags = [&](const uint16_t* A, const uint16_t* B, int kk, bf16x8_t (&a)[FI], bf16x8_t (&b)[FJ]) {
+        const int ch = 2 * kk + (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < FI; ++i)
+            a[i] = *reinterpret_cast<const bf16x8_t*>(A + lds_off(wm * TM + i * 32 + (lane & 31), ch));
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
+            b[j] = *reinterpret_cast<const bf16x8_t*>(B + lds_off(wn * TN + j * 32 + (lane & 31), ch));
+    };
+
+    // One K step: MFMAs of step kt from one stage; the conversion of step
+    // kt + 1 from `ready` into the other stage and the loads of step kt + 2
+    // into `next`, spread evenly over the MFMA slots; then a barrier.
+    constexpr int NSLOT = FI * FJ * (BK / 16);
+    constexpr int BP = 4 * CPTB;
+    auto step = [&](int kt, Regs& next, const Regs& ready) {
+        __builtin_amdgcn_sched_barrier(0);
+        const uint16_t* As = lds + (kt & 1) * (SA + SB);
+        const uint16_t* Bs = As + SA;
+        uint16_t* Ad = lds + ((kt + 1) & 1) * (SA + SB);
+        uint16_t* Bd = Ad + SA;
+        bf16x8_t fa[2][FI], fb[2][FJ];
+        load_frags(As, Bs, 0, fa[0], fb[0]);
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            if (kk + 1 < BK / 16) load_frags(As, Bs, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < FI * FJ; ++t) {
+                const int u = kk * FI * FJ + t;
+                const int i = t / FJ, j = t % FJ;
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j], acc[i][j], 0, 0, 0);
+#pragma unroll
+                for (int l = u * NLOAD / NSLOT; l < (u + 1) * NLOAD / NSLOT; ++l) {
+                    issue_load_item(kt + 2, next, l);
+                    asm volatile("" ::: "memory");
+                }
+#pragma unroll
+                for (int pr = u * BP / NSLOT; pr < (u + 1) * BP / NSLOT; ++pr) b_pair(pr, ready, Bd);
+#pragma unroll
+                for (int ai = u * A_ITEMS / NSLOT; ai < (u + 1) * A_ITEMS / NSLOT; ++ai) a_item(ai, ready, Ad);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        __syncthreads();
+    };
+
+#pragma unroll
+    for (int it = 0; it < NLOAD; ++it) issue_load_item(0, r0, it);
+#pragma unroll
+    for (int it = 0; it < NLOAD; ++it) issue_load_item(1, r1, it);
+#pragma unroll
+    for (int ai = 0; ai < A_ITEMS; ++ai) a_item(ai, r0, lds);
+#pragma unroll
+    for (int pr = 0; pr < BP; ++pr) b_pair(pr, r0, lds + SA);
+    __syncthreads();
+    int kt = 0;
+    for (; kt + 2 <= KT; kt += 2) {
+        step(kt, r0, r1);
+        step(kt + 1, r1, r0);
+    }
+    if (kt < KT) step(kt, r0, r1);
+
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) {
+            const int lc = wn * TN + j * 32 + (lane & 31);
+            const int64_t col = n_base + lc;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int lr = wm * TM + i * 32 + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
+                const int64_t row = m_base + lr;
+                if (job.part >= 0) {
+                    p.ws[job.part * (TBM * TBN) + lr * TBN + lc] = acc[i][j][r];
+                } else if (row < M && col < N) {
+                    float y = acc[i][j][r];
+                    if constexpr (XF8) y *= p.xscale[row];
+                    p.Y[row * N + col] = float_to_bf16_bits(y);
+                }
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
 // W4A16, M >= 128: activations straight from global memory into LDS.
 //
 // Same 256 x 256 tile, K step 64 and 2 x 2 waves of 128 x 128 outputs as
@@ -789,8 +1015,8 @@ __global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
 // fp32 sum of its `splits` partials in split order, times the row scale
 // (W4A8), rounded to bf16.  A thread takes four consecutive columns of one
 // tile row (16-byte loads; consecutive lanes read consecutive addresses).
+template <int BM, int BN>
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(MulParams p) {
-    using namespace big;
     const int64_t e4 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;   // element of the split tiles
     const int64_t j = e4 / (BM * BN);
     const int lr = static_cast<int>((e4 % (BM * BN)) / BN), lc = static_cast<int>(e4 % BN);
@@ -828,10 +1054,37 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(MulParams p) {
 //  * otherwise the tiles of the last, partial round are split, so that the
 //    round uses every compute unit and takes a fraction of a tile's time.
 // At most 16 splits, each of at least 8 K steps of 64.
+#ifndef W4_MID_MAXM
+#define W4_MID_MAXM 128     // the mid-size tiles serve M up to this (above the streaming kernel's range)
+#endif
+#ifndef W4_MID_BM
+#define W4_MID_BM 64        // tile rows of the mid-size kernel (64 or 128)
+#endif
+#ifndef W4_MID_WGS
+#define W4_MID_WGS 512      // workgroups the mid-size K split aims for (two or three share a compute unit)
+#endif
+bool use_mid(int64_t M, int64_t K) { return M <= W4_MID_MAXM && K % big::BK == 0; }
+
+// Mid-size tiles: when there are fewer tiles than the target, every tile is
+// split along K (at most 16 ways, each of at least 4 steps of 64).
 GemmSplit gemm_split(int64_t M, int64_t K, int64_t N) {
     constexpr int64_t kCUs = 256;
-    GemmSplit g{1, 0, 0};
-    if (M < 128 || K % big::BK != 0 || N <= 0) return g;
+    GemmSplit g{1, 0, 0, big::BM, big::BN};
+    if (N <= 0 || K % big::BK != 0) return g;
+    if (use_mid(M, K)) {
+        g.bm = W4_MID_BM;
+        g.bn = 128;
+        g.tiles = ((N + g.bn - 1) / g.bn) * ((M + g.bm - 1) / g.bm);
+        g.t0 = g.tiles;
+        int64_t s = (W4_MID_WGS + g.tiles - 1) / g.tiles;
+        if (s > (K / big::BK) / 4) s = (K / big::BK) / 4;
+        if (s > 16) s = 16;
+        if (s < 2) return g;
+        g.splits = static_cast<int>(s);
+        g.t0 = 0;
+        return g;
+    }
+    if (M < 128) return g;
     g.tiles = ((N + big::BN - 1) / big::BN) * ((M + big::BM - 1) / big::BM);
     g.t0 = g.tiles;
 #ifndef W4_TAIL_SPLIT
@@ -851,7 +1104,7 @@ GemmSplit gemm_split(int64_t M, int64_t K, int64_t N) {
 size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
     const GemmSplit g = gemm_split(M, K, N);
     if (g.splits == 1) return 0;
-    return static_cast<size_t>(g.tiles - g.t0) * g.splits * big::BM * big::BN * sizeof(float);
+    return static_cast<size_t>(g.tiles - g.t0) * g.splits * g.bm * g.bn * sizeof(float);
 }
 
 // wave grid of the register-path kernel (used for E4M3 activations): 4 x 2
@@ -862,8 +1115,35 @@ size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
 #endif
 constexpr int kBigWM = W4_BIG_WM, kBigWN = W4_BIG_WN;
 
+template <int TBM, bool XF8>
+hipError_t launch_mid(const MulParams& p, hipStream_t stream) {
+    constexpr int TBN = 128;
+    const int64_t tiles = ((p.N + TBN - 1) / TBN) * ((p.M + TBM - 1) / TBM);
+    MulParams q = p;
+    if (q.splits <= 1) {
+        q.splits = 1;
+        q.split_t0 = tiles;
+        q.ws = nullptr;
+    }
+    if (q.splits > q.K / big::BK || q.split_t0 < 0 || q.split_t0 > tiles || (q.splits > 1 && !q.ws))
+        return hipErrorInvalidValue;
+    const int64_t wgs = q.split_t0 + (tiles - q.split_t0) * q.splits;
+    hipLaunchKernelGGL((gemm_mid_kernel<TBM, TBN, 2, 2, XF8>), dim3(static_cast<unsigned>(wgs)), dim3(256), 0, stream, q);
+    if (q.splits > 1 && q.split_t0 < tiles) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t blocks = (tiles - q.split_t0) * (TBM * TBN / 1024);
+        hipLaunchKernelGGL((splitk_reduce_kernel<TBM, TBN>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, q);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm(const MulParams& p, hipStream_t stream) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
+    if (use_mid(p.M, p.K)) {
+        constexpr int bm = W4_MID_BM;
+        return p.x_fp8 ? launch_mid<bm, true>(p, stream) : launch_mid<bm, false>(p, stream);
+    }
     if (p.M >= 128 && p.K % big::BK == 0) {
         // the split schedule the workspace was sized for; every split keeps
         // at least one K step
@@ -891,7 +1171,7 @@ hipError_t launch_gemm(const MulParams& p, hipStream_t stream) {
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
             const int64_t blocks = (tiles - q.split_t0) * (big::BM * big::BN / 1024);
-            hipLaunchKernelGGL(splitk_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, q);
+            hipLaunchKernelGGL((splitk_reduce_kernel<big::BM, big::BN>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, q);
         }
         return hipGetLastError();
     }

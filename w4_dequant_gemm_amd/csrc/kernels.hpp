@@ -97,6 +97,7 @@ struct GemmSplit {
     int splits;
     int64_t t0;        // first split tile
     int64_t tiles;     // all output tiles
+    int bm, bn;        // output tile of the kernel the schedule is for
 };
 GemmSplit gemm_split(int64_t M, int64_t K, int64_t N);
 size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
