@@ -225,6 +225,32 @@ def main():
                                                "two_products_us": round(msa * 1e3, 3)}
             log(f"[bench] W4A16 8B gate+up M={M}: fused {msf*1e3:.2f} us ({by/(msf*1e-3)/1e9:.1f} GB/s), "
                 f"two products {msa*1e3:.2f} us")
+        # the same pair at prefill (M = 2048): the tiled pair GEMM against the
+        # two GEMMs followed by torch's SiLU-and-multiply
+        M = 2048
+        x = bf16(synth.activations_bf16_bits(wl8, M, Ku))
+        h = torch.empty((M, Nu), dtype=torch.bfloat16, device=dev)
+        ya = torch.empty((M, Nu), dtype=torch.bfloat16, device=dev)
+        yb = torch.empty((M, Nu), dtype=torch.bfloat16, device=dev)
+        wsb = w4.w4_gemm_workspace_bytes(M, Ku, Nu)
+        ws = torch.empty((max(wsb, 16),), dtype=torch.uint8, device=dev)
+
+        def fused_p():
+            w4.w4a16_gate_up(x, ups[0], ups[1], G, "silu", H=h)
+
+        def apart_p():
+            w4.w4a16_gemm(x, ups[0]["wq"], ups[0]["sz"], G, Y=ya, workspace=ws)
+            w4.w4a16_gemm(x, ups[1]["wq"], ups[1]["sz"], G, Y=yb, workspace=ws)
+            torch.mul(torch.nn.functional.silu(ya), yb, out=h)
+        msf = timer.time(fused_p, 10, 3)
+        msa = timer.time(apart_p, 10, 3)
+        fl = 2 * 2.0 * M * Nu * Ku
+        extra["w4a16_gate_up_8b_m2048"] = {"ms": round(msf, 4), "TFLOP/s": round(fl / (msf * 1e-3) / 1e12, 1),
+                                           "two_gemms_and_act_ms": round(msa, 4)}
+        log(f"[bench] W4A16 8B gate+up M=2048: fused {msf:.3f} ms ({fl/(msf*1e-3)/1e12:.1f} TFLOP/s), "
+            f"two GEMMs + SiLU*mul {msa:.3f} ms")
+        del x, h, ya, yb, ws
+
         # NF4 comparator at M = 1: the same up/down weights in NF4 (blocks of
         # 64, double-quantized scales), same rotation of copies
         for name, idx, x in (("up", 0, x_up), ("down", 1, x_dn)):

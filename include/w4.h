@@ -202,11 +202,15 @@ int w4a8_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const
  * activations and their row scale, exactly as w4a8_gemm), the activation and
  * product in fp32, one rounding to bf16.  act: W4_ACT_SILU, x / (1 + e^-x)
  * (SwiGLU blocks), or W4_ACT_GELU_TANH, 0.5 x (1 + tanh(sqrt(2/pi) (x +
- * 0.044715 x^3))) (GeGLU blocks).  The weight-streaming kernel reads both
- * matrices at the same 16 output columns per workgroup; H feeds the down
+ * 0.044715 x^3))) (GeGLU blocks).  Up to 32 rows the weight-streaming
+ * kernel reads both matrices at the same 16 output columns per workgroup;
+ * above, a tiled MFMA GEMM holds 128 columns of each weight per workgroup
+ * (one wave column sums the gate products, the other the up products of the
+ * same outputs) and needs K to be a multiple of 64 (else W4_EUNSUPPORTED).
+ * No workspace: the tiled form does not split K.  H feeds the down
  * projection (w4a8_gemm on one or two rows quantizes it to E4M3 inside its
  * own kernel).
- *   X            [M, K] bf16 in; 0 <= M <= 32 (larger M: W4_EUNSUPPORTED).
+ *   X            [M, K] bf16 in, M >= 0.
  *   wq_gate, sz_gate, wq_up, sz_up: two [N, K] weights in the GPU layout of
  *                w4_prepack, with the same G.
  *   H            [M, N] bf16 out.

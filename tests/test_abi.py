@@ -144,8 +144,8 @@ def test_gate_up_validation(lib):
     import w4_dequant_gemm_amd as w4
     fake = ctypes.c_void_p(0x1000)
     g = lib.w4a16_gate_up
-    assert g(fake, 33, 4096, fake, fake, fake, fake, 64, 128, 1, fake, None) == 2     # M > 32
-    assert "at most 32" in w4.w4_last_error()
+    assert g(fake, 33, 4000, fake, fake, fake, fake, 64, 32, 1, fake, None) == 2      # tiled form, K % 64 != 0
+    assert "multiple of 64" in w4.w4_last_error()
     assert g(fake, 1, 4096, fake, fake, fake, fake, 64, 128, 3, fake, None) == 1      # unknown activation
     assert g(fake, 1, 4096, fake, fake, None, fake, 64, 128, 1, fake, None) == 1      # no up weights
     assert g(None, 0, 4096, None, None, None, None, 64, 128, 1, None, None) == 0      # nothing to do

@@ -382,15 +382,17 @@ def test_gate_up_products(kind):
     # gate and up projections in one pass with the activation-and-multiply
     # epilogue, against act(X Wg'^T) * (X Wu'^T) in float64: 8B-class rows
     # (gate and up are disjoint row ranges of the 8B up weight), one to 32
-    # activation rows, both activations; and a ragged N with symmetric G = 32
-    # weights (the dequantizing form for more than two rows)
+    # activation rows in the streaming kernel and 48, 100, 300 in the tiled
+    # pair GEMM (64-, 128- and 256-row tiles), both activations; and a ragged
+    # N with symmetric G = 32 weights (the dequantizing form for more than
+    # two rows, and the tiled form at 70 rows)
     require_gpu()
     import torch
     import w4_dequant_gemm_amd as w4
     wl = synth.WORKLOADS["llama8b_decode"]
     W = synth.weight(wl, 0, rows=2048)
-    cases = [(W[:1024], W[1024:], 128, "asym", (1, 2, 3, 16, 32)),
-             (W[:1000, :1536], W[1000:2000, :1536], 32, "sym", (1, 2, 5))]
+    cases = [(W[:1024], W[1024:], 128, "asym", (1, 2, 3, 16, 32, 48, 100, 300)),
+             (W[:1000, :1536], W[1000:2000, :1536], 32, "sym", (1, 2, 5, 70))]
     for Wg, Wu, G, mode, Ms in cases:
         qg = oracle.quantize(np.ascontiguousarray(Wg), G, mode)
         qu = oracle.quantize(np.ascontiguousarray(Wu), G, mode)
@@ -413,8 +415,13 @@ def test_gate_up_products(kind):
                 torch.cuda.synchronize()
                 err = oracle.rel_error(want, H.float().cpu().numpy())
                 assert err <= REL_TOL, f"{kind} {act} M={M}: relative error {err:.3e}"
+    # above 32 rows the tiled form needs K to be a multiple of 64
+    Wr = synth.normal_matrix(62, 64, 1568, 0.05)
+    qr = oracle.quantize(Wr, 32, "asym")
+    pr_, _ = prepack_dev(qr)
     with pytest.raises(w4.W4Error):
-        w4.w4a16_gate_up(bf16_dev(_x("llama8b_decode", 33, 4096)), pg, pu, 32, "silu")
+        w4.w4a16_gate_up(bf16_dev(_x("llama8b_decode", 33, 1568)), pr_, pr_, 32, "silu")
+    w4.w4a16_gate_up(bf16_dev(_x("llama8b_decode", 32, 1568)), pr_, pr_, 32, "silu")
 
 
 def test_mid_size_products():

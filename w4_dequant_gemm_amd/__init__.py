@@ -357,7 +357,7 @@ def w4a8_gemm(X: torch.Tensor, wq: torch.Tensor, sz: torch.Tensor, G: int, *, Y=
 
 def w4a16_gate_up(X: torch.Tensor, gate: dict, up: dict, G: int, act="silu", *, H=None, stream=None):
     """Gate and up projections in one pass: ``H = bf16(act(X . Wg'^T) * (X . Wu'^T))``
-    for bf16 ``X[M, K]`` (M <= 32); ``gate`` and ``up`` are GPU layouts from
+    for bf16 ``X[M, K]`` (above 32 rows K must be a multiple of 64); ``gate`` and ``up`` are GPU layouts from
     ``w4_prepack`` (``wq``, ``sz``); ``act`` is ``"silu"`` or ``"gelu_tanh"``."""
     M, K = X.shape
     N = gate["wq"].shape[0]

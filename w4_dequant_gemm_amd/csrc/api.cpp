@@ -197,10 +197,17 @@ int check_nf4_shape(const char* fn, int64_t N, int64_t K) {
 int gate_up_common(const char* fn, const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq_gate,
                    const uint32_t* sz_gate, const uint32_t* wq_up, const uint32_t* sz_up, int64_t N, int G, int act,
                    uint16_t* H) {
-    W4_TRY(mul_common(fn, X, M, K, wq_gate, sz_gate, N, G, H, nullptr, 0));
-    if (M > w4::kGateUpMaxM)
-        return fail(W4_EUNSUPPORTED, "%s: M = %lld rows; the fused gate and up product takes at most %lld", fn,
-                    static_cast<long long>(M), static_cast<long long>(w4::kGateUpMaxM));
+    W4_TRY(check_group(fn, N, K, G));
+    if (M < 0) return fail(W4_EINVAL, "%s: M = %lld must be >= 0", fn, static_cast<long long>(M));
+    if (M > 0 && N > 0) {
+        W4_REQUIRE_PTR(fn, X);
+        W4_REQUIRE_PTR(fn, wq_gate);
+        W4_REQUIRE_PTR(fn, sz_gate);
+        W4_REQUIRE_PTR(fn, H);
+    }
+    if (M > w4::kGateUpMaxM && K % 64 != 0)
+        return fail(W4_EUNSUPPORTED, "%s: M = %lld rows take the tiled form, which needs K a multiple of 64 (K = %lld)",
+                    fn, static_cast<long long>(M), static_cast<long long>(K));
     if (act != W4_ACT_SILU && act != W4_ACT_GELU_TANH)
         return fail(W4_EINVAL, "%s: act = %d is neither W4_ACT_SILU nor W4_ACT_GELU_TANH", fn, act);
     if (M == 0 || N == 0) return W4_OK;
@@ -300,6 +307,7 @@ int w4a16_gate_up(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq_ga
     p.wq2 = wq_up;
     p.sz2 = sz_up;
     p.act = act;
+    if (M > w4::kGateUpMaxM) return hip_status(w4::launch_gemm_pair(p, stream), fn);
     return hip_status(w4::launch_skinny(p, stream), fn);
 }
 
@@ -315,6 +323,15 @@ int w4a8_gate_up(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq_gat
     p.wq2 = wq_up;
     p.sz2 = sz_up;
     p.act = act;
+    if (M > w4::kGateUpMaxM) {
+        w4::RowQuantParams rq{X, M, K, xq, xscale};
+        W4_TRY(hip_status(w4::launch_rowquant(rq, stream), fn));
+        p.X = xq;
+        p.xscale = xscale;
+        p.xq_out = nullptr;
+        p.xscale_out = nullptr;
+        return hip_status(w4::launch_gemm_pair(p, stream), fn);
+    }
     if (!w4::skinny_quantizes_rows(M, K)) {
         w4::RowQuantParams rq{X, M, K, xq, xscale};
         W4_TRY(hip_status(w4::launch_rowquant(rq, stream), fn));

@@ -104,6 +104,15 @@ __device__ __forceinline__ TiledRow tiled_row(const uint32_t* wq, const uint32_t
     return r;
 }
 
+// Activation of the gate projection in a gated MLP: SiLU x / (1 + e^-x)
+// (SwiGLU) or the tanh form of GELU, 0.5 x (1 + tanh(sqrt(2/pi) (x +
+// 0.044715 x^3))) (GeGLU), in fp32.
+__device__ __forceinline__ float activation(int act, float x) {
+    if (act == 1) return x / (1.0f + expf(-x));
+    const float t = 0.7978845608028654f * (x + 0.044715f * x * x * x);
+    return 0.5f * x * (1.0f + tanhf(t));
+}
+
 // Butterfly sum over the 64 lanes of a wavefront; every lane gets the total.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -509,7 +509,12 @@ __device__ __forceinline__ big::TileJob tile_job_t(const MulParams& p) {
     return t;
 }
 
-template <int TBM, int TBN, int WM, int WN, bool XF8>
+// PAIR: the gated MLP front half.  The B tile holds TBN / 2 columns of the
+// gate weight (rows 0 .. TBN/2 - 1) and the same columns of the up weight
+// (rows TBN/2 ..), so with two wave columns the waves of column 0 sum
+// gate products and those of column 1 up products for the same outputs; at
+// the end the up sums go through LDS and H = bf16(act(gate) * up).
+template <int TBM, int TBN, int WM, int WN, bool XF8, bool PAIR = false>
 __global__ void __launch_bounds__(64 * WM * WN) gemm_mid_kernel(MulParams p) {
     using big::BK;
     using big::lds_off;
@@ -522,6 +527,8 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_mid_kernel(MulParams p) {
     constexpr int ALD = CPTA * 8 * XB / 16;                  // 16-byte activation loads per thread and step
     constexpr int SZN = CPTB / 4;
     static_assert(FI >= 1 && FJ >= 1 && TPRA >= 1 && TPRB >= 1 && ALD >= 1 && CPTB % 4 == 0, "tile split");
+    static_assert(!PAIR || (WN == 2 && TN == TBN / 2), "pair tiles: one wave column per weight");
+    constexpr int OUTN = PAIR ? TBN / 2 : TBN;                 // output columns per tile
     constexpr int SA = TBM * BK, SB = TBN * BK;               // bf16 elements per stage and operand
     __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (SA + SB)];
 
@@ -529,7 +536,7 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_mid_kernel(MulParams p) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
-    const big::TileJob job = tile_job_t<TBM, TBN>(p);
+    const big::TileJob job = tile_job_t<TBM, OUTN>(p);
     const int64_t m_base = job.m_base, n_base = job.n_base;
     const int64_t M = p.M, N = p.N, K = p.K;
     const int kb = job.kb, KT = job.KT;
@@ -545,11 +552,12 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_mid_kernel(MulParams p) {
 
     const int a_row = tid / TPRA, a_c0 = (tid % TPRA) * CPTA;
     const int b_row = tid / TPRB, b_c0 = (tid % TPRB) * CPTB;
-    int64_t bn = n_base + b_row;
+    const bool b_up = PAIR && b_row >= OUTN;
+    int64_t bn = n_base + (PAIR ? b_row % OUTN : b_row);
     bn = bn < N ? bn : N - 1;               // rows past N or M compute values never stored
     int64_t am = m_base + a_row;
     am = am < M ? am : M - 1;
-    const TiledRow brow = tiled_row(p.wq, p.sz, bn, N, K, p.G);
+    const TiledRow brow = tiled_row(b_up ? p.wq2 : p.wq, b_up ? p.sz2 : p.sz, bn, N, K, p.G);
     // activation row address with its provenance hidden (see gemm256_kernel)
     uint64_t arow_addr = reinterpret_cast<uint64_t>(static_cast<const uint8_t*>(p.X) + (am * K + a_c0 * 8) * XB);
     asm volatile("" : "+v"(arow_addr));
@@ -677,6 +685,42 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_mid_kernel(MulParams p) {
     }
     if (kt < KT) step(kt, r0, r1);
 
+    if constexpr (PAIR) {
+        // up sums of wave (wm, 1) to LDS in register order, read back by wave
+        // (wm, 0), whose registers hold the gate sums of the same outputs
+        static_assert(TBM * TN * 4 <= 2 * (SA + SB) * 2, "the up sums fit the operand stages");
+        float* up = reinterpret_cast<float*>(lds) + wm * (FI * FJ * 16 * 64);
+        __syncthreads();
+        if (wn == 1) {
+#pragma unroll
+            for (int i = 0; i < FI; ++i)
+#pragma unroll
+                for (int j = 0; j < FJ; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) up[((i * FJ + j) * 16 + r) * 64 + lane] = acc[i][j][r];
+        }
+        __syncthreads();
+        if (wn == 0) {
+#pragma unroll
+            for (int i = 0; i < FI; ++i)
+#pragma unroll
+                for (int j = 0; j < FJ; ++j) {
+                    const int64_t col = n_base + j * 32 + (lane & 31);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int64_t row = m_base + wm * TM + i * 32 + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
+                        if (row < M && col < N) {
+                            const float rs = XF8 ? p.xscale[row] : 1.0f;
+                            const float g = acc[i][j][r] * rs;
+                            const float u = up[((i * FJ + j) * 16 + r) * 64 + lane] * rs;
+                            p.Y[row * N + col] = float_to_bf16_bits(activation(p.act, g) * u);
+                        }
+                    }
+                }
+        }
+        return;
+    }
+
 #pragma unroll
     for (int i = 0; i < FI; ++i)
 #pragma unroll
@@ -737,6 +781,12 @@ __device__ __forceinline__ int swz(int row) { return big::swizzle_fn(W4_DSWZ, ro
 __device__ __forceinline__ int lds_off(int row, int c) { return row * BK + ((c ^ swz(row)) << 3); }
 }  // namespace dma
 
+// PAIR: the gated MLP front half on 256 x 128 output tiles.  Weight rows
+// 0 .. 127 of the B tile are 128 columns of the gate weight, rows 128 .. 255
+// the same columns of the up weight, so wave column 0 sums gate products and
+// wave column 1 up products of the same outputs; after the loop the up sums
+// pass through LDS and H = bf16(act(gate) * up).  No K split.
+template <bool PAIR>
 __global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
     using namespace dma;
     constexpr int FI = 4, FJ = 4;
@@ -752,7 +802,7 @@ __global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
-    const big::TileJob job = big::tile_job(p);
+    const big::TileJob job = PAIR ? tile_job_t<BM, BN / 2>(p) : big::tile_job(p);
     const int64_t m_base = job.m_base, n_base = job.n_base;
     const int64_t M = p.M, N = p.N, K = p.K;
     const int kb = job.kb, KT = job.KT;      // this workgroup's K steps
@@ -801,9 +851,10 @@ __global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
     };
 
     // Weights: thread tid owns row tid of the tile (8 code words per step)
-    int64_t bn = n_base + tid;
+    const bool b_up = PAIR && tid >= BN / 2;
+    int64_t bn = n_base + (PAIR ? tid % (BN / 2) : tid);
     bn = bn < N ? bn : N - 1;
-    const TiledRow brow = tiled_row(p.wq, p.sz, bn, N, K, p.G);
+    const TiledRow brow = tiled_row(b_up ? p.wq2 : p.wq, b_up ? p.sz2 : p.sz, bn, N, K, p.G);
     struct Regs {
         u32x4_t q[CPT / 4];
         uint32_t s[SZN];
@@ -994,6 +1045,50 @@ __global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
     __builtin_amdgcn_s_waitcnt(0);
     asm volatile("" ::: "memory");
 
+    if constexpr (PAIR) {
+        // one wave row at a time: its gate sums (wave (h, 0)) and up sums
+        // (wave (h, 1)), 64 KB each in register order, go to LDS (lds_a0/a1
+        // and lds_b0/b1), then all threads form the 128 x 128 outputs of the
+        // half row by row (coalesced stores, one copy of the activation code)
+        constexpr int kHalf = STAGE / 2;      // floats per 32 KB stage
+        float* const g0 = reinterpret_cast<float*>(lds_a0);
+        float* const g1 = reinterpret_cast<float*>(lds_a1);
+        float* const u0 = reinterpret_cast<float*>(lds_b0);
+        float* const u1 = reinterpret_cast<float*>(lds_b1);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            __syncthreads();
+            if (wm == hh) {
+                float* lo = wn == 0 ? g0 : u0;
+                float* hi = wn == 0 ? g1 : u1;
+#pragma unroll
+                for (int i = 0; i < FI; ++i)
+#pragma unroll
+                    for (int j = 0; j < FJ; ++j)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int e = ((i * FJ + j) * 16 + r) * 64 + lane;
+                            (e < kHalf ? lo : hi)[e % kHalf] = acc[i][j][r];
+                        }
+            }
+            __syncthreads();
+            for (int o = tid; o < 128 * 128; o += NT) {
+                const int lr = o >> 7, lc = o & 127;
+                const int64_t row = m_base + hh * 128 + lr, col = n_base + lc;
+                if (row >= M || col >= N) continue;
+                // register order of output (lr, lc) in the wave's 128 x 128 tile
+                const int rr = lr & 31;
+                const int r = (rr >> 3) * 4 + (rr & 3);
+                const int ln = ((rr >> 2) & 1) * 32 + (lc & 31);
+                const int e = (((lr >> 5) * FJ + (lc >> 5)) * 16 + r) * 64 + ln;
+                const float g = e < kHalf ? g0[e] : g1[e - kHalf];
+                const float u = e < kHalf ? u0[e] : u1[e - kHalf];
+                p.Y[row * N + col] = float_to_bf16_bits(activation(p.act, g) * u);
+            }
+        }
+        return;
+    }
+
     // epilogue: register r of lane l holds row (r%4) + 4(l/32) + 8(r/4), column l%32
 #pragma unroll
     for (int i = 0; i < FI; ++i)
@@ -1138,6 +1233,39 @@ hipError_t launch_mid(const MulParams& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int TBM, bool XF8>
+hipError_t launch_pair_t(const MulParams& p, hipStream_t stream) {
+    constexpr int OUTN = 128;
+    const int64_t tiles = ((p.N + OUTN - 1) / OUTN) * ((p.M + TBM - 1) / TBM);
+    MulParams q = p;
+    q.splits = 1;
+    q.split_t0 = tiles;
+    q.ws = nullptr;
+    hipLaunchKernelGGL((gemm_mid_kernel<TBM, 2 * OUTN, 2, 2, XF8, true>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0,
+                       stream, q);
+    return hipGetLastError();
+}
+
+// Gate and up GEMM (M above the streaming kernel's pair range): output tiles
+// of TBM rows (64, 128 or 256 by M) by 128 columns, no K split.
+hipError_t launch_gemm_pair(const MulParams& p, hipStream_t stream) {
+    if (p.M == 0 || p.N == 0) return hipSuccess;
+    if (p.K % big::BK != 0 || !p.wq2 || !p.sz2) return hipErrorInvalidValue;
+    if (!p.x_fp8 && p.M >= 256) {
+        // W4A16: the activations-direct-to-LDS kernel on 256 x 128 output tiles
+        const int64_t tiles = ((p.N + big::BN / 2 - 1) / (big::BN / 2)) * ((p.M + big::BM - 1) / big::BM);
+        MulParams q = p;
+        q.splits = 1;
+        q.split_t0 = tiles;
+        q.ws = nullptr;
+        hipLaunchKernelGGL(gemm256_dma_kernel<true>, dim3(static_cast<unsigned>(tiles)), dim3(dma::NT), 0, stream, q);
+        return hipGetLastError();
+    }
+    if (p.M <= 64) return p.x_fp8 ? launch_pair_t<64, true>(p, stream) : launch_pair_t<64, false>(p, stream);
+    if (p.M <= 128) return p.x_fp8 ? launch_pair_t<128, true>(p, stream) : launch_pair_t<128, false>(p, stream);
+    return p.x_fp8 ? launch_pair_t<256, true>(p, stream) : launch_pair_t<256, false>(p, stream);
+}
+
 hipError_t launch_gemm(const MulParams& p, hipStream_t stream) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
     if (use_mid(p.M, p.K)) {
@@ -1164,7 +1292,7 @@ hipError_t launch_gemm(const MulParams& p, hipStream_t stream) {
         if (q.x_fp8)
             hipLaunchKernelGGL((gemm256_kernel<kBigWM, kBigWN, true>), grid, dim3(64 * kBigWM * kBigWN), 0, stream, q);
         else if (W4_DMA)
-            hipLaunchKernelGGL(gemm256_dma_kernel, grid, dim3(dma::NT), 0, stream, q);
+            hipLaunchKernelGGL(gemm256_dma_kernel<false>, grid, dim3(dma::NT), 0, stream, q);
         else
             hipLaunchKernelGGL((gemm256_kernel<kBigWM, kBigWN, false>), grid, dim3(64 * kBigWM * kBigWN), 0, stream, q);
         if (q.splits > 1 && q.split_t0 < tiles) {

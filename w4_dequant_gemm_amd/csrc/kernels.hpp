@@ -77,7 +77,8 @@ struct MulParams {
     const uint32_t* sz2 = nullptr;
     int act = 0;
 };
-// largest M of the fused gate and up product
+// largest M of the streaming kernel's gate and up pass; above it the tiled
+// pair GEMM (K a multiple of 64) takes the fused product
 constexpr int64_t kGateUpMaxM = 32;
 // Which kernel runs a product: M <= kSkinnyMaxM: the weight-streaming
 // kernels (dot form for one or two rows, MFMA form above); larger M: the
@@ -91,6 +92,8 @@ hipError_t launch_skinny(const MulParams& p, hipStream_t stream);
 // (one or two rows whose bf16 activations fit the kernel's LDS staging)
 bool skinny_quantizes_rows(int64_t M, int64_t K);
 hipError_t launch_gemm(const MulParams& p, hipStream_t stream);
+// gate and up in one tiled GEMM (p.wq2 / p.sz2 / p.act set; K a multiple of 64)
+hipError_t launch_gemm_pair(const MulParams& p, hipStream_t stream);
 // K-split schedule of the tiled GEMM for an [M, K] x [N, K] product
 // (splits = 1: none) and the fp32 workspace bytes it needs
 struct GemmSplit {

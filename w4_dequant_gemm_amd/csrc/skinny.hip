@@ -48,15 +48,6 @@ typedef float float4_v __attribute__((ext_vector_type(4)));
 
 constexpr int kStepK = 128;   // k per wave and step (4 quarters of 32)
 
-// Activation of the gate projection in a gated MLP: SiLU x / (1 + e^-x)
-// (SwiGLU) or the tanh form of GELU, 0.5 x (1 + tanh(sqrt(2/pi) (x +
-// 0.044715 x^3))) (GeGLU), in fp32.
-__device__ __forceinline__ float activation(int act, float x) {
-    if (act == 1) return x / (1.0f + expf(-x));
-    const float t = 0.7978845608028654f * (x + 0.044715f * x * x * x);
-    return 0.5f * x * (1.0f + tanhf(t));
-}
-
 // weight steps in flight per wave (fewer with more activation rows, whose
 // fragments take the registers)
 #ifndef W4_SK_DEPTH
