@@ -401,15 +401,8 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm256_kernel(MulParams p) {
     // read from LDS at the start of each 16-k sub-step.
     constexpr int NSLOT = FI * FJ * (BK / 16);
     static_assert(NSLOT >= 2 * 4 * CPT && NSLOT >= 4 * A_ITEMS, "conversion work must fit the MFMA slots");
-#ifndef W4_SPREAD
-#define W4_SPREAD 1
-#endif
     constexpr int LOAD_EVERY = NSLOT / NLOAD;
     auto step = [&](int kt, Regs& next, const Regs& ready) {
-        if (!W4_SPREAD) {
-            issue_loads(kt + 2, next);
-            asm volatile("" ::: "memory");
-        }
         __builtin_amdgcn_sched_barrier(0);
         const uint16_t* As = lds + (kt & 1) * 2 * STAGE;
         const uint16_t* Bs = As + STAGE;
@@ -428,7 +421,7 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm256_kernel(MulParams p) {
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j], acc[i][j], 0, 0, 0);
                 if (u % 2 == 1 && u / 2 < 4 * CPT) b_pair(u / 2, ready, Bd);
                 if (u % 4 == 0 && u / 4 < A_ITEMS) a_item(u / 4, ready, Ad);
-                if (W4_SPREAD && u % LOAD_EVERY == 0 && u / LOAD_EVERY < NLOAD) {
+                if (u % LOAD_EVERY == 0 && u / LOAD_EVERY < NLOAD) {
                     issue_load_item(kt + 2, next, u / LOAD_EVERY);
                     asm volatile("" ::: "memory");
                 }
@@ -748,22 +741,18 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_mid_kernel(MulParams p) {
 // Same 256 x 256 tile, K step 64 and 2 x 2 waves of 128 x 128 outputs as
 // above, but the bf16 activations never pass through registers: each wave
 // issues global_load_lds_dwordx4 (lane l's 16 bytes land at the
-// instruction's LDS base + 16 l) one K step ahead, at the start of the step,
-// into the idle one of two activation stages.  The weight codes still come
-// through registers two steps ahead and are dequantized into two bf16
-// weight stages.  LDS: 2 x 32 KB + 2 x 32 KB, four separate arrays, so that
-// with the loop unrolled by two every access names its stage statically
-// and the compiler can tell the direct-to-LDS writes from the reads of the
-// other stage.
+// instruction's LDS base + 16 l) two K steps ahead into the free one of three
+// activation stages.  The weight codes come through registers two steps
+// ahead and are dequantized into two bf16 weight stages.  LDS: 3 x 32 KB +
+// 2 x 32 KB = 160 KB, five separate arrays, so that with the loop unrolled by
+// six every access names its stage statically.
 //
 // The compiler does not order direct-to-LDS writes against the LDS reads of
-// later steps, so every step ends with an explicit wait for all global loads
-// and LDS stores, then the workgroup barrier.  Loads past the last
-// step are clamped to it (same count every step), and the loop ends with a
-// full wait so that nothing writes LDS after the workgroup has finished.
-#ifndef W4_A3
-#define W4_A3 1
-#endif
+// later steps, so every step ends with an explicit wait for all loads issued
+// before it and for its LDS stores, then the workgroup barrier.  Loads past
+// the last step are clamped to it (same count every step), and the loop ends
+// with a full wait so that nothing writes LDS after the workgroup has
+// finished.
 namespace dma {
 constexpr int BM = 256, BN = 256, BK = 64, NW = 4, NT = 64 * NW;
 constexpr int STAGE = 256 * BK;                       // bf16 elements per stage
@@ -772,8 +761,6 @@ constexpr int CPT = BK / 8;                           // code words per thread a
 constexpr int SZN = CPT / 4;                          // scale/zero words per thread and step
 constexpr int BLOAD = CPT / 4 + SZN;                  // weight loads per thread and step (4)
 constexpr int NSLOT = 4 * 4 * (BK / 16);              // MFMAs per wave and step (64)
-typedef uint32_t __attribute__((address_space(1))) global_u32;
-typedef uint32_t __attribute__((address_space(3))) lds_u32;
 #ifndef W4_DSWZ
 #define W4_DSWZ 3
 #endif
@@ -794,9 +781,7 @@ __global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
     __shared__ __attribute__((aligned(16))) uint16_t lds_a1[STAGE];
     __shared__ __attribute__((aligned(16))) uint16_t lds_b0[STAGE];
     __shared__ __attribute__((aligned(16))) uint16_t lds_b1[STAGE];
-#if W4_A3
     __shared__ __attribute__((aligned(16))) uint16_t lds_a2[STAGE];   // 160 KB in all
-#endif
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -834,7 +819,6 @@ __global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
         // chunk whose swizzled position that is
         const int chunk = (lane & 7) ^ swz(a_row0 + 8 * it);
         const uint16_t* src = a_src + chunk * 8 + m * K + static_cast<int64_t>(kt) * BK;
-#if W4_A3
         // Issued as plain instructions: the compiler cannot tell the three
         // activation stages apart and would otherwise wait for every pending
         // direct-to-LDS load before any LDS read.  There is no register
@@ -844,10 +828,6 @@ __global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
         const uint32_t m0 = __builtin_amdgcn_readfirstlane(
             static_cast<uint32_t>(reinterpret_cast<uintptr_t>(stage + (wave * ADMA + it) * 512)));
         asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
-#else
-        __builtin_amdgcn_global_load_lds((const global_u32*)(const void*)src,
-                                         (lds_u32*)(void*)(stage + (wave * ADMA + it) * 512), 16, 0, 0);
-#endif
     };
 
     // Weights: thread tid owns row tid of the tile (8 code words per step)
@@ -892,57 +872,8 @@ __global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
             b[j] = *reinterpret_cast<const bf16x8_t*>(B + lds_off(wn * 128 + j * 32 + (lane & 31), ch));
     };
 
-    // All global loads (the next step's activations and the weights of the
-    // step after) and all LDS stores done, then the barrier.  The wait is the
-    // builtin, which the compiler's own wait insertion takes into account, so
-    // that the next step starts with nothing outstanding (with direct-to-LDS
-    // loads in flight the compiler would otherwise wait for every load before
-    // the first use of a weight register); the empty asm statements keep
-    // memory accesses on their side of the barrier.
-    auto step_end = [&]() {
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt(0);        // vmcnt, expcnt and lgkmcnt all 0
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-    };
+    static_assert(NSLOT == 2 * 4 * CPT && 4 * ADMA <= NSLOT && 4 * BLOAD <= NSLOT, "slot plan");
 
-    // One K step from stage S: MFMA slot u is followed by the direct-to-LDS
-    // load u of the next step (u < ADMA), B pair u / 2 of the next step (odd
-    // u) and, after all activation loads, weight load (u - 8) / 4 of the step
-    // after next (u = 8, 12, ...); a scheduling barrier after every slot
-    // keeps that order.  The fragments of the next 16 k are read at the start
-    // of each 16-k sub-step.
-    auto step = [&](int kt, auto S, Regs& next, const Regs& ready) {
-        constexpr int s = decltype(S)::value;
-        const uint16_t* As = s ? lds_a1 : lds_a0;
-        const uint16_t* Bs = s ? lds_b1 : lds_b0;
-        uint16_t* Ad = s ? lds_a0 : lds_a1;
-        uint16_t* Bd = s ? lds_b0 : lds_b1;
-        bf16x8_t fa[2][FI], fb[2][FJ];
-        load_frags(As, Bs, 0, fa[0], fb[0]);
-#pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            if (kk + 1 < BK / 16) load_frags(As, Bs, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int t = 0; t < FI * FJ; ++t) {
-                const int u = kk * FI * FJ + t;
-                const int i = t / FJ, j = t % FJ;
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j], acc[i][j], 0, 0, 0);
-                if (u < ADMA) dma_item(kt + 1, Ad, u);
-                if (u % 2 == 1) b_pair(u / 2, ready, Bd);
-                if (u >= ADMA && u % 4 == 0 && (u - ADMA) / 4 < BLOAD) {
-                    load_item(kt + 2, next, (u - ADMA) / 4);
-                    asm volatile("" ::: "memory");
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-        step_end();
-    };
-    static_assert(NSLOT == 2 * 4 * CPT && ADMA + 4 * BLOAD <= NSLOT, "slot plan");
-
-#if W4_A3
     // Three activation stages: step kt reads stage kt % 3 and sends the
     // activations of step kt + 2 to stage (kt + 2) % 3, so a direct-to-LDS
     // load has two steps to land.  A step ends waiting only for what was
@@ -1020,28 +951,6 @@ __global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
         if (kt + 4 < KT) step3(kt + 4, I1{}, I0{}, r0, r1);
         if (kt + 5 < KT) step3(kt + 5, I2{}, I1{}, r1, r0);
     }
-#else
-    // prologue: activations of step 0, weights of steps 0 and 1, dequantize step 0
-    Regs r0, r1;
-#pragma unroll
-    for (int it = 0; it < ADMA; ++it) dma_item(0, lds_a0, it);
-#pragma unroll
-    for (int it = 0; it < BLOAD; ++it) load_item(0, r0, it);
-#pragma unroll
-    for (int it = 0; it < BLOAD; ++it) load_item(1, r1, it);
-#pragma unroll
-    for (int pr = 0; pr < 4 * CPT; ++pr) b_pair(pr, r0, lds_b0);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0);           // vmcnt, expcnt and lgkmcnt all 0
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    int kt = 0;
-    for (; kt + 2 <= KT; kt += 2) {
-        step(kt, std::integral_constant<int, 0>{}, r0, r1);
-        step(kt + 1, std::integral_constant<int, 1>{}, r1, r0);
-    }
-    if (kt < KT) step(kt, std::integral_constant<int, 0>{}, r0, r1);
-#endif
     __builtin_amdgcn_s_waitcnt(0);
     asm volatile("" ::: "memory");
 
@@ -1286,15 +1195,10 @@ hipError_t launch_gemm(const MulParams& p, hipStream_t stream) {
             return hipErrorInvalidValue;
         const int64_t wgs = q.split_t0 + (tiles - q.split_t0) * q.splits;
         const dim3 grid(static_cast<unsigned>(wgs));
-#ifndef W4_DMA
-#define W4_DMA 1
-#endif
         if (q.x_fp8)
             hipLaunchKernelGGL((gemm256_kernel<kBigWM, kBigWN, true>), grid, dim3(64 * kBigWM * kBigWN), 0, stream, q);
-        else if (W4_DMA)
-            hipLaunchKernelGGL(gemm256_dma_kernel<false>, grid, dim3(dma::NT), 0, stream, q);
         else
-            hipLaunchKernelGGL((gemm256_kernel<kBigWM, kBigWN, false>), grid, dim3(64 * kBigWM * kBigWN), 0, stream, q);
+            hipLaunchKernelGGL(gemm256_dma_kernel<false>, grid, dim3(dma::NT), 0, stream, q);
         if (q.splits > 1 && q.split_t0 < tiles) {
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;

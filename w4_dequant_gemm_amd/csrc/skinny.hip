@@ -506,10 +506,7 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
             }
         __syncthreads();
     }
-#ifndef W4_DOTL_PIPE
-#define W4_DOTL_PIPE 1
-#endif
-    if constexpr (DOTL && W4_DOTL_PIPE) {
+    if constexpr (DOTL) {
         // Rolling pipeline: each buffer is refilled with the step kDepth
         // ahead as soon as it has been multiplied, so kDepth steps stay in
         // flight.  While every refill is a real step the loads are
