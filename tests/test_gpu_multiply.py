@@ -477,3 +477,34 @@ def test_mid_size_products():
         got8 = Y8.float().cpu().numpy()[np.ix_(rows, cols)]
         assert oracle.rel_error(want, got) <= REL_TOL
         assert oracle.rel_error(want8, got8) <= REL_TOL
+
+
+def test_gate_up_full_8b_shapes_sampled():
+    # the fused gate and up product at the 8B shapes (two 14336 x 4096
+    # weights) in the launch configurations the bench times: M = 1 and 16
+    # (streaming kernel) and M = 2048 (tiled pair GEMM), on sampled outputs
+    require_gpu()
+    import torch
+    import w4_dequant_gemm_amd as w4
+    wl = synth.WORKLOADS["llama8b_decode"]
+    Wg = synth.weight(wl, 0)
+    Wu = synth.normal_matrix(63, *Wg.shape, 0.015)
+    qg = oracle.quantize(Wg, 128, "asym")
+    qu = oracle.quantize(Wu, 128, "asym")
+    pg, G = prepack_dev(qg)
+    pu, _ = prepack_dev(qu)
+    N, K = Wg.shape
+    rng = np.random.default_rng(64)
+    cols = np.sort(rng.choice(N, 256, replace=False))
+    for M in (1, 16, 2048):
+        rows = np.arange(M) if M <= 16 else np.sort(rng.choice(M, 24, replace=False))
+        Xb = synth.activations_bf16_bits(wl, M, K)
+        print(f"[gate_up full] M={M}", flush=True)
+        H = w4.w4a16_gate_up(bf16_dev(Xb), pg, pu, G, "silu")
+        H8, xq, xs = w4.w4a8_gate_up(bf16_dev(Xb), pg, pu, G, "silu")
+        torch.cuda.synchronize()
+        want = oracle.gate_up_ref(Xb, qg, qu, G, "asym", "silu", rows=rows, cols=cols)
+        want8, rq, rs = oracle.gate_up_ref(Xb, qg, qu, G, "asym", "silu", kind="w4a8", rows=rows, cols=cols)
+        assert_bits_equal(host(xq), rq, "E4M3 activations")
+        assert oracle.rel_error(want, H.float().cpu().numpy()[np.ix_(rows, cols)]) <= REL_TOL
+        assert oracle.rel_error(want8, H8.float().cpu().numpy()[np.ix_(rows, cols)]) <= REL_TOL

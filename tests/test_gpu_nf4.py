@@ -61,3 +61,37 @@ def test_nf4_ragged_and_zero_blocks():
         got = y.float().cpu().numpy()
         assert got[0] == 0.0
         assert oracle.rel_error(want[1:], got[1:]) <= REL_TOL
+
+
+def test_nf4_full_8b_shapes_sampled():
+    # the full 8B up and down weights, quantized and multiplied in the launch
+    # configuration the bench times; checked on row chunks that start and end
+    # on second-level group boundaries (4 rows of K = 4096 or 8 rows of
+    # K = 14336 hold whole groups of 256 blocks), so the oracle quantizes each
+    # chunk as a matrix of its own with the same groups
+    require_gpu()
+    import torch
+    import w4_dequant_gemm_amd as w4
+    wl = synth.WORKLOADS["llama8b_decode"]
+    for idx in (0, 1):
+        W = synth.weight(wl, idx)
+        N, K = W.shape
+        nb = K // 64
+        span = 4 if K == 4096 else 8
+        assert (span * nb) % 256 == 0
+        print(f"[nf4 full] idx={idx} N={N} K={K}", flush=True)
+        out = w4.w4_nf4_quantize(to_dev(W))
+        xb = synth.activations_bf16_bits(wl, 1, K)[0]
+        y = w4.w4_nf4_gemv(bf16_dev(xb), out)
+        torch.cuda.synchronize()
+        packed, aq, c2 = host(out["packed"]), host(out["absmax_q"]), host(out["absmax_c2"])
+        yg = y.float().cpu().numpy()
+        for r0 in (0, (N // 2 // span) * span, N - span):
+            ref = oracle.nf4_quantize(W[r0:r0 + span])
+            b0 = r0 * nb
+            assert_bits_equal(packed[r0:r0 + span], ref["packed"], f"codes rows {r0}..")
+            assert_bits_equal(aq[b0:b0 + span * nb], ref["absmax_q"], f"block scales rows {r0}..")
+            g0 = b0 // 256
+            assert_bits_equal(c2[g0:g0 + ref["c2"].size].view(np.uint32), ref["c2"].view(np.uint32), f"c2 rows {r0}..")
+            want = oracle.nf4_gemv_ref(xb, ref["codes"], ref["absmax_q"], ref["c2"])
+            assert oracle.rel_error(want, yg[r0:r0 + span]) <= REL_TOL
