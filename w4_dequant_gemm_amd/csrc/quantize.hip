@@ -15,7 +15,10 @@
 // is built with -ffp-contract=off and the pragma below), correctly rounded
 // division, v_rndne for half-to-even rounding, v_cvt_f16_f32 for the fp16
 // scale.  The error of a group is added by a fixed pairwise halving tree:
-// a[j] += a[j + len] for len = G/2, G/4, ..., 1.
+// a[j] += a[j + len] for len = G/2, G/4, ..., 1.  In the search, rne(w / s)
+// comes from w times the correctly rounded 1/s, which rounds to the same
+// integer except within 2^-22 |w/s| of a half-integer; a candidate with any
+// weight that close is recomputed with divisions (err2_fast).
 //
 // Mapping: one lane owns one group; its G weights stay in registers for the
 // whole search, so the tree runs inside the lane with no cross-lane traffic
@@ -45,6 +48,23 @@ __device__ __forceinline__ float err2(float w, float s, float zf) {
     return e * e;
 }
 
+// The same with rne(w/s) taken from t = w * inv, inv = 1/s correctly
+// rounded: t is within 2^-22 |t| of the correctly rounded quotient (two
+// roundings of 2^-24 each), so both round to the same integer unless t lies
+// within that distance of a half-integer.  Such a weight (a margin of
+// 2^-20 |t| is used, or a NaN) sets `near`, and the caller redoes the
+// candidate with exact divisions; otherwise the result is the same bits.
+template <bool ASYM>
+__device__ __forceinline__ float err2_fast(float w, float s, float zf, float inv, bool& near) {
+    const float tq = w * inv;
+    const float t = rintf(tq);
+    near |= !(fabsf(fabsf(tq - t) - 0.5f) > fabsf(tq) * 0x1p-20f);
+    float q = fminf(fmaxf(t + zf, Grid<ASYM>::lo), Grid<ASYM>::hi);
+    float xr = (q - zf) * s;
+    float e = w - xr;
+    return e * e;
+}
+
 // Node (J, LEN) of the halving tree: after the passes for lengths G/2 .. LEN,
 // a[J] = node(J, 2 LEN) + node(J + LEN, 2 LEN); the leaves of the first pass
 // are e2[J] + e2[J + G/2].  Evaluated depth first to keep few partials live.
@@ -56,6 +76,15 @@ struct Tree {
         } else {
             float a = Tree<G, J, 2 * LEN, ASYM>::eval(v, s, zf);
             float b = Tree<G, J + LEN, 2 * LEN, ASYM>::eval(v, s, zf);
+            return a + b;
+        }
+    }
+    static __device__ __forceinline__ float eval_fast(const float* v, float s, float zf, float inv, bool& near) {
+        if constexpr (LEN == G / 2) {
+            return err2_fast<ASYM>(v[J], s, zf, inv, near) + err2_fast<ASYM>(v[J + G / 2], s, zf, inv, near);
+        } else {
+            float a = Tree<G, J, 2 * LEN, ASYM>::eval_fast(v, s, zf, inv, near);
+            float b = Tree<G, J + LEN, 2 * LEN, ASYM>::eval_fast(v, s, zf, inv, near);
             return a + b;
         }
     }
@@ -114,7 +143,9 @@ __global__ void __launch_bounds__(256) quantize_kernel(QuantizeParams p) {
             sb = 0x3C00u;
         }
         const float zf = ASYM ? rintf(-lo / s) : 0.0f;
-        const float e = Tree<G, 0, 1, ASYM>::eval(v, s, zf);
+        bool near = false;
+        float e = Tree<G, 0, 1, ASYM>::eval_fast(v, s, zf, 1.0f / s, near);
+        if (near) e = Tree<G, 0, 1, ASYM>::eval(v, s, zf);   // rare: some w / s next to a half-integer
         if (p.sse) p.sse[grp * p.n_fracs + i] = e;
         if (i == 0 || e < best_err) {
             best = i;
@@ -240,8 +271,14 @@ __global__ void __launch_bounds__(kRowThreads) quantize_row_kernel(QuantizeParam
         const float zf = ASYM ? rintf(-lo / s) : 0.0f;
         // the tree: levels inside the thread, then LDS, then shuffles
         float a[RPT];
+        bool near = false;
+        const float inv = 1.0f / s;
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) a[i] = i < n_in ? err2<ASYM>(v[i], s, zf) : 0.0f;
+        for (int i = 0; i < RPT; ++i) a[i] = i < n_in ? err2_fast<ASYM>(v[i], s, zf, inv, near) : 0.0f;
+        if (near) {                          // rare: some w / s next to a half-integer
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) a[i] = i < n_in ? err2<ASYM>(v[i], s, zf) : 0.0f;
+        }
 #pragma unroll
         for (int len = RPT / 2; len >= 1; len /= 2)
 #pragma unroll
