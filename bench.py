@@ -33,6 +33,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA
+VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12   # plain (unpacked) fp32 VALU lane operations, 39.3 T/s
 
 
 def log(*a):
@@ -343,6 +344,13 @@ def main():
                 w4.w4_quantize_blockwise(W, 128, "asym", fr, packed=packed, scale=scale, zero=zero, clip_idx=clip)
             ms = timer.time(quant, 5, 1)
             qbytes = N * K * 4 + N * K // 2 + N * (K // 128) * 5
+            # ALU roofline: about 9 VALU operations per weight and candidate
+            # (range, scale, zero, code, reconstruction, squared error, tree
+            # add) against 256 CUs x 64 lanes x 2.4 GHz of plain fp32 VALU
+            q_ops = 9.0 * N * K * len(fr)
+            q_tops = q_ops / (ms * 1e-3) / 1e12
+            extra["quantize_70b_clip11_alu"] = {"bound": "alu", "achieved": round(q_tops, 2), "peak": VALU_PEAK_TOPS,
+                                                "unit": "Tops/s", "frac": round(q_tops / VALU_PEAK_TOPS, 4)}
             extra["quantize_70b_clip11"] = {"ms": round(ms, 3), "GB/s": round(qbytes / (ms * 1e-3) / 1e9, 1),
                                             "weights_per_s": round(N * K / (ms * 1e-3), 0)}
             log(f"[bench] quantize 70B (11 candidates): {ms:.3f} ms, {qbytes/(ms*1e-3)/1e9:.1f} GB/s")
