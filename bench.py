@@ -67,11 +67,17 @@ KERNEL_SOURCES = ("w4_dequant_gemm_amd/csrc/skinny.hip", "w4_dequant_gemm_amd/cs
 
 
 def kernel_source_digest():
+    """First 16 hex digits of sha256 over the code of KERNEL_SOURCES (in
+    order), with comments and blank lines removed: an edit of a comment
+    leaves the measured figures valid, any change of code does not."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+        code = [re.sub(r"//.*$", "", line).rstrip() for line in text.splitlines()]
+        h.update("\n".join(line for line in code if line.strip()).encode())
     return h.hexdigest()[:16]
 
 

@@ -13,9 +13,14 @@
 // W4A8 reads the E4M3 activations produced by the row quantizer, widens them
 // exactly to bf16 and multiplies by the row scale in the epilogue.
 //
-// Tile: 128 x 128 outputs per 256-thread workgroup (2 x 2 waves of 64 x 64),
-// K step 32.  Rows of X beyond M and rows of W beyond N read as zero; the
-// epilogue stores only in-range outputs.
+// Kernels, by M (K a multiple of 64 unless noted):
+//   64 < M <= 128    gemm_mid_kernel, 64 x 128 tiles, K split towards 512 workgroups
+//   M > 128, W4A16   gemm256_dma_kernel, 256 x 256 tiles, activations direct to LDS
+//   M > 128, W4A8    gemm256_kernel, 256 x 256 tiles, activations through registers
+//   K % 64 != 0      gemm_kernel, 128 x 128 tiles, K step 32
+// and the gate + up pair (above 32 rows) on the same kernels with a B tile
+// that interleaves the two weights.  Rows of X beyond M and rows of W beyond
+// N are clamped or read as zero; the epilogues store only in-range outputs.
 #include <type_traits>
 
 #include "device.hpp"

@@ -60,12 +60,12 @@ struct MulParams {
     // writes the E4M3 codes and row scales here
     uint8_t* xq_out = nullptr;
     float* xscale_out = nullptr;
-    // K split across workgroups (256 x 256 GEMM only): output tiles
-    // split_t0 .. tiles - 1 (row-major over the tile grid) are each computed
-    // by `splits` workgroups over consecutive K ranges, which write fp32
-    // partial tiles to ws [tile - split_t0][split][256 x 256]; a second
-    // kernel adds them in split order, applies the row scale and rounds to
-    // bf16.  Tiles before split_t0 are computed whole.
+    // K split across workgroups (the 64 x 128 and 256 x 256 GEMMs): output
+    // tiles split_t0 .. tiles - 1 (row-major over the tile grid) are each
+    // computed by `splits` workgroups over consecutive K ranges, which write
+    // fp32 partial tiles to ws [tile - split_t0][split][tile rows x columns];
+    // a second kernel adds them in split order, applies the row scale and
+    // rounds to bf16.  Tiles before split_t0 are computed whole.
     int splits = 1;
     int64_t split_t0 = 0;
     float* ws = nullptr;
@@ -82,7 +82,8 @@ struct MulParams {
 constexpr int64_t kGateUpMaxM = 32;
 // Which kernel runs a product: M <= kSkinnyMaxM: the weight-streaming
 // kernels (dot form for one or two rows, MFMA form above); larger M: the
-// tiled MFMA GEMM.
+// tiled MFMA GEMM (64 x 128 tiles up to 128 rows, 256 x 256 above; 128 x 128
+// tiles when K is not a multiple of 64).
 #ifndef W4_SKINNY_MAX
 #define W4_SKINNY_MAX 64
 #endif
