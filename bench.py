@@ -199,10 +199,13 @@ def main():
             xd = bf16(synth.activations_bf16_bits(wl8, M, Kd))
             yu = torch.empty((M, Nu), dtype=torch.bfloat16, device=dev)
             yd = torch.empty((M, Nd), dtype=torch.bfloat16, device=dev)
-            for name, x, y, ws, N, K in (("up", xu, yu, ups, Nu, Ku), ("down", xd, yd, downs, Nd, Kd)):
-                def run(x=x, y=y, ws=ws):
+            for name, x, y, wts, N, K in (("up", xu, yu, ups, Nu, Ku), ("down", xd, yd, downs, Nd, Kd)):
+                # the optional workspace of the streaming kernel's K split
+                wsp = torch.empty((max(w4.w4_gemm_workspace_bytes(M, K, N), 16),), dtype=torch.uint8, device=dev)
+
+                def run(x=x, y=y, wts=wts, wsp=wsp):
                     for i in range(L):
-                        w4.w4a16_gemm(x, ws[i]["wq"], ws[i]["sz"], G, Y=y)
+                        w4.w4a16_gemm(x, wts[i]["wq"], wts[i]["sz"], G, Y=y, workspace=wsp)
                 ms = timer.time(run, 20, 3) / L
                 gbs = mul_bytes(M, N, K, G) / (ms * 1e-3) / 1e9
                 extra[f"w4a16_gemv_8b_{name}_m{M}"] = {"us": round(ms * 1e3, 3), "GB/s": round(gbs, 1),

@@ -152,12 +152,16 @@ int w4_quantize_rows_e4m3(const uint16_t* X, int64_t M, int64_t K, uint8_t* xq, 
                           hipStream_t stream);
 
 /*
- * w4_gemm_workspace_bytes -- bytes of device workspace that w4a16_gemm and
- * w4a8_gemm need for a product of M rows, reduction K and N outputs.  It is 0
- * for most shapes (64 rows or fewer, or enough output tiles to fill the GPU);
- * a product with more rows but few 256 x 256 output tiles splits K across
- * workgroups and needs splits * M * N * 4 bytes for the fp32 partial sums.
- * Depends on the shape only; 0 for shapes the products reject.
+ * w4_gemm_workspace_bytes -- bytes of device workspace for the fastest
+ * schedule of w4a16_gemm and w4a8_gemm on a product of M rows, reduction K
+ * and N outputs: splits * M * N * 4 bytes of fp32 partial sums when the
+ * product splits K across workgroups, else 0.  Above 64 rows the tiled GEMM
+ * needs it (a product with few output tiles splits K).  From 3 to 64 rows it
+ * is optional: with it, the weight-streaming kernel splits K when its widest
+ * column blocks are fewer than the compute units (wider blocks re-read the
+ * activations less often); without it (NULL or fewer bytes) the same product
+ * runs unsplit.  1 or 2 rows never use one.  Depends on the shape only; 0
+ * for shapes the products reject.
  */
 size_t w4_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
 
@@ -171,7 +175,8 @@ size_t w4_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
  *   workspace: device memory of workspace_bytes >= w4_gemm_workspace_bytes(M,
  *      K, N) bytes, 16-byte aligned, owned by the caller; its contents on
  *      entry do not matter and are overwritten.  May be NULL when that size
- *      is 0.  Calls in flight at the same time need separate workspaces.
+ *      is 0, or when M <= 64 (the split is then not used).  Calls in flight
+ *      at the same time need separate workspaces.
  *      Too small or NULL when needed: W4_EINVAL.
  *   With a split K the partial sums are added in a fixed order: results do
  *   not depend on timing.

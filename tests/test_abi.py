@@ -99,7 +99,12 @@ def test_gemm_workspace_sizes_and_checks(lib):
     assert ws(2048, 8192, 28672) == 128 * 2 * tile          # 896 tiles: the last 128 in halves
     assert ws(2048, 8192, 32768) == 0                        # 1024 tiles: four full rounds
     assert ws(300, 4096, 33000) == 2 * 8 * tile              # 258 tiles: the last 2 in eighths
-    assert ws(64, 15360, 3840) == 0                          # weight-streaming kernel
+    assert ws(64, 3840, 15360) == 0                          # weight-streaming kernel, enough column blocks
+    assert ws(64, 15360, 3840) == 2 * 64 * 3840 * 4          # streaming kernel, optional K split in 2
+    assert ws(16, 14336, 4096) == 4 * 16 * 4096 * 4          # 64 blocks of 64 columns: 4 K ranges
+    assert ws(2, 14336, 4096) == 0 and ws(1, 14336, 4096) == 0
+    assert ws(16, 4096, 14336) == 0                          # 32-column blocks already: no split
+    assert ws(8, 14336, 4096) == 0                           # activation re-reads below 4x the weights
     # 64 < M <= 128: 64 x 128 tiles, split along K towards 512 workgroups,
     # at most 16 ways and at least 4 K steps of 64 each
     mid = 64 * 128 * 4

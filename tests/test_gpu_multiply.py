@@ -508,3 +508,41 @@ def test_gate_up_full_8b_shapes_sampled():
         assert_bits_equal(host(xq), rq, "E4M3 activations")
         assert oracle.rel_error(want, H.float().cpu().numpy()[np.ix_(rows, cols)]) <= REL_TOL
         assert oracle.rel_error(want8, H8.float().cpu().numpy()[np.ix_(rows, cols)]) <= REL_TOL
+
+
+def test_streaming_k_split_products():
+    # 3..64 rows whose widest column blocks are fewer than the compute units:
+    # with a workspace the streaming kernel splits K into ranges (fp32
+    # partials, summed by a second kernel), without one it runs unsplit; both
+    # against the oracle and against each other, on a ragged N (16 blocks of
+    # 64 columns and 15 K ranges, or 32 of 32 and 8 for four row blocks),
+    # W4A16 and W4A8, NaNs in the workspace on entry
+    require_gpu()
+    import torch
+    import w4_dequant_gemm_amd as w4
+    N, K = 1000, 8192
+    W = synth.normal_matrix(65, N, K, 0.02)
+    q = oracle.quantize(W, 128, "asym")
+    pk, G = prepack_dev(q)
+    none = torch.empty((0,), dtype=torch.uint8, device="cuda")
+    for M in (16, 40, 64):
+        Xb = synth.to_bf16_bits(synth.normal_matrix(66 + M, M, K))
+        need = w4.w4_gemm_workspace_bytes(M, K, N)
+        assert need == (15 if M <= 16 else 8) * M * N * 4      # 16 blocks of 64 columns, or 32 of 32
+        ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device="cuda")
+        print(f"[k-split] M={M} N={N} K={K} workspace={need}", flush=True)
+        Ys = w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G, workspace=ws)
+        Yu = w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G, workspace=none)
+        Y8s, xq, xs = w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G, workspace=ws)
+        Y8u, _, _ = w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G, workspace=none)
+        torch.cuda.synchronize()
+        want = oracle.gemm_ref(oracle.bf16_bits_to_f64(Xb), q["packed"], q["scale"], q["zero"], G, "asym")
+        want8, rq, _ = oracle.w4a8_ref(Xb, q["packed"], q["scale"], q["zero"], G, "asym")
+        assert_bits_equal(host(xq), rq, "E4M3 activations")
+        for got, ref, what in ((Ys, want, "w4a16 split"), (Yu, want, "w4a16 unsplit"),
+                               (Y8s, want8, "w4a8 split"), (Y8u, want8, "w4a8 unsplit")):
+            err = oracle.rel_error(ref, got.float().cpu().numpy())
+            assert err <= REL_TOL, f"{what} M={M}: relative error {err:.3e}"
+        # the two schedules differ only in the order of fp32 additions
+        d = (Ys.float() - Yu.float()).abs().max().item()
+        assert d <= 2 ** -6 * Yu.float().abs().max().item()

@@ -127,6 +127,18 @@ int mul_common(const char* fn, const uint16_t* X, int64_t M, int64_t K, const ui
     return W4_OK;
 }
 
+// the streaming kernel's K split when the caller gave a workspace large enough
+// for it (optional: without one the product runs unsplit)
+w4::MulParams with_skinny_split(w4::MulParams p, void* workspace, size_t workspace_bytes) {
+    const int s = w4::skinny_splits(p.M, p.K, p.N, p.x_fp8 ? 1 : 2);
+    if (s > 1 && workspace && aligned16(workspace) &&
+        workspace_bytes >= w4::skinny_workspace_bytes(p.M, p.K, p.N)) {
+        p.splits = s;
+        p.ws = static_cast<float*>(workspace);
+    }
+    return p;
+}
+
 // the tiled-GEMM launch of a product, with the K split that its workspace was sized for
 w4::MulParams with_split(w4::MulParams p, void* workspace) {
     const w4::GemmSplit g = w4::gemm_split(p.M, p.K, p.N);
@@ -262,7 +274,8 @@ int w4_quantize_rows_e4m3(const uint16_t* X, int64_t M, int64_t K, uint8_t* xq, 
 }
 
 size_t w4_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
-    if (M <= w4::kSkinnyMaxM || K <= 0 || N <= 0) return 0;
+    if (M <= 0 || K <= 0 || N <= 0) return 0;
+    if (M <= w4::kSkinnyMaxM) return w4::skinny_workspace_bytes(M, K, N);   // optional
     return w4::gemm_workspace_bytes(M, K, N);
 }
 
@@ -272,7 +285,8 @@ int w4a16_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, cons
     W4_TRY(mul_common(fn, X, M, K, wq, sz, N, G, Y, workspace, workspace_bytes));
     if (M == 0 || N == 0) return W4_OK;
     w4::MulParams p{X, nullptr, M, K, N, G, wq, sz, Y, false};
-    if (M <= w4::kSkinnyMaxM) return hip_status(w4::launch_skinny(p, stream), fn);
+    if (M <= w4::kSkinnyMaxM)
+        return hip_status(w4::launch_skinny(with_skinny_split(p, workspace, workspace_bytes), stream), fn);
     return hip_status(w4::launch_gemm(with_split(p, workspace), stream), fn);
 }
 
@@ -292,7 +306,8 @@ int w4a8_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const
     w4::RowQuantParams rq{X, M, K, xq, xscale};
     W4_TRY(hip_status(w4::launch_rowquant(rq, stream), fn));
     w4::MulParams p{xq, xscale, M, K, N, G, wq, sz, Y, true};
-    if (M <= w4::kSkinnyMaxM) return hip_status(w4::launch_skinny(p, stream), fn);
+    if (M <= w4::kSkinnyMaxM)
+        return hip_status(w4::launch_skinny(with_skinny_split(p, workspace, workspace_bytes), stream), fn);
     return hip_status(w4::launch_gemm(with_split(p, workspace), stream), fn);
 }
 

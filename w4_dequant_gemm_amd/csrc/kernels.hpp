@@ -60,7 +60,9 @@ struct MulParams {
     // writes the E4M3 codes and row scales here
     uint8_t* xq_out = nullptr;
     float* xscale_out = nullptr;
-    // K split across workgroups (the 64 x 128 and 256 x 256 GEMMs): output
+    // K split across workgroups.  Streaming kernel (splits > 1, M >= 3): K
+    // ranges of whole steps, partial sums in ws [range][M][N].  The 64 x 128
+    // and 256 x 256 GEMMs: output
     // tiles split_t0 .. tiles - 1 (row-major over the tile grid) are each
     // computed by `splits` workgroups over consecutive K ranges, which write
     // fp32 partial tiles to ws [tile - split_t0][split][tile rows x columns];
@@ -89,6 +91,11 @@ constexpr int64_t kGateUpMaxM = 32;
 #endif
 constexpr int64_t kSkinnyMaxM = W4_SKINNY_MAX;
 hipError_t launch_skinny(const MulParams& p, hipStream_t stream);
+// K ranges of the streaming kernel's split for this shape and activation
+// width in bytes (1: no split), and the fp32 partial sums it needs (sized for
+// bf16): an optional workspace (without one the product runs unsplit)
+int skinny_splits(int64_t M, int64_t K, int64_t N, int xbytes);
+size_t skinny_workspace_bytes(int64_t M, int64_t K, int64_t N);
 // true when a W4A8 product of M rows quantizes its activation rows itself
 // (one or two rows whose bf16 activations fit the kernel's LDS staging)
 bool skinny_quantizes_rows(int64_t M, int64_t K);

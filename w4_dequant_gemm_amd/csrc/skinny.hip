@@ -105,10 +105,19 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
     const int64_t M = p.M, N = p.N, K = p.K;
     // gate and up in one pass: both blocks cover the same 16 columns (FJ = 2)
     const bool pair = p.wq2 != nullptr;
-    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * (pair ? 16 : 16 * FJ);
+    const int KS = static_cast<int>((K + kStepK - 1) / kStepK);
+    // K split across workgroups (MFMA forms, p.splits > 1): workgroup b
+    // covers column block b % nblk and the steps [ks0, ks1) of K range
+    // b / nblk, and writes fp32 partial sums to ws [range][M][N]
+    const int64_t cols = pair ? 16 : 16 * FJ;
+    const int64_t nblk = (N + cols - 1) / cols;
+    const bool ksplit = !DOT && p.splits > 1;
+    const int kr = ksplit ? static_cast<int>(blockIdx.x / nblk) : 0;
+    const int ks0 = ksplit ? kr * KS / p.splits : 0;
+    const int ks1 = ksplit ? (kr + 1) * KS / p.splits : KS;
+    const int64_t n0 = (ksplit ? blockIdx.x % nblk : static_cast<int64_t>(blockIdx.x)) * cols;
     const int64_t words_row = K / 8, groups_row = K / p.G;
     const int g_shift = group_shift(p.G);
-    const int KS = static_cast<int>((K + kStepK - 1) / kStepK);
 
     // lane's column in each block and row in each 16-row block (clamped:
     // columns past N and rows past M compute values that are never stored)
@@ -375,7 +384,7 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
                 // its own step: a step past K reloads the last one (a cache
                 // hit) and is not multiplied
                 load_b(st < KS ? st : KS - 1, bq[d]);
-            } else if (st < KS) {
+            } else if (st < ks1) {
                 load_b(st, bq[d]);
                 load_a(st, aq[d]);
             }
@@ -383,7 +392,7 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
     };
-    int step = wave;                     // every wave has at least one step
+    int step = ks0 + wave;               // every wave has at least one step
     issue(step);
     if constexpr (DOTL) {
         // stage the activations while the first weights are in flight:
@@ -540,9 +549,9 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
         while (true) {
 #pragma unroll
             for (int d = 0; d < kDepth; ++d)
-                if (step + d * wk < KS) compute(bq[d], aq[d], step + d * wk);
+                if (step + d * wk < ks1) compute(bq[d], aq[d], step + d * wk);
             step += kDepth * wk;
-            if (step >= KS) break;
+            if (step >= ks1) break;
             issue(step);
         }
     }
@@ -630,10 +639,26 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
         for (int w = 0; w < wk; ++w) y += red[w * TILE + o];
         const int64_t n = n0 + col;
         if (row < M && n < N) {
-            if constexpr (XF8) y *= p.xscale[row];
-            p.Y[static_cast<int64_t>(row) * N + n] = float_to_bf16_bits(y);
+            if (ksplit) {
+                p.ws[(static_cast<int64_t>(kr) * M + row) * N + n] = y;
+            } else {
+                if constexpr (XF8) y *= p.xscale[row];
+                p.Y[static_cast<int64_t>(row) * N + n] = float_to_bf16_bits(y);
+            }
         }
     }
+}
+
+// Sum of the K-split partials of the streaming kernel: Y = bf16(sum over the
+// ranges in order, times the row scale for W4A8).
+__global__ void __launch_bounds__(256) skinny_reduce_kernel(MulParams p) {
+    const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t mn = p.M * p.N;
+    if (e >= mn) return;
+    float y = p.ws[e];
+    for (int z = 1; z < p.splits; ++z) y += p.ws[z * mn + e];
+    if (p.x_fp8) y *= p.xscale[e / p.N];
+    p.Y[e] = float_to_bf16_bits(y);
 }
 
 // LDS words of one staged activation row: 16 bf16 pairs and one sum per
@@ -644,11 +669,18 @@ template <int MB, int FJ, bool XF8, int MODE>
 hipError_t launch_skinny_c(const MulParams& p, int wk, hipStream_t stream) {
     const int64_t cols = p.wq2 ? 16 : 16 * FJ;       // output columns per workgroup
     if (p.wq2 && FJ != 2) return hipErrorInvalidValue;
-    const int64_t blocks = (p.N + cols - 1) / cols;
+    const bool split = MODE < kDot && p.splits > 1;
+    const int64_t blocks = (p.N + cols - 1) / cols * (split ? p.splits : 1);
     size_t lds = static_cast<size_t>(wk) * (MODE >= kDot ? 16 : 256) * MB * FJ * sizeof(float);
     if (MODE == kDotLds || MODE == kDotLdsQ) lds += static_cast<size_t>(MB) * staged_words_row(p.K) * sizeof(uint32_t);
     hipLaunchKernelGGL((gemm_skinny_kernel<MB, FJ, XF8, MODE>), dim3(static_cast<unsigned>(blocks)), dim3(64 * wk), lds,
                        stream, p, wk);
+    if (split) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(skinny_reduce_kernel, dim3(static_cast<unsigned>((p.M * p.N + 255) / 256)), dim3(256), 0,
+                           stream, p);
+    }
     return hipGetLastError();
 }
 
@@ -676,6 +708,48 @@ hipError_t launch_skinny_m(const MulParams& p, int fj, int wk, hipStream_t strea
 
 }  // namespace
 
+#ifndef W4_SK_FJMAX
+#define W4_SK_FJMAX 4
+#endif
+#ifndef W4_SK_MINBLK
+#define W4_SK_MINBLK 240
+#endif
+#ifndef W4_SK_SPLIT_MINSTEPS
+#define W4_SK_SPLIT_MINSTEPS 4
+#endif
+
+// K split of the MFMA forms (3 <= M <= 64).  Every workgroup reads the whole
+// activation block [M, K] from L2, once per column block; the unsplit
+// schedule narrows the blocks until there are about as many as compute
+// units, so its activation reads come to M x (bytes per activation) / (8 FJ)
+// times the weight bytes.  Where that reaches four, K is cut into ranges
+// instead: the widest column blocks the registers allow (64 columns, 32 for
+// four row blocks), one workgroup per (block, range), at most 16 ranges of
+// at least four 128-k steps, and a second kernel sums the ranges (below
+// that ratio its launch costs more than the reads save).  The ranges depend
+// on the shape and the activation width; the workspace is sized for bf16,
+// the wider.
+int skinny_splits(int64_t M, int64_t K, int64_t N, int xbytes) {
+    if (M < 3 || M > kSkinnyMaxM || K <= 0 || N <= 0) return 1;
+    const int mb = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+    const int fj = mb == 4 ? 2 : W4_SK_FJMAX;
+    int fju = fj;                                    // the unsplit schedule's column blocks
+    while (fju > 1 && (N + 16 * fju - 1) / (16 * fju) < W4_SK_MINBLK) fju /= 2;
+    if (M * xbytes < 32 * fju) return 1;
+    const int64_t nblk = (N + 16 * fj - 1) / (16 * fj);
+    if (nblk >= W4_SK_MINBLK) return 1;
+    const int64_t ks = (K + kStepK - 1) / kStepK;
+    int64_t s = (W4_SK_MINBLK + nblk - 1) / nblk;
+    if (s > ks / W4_SK_SPLIT_MINSTEPS) s = ks / W4_SK_SPLIT_MINSTEPS;
+    if (s > 16) s = 16;
+    return s < 2 ? 1 : static_cast<int>(s);
+}
+
+size_t skinny_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+    const int s = skinny_splits(M, K, N, 2);
+    return s > 1 ? static_cast<size_t>(s) * M * N * sizeof(float) : 0;
+}
+
 bool skinny_quantizes_rows(int64_t M, int64_t K) {
 #ifndef W4_DOT_LDS_MAX
 #define W4_DOT_LDS_MAX 65536
@@ -692,12 +766,6 @@ bool skinny_quantizes_rows(int64_t M, int64_t K) {
 // least eight steps each.
 hipError_t launch_skinny(const MulParams& p, hipStream_t stream) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
-#ifndef W4_SK_FJMAX
-#define W4_SK_FJMAX 4
-#endif
-#ifndef W4_SK_MINBLK
-#define W4_SK_MINBLK 240
-#endif
 #ifndef W4_SK_WKMAX
 #define W4_SK_WKMAX 8
 #endif
@@ -721,15 +789,19 @@ hipError_t launch_skinny(const MulParams& p, hipStream_t stream) {
     // two rows with four column blocks would not fit 128 registers a lane
     int fj = dotm ? (p.M == 2 && W4_DOT_FJMAX > 2 ? 2 : W4_DOT_FJMAX) : (mb == 4 ? 2 : W4_SK_FJMAX);
     const int minblk = dotm ? W4_DOT_MINBLK : W4_SK_MINBLK;
-    while (fj > 1 && (p.N + 16 * fj - 1) / (16 * fj) < minblk) fj /= 2;
+    // a K split (workspace given) keeps the widest blocks; otherwise narrower
+    // blocks give enough workgroups
+    const bool split = !dotm && !p.wq2 && p.splits > 1;
+    if (!split)
+        while (fj > 1 && (p.N + 16 * fj - 1) / (16 * fj) < minblk) fj /= 2;
     if (p.wq2) {
         // gate and up: two blocks over the same 16 columns (at most 32 rows)
         if (mb > 2) return hipErrorInvalidValue;
         fj = 2;
     }
-    const int64_t blocks = p.wq2 ? (p.N + 15) / 16 : (p.N + 16 * fj - 1) / (16 * fj);
-    const int64_t ks = (p.K + kStepK - 1) / kStepK;
-    const int64_t minsteps = dotm ? W4_DOT_MINSTEPS : W4_SK_MINSTEPS;
+    const int64_t blocks = (p.wq2 ? (p.N + 15) / 16 : (p.N + 16 * fj - 1) / (16 * fj)) * (split ? p.splits : 1);
+    const int64_t ks = (p.K + kStepK - 1) / kStepK / (split ? p.splits : 1);
+    const int64_t minsteps = dotm ? W4_DOT_MINSTEPS : (split ? W4_SK_SPLIT_MINSTEPS : W4_SK_MINSTEPS);
     int64_t wk = ((dotm ? W4_DOT_WAVES : 4096) + blocks - 1) / blocks;
     if (wk > ks / minsteps) wk = ks / minsteps;
 #ifndef W4_DOT_WKMAX
