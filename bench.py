@@ -259,7 +259,20 @@ def main():
                                            "two_gemms_and_act_ms": round(msa, 4)}
         log(f"[bench] W4A16 8B gate+up M=2048: fused {msf:.3f} ms ({fl/(msf*1e-3)/1e12:.1f} TFLOP/s), "
             f"two GEMMs + SiLU*mul {msa:.3f} ms")
-        del x, h, ya, yb, ws
+        # W4A8 form of the same pair (row quantization included), M = 256 and 2048
+        for M8 in (256, 2048):
+            x8 = x[:M8]
+            h8 = h[:M8]
+            xq8 = torch.empty((M8, Ku), dtype=torch.uint8, device=dev)
+            xs8 = torch.empty((M8,), dtype=torch.float32, device=dev)
+
+            def fused8(x8=x8, h8=h8, xq8=xq8, xs8=xs8):
+                w4.w4a8_gate_up(x8, ups[0], ups[1], G, "silu", H=h8, xq=xq8, xscale=xs8)
+            ms8 = timer.time(fused8, 10, 3)
+            fl8 = 2 * 2.0 * M8 * Nu * Ku
+            extra[f"w4a8_gate_up_8b_m{M8}"] = {"ms": round(ms8, 4), "TFLOP/s": round(fl8 / (ms8 * 1e-3) / 1e12, 1)}
+            log(f"[bench] W4A8 8B gate+up M={M8}: fused {ms8:.3f} ms ({fl8/(ms8*1e-3)/1e12:.1f} TFLOP/s, incl. row quant)")
+        del x, h, ya, yb, ws, x8, h8, xq8, xs8
 
         # NF4 comparator at M = 1: the same up/down weights in NF4 (blocks of
         # 64, double-quantized scales), same rotation of copies

@@ -382,8 +382,10 @@ def test_gate_up_products(kind):
     # gate and up projections in one pass with the activation-and-multiply
     # epilogue, against act(X Wg'^T) * (X Wu'^T) in float64: 8B-class rows
     # (gate and up are disjoint row ranges of the 8B up weight), one to 32
-    # activation rows in the streaming kernel and 48, 100, 300 in the tiled
-    # pair GEMM (64-, 128- and 256-row tiles), both activations; and a ragged
+    # activation rows in the streaming kernel and 48 to 300 in the tiled pair
+    # GEMM (64-row tiles, 128-row tiles on both sides of M = 128 and at 256,
+    # and W4A16 at 300 the 256-row direct-to-LDS tiles), both activations;
+    # and a ragged
     # N with symmetric G = 32 weights (the dequantizing form for more than
     # two rows, and the tiled form at 70 rows)
     require_gpu()
@@ -391,7 +393,7 @@ def test_gate_up_products(kind):
     import w4_dequant_gemm_amd as w4
     wl = synth.WORKLOADS["llama8b_decode"]
     W = synth.weight(wl, 0, rows=2048)
-    cases = [(W[:1024], W[1024:], 128, "asym", (1, 2, 3, 16, 32, 48, 100, 300)),
+    cases = [(W[:1024], W[1024:], 128, "asym", (1, 2, 3, 16, 32, 48, 100, 200, 256, 300)),
              (W[:1000, :1536], W[1000:2000, :1536], 32, "sym", (1, 2, 5, 70))]
     for Wg, Wu, G, mode, Ms in cases:
         qg = oracle.quantize(np.ascontiguousarray(Wg), G, mode)

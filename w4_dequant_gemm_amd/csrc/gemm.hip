@@ -18,8 +18,9 @@
 //   M > 128, W4A16   gemm256_dma_kernel, 256 x 256 tiles, activations direct to LDS
 //   M > 128, W4A8    gemm256_kernel, 256 x 256 tiles, activations through registers
 //   K % 64 != 0      gemm_kernel, 128 x 128 tiles, K step 32
-// and the gate + up pair (above 32 rows) on the same kernels with a B tile
-// that interleaves the two weights.  Rows of X beyond M and rows of W beyond
+// and the gate + up pair (above 32 rows) on gemm_mid_kernel (64- or 128-row
+// tiles) or, W4A16 above 256 rows, gemm256_dma_kernel, with a B tile that
+// interleaves the two weights.  Rows of X beyond M and rows of W beyond
 // N are clamped or read as zero; the epilogues store only in-range outputs.
 #include <type_traits>
 
@@ -1160,12 +1161,18 @@ hipError_t launch_pair_t(const MulParams& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Gate and up GEMM (M above the streaming kernel's pair range): output tiles
-// of TBM rows (64, 128 or 256 by M) by 128 columns, no K split.
+// Gate and up GEMM (M above the streaming kernel's pair range), no K split:
+// W4A16 above 256 rows on 256 x 128 output tiles of the direct-to-LDS
+// kernel; otherwise output tiles of 64 (M <= 64) or 128 rows by 128 columns.
+// Measured on the 8B gate / up shapes (two 14336 x 4096): at M = 256 the
+// 128-row tiles take 98 us against 138 us for one row of 256-row tiles (224
+// workgroups against 112); from M = 384 the 256-row kernel is ahead
+// (151 / 179 us).  A 256-row form of the 128-row kernel spilled and ran
+// tens of times slower.
 hipError_t launch_gemm_pair(const MulParams& p, hipStream_t stream) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
     if (p.K % big::BK != 0 || !p.wq2 || !p.sz2) return hipErrorInvalidValue;
-    if (!p.x_fp8 && p.M >= 256) {
+    if (!p.x_fp8 && p.M > 256) {
         // W4A16: the activations-direct-to-LDS kernel on 256 x 128 output tiles
         const int64_t tiles = ((p.N + big::BN / 2 - 1) / (big::BN / 2)) * ((p.M + big::BM - 1) / big::BM);
         MulParams q = p;
@@ -1176,8 +1183,7 @@ hipError_t launch_gemm_pair(const MulParams& p, hipStream_t stream) {
         return hipGetLastError();
     }
     if (p.M <= 64) return p.x_fp8 ? launch_pair_t<64, true>(p, stream) : launch_pair_t<64, false>(p, stream);
-    if (p.M <= 128) return p.x_fp8 ? launch_pair_t<128, true>(p, stream) : launch_pair_t<128, false>(p, stream);
-    return p.x_fp8 ? launch_pair_t<256, true>(p, stream) : launch_pair_t<256, false>(p, stream);
+    return p.x_fp8 ? launch_pair_t<128, true>(p, stream) : launch_pair_t<128, false>(p, stream);
 }
 
 hipError_t launch_gemm(const MulParams& p, hipStream_t stream) {
