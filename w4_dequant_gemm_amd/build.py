@@ -16,6 +16,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 OUT = os.path.join(HERE, "libw4.so")
+# measurement-only streaming-read kernel (bench.py), a library of its own
+PROBE_SRC = "probe_read.hip"
+PROBE_OUT = os.path.join(HERE, "libw4probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -63,6 +66,9 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     tmp = OUT + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, OUT)
+    ptmp = PROBE_OUT + ".tmp"
+    _run([HIPCC, *HIP_FLAGS, "-shared", os.path.join(CSRC, PROBE_SRC), "-o", ptmp], verbose)
+    os.replace(ptmp, PROBE_OUT)
     return OUT
 
 
