@@ -5,9 +5,9 @@
 // reality"), so each packed weight tile is dequantized once per workgroup into
 // LDS and then reused by every activation row of the workgroup tile:
 //
-//   global (4-bit GPU layout) -> registers: (128 + u) as bf16 via AND-OR,
-//   widened to fp32, W' = (128 + u) s - (128 + z) s (exact in fp32: every
-//   product has fewer than 24 significant bits), rounded to bf16 (RNE)
+//   global (4-bit GPU layout) -> registers: fp16 1024 + u (or 1024 + 16 u)
+//   via AND-OR, W' = (1024 + u) s - (1024 + z) s by mixed-precision FMAs
+//   (exact in fp32; PairDequant below), rounded to bf16 (RNE)
 //   -> LDS -> v_mfma_f32_32x32x16_bf16 with fp32 accumulation -> bf16 out.
 //
 // W4A8 reads the E4M3 activations produced by the row quantizer, widens them
@@ -29,6 +29,37 @@
 
 namespace w4 {
 namespace {
+
+// Dequantization of one code word (8 consecutive k of one row: code 2i at
+// bits 4i, code 2i + 1 at bits 16 + 4i) into four bf16 pairs.  Pairs 0 and 2
+// take one AND-OR with 0x000F000F (of the word, and of the word >> 8) into
+// the low mantissa bits of fp16 1024, giving 1024 + u (unit in the last
+// place 1); pairs 1 and 3 take an AND-OR with 0x00F000F0 of the same
+// operands, giving 1024 + 16 u (still inside the 10-bit mantissa).  Then
+// W' = (1024 + u) s - (1024 + z) s, or (1024 + 16 u) (s / 16) - (64 + z) s,
+// by two mixed-precision FMAs per pair (fp16 operands, fp32 result; exact:
+// s / 16 is exact and every product and sum has at most 23 significant
+// bits), and one rounding to a bf16 pair.  Both forms give the same value.
+struct PairDequant {
+    uint32_t bias;                 // two fp16 1024.0 (0x64006400), in a register
+    float sc = 0.0f, cs = 0.0f, sc16 = 0.0f, cs16 = 0.0f;
+    // the scale / zero word of the group: fp16 s in bits 0-15, z in 16-31
+    __device__ __forceinline__ void group(uint32_t sz) {
+        const float z = half_bits_to_float(sz >> 16);
+        sc = half_bits_to_float(sz);
+        cs = -(1024.0f + z) * sc;
+        sc16 = sc * 0.0625f;
+        cs16 = -(64.0f + z) * sc;
+    }
+    __device__ __forceinline__ uint32_t pair(uint32_t w, int i) const {
+        const uint32_t src = i < 2 ? w : w >> 8;
+        const uint32_t h = (src & ((i & 1) ? 0x00F000F0u : 0x000F000Fu)) | bias;
+        const _Float16 lo = __builtin_bit_cast(_Float16, static_cast<uint16_t>(h & 0xFFFFu));
+        const _Float16 hi = __builtin_bit_cast(_Float16, static_cast<uint16_t>(h >> 16));
+        const float s = (i & 1) ? sc16 : sc, c = (i & 1) ? cs16 : cs;
+        return pack_bf16x2(fmaf(static_cast<float>(lo), s, c), fmaf(static_cast<float>(hi), s, c));
+    }
+};
 
 namespace small {
 constexpr int BM = 128, BN = 128, BK = 32;
@@ -323,26 +354,16 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm256_kernel(MulParams p) {
     };
 
     // ---- operand conversion, split into small work items -------------------
-    // B: code word j (8 k) of the thread's row holds four pairs of codes; pair
-    // i becomes two fp16 values 1024 + u with one AND-OR (the nibbles land in
-    // the low mantissa bits of fp16 1024, whose unit in the last place is 1),
-    // then W' = (1024 + u) s - (1024 + z) s by two mixed-precision FMAs (fp16
-    // operands, fp32 result; exact: every term has at most 23 significant
-    // bits) and one rounding to a bf16 pair.  The fourth pair of a word
-    // completes a 16-byte LDS row chunk.
+    // B: code word j (8 k) of the thread's row holds four pairs of codes,
+    // each dequantized to a bf16 pair by PairDequant; the fourth pair of a
+    // word completes a 16-byte LDS row chunk.
     const uint32_t bias16 = opaque_vgpr(0x64006400u);   // two fp16 1024.0
-    float b_sc = 0.0f, b_cs = 0.0f;
+    PairDequant dq{bias16};
     uint32_t b_out[4];
     auto b_pair = [&](int pr, const Regs& r, uint16_t* B) {
         const int j = pr / 4, i = pr % 4;
-        if (i == 0 && j % 4 == 0) {
-            b_sc = half_bits_to_float(r.s[j / 4]);
-            b_cs = -(1024.0f + half_bits_to_float(r.s[j / 4] >> 16)) * b_sc;
-        }
-        const uint32_t h = ((r.q[j / 4][j % 4] >> (4 * i)) & 0x000F000Fu) | bias16;
-        const _Float16 lo = __builtin_bit_cast(_Float16, static_cast<uint16_t>(h & 0xFFFFu));
-        const _Float16 hi = __builtin_bit_cast(_Float16, static_cast<uint16_t>(h >> 16));
-        b_out[i] = pack_bf16x2(fmaf(static_cast<float>(lo), b_sc, b_cs), fmaf(static_cast<float>(hi), b_sc, b_cs));
+        if (i == 0 && j % 4 == 0) dq.group(r.s[j / 4]);
+        b_out[i] = dq.pair(r.q[j / 4][j % 4], i);
         if (i == 3)
             *reinterpret_cast<uint4*>(B + lds_off(o_row, o_c0 + j)) = make_uint4(b_out[0], b_out[1], b_out[2], b_out[3]);
     };
@@ -586,18 +607,12 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_mid_kernel(MulParams p) {
 
     // conversion items (as in gemm256_kernel)
     const uint32_t bias16 = opaque_vgpr(0x64006400u);
-    float b_sc = 0.0f, b_cs = 0.0f;
+    PairDequant dq{bias16};
     uint32_t b_out[4];
     auto b_pair = [&](int pr, const Regs& r, uint16_t* B) {
         const int j = pr / 4, i = pr % 4;
-        if (i == 0 && j % 4 == 0) {
-            b_sc = half_bits_to_float(r.s[j / 4]);
-            b_cs = -(1024.0f + half_bits_to_float(r.s[j / 4] >> 16)) * b_sc;
-        }
-        const uint32_t h = ((r.q[j / 4][j % 4] >> (4 * i)) & 0x000F000Fu) | bias16;
-        const _Float16 lo = __builtin_bit_cast(_Float16, static_cast<uint16_t>(h & 0xFFFFu));
-        const _Float16 hi = __builtin_bit_cast(_Float16, static_cast<uint16_t>(h >> 16));
-        b_out[i] = pack_bf16x2(fmaf(static_cast<float>(lo), b_sc, b_cs), fmaf(static_cast<float>(hi), b_sc, b_cs));
+        if (i == 0 && j % 4 == 0) dq.group(r.s[j / 4]);
+        b_out[i] = dq.pair(r.q[j / 4][j % 4], i);
         if (i == 3)
             *reinterpret_cast<uint4*>(B + lds_off(b_row, b_c0 + j)) = make_uint4(b_out[0], b_out[1], b_out[2], b_out[3]);
     };
@@ -851,20 +866,14 @@ __global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
         else r.s[it - CPT / 4] = brow.group((kt * BK + 32 * (it - CPT / 4)) >> g_shift);
     };
 
-    // dequantization of one pair of codes (see gemm256_kernel)
+    // dequantization of one pair of codes (PairDequant)
     const uint32_t bias16 = opaque_vgpr(0x64006400u);
-    float b_sc = 0.0f, b_cs = 0.0f;
+    PairDequant dq{bias16};
     uint32_t b_out[4];
     auto b_pair = [&](int pr, const Regs& r, uint16_t* B) {
         const int j = pr / 4, i = pr % 4;
-        if (i == 0 && j % 4 == 0) {
-            b_sc = half_bits_to_float(r.s[j / 4]);
-            b_cs = -(1024.0f + half_bits_to_float(r.s[j / 4] >> 16)) * b_sc;
-        }
-        const uint32_t h = ((r.q[j / 4][j % 4] >> (4 * i)) & 0x000F000Fu) | bias16;
-        const _Float16 lo = __builtin_bit_cast(_Float16, static_cast<uint16_t>(h & 0xFFFFu));
-        const _Float16 hi = __builtin_bit_cast(_Float16, static_cast<uint16_t>(h >> 16));
-        b_out[i] = pack_bf16x2(fmaf(static_cast<float>(lo), b_sc, b_cs), fmaf(static_cast<float>(hi), b_sc, b_cs));
+        if (i == 0 && j % 4 == 0) dq.group(r.s[j / 4]);
+        b_out[i] = dq.pair(r.q[j / 4][j % 4], i);
         if (i == 3) *reinterpret_cast<uint4*>(B + lds_off(tid, j)) = make_uint4(b_out[0], b_out[1], b_out[2], b_out[3]);
     };
 
