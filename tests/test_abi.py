@@ -41,6 +41,26 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, name), f"{name} declared in w4.h but not exported"
 
 
+def test_read_probe_library_is_separate(lib):
+    # the measurement-only streaming-read kernel lives in its own library;
+    # the product library does not export it, and the probe rejects bad
+    # arguments before any launch
+    path = os.path.join(ROOT, "w4_dequant_gemm_amd", "libw4probe.so")
+    assert os.path.exists(path), "libw4probe.so is built beside libw4.so"
+    probe = ctypes.CDLL(path)
+    fn = probe.w4probe_stream_read
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                   ctypes.c_void_p]
+    assert not hasattr(lib, "w4probe_stream_read")
+    fake = (ctypes.c_void_p * 1)(4096)
+    assert fn(None, 1, 1024, 1, 64, ctypes.c_void_p(4096), None) == 1       # no buffer list
+    assert fn(fake, 1, 1000, 1, 64, ctypes.c_void_p(4096), None) == 1       # not a multiple of 16
+    assert fn(fake, 1, 1024, 1, 0, ctypes.c_void_p(4096), None) == 1        # no workgroups
+    assert fn(fake, 1, 1024, 1, 64, None, None) == 1                        # no sink
+    assert fn(fake, 0, 1024, 1, 64, ctypes.c_void_p(4096), None) == 1       # empty buffer list
+
+
 def test_status_strings(lib):
     import w4_dequant_gemm_amd as w4
     assert w4.w4_abi_version() == 2

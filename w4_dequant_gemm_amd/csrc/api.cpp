@@ -1,6 +1,8 @@
-// C ABI of the W4 library: argument checks, then one launch on the caller's
-// stream.  No allocation, no state beyond a thread-local error message, no
-// fallback: anything the kernels do not run is rejected before launch.
+// C ABI of the W4 library: argument checks, then the launches of the call on
+// the caller's stream (one kernel, or two where a row quantization or a split
+// sum goes with it).  No allocation, no state beyond a thread-local error
+// message and the NF4 level table (computed once), no fallback: anything the
+// kernels do not run is rejected before launch.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
