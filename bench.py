@@ -423,8 +423,8 @@ def main():
             extra["w4a8_gemm_70b_m2048"] = {"ms": round(ms8, 4), "TFLOP/s": round(t8, 1)}
             result["roofline_gemm"] = {"bound": "mfma", "achieved": round(t16, 1), "peak": BF16_PEAK_TFLOPS,
                                        "unit": "TFLOP/s", "frac": round(t16 / BF16_PEAK_TFLOPS, 4),
-                                       "traffic": measured_traffic("gemm256_dma_w4a16_70b_m2048"),
-                                       "kernel": "gemm256_dma_kernel<false> + splitk_reduce_kernel<256, 256> (the whole W4A16 "
+                                       "traffic": measured_traffic("gemm256_breg_w4a16_70b_m2048"),
+                                       "kernel": "gemm256_breg_kernel<false> + splitk_reduce_kernel<256, 256> (the whole W4A16 "
                                                  "call, M=2048: 768 tiles whole, the last 128 in two K halves)",
                                        "flops_per_launch": flops, "avg_launch_us": round(ms16 * 1e3, 1)}
             log(f"[bench] 70B GEMM M=2048: W4A16 {ms16:.3f} ms = {t16:.1f} TFLOP/s; "

@@ -15,12 +15,13 @@
 //
 // Kernels, by M (K a multiple of 64 unless noted):
 //   64 < M <= 128    gemm_mid_kernel, 64 x 128 tiles, K split towards 512 workgroups
-//   M > 128, W4A16   gemm256_dma_kernel, 256 x 256 tiles, activations direct to LDS
+//   M > 128, W4A16   gemm256_breg_kernel, 256 x 256 tiles, activations direct to
+//                    LDS, weights dequantized straight into MFMA operands
 //   M > 128, W4A8    gemm256_kernel, 256 x 256 tiles, activations through registers
 //   K % 64 != 0      gemm_kernel, 128 x 128 tiles, K step 32
 // and the gate + up pair (above 32 rows) on gemm_mid_kernel (64- or 128-row
-// tiles) or, W4A16 above 256 rows, gemm256_dma_kernel, with a B tile that
-// interleaves the two weights.  Rows of X beyond M and rows of W beyond
+// tiles, a B tile that interleaves the two weights) or, W4A16 above 256 rows,
+// gemm256_breg_kernel (two waves on each weight).  Rows of X beyond M and rows of W beyond
 // N are clamped or read as zero; the epilogues store only in-range outputs.
 #include <type_traits>
 
@@ -757,61 +758,65 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_mid_kernel(MulParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// W4A16, M >= 128: activations straight from global memory into LDS.
+// W4A16, M > 128: activations straight from global memory into LDS, weights
+// dequantized straight into MFMA operands.
 //
-// Same 256 x 256 tile, K step 64 and 2 x 2 waves of 128 x 128 outputs as
-// above, but the bf16 activations never pass through registers: each wave
-// issues global_load_lds_dwordx4 (lane l's 16 bytes land at the
-// instruction's LDS base + 16 l) two K steps ahead into the free one of three
-// activation stages.  The weight codes come through registers two steps
-// ahead and are dequantized into two bf16 weight stages.  LDS: 3 x 32 KB +
-// 2 x 32 KB = 160 KB, five separate arrays, so that with the loop unrolled by
-// six every access names its stage statically.
+// 256 x 256 tile, K step 64, four waves side by side: wave w owns output
+// columns 64 w .. 64 w + 63 for all 256 rows (8 x 2 blocks of
+// v_mfma_f32_32x32x16_bf16, 256 accumulators).  The bf16 activations never
+// pass through registers: each wave issues global_load_lds_dwordx4 (lane l's
+// 16 bytes land at the instruction's LDS base + 16 l) two K steps ahead into
+// the free one of three 32 KB activation stages (chunk swizzle (row ^ row >>
+// 3) & 7), separate arrays so that with the loop unrolled by six every access
+// names its stage statically.  No two waves share a weight column, so the
+// weights never pass through LDS: lane (c, h) loads the 16 bytes of codes of
+// its column c in the 32-k chunk h of a step two steps ahead and
+// dequantizes them one step ahead into operand registers.  Inside a 64-k
+// step the k order is permuted the same way for A and B: lane half h of
+// k-step kk holds k = 32 h + 8 kk .. + 7.  Against a 2 x 2 wave grid sharing
+// a dequantized B tile in LDS this reads as many fragment bytes from LDS and
+// writes none for the weights (160 KB of LDS traffic per step and compute
+// unit instead of 192 KB), with the same dequantization work per lane.
 //
 // The compiler does not order direct-to-LDS writes against the LDS reads of
 // later steps, so every step ends with an explicit wait for all loads issued
-// before it and for its LDS stores, then the workgroup barrier.  Loads past
-// the last step are clamped to it (same count every step), and the loop ends
-// with a full wait so that nothing writes LDS after the workgroup has
-// finished.
-namespace dma {
+// before it, then the workgroup barrier.  Loads past the last step are
+// clamped to it (same count every step), and the loop ends with a full wait
+// so that nothing writes LDS after the workgroup has finished.
+//
+// PAIR: the gated MLP front half on 256 x 128 output tiles.  Waves 0 and 1
+// sum gate products of output columns 0 .. 63 and 64 .. 127, waves 2 and 3
+// up products of the same columns, so wave 2 + w holds the up sums of wave
+// w's gate sums register for register; after the loop both pass through LDS
+// in register order and H = bf16(act(gate) * up).  No K split.
+namespace breg {
 constexpr int BM = 256, BN = 256, BK = 64, NW = 4, NT = 64 * NW;
-constexpr int STAGE = 256 * BK;                       // bf16 elements per stage
-constexpr int ADMA = BM * BK * 2 / (1024 * NW);       // direct-to-LDS loads per wave and step (8)
-constexpr int CPT = BK / 8;                           // code words per thread and step (8)
-constexpr int SZN = CPT / 4;                          // scale/zero words per thread and step
-constexpr int BLOAD = CPT / 4 + SZN;                  // weight loads per thread and step (4)
-constexpr int NSLOT = 4 * 4 * (BK / 16);              // MFMAs per wave and step (64)
+constexpr int STAGE = BM * BK;                    // bf16 elements per activation stage
+constexpr int ADMA = BM * BK * 2 / (1024 * NW);   // direct-to-LDS loads per wave and step (8)
+constexpr int FJ = 2;                             // 32-column blocks per wave
+constexpr int BLOAD = 2 * FJ;                     // code and scale/zero loads per lane and step
 #ifndef W4_DSWZ
 #define W4_DSWZ 3
 #endif
 __device__ __forceinline__ int swz(int row) { return big::swizzle_fn(W4_DSWZ, row); }
-__device__ __forceinline__ int lds_off(int row, int c) { return row * BK + ((c ^ swz(row)) << 3); }
-}  // namespace dma
+}  // namespace breg
 
-// PAIR: the gated MLP front half on 256 x 128 output tiles.  Weight rows
-// 0 .. 127 of the B tile are 128 columns of the gate weight, rows 128 .. 255
-// the same columns of the up weight, so wave column 0 sums gate products and
-// wave column 1 up products of the same outputs; after the loop the up sums
-// pass through LDS and H = bf16(act(gate) * up).  No K split.
 template <bool PAIR>
-__global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
-    using namespace dma;
-    constexpr int FI = 4, FJ = 4;
+__global__ void __launch_bounds__(breg::NT) gemm256_breg_kernel(MulParams p) {
+    using namespace breg;
+    constexpr int FI = 8;
     __shared__ __attribute__((aligned(16))) uint16_t lds_a0[STAGE];
     __shared__ __attribute__((aligned(16))) uint16_t lds_a1[STAGE];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_b0[STAGE];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_b1[STAGE];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_a2[STAGE];   // 160 KB in all
+    __shared__ __attribute__((aligned(16))) uint16_t lds_a2[STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
+    const int h = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
     const big::TileJob job = PAIR ? tile_job_t<BM, BN / 2>(p) : big::tile_job(p);
     const int64_t m_base = job.m_base, n_base = job.n_base;
     const int64_t M = p.M, N = p.N, K = p.K;
-    const int kb = job.kb, KT = job.KT;      // this workgroup's K steps
+    const int kb = job.kb, KT = job.KT;
     const int g_shift = group_shift(p.G);
 
     float16_t acc[FI][FJ];
@@ -822,22 +827,18 @@ __global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // Activations: load i of this wave fills LDS rows 8 (wave * ADMA + i) ..
+    // activations: load i of this wave fills LDS rows 8 (wave * ADMA + i) ..
     // + 7 of a stage; lane l writes row + l / 8 at chunk position l % 8, so
-    // it loads the chunk that the swizzle of lds_off puts there: (l % 8) ^
-    // swz(row), with swz(row) = (row ^ (row >> 3)) & 7 (the fastest of the
-    // XOR forms measured for this kernel).  Rows past M read row M - 1 and
-    // compute outputs that are never stored.
+    // it loads the chunk that the swizzle puts there, (l % 8) ^ swz(row).
+    // Rows past M read row M - 1 and compute outputs that are never stored.
     const int a_row0 = 8 * wave * ADMA + (lane >> 3);
-    int64_t a_m = m_base + a_row0;
+    const int64_t a_m = m_base + a_row0;
     const int64_t a_last = M - 1;
     const uint16_t* a_src = static_cast<const uint16_t*>(p.X);
     auto dma_item = [&](int kt, uint16_t* stage, int it) {
         kt = (kt < KT ? kt : KT - 1) + kb;
         int64_t m = a_m + 8 * it;
         m = m < a_last ? m : a_last;
-        // lane l lands at chunk position l % 8 of its row, so it loads the
-        // chunk whose swizzled position that is
         const int chunk = (lane & 7) ^ swz(a_row0 + 8 * it);
         const uint16_t* src = a_src + chunk * 8 + m * K + static_cast<int64_t>(kt) * BK;
         // Issued as plain instructions: the compiler cannot tell the three
@@ -851,54 +852,63 @@ __global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
         asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
     };
 
-    // Weights: thread tid owns row tid of the tile (8 code words per step)
-    const bool b_up = PAIR && tid >= BN / 2;
-    int64_t bn = n_base + (PAIR ? tid % (BN / 2) : tid);
-    bn = bn < N ? bn : N - 1;
-    const TiledRow brow = tiled_row(b_up ? p.wq2 : p.wq, b_up ? p.sz2 : p.sz, bn, N, K, p.G);
+    // weights: column n_base + 64 wave + 32 jb + lane % 32 (PAIR: of the
+    // gate weight for waves 0 and 1, of the up weight at 64 (wave - 2) for
+    // waves 2 and 3), clamped to N - 1 (its outputs are not stored); 32-k
+    // chunk 2 kt + h of step kt
+    const bool b_up = PAIR && wave >= 2;
+    const int wcol = PAIR ? 64 * (wave & 1) : 64 * wave;
+    TiledRow brow[FJ];
+#pragma unroll
+    for (int jb = 0; jb < FJ; ++jb) {
+        int64_t bn = n_base + wcol + 32 * jb + (lane & 31);
+        bn = bn < N ? bn : N - 1;
+        brow[jb] = tiled_row(b_up ? p.wq2 : p.wq, b_up ? p.sz2 : p.sz, bn, N, K, p.G);
+    }
     struct Regs {
-        u32x4_t q[CPT / 4];
-        uint32_t s[SZN];
+        u32x4_t q[FJ];
+        uint32_t s[FJ];
     };
     auto load_item = [&](int kt, Regs& r, int it) {
         kt = (kt < KT ? kt : KT - 1) + kb;
-        if (it < CPT / 4) r.q[it] = *reinterpret_cast<const u32x4_t*>(brow.tile_ptr(static_cast<int64_t>(kt) * (BK / 32) + it));
-        else r.s[it - CPT / 4] = brow.group((kt * BK + 32 * (it - CPT / 4)) >> g_shift);
+        if (it < FJ) r.q[it] = *reinterpret_cast<const u32x4_t*>(brow[it].tile_ptr(static_cast<int64_t>(kt) * 2 + h));
+        else r.s[it - FJ] = brow[it - FJ].group((kt * BK + 32 * h) >> g_shift);
     };
-
-    // dequantization of one pair of codes (PairDequant)
+    // dequantized operands of one step: [kk][jb], word kk of the chunk
+    struct BOps {
+        u32x4_t b[BK / 16][FJ];
+    };
     const uint32_t bias16 = opaque_vgpr(0x64006400u);
-    PairDequant dq{bias16};
-    uint32_t b_out[4];
-    auto b_pair = [&](int pr, const Regs& r, uint16_t* B) {
-        const int j = pr / 4, i = pr % 4;
-        if (i == 0 && j % 4 == 0) dq.group(r.s[j / 4]);
-        b_out[i] = dq.pair(r.q[j / 4][j % 4], i);
-        if (i == 3) *reinterpret_cast<uint4*>(B + lds_off(tid, j)) = make_uint4(b_out[0], b_out[1], b_out[2], b_out[3]);
+    PairDequant dq[FJ] = {PairDequant{bias16}, PairDequant{bias16}};
+    auto b_pair = [&](int pr, const Regs& r, BOps& o) {
+        const int kk = pr >> 3, jb = (pr >> 2) & 1, i = pr & 3;
+        if (kk == 0 && i == 0) dq[jb].group(r.s[jb]);
+        o.b[kk][jb][i] = dq[jb].pair(r.q[jb][kk], i);
     };
-
-    auto load_frags = [&](const uint16_t* A, const uint16_t* B, int kk, bf16x8_t (&a)[FI], bf16x8_t (&b)[FJ]) {
-        const int ch = 2 * kk + (lane >> 5);
+    // LDS byte offset of the lane's A fragment in row block i (rows 32 i +
+    // lane % 32) at k-step kk: 4096 i + aoff[kk][i % 2], since the chunk
+    // swizzle of row 32 i + r is swz(r) ^ 4 (i % 2)
+    uint32_t aoff[BK / 16][2];
 #pragma unroll
-        for (int i = 0; i < FI; ++i)
-            a[i] = *reinterpret_cast<const bf16x8_t*>(A + lds_off(wm * 128 + i * 32 + (lane & 31), ch));
+    for (int kk = 0; kk < BK / 16; ++kk)
 #pragma unroll
-        for (int j = 0; j < FJ; ++j)
-            b[j] = *reinterpret_cast<const bf16x8_t*>(B + lds_off(wn * 128 + j * 32 + (lane & 31), ch));
+        for (int ip = 0; ip < 2; ++ip) {
+            const int r = lane & 31;
+            aoff[kk][ip] = static_cast<uint32_t>(r * (BK * 2) + ((((4 * h + kk) ^ (4 * ip)) ^ swz(r)) << 4));
+        }
+    auto frag_a = [&](const uint16_t* A, int kk, int i) -> bf16x8_t {
+        return *reinterpret_cast<const bf16x8_t*>(reinterpret_cast<const char*>(A) + i * 4096 + aoff[kk][i & 1]);
     };
+    auto load_a = [&](const uint16_t* A, int kk, bf16x8_t (&a)[FI]) {
+#pragma unroll
+        for (int i = 0; i < FI; ++i) a[i] = frag_a(A, kk, i);
+    };
+    constexpr int NSLOT = FI * FJ * (BK / 16);
+    static_assert(NSLOT == 64 && 4 * ADMA <= NSLOT && 4 * BLOAD <= NSLOT && NSLOT / 2 == 4 * FJ * (BK / 16), "slot plan");
 
-    static_assert(NSLOT == 2 * 4 * CPT && 4 * ADMA <= NSLOT && 4 * BLOAD <= NSLOT, "slot plan");
-
-    // Three activation stages: step kt reads stage kt % 3 and sends the
-    // activations of step kt + 2 to stage (kt + 2) % 3, so a direct-to-LDS
-    // load has two steps to land.  A step ends waiting only for what was
-    // issued before it (the 12 global loads of the step itself stay in
-    // flight) and for its LDS stores, then the barrier.
     constexpr int kStepLoads = ADMA + BLOAD;
-    static_assert(kStepLoads < 64, "vmcnt field");
     auto step_end3 = [&]() {
         asm volatile("" ::: "memory");
-        // vmcnt = kStepLoads (bits 3:0 and 15:14), expcnt 7 (no wait), lgkmcnt 0
         __builtin_amdgcn_s_waitcnt((kStepLoads & 15) | (7 << 4) | ((kStepLoads >> 4) << 14));
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
@@ -907,39 +917,40 @@ __global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
         constexpr int s3 = decltype(S)::value;
         return s3 == 0 ? lds_a0 : (s3 == 1 ? lds_a1 : lds_a2);
     };
-    auto step3 = [&](int kt, auto SA, auto SB, Regs& next, const Regs& ready) {
-        constexpr int sa = decltype(SA)::value, sb = decltype(SB)::value;
+    // step kt: MFMAs on the operands `cur` (dequantized during step kt - 1);
+    // the codes `ready` (step kt + 1) are dequantized into `nxt`, and the
+    // weights of step kt + 2 load into `next`
+    auto step3 = [&](int kt, auto SA, Regs& next, const Regs& ready, const BOps& cur, BOps& nxt) {
+        constexpr int sa = decltype(SA)::value;
         const uint16_t* As = stage_a(std::integral_constant<int, sa>{});
         uint16_t* Ad = stage_a(std::integral_constant<int, (sa + 2) % 3>{});
-        const uint16_t* Bs = sb ? lds_b1 : lds_b0;
-        uint16_t* Bd = sb ? lds_b0 : lds_b1;
-        bf16x8_t fa[2][FI], fb[2][FJ];
-        load_frags(As, Bs, 0, fa[0], fb[0]);
+        // one set of A fragments: fragment i is reloaded for k-step kk + 1
+        // right after its last use in k-step kk
+        bf16x8_t fa[FI];
+        load_a(As, 0, fa);
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
-            if (kk + 1 < BK / 16) load_frags(As, Bs, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int t = 0; t < FI * FJ; ++t) {
                 const int u = kk * FI * FJ + t;
                 const int i = t / FJ, j = t % FJ;
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j], acc[i][j], 0, 0, 0);
-                // weight loads first (slots 0, 4, 8, 12), then the
-                // activation loads (slots 2, 6, ..., 30): the next step's
-                // first dequantization then waits only for the weights
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], __builtin_bit_cast(bf16x8_t, cur.b[kk][j]),
+                                                                    acc[i][j], 0, 0, 0);
+                if (j == FJ - 1 && kk + 1 < BK / 16) fa[i] = frag_a(As, kk + 1, i);
                 if (u % 4 == 0 && u / 4 < BLOAD) {
                     load_item(kt + 2, next, u / 4);
                     asm volatile("" ::: "memory");
                 }
                 if (u % 4 == 2 && u / 4 < ADMA) dma_item(kt + 2, Ad, u / 4);
-                if (u % 2 == 1) b_pair(u / 2, ready, Bd);
+                if (u % 2 == 1) b_pair(u / 2, ready, nxt);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
         step_end3();
     };
-    // prologue: activations of steps 0 and 1, weights of steps 0 and 1, dequantize step 0
     Regs r0, r1;
+    BOps o0, o1;
 #pragma unroll
     for (int it = 0; it < ADMA; ++it) dma_item(0, lds_a0, it);
 #pragma unroll
@@ -949,82 +960,76 @@ __global__ void __launch_bounds__(dma::NT) gemm256_dma_kernel(MulParams p) {
 #pragma unroll
     for (int it = 0; it < BLOAD; ++it) load_item(1, r1, it);
 #pragma unroll
-    for (int pr = 0; pr < 4 * CPT; ++pr) b_pair(pr, r0, lds_b0);
+    for (int pr = 0; pr < NSLOT / 2; ++pr) b_pair(pr, r0, o0);
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0);           // vmcnt, expcnt and lgkmcnt all 0
+    __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
-    // stage of A cycles with period 3, of B and the registers with period 2
+    // A stages cycle with period 3, code registers and operands with period 2
     for (int kt = 0; kt < KT; kt += 6) {
-        step3(kt, I0{}, I0{}, r0, r1);
-        if (kt + 1 < KT) step3(kt + 1, I1{}, I1{}, r1, r0);
-        if (kt + 2 < KT) step3(kt + 2, I2{}, I0{}, r0, r1);
-        if (kt + 3 < KT) step3(kt + 3, I0{}, I1{}, r1, r0);
-        if (kt + 4 < KT) step3(kt + 4, I1{}, I0{}, r0, r1);
-        if (kt + 5 < KT) step3(kt + 5, I2{}, I1{}, r1, r0);
+        step3(kt, I0{}, r0, r1, o0, o1);
+        if (kt + 1 < KT) step3(kt + 1, I1{}, r1, r0, o1, o0);
+        if (kt + 2 < KT) step3(kt + 2, I2{}, r0, r1, o0, o1);
+        if (kt + 3 < KT) step3(kt + 3, I0{}, r1, r0, o1, o0);
+        if (kt + 4 < KT) step3(kt + 4, I1{}, r0, r1, o0, o1);
+        if (kt + 5 < KT) step3(kt + 5, I2{}, r1, r0, o1, o0);
     }
     __builtin_amdgcn_s_waitcnt(0);
     asm volatile("" ::: "memory");
 
+    // epilogue: register r of lane l holds row (r%4) + 4(l/32) + 8(r/4), column l%32
     if constexpr (PAIR) {
-        // one wave row at a time: its gate sums (wave (h, 0)) and up sums
-        // (wave (h, 1)), 64 KB each in register order, go to LDS (lds_a0/a1
-        // and lds_b0/b1), then all threads form the 128 x 128 outputs of the
-        // half row by row (coalesced stores, one copy of the activation code)
-        constexpr int kHalf = STAGE / 2;      // floats per 32 KB stage
-        float* const g0 = reinterpret_cast<float*>(lds_a0);
-        float* const g1 = reinterpret_cast<float*>(lds_a1);
-        float* const u0 = reinterpret_cast<float*>(lds_b0);
-        float* const u1 = reinterpret_cast<float*>(lds_b1);
+        // four rounds (w, hh): gate wave w and up wave 2 + w put the sums of
+        // their row blocks 4 hh .. 4 hh + 3 (32 KB each, register order) in
+        // lds_a0 and lds_a1; then all threads form the 128 x 64 outputs of
+        // the round row by row (coalesced stores, one copy of the
+        // activation code)
+        constexpr int kQ = 4 * FJ * 16 * 64;      // floats per wave and round (32 KB)
+        float* const g_l = reinterpret_cast<float*>(lds_a0);
+        float* const u_l = reinterpret_cast<float*>(lds_a1);
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            __syncthreads();
-            if (wm == hh) {
-                float* lo = wn == 0 ? g0 : u0;
-                float* hi = wn == 0 ? g1 : u1;
+        for (int w = 0; w < 2; ++w)
 #pragma unroll
-                for (int i = 0; i < FI; ++i)
+            for (int hh = 0; hh < 2; ++hh) {
+                __syncthreads();
+                if (wave == w || wave == 2 + w) {
+                    float* dst = wave == w ? g_l : u_l;
 #pragma unroll
-                    for (int j = 0; j < FJ; ++j)
+                    for (int i = 0; i < 4; ++i)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int e = ((i * FJ + j) * 16 + r) * 64 + lane;
-                            (e < kHalf ? lo : hi)[e % kHalf] = acc[i][j][r];
-                        }
+                        for (int j = 0; j < FJ; ++j)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) dst[((i * FJ + j) * 16 + r) * 64 + lane] = acc[4 * hh + i][j][r];
+                }
+                __syncthreads();
+                for (int o = tid; o < kQ; o += NT) {
+                    const int lr = o >> 6, lc = o & 63;          // row in the round's 128, column in the wave's 64
+                    const int64_t row = m_base + 128 * hh + lr, col = n_base + 64 * w + lc;
+                    if (row >= M || col >= N) continue;
+                    // register order of (lr, lc): block (lr / 32, lc / 32), register
+                    // (rr / 8) 4 + rr % 4 of lane ((rr / 4) % 2) 32 + lc % 32, rr = lr % 32
+                    const int rr = lr & 31;
+                    const int e = ((((lr >> 5) * FJ + (lc >> 5)) * 16 + (rr >> 3) * 4 + (rr & 3)) * 64) +
+                                  ((rr >> 2) & 1) * 32 + (lc & 31);
+                    p.Y[row * N + col] = float_to_bf16_bits(activation(p.act, g_l[e]) * u_l[e]);
+                }
             }
-            __syncthreads();
-            for (int o = tid; o < 128 * 128; o += NT) {
-                const int lr = o >> 7, lc = o & 127;
-                const int64_t row = m_base + hh * 128 + lr, col = n_base + lc;
-                if (row >= M || col >= N) continue;
-                // register order of output (lr, lc) in the wave's 128 x 128 tile
-                const int rr = lr & 31;
-                const int r = (rr >> 3) * 4 + (rr & 3);
-                const int ln = ((rr >> 2) & 1) * 32 + (lc & 31);
-                const int e = (((lr >> 5) * FJ + (lc >> 5)) * 16 + r) * 64 + ln;
-                const float g = e < kHalf ? g0[e] : g1[e - kHalf];
-                const float u = e < kHalf ? u0[e] : u1[e - kHalf];
-                p.Y[row * N + col] = float_to_bf16_bits(activation(p.act, g) * u);
-            }
-        }
         return;
     }
-
-    // epilogue: register r of lane l holds row (r%4) + 4(l/32) + 8(r/4), column l%32
 #pragma unroll
     for (int i = 0; i < FI; ++i)
 #pragma unroll
         for (int j = 0; j < FJ; ++j) {
-            const int lc = wn * 128 + j * 32 + (lane & 31);
+            const int lc = 64 * wave + 32 * j + (lane & 31);
             const int64_t col = n_base + lc;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int lr = wm * 128 + i * 32 + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
+                const int lr = i * 32 + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
                 const int64_t row = m_base + lr;
-                if (job.part >= 0) p.ws[job.part * (BM * BN) + lr * BN + lc] = acc[i][j][r];   // partial tile of a K split
+                if (job.part >= 0) p.ws[job.part * (BM * BN) + lr * BN + lc] = acc[i][j][r];
                 else if (row < M && col < N) p.Y[row * N + col] = float_to_bf16_bits(acc[i][j][r]);
             }
         }
@@ -1182,13 +1187,13 @@ hipError_t launch_gemm_pair(const MulParams& p, hipStream_t stream) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
     if (p.K % big::BK != 0 || !p.wq2 || !p.sz2) return hipErrorInvalidValue;
     if (!p.x_fp8 && p.M > 256) {
-        // W4A16: the activations-direct-to-LDS kernel on 256 x 128 output tiles
+        // W4A16: gemm256_breg_kernel on 256 x 128 output tiles
         const int64_t tiles = ((p.N + big::BN / 2 - 1) / (big::BN / 2)) * ((p.M + big::BM - 1) / big::BM);
         MulParams q = p;
         q.splits = 1;
         q.split_t0 = tiles;
         q.ws = nullptr;
-        hipLaunchKernelGGL(gemm256_dma_kernel<true>, dim3(static_cast<unsigned>(tiles)), dim3(dma::NT), 0, stream, q);
+        hipLaunchKernelGGL(gemm256_breg_kernel<true>, dim3(static_cast<unsigned>(tiles)), dim3(breg::NT), 0, stream, q);
         return hipGetLastError();
     }
     if (p.M <= 64) return p.x_fp8 ? launch_pair_t<64, true>(p, stream) : launch_pair_t<64, false>(p, stream);
@@ -1218,7 +1223,7 @@ hipError_t launch_gemm(const MulParams& p, hipStream_t stream) {
         if (q.x_fp8)
             hipLaunchKernelGGL((gemm256_kernel<kBigWM, kBigWN, true>), grid, dim3(64 * kBigWM * kBigWN), 0, stream, q);
         else
-            hipLaunchKernelGGL(gemm256_dma_kernel<false>, grid, dim3(dma::NT), 0, stream, q);
+            hipLaunchKernelGGL(gemm256_breg_kernel<false>, grid, dim3(breg::NT), 0, stream, q);
         if (q.splits > 1 && q.split_t0 < tiles) {
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
