@@ -887,14 +887,15 @@ __global__ void __launch_bounds__(breg::NT) gemm256_breg_kernel(MulParams p) {
     };
     // LDS byte offset of the lane's A fragment in row block i (rows 32 i +
     // lane % 32) at k-step kk: 4096 i + aoff[kk][i % 2], since the chunk
-    // swizzle of row 32 i + r is swz(r) ^ 4 (i % 2)
+    // swizzle of row 32 i + r depends on i only through i % 2 (for swizzle 3,
+    // (row ^ row >> 3) & 7, it is swz(r) ^ 4 (i % 2))
     uint32_t aoff[BK / 16][2];
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk)
 #pragma unroll
         for (int ip = 0; ip < 2; ++ip) {
             const int r = lane & 31;
-            aoff[kk][ip] = static_cast<uint32_t>(r * (BK * 2) + ((((4 * h + kk) ^ (4 * ip)) ^ swz(r)) << 4));
+            aoff[kk][ip] = static_cast<uint32_t>(r * (BK * 2) + (((4 * h + kk) ^ swz(32 * ip + r)) << 4));
         }
     auto frag_a = [&](const uint16_t* A, int kk, int i) -> bf16x8_t {
         return *reinterpret_cast<const bf16x8_t*>(reinterpret_cast<const char*>(A) + i * 4096 + aoff[kk][i & 1]);
