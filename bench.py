@@ -340,8 +340,9 @@ def main():
                 y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
                 xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
                 xs = torch.empty((M,), dtype=torch.float32, device=dev)
-                # split-K partial sums for shapes with few output tiles
-                ws = torch.empty((max(w4.w4_gemm_workspace_bytes(M, K, N), 16),), dtype=torch.uint8, device=dev)
+                # split-K partial sums for shapes with few output tiles, and above
+                # 128 rows the widened activations (the fastest W4A8 schedule)
+                ws = torch.empty((max(w4.w4a8_gemm_workspace_bytes(M, K, N), 16),), dtype=torch.uint8, device=dev)
 
                 def run(x=x, y=y, xq=xq, xs=xs, ws=ws, copies=copies):
                     for c in copies:
@@ -410,8 +411,9 @@ def main():
             xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
             xs = torch.empty((M,), dtype=torch.float32, device=dev)
             flops = 2.0 * M * N * K
-            # fp32 partial tiles of the last round's tiles, whose K is split
-            ws = torch.empty((max(w4.w4_gemm_workspace_bytes(M, K, N), 16),), dtype=torch.uint8, device=dev)
+            # fp32 partial tiles of the last round's tiles, whose K is split,
+            # and (W4A8) the widened activations: the fastest schedule of both
+            ws = torch.empty((max(w4.w4a8_gemm_workspace_bytes(M, K, N), 16),), dtype=torch.uint8, device=dev)
             # 50 untimed calls (about 50 ms) first: the clocks ramp up under
             # sustained matrix work, and a cold start would time the ramp
             ms16 = timer.time(lambda: w4.w4a16_gemm(X, pk["wq"], pk["sz"], 128, Y=Y, workspace=ws), 20, 50)

@@ -166,6 +166,20 @@ int w4_quantize_rows_e4m3(const uint16_t* X, int64_t M, int64_t K, uint8_t* xq, 
 size_t w4_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
 
 /*
+ * w4a8_gemm_workspace_bytes -- bytes of device workspace for the fastest
+ * schedule of w4a8_gemm: w4_gemm_workspace_bytes, and above 128 rows (K a
+ * multiple of 64, at least 256 output tiles of 256 x 256, i.e. a whole
+ * round over the compute units) also room for the row-quantized activations widened
+ * exactly to bf16 (M * K * 2 bytes after the split partials, at a 256-byte
+ * aligned offset).  With that much, w4a8_gemm runs the bf16 tiled kernel on
+ * the widened codes (same products: every finite E4M3 value is a bf16
+ * value); with only w4_gemm_workspace_bytes it runs a kernel that widens
+ * the E4M3 codes itself.  Both are exact widenings of the same activations;
+ * results may differ in the fp32 summation order only.
+ */
+size_t w4a8_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
+
+/*
  * w4a16_gemm -- W4A16: Y = bf16(X . W'^T) with W'[n, k] = (u - zero) * scale
  * from the GPU layout, fp32 accumulation, bf16 output (round to nearest
  * even).  One entry point for every M: up to 64 rows run a kernel that
@@ -191,6 +205,8 @@ int w4a16_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, cons
  *   X  [M, K] bf16 in.
  *   xq [M, K] bytes and xscale [M] fp32: device buffers the call fills (they
  *      are the operands of the multiply and are left for the caller to read).
+ *   workspace: at least w4_gemm_workspace_bytes(M, K, N) where that is
+ *      required; w4a8_gemm_workspace_bytes(M, K, N) for the fastest schedule.
  *   Other arguments as for w4a16_gemm.
  */
 int w4a8_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const uint32_t* sz,
@@ -210,8 +226,8 @@ int w4a8_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const
  * 0.044715 x^3))) (GeGLU blocks).  Up to 32 rows the weight-streaming
  * kernel reads both matrices at the same 16 output columns per workgroup;
  * above, a tiled MFMA GEMM holds 128 columns of each weight per workgroup
- * (one wave column sums the gate products, the other the up products of the
- * same outputs) and needs K to be a multiple of 64 (else W4_EUNSUPPORTED).
+ * (some of its waves sum the gate products, the others the up products of
+ * the same outputs) and needs K to be a multiple of 64 (else W4_EUNSUPPORTED).
  * No workspace: the tiled form does not split K.  H feeds the down
  * projection (w4a8_gemm on one or two rows quantizes it to E4M3 inside its
  * own kernel).

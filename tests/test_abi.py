@@ -30,7 +30,8 @@ def lib():
 def test_header_declares_the_boundary():
     names = _declared()
     for n in ("w4_quantize_blockwise", "w4_mse_clip_search", "w4_prepack", "w4_quantize_rows_e4m3",
-              "w4a16_gemm", "w4a8_gemm", "w4_gemm_workspace_bytes", "w4_status_string", "w4_last_error",
+              "w4a16_gemm", "w4a8_gemm", "w4_gemm_workspace_bytes", "w4a8_gemm_workspace_bytes",
+              "w4_status_string", "w4_last_error",
               "w4_abi_version", "w4_portable_save", "w4_portable_info_read", "w4_portable_load",
               "w4a16_gate_up", "w4a8_gate_up", "w4_nf4_levels", "w4_nf4_quantize", "w4_nf4_gemv"):
         assert n in names
@@ -135,6 +136,19 @@ def test_gemm_workspace_sizes_and_checks(lib):
     assert ws(256, 96, 3840) == 0                            # K not a multiple of 64: 128 x 128 tiles
     assert ws(256, 512, 256) == 0                            # too few K steps to split
     assert ws(-1, 512, 256) == 0 and ws(256, 0, 256) == 0
+    # W4A8's fastest schedule above 128 rows (K % 64 == 0) with at least 256
+    # output tiles adds the widened activations, M * K * 2 bytes at a
+    # 256-byte aligned offset after the partials; elsewhere it is the same as
+    # the required workspace
+    ws8 = lib.w4a8_gemm_workspace_bytes
+    assert ws8(2048, 8192, 28672) == 128 * 2 * tile + 2048 * 8192 * 2
+    assert ws8(2048, 8192, 32768) == 2048 * 8192 * 2
+    assert ws8(300, 4096, 33000) == 2 * 8 * tile + 300 * 4096 * 2       # 258 tiles
+    assert ws8(1024, 512, 16384) == 1024 * 512 * 2                       # 256 tiles, none split
+    for shape in ((128, 3840, 15360), (64, 15360, 3840), (16, 14336, 4096), (256, 96, 3840), (1, 4096, 14336),
+                  (256, 15360, 3840), (256, 3840, 15360), (129, 128, 256), (1024, 512, 16128)):
+        assert ws8(*shape) == ws(*shape), shape
+    assert ws8(-1, 512, 256) == 0 and ws8(256, 512, 0) == 0
     # a shape that needs one: NULL or too small is rejected before any launch
     fake = ctypes.c_void_p(0x1000)
     need = ws(256, 15360, 3840)

@@ -288,6 +288,49 @@ def test_split_k_products():
         w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G, workspace=ws[:16])
 
 
+def test_w4a8_widened_activations():
+    # above 128 rows, with at least 256 output tiles, a workspace of
+    # w4a8_gemm_workspace_bytes lets the row quantizer also write the E4M3
+    # codes widened to bf16, and the bf16 tiled kernel runs on them (row
+    # scales in its epilogue or split sum); with the required minimum the
+    # E4M3 kernel runs.  Both match the oracle on sampled outputs, with the
+    # same codes and scales: 258 tiles of a ragged N with the last two split
+    # (workspace full of NaNs on entry), 256 whole tiles with G = 64, and the
+    # 12B down shape at M = 256, whose 15 tiles take no widened copy
+    require_gpu()
+    import torch
+    import w4_dequant_gemm_amd as w4
+    cases = [("258 tiles", synth.normal_matrix(54, 33000, 1024, 0.02), 300, 128, True),
+             ("256 tiles, G = 64", synth.normal_matrix(55, 16384, 512, 0.02), 1024, 64, True),
+             ("12B down", synth.weight(synth.WORKLOADS["gemma12b_w4a8"], 1), 256, 128, False)]
+    for name, W, M, G, widened in cases:
+        q = oracle.quantize(np.ascontiguousarray(W), G, "asym")
+        pk, G = prepack_dev(q)
+        N, K = W.shape
+        fast, least = w4.w4a8_gemm_workspace_bytes(M, K, N), w4.w4_gemm_workspace_bytes(M, K, N)
+        assert fast >= least + M * K * 2 if widened else fast == least, (name, fast, least)
+        Xb = synth.to_bf16_bits(synth.normal_matrix(56, M, K))
+        r, c = _rows_cols(M, N, 64, 1024, seed=M)
+        r = np.unique(np.concatenate([r, np.arange(M - 4, M)]))      # the last (partial) row tile
+        c = np.unique(np.concatenate([c, np.arange(N - 8, N)]))      # the ragged last column tile
+        want, rq, rs = oracle.w4a8_ref(Xb, q["packed"], q["scale"], q["zero"], G, "asym", rows=r, cols=c)
+        outs = []
+        for label, nbytes in (("fastest", fast), ("required", least)):
+            print(f"[w4a8 {label} workspace] {name} M={M} K={K} N={N} bytes={nbytes}", flush=True)
+            ws = torch.full((max(nbytes, 16) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+            Y, xq, xs = w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G, workspace=ws)
+            torch.cuda.synchronize()
+            assert_bits_equal(host(xq), rq, "E4M3 activations")
+            assert_bits_equal(host(xs).view(np.uint32), rs.view(np.uint32), "row scales")
+            got = Y.float().cpu().numpy()[np.ix_(r, c)]
+            err = oracle.rel_error(want, got)
+            assert err <= REL_TOL, f"{label} {name}: relative error {err:.3e}"
+            outs.append(got)
+        # the same activations and weights: the two kernels differ only in
+        # the fp32 summation order
+        assert oracle.rel_error(outs[1].astype(np.float64), outs[0]) <= 1e-3
+
+
 def test_split_last_round_products():
     # 258 output tiles over 256 compute units: the first 256 tiles whole, the
     # last two (rows 256..299, columns 32512..32999, ragged in both) in eight

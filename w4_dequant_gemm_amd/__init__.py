@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "W4Error", "SYM", "ASYM", "MAX_FRACS", "lib", "library_path",
     "w4_quantize_blockwise", "w4_mse_clip_search", "w4_prepack", "w4_quantize_rows_e4m3",
-    "w4a16_gemm", "w4a8_gemm", "w4_gemm_workspace_bytes", "w4_status_string", "w4_last_error",
+    "w4a16_gemm", "w4a8_gemm", "w4_gemm_workspace_bytes", "w4a8_gemm_workspace_bytes", "w4_status_string",
+    "w4_last_error",
     "w4_abi_version", "w4_portable_save", "w4_portable_info_read", "w4_portable_load",
     "w4a16_gate_up", "w4a8_gate_up", "ACT_SILU", "ACT_GELU_TANH",
     "w4_nf4_levels", "w4_nf4_quantize", "w4_nf4_gemv",
@@ -77,6 +78,8 @@ def lib():
     L.w4a8_gemm.argtypes = [P, i64, i64, P, P, i64, I, P, P, P, P, sz_t, P]
     L.w4_gemm_workspace_bytes.argtypes = [i64, i64, i64]
     L.w4_gemm_workspace_bytes.restype = sz_t
+    L.w4a8_gemm_workspace_bytes.argtypes = [i64, i64, i64]
+    L.w4a8_gemm_workspace_bytes.restype = sz_t
     L.w4a16_gate_up.argtypes = [P, i64, i64, P, P, P, P, i64, I, I, P, P]
     L.w4a8_gate_up.argtypes = [P, i64, i64, P, P, P, P, i64, I, I, P, P, P, P]
     L.w4a16_gate_up.restype = I
@@ -151,10 +154,11 @@ def _empty(shape, dtype, device):
     return torch.empty(shape, dtype=dtype, device=device)
 
 
-def _workspace(M: int, K: int, N: int, device, workspace, stream):
+def _workspace(M: int, K: int, N: int, device, workspace, stream, w4a8=False):
     """(pointer, bytes) of the product's workspace: the caller's tensor, or a
-    new byte tensor when the shape needs one (kept alive on ``stream``)."""
-    need = w4_gemm_workspace_bytes(M, K, N)
+    new byte tensor of the fastest schedule's size when the shape uses one
+    (kept alive on ``stream``)."""
+    need = w4a8_gemm_workspace_bytes(M, K, N) if w4a8 else w4_gemm_workspace_bytes(M, K, N)
     if workspace is None:
         if need == 0:
             return None, 0
@@ -321,6 +325,12 @@ def w4_gemm_workspace_bytes(M: int, K: int, N: int) -> int:
     return int(lib().w4_gemm_workspace_bytes(M, K, N))
 
 
+def w4a8_gemm_workspace_bytes(M: int, K: int, N: int) -> int:
+    """Workspace bytes for the fastest ``w4a8_gemm`` schedule (above 128 rows
+    also the widened activations); at least ``w4_gemm_workspace_bytes``."""
+    return int(lib().w4a8_gemm_workspace_bytes(M, K, N))
+
+
 def w4a16_gemm(X: torch.Tensor, wq: torch.Tensor, sz: torch.Tensor, G: int, *, Y=None, workspace=None,
                stream=None):
     """``Y[M, N] = bf16(X . W'^T)`` from bf16 ``X[M, K]`` and the GPU-layout weights.
@@ -347,7 +357,7 @@ def w4a8_gemm(X: torch.Tensor, wq: torch.Tensor, sz: torch.Tensor, G: int, *, Y=
     Y = _empty((M, N), torch.bfloat16, dev) if Y is None else Y
     xq = _empty((M, K), torch.uint8, dev) if xq is None else xq
     xscale = _empty((M,), torch.float32, dev) if xscale is None else xscale
-    ws, ws_bytes = _workspace(M, K, N, dev, workspace, stream)
+    ws, ws_bytes = _workspace(M, K, N, dev, workspace, stream, w4a8=True)
     rc = lib().w4a8_gemm(_dev(X, "X", torch.bfloat16), M, K, _dev(wq, "wq"), _dev(sz, "sz"), N, G,
                          _dev(Y, "Y", torch.bfloat16), _dev(xq, "xq"), _dev(xscale, "xscale", torch.float32),
                          ws, ws_bytes, _stream(dev, stream))

@@ -281,6 +281,13 @@ size_t w4_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
     return w4::gemm_workspace_bytes(M, K, N);
 }
 
+size_t w4a8_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+    if (M <= 0 || K <= 0 || N <= 0) return 0;
+    if (M <= w4::kSkinnyMaxM) return w4::skinny_workspace_bytes(M, K, N);   // optional
+    const size_t xw = w4::gemm_xw_bytes(M, K, N);
+    return xw ? w4::gemm_xw_offset(M, K, N) + xw : w4::gemm_workspace_bytes(M, K, N);
+}
+
 int w4a16_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const uint32_t* sz, int64_t N,
                int G, uint16_t* Y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     const char* fn = "w4a16_gemm";
@@ -305,9 +312,17 @@ int w4a8_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const
         w4::MulParams p{X, nullptr, M, K, N, G, wq, sz, Y, true, xq, xscale};
         return hip_status(w4::launch_skinny(p, stream), fn);
     }
-    w4::RowQuantParams rq{X, M, K, xq, xscale};
+    // above 128 rows, a workspace that also holds the widened activations
+    // (w4a8_gemm_workspace_bytes) lets the row quantizer write them and the
+    // bf16 tiled kernel run on them
+    uint16_t* xw = nullptr;
+    const size_t xw_bytes = M > w4::kSkinnyMaxM ? w4::gemm_xw_bytes(M, K, N) : 0;
+    if (xw_bytes && workspace && workspace_bytes >= w4::gemm_xw_offset(M, K, N) + xw_bytes)
+        xw = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + w4::gemm_xw_offset(M, K, N));
+    w4::RowQuantParams rq{X, M, K, xq, xscale, xw};
     W4_TRY(hip_status(w4::launch_rowquant(rq, stream), fn));
     w4::MulParams p{xq, xscale, M, K, N, G, wq, sz, Y, true};
+    p.xw = xw;
     if (M <= w4::kSkinnyMaxM)
         return hip_status(w4::launch_skinny(with_skinny_split(p, workspace, workspace_bytes), stream), fn);
     return hip_status(w4::launch_gemm(with_split(p, workspace), stream), fn);

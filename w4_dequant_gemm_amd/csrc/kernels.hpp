@@ -43,6 +43,7 @@ struct RowQuantParams {
     int64_t M, K;
     uint8_t* xq;             // [M, K] e4m3
     float* xscale;           // [M]
+    uint16_t* xw = nullptr;  // [M, K] the same codes widened exactly to bf16, or null
 };
 hipError_t launch_rowquant(const RowQuantParams& p, hipStream_t stream);
 
@@ -60,6 +61,11 @@ struct MulParams {
     // writes the E4M3 codes and row scales here
     uint8_t* xq_out = nullptr;
     float* xscale_out = nullptr;
+    // W4A8 above 128 rows: the E4M3 activations widened exactly to bf16 (the
+    // row quantizer writes them into the caller's workspace when it is large
+    // enough); the tiled product then runs the bf16 kernel on them and scales
+    // rows in its epilogue or split sum.  Null: the E4M3 kernel.
+    const uint16_t* xw = nullptr;
     // K split across workgroups.  Streaming kernel (splits > 1, M >= 3): K
     // ranges of whole steps, partial sums in ws [range][M][N].  The 64 x 128
     // and 256 x 256 GEMMs: output
@@ -112,6 +118,12 @@ struct GemmSplit {
 };
 GemmSplit gemm_split(int64_t M, int64_t K, int64_t N);
 size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
+// W4A8 tiled product above 128 rows with at least 256 output tiles: byte
+// offset (after the split partials, 256-byte aligned) and size of the
+// widened activations in the workspace; gemm_xw_bytes is 0 where the product
+// takes none
+size_t gemm_xw_offset(int64_t M, int64_t K, int64_t N);
+size_t gemm_xw_bytes(int64_t M, int64_t K, int64_t N);
 
 // NF4 comparator (normal-quantile levels, blocks of 64, double-quantized scales)
 constexpr int64_t kNf4MaxK = 32768;             // one 32-k chunk per lane of a 1024-lane workgroup

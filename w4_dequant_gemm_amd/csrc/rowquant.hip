@@ -58,6 +58,18 @@ __global__ void __launch_bounds__(256) rowquant_kernel(RowQuantParams p) {
         int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
         hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
         out[i] = make_uint2(static_cast<uint32_t>(lo), static_cast<uint32_t>(hi));
+        if (p.xw) {
+            // the same codes widened to bf16 (exact: every finite E4M3 value
+            // is a bf16 value), two per conversion with scale 1
+            const uint32_t c[2] = {static_cast<uint32_t>(lo), static_cast<uint32_t>(hi)};
+            uint32_t wv[4];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                wv[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[j], 1.0f, false));
+                wv[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[j], 1.0f, true));
+            }
+            reinterpret_cast<uint4*>(p.xw + m * p.K)[i] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        }
     }
 }
 
