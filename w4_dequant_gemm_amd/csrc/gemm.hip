@@ -944,7 +944,9 @@ __global__ void __launch_bounds__(breg::NT) gemm256_breg_kernel(MulParams p) {
                     asm volatile("" ::: "memory");
                 }
                 if (u % 4 == 2 && u / 4 < ADMA) dma_item(kt + 2, Ad, u / 4);
-                if (u % 2 == 1) b_pair(u / 2, ready, nxt);
+                // dequantization on the even slots (measured slightly ahead
+                // of the odd ones: 0.824 against 0.829 ms on the 70B shape)
+                if (u % 2 == 0) b_pair(u / 2, ready, nxt);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
