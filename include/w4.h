@@ -25,9 +25,9 @@
  *    Y[M, N] = X[M, K] . W'^T.
  *  - Every pointer argument is a DEVICE pointer on the current HIP device,
  *    owned by the caller, except where a parameter says "host".  The library
- *    allocates no memory and keeps no state besides a thread-local message for
- *    the last failed call; the products take their scratch memory from the
- *    caller (w4_gemm_workspace_bytes).
+ *    allocates no memory.  Its state is a thread-local message for the last
+ *    failed call and the NF4 level table; the products take their scratch
+ *    memory from the caller (w4_gemm_workspace_bytes).
  *  - Device pointers must be 16-byte aligned.
  *  - Every call is asynchronous on `stream` (0 = the null stream).  Arguments
  *    are checked on the host before any launch: a violated precondition
@@ -68,6 +68,10 @@ extern "C" {
 /*
  * w4_quantize_blockwise -- quantize W[N, K] (fp32) in groups of G consecutive
  * weights along K, with an optional MSE clip search.
+ * Follows gsantana.dev "Quantizing LLMs Without Guesswork", "Scale and zero
+ * point" (both formulas) and "Granularity: who shares a scale"; gowda.ai "LLM
+ * fast inference", "Achievement 1" (unsigned codes 0..15 with an integer zero
+ * point, 16-bit scale and zero) and "MSE clipping" (the candidate search).
  *
  * For every group the candidate ranges are, for each fraction f in `fracs`:
  *   asym: f == 1 -> [min, max]; f < 1 -> [mid - f*h, mid + f*h] with
@@ -109,7 +113,10 @@ int w4_quantize_blockwise(const float* W, int64_t N, int64_t K, int G, int mode,
 /*
  * w4_mse_clip_search -- the search of w4_quantize_blockwise alone: for every
  * group, the index of the chosen fraction and optionally every candidate's
- * error.  Arguments as for w4_quantize_blockwise, plus:
+ * error.  Follows gowda.ai "LLM fast inference", "MSE clipping" (ranges
+ * contracted about the observed midpoint, the block error including clipped
+ * values, the plain quantizer kept unless a candidate is strictly better).
+ * Arguments as for w4_quantize_blockwise, plus:
  *   clip_idx [N, K/G] bytes out (required).
  *   sse      [N, K/G, n_fracs] fp32 out, the candidates' squared-error sums
  *            exactly as compared by the search; may be NULL.
@@ -121,6 +128,10 @@ int w4_mse_clip_search(const float* W, int64_t N, int64_t K, int G, int mode,
 /*
  * w4_prepack -- rearrange the portable packing into the layout the multiply
  * kernels read ("GPU layout"), once per weight, without requantizing.
+ * Follows gowda.ai "LLM fast inference", "MSE clipping" (last paragraph: the
+ * portable packed codes, scales and zero terms are rearranged into a
+ * GPU-specific layout without dequantizing) and "Runtime" (load-time
+ * specialization of the checkpoint for the kernel).
  *   packed  [N, K/2] canonical bytes in (as written by w4_quantize_blockwise).
  *   scale   [N, K/G] fp16 in;  zero [N, K/G] fp16 in (W4_ASYM), NULL (W4_SYM).
  *   wq      N*K/8 uint32 out.  The 8 codes of row n, k = 8j..8j+7, form one
@@ -141,7 +152,9 @@ int w4_prepack(const uint8_t* packed, const uint16_t* scale, const uint16_t* zer
                int64_t K, int G, int mode, uint32_t* wq, uint32_t* sz, hipStream_t stream);
 
 /*
- * w4_quantize_rows_e4m3 -- dynamic per-row FP8 quantization of activations:
+ * w4_quantize_rows_e4m3 -- dynamic per-row FP8 quantization of activations
+ * (gowda.ai "LLM fast inference", "Achievement 2"; gsantana.dev "Number
+ * formats: what the bits buy" for E4M3):
  *   xscale[m] = max(max_k |x[m, k]| / 448, 1e-8)   (fp32)
  *   xq[m, k]  = e4m3(fl32(x[m, k] / xscale[m]))      (round to nearest even,
  *                                                     saturating to +-448)
@@ -154,7 +167,9 @@ int w4_quantize_rows_e4m3(const uint16_t* X, int64_t M, int64_t K, uint8_t* xq, 
 /*
  * w4_gemm_workspace_bytes -- bytes of device workspace for the fastest
  * schedule of w4a16_gemm and w4a8_gemm on a product of M rows, reduction K
- * and N outputs: splits * M * N * 4 bytes of fp32 partial sums when the
+ * and N outputs (the scratch of the products that gowda.ai "LLM fast
+ * inference", "Achievement 2", defines; FP32 partial sums of one output are
+ * added in a fixed order): splits * M * N * 4 bytes of fp32 partial sums when the
  * product splits K across workgroups, else 0.  Above 64 rows the tiled GEMM
  * needs it (a product with few output tiles splits K).  From 3 to 64 rows it
  * is optional: with it, the weight-streaming kernel splits K when its widest
@@ -167,7 +182,7 @@ size_t w4_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
 
 /*
  * w4a8_gemm_workspace_bytes -- bytes of device workspace for the fastest
- * schedule of w4a8_gemm: w4_gemm_workspace_bytes, and above 128 rows (K a
+ * schedule of w4a8_gemm (gowda.ai "LLM fast inference", "Achievement 2"): w4_gemm_workspace_bytes, and above 128 rows (K a
  * multiple of 64, at least 256 output tiles of 256 x 256, i.e. a whole
  * round over the compute units) also room for the row-quantized activations widened
  * exactly to bf16 (M * K * 2 bytes after the split partials, at a 256-byte
@@ -182,7 +197,11 @@ size_t w4a8_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
 /*
  * w4a16_gemm -- W4A16: Y = bf16(X . W'^T) with W'[n, k] = (u - zero) * scale
  * from the GPU layout, fp32 accumulation, bf16 output (round to nearest
- * even).  One entry point for every M: up to 64 rows run a kernel that
+ * even).  Follows gsantana.dev "Quantizing LLMs Without Guesswork",
+ * "Weight-only methods: GPTQ, AWQ and the file formats" (weights dequantized
+ * inside the matmul, arithmetic in 16-bit), "Scale and zero point" (the
+ * reconstruction (q - z) s) and "The Problem & Context" (decode reads every
+ * weight once).  One entry point for every M: up to 64 rows run a kernel that
  * streams the weights once (bandwidth bound), larger M a tiled bf16-MFMA
  * GEMM.
  *   X  [M, K] bf16 in;  wq, sz as written by w4_prepack;  Y [M, N] bf16 out.
@@ -201,7 +220,10 @@ int w4a16_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, cons
 /*
  * w4a8_gemm -- W4A8: each activation row is quantized to E4M3 exactly as by
  * w4_quantize_rows_e4m3, then Y = bf16(xscale[m] * sum_k e4m3(xq[m, k]) *
- * W'[n, k]) with fp32 accumulation.
+ * W'[n, k]) with fp32 accumulation.  Follows gowda.ai "LLM fast inference",
+ * "Achievement 2: 8-bit activations without a calibration set" (per-row
+ * dynamic E4M3, FP32 accumulation, the row scale in the epilogue, BF16
+ * result).
  *   X  [M, K] bf16 in.
  *   xq [M, K] bytes and xscale [M] fp32: device buffers the call fills (they
  *      are the operands of the multiply and are left for the caller to read).

@@ -10,8 +10,9 @@ contraction for the quantizer, float64 for the products).  This module only
 marshals NumPy arrays into it, plus two host-side formulas from the pages that
 need no compiled code:
 
-* ``rel_error`` -- the Frobenius relative error of gsantana.dev, "Quantizing
-  LLMs Without Guesswork", section "Quantize, then dequantize";
+* ``frobenius_gap`` -- the error measure of gsantana.dev, "Quantizing LLMs
+  Without Guesswork", section "Quantize, then dequantize" (Frobenius norm of
+  the difference over that of the reference);
 * ``bits_per_weight`` -- the storage accounting of the same section, and of
   gowda.ai "LLM fast inference", "Achievement 1" (16-bit scale and 16-bit zero
   per group).
@@ -343,11 +344,11 @@ def nf4_bits_per_weight() -> float:
 
 # ----------------------------------------------------------- host formulas
 
-def rel_error(reference: np.ndarray, approx: np.ndarray) -> float:
-    """||reference - approx||_F / ||reference||_F."""
-    r = np.asarray(reference, dtype=np.float64)
-    a = np.asarray(approx, dtype=np.float64)
-    return float(np.linalg.norm(r - a) / np.linalg.norm(r))
+def frobenius_gap(want: np.ndarray, got: np.ndarray) -> float:
+    """Distance of ``got`` from ``want`` in the Frobenius norm, relative to the
+    norm of ``want`` (both taken as float64)."""
+    d = np.asarray(want, dtype=np.float64) - np.asarray(got, dtype=np.float64)
+    return float(np.sqrt(np.sum(d * d)) / np.sqrt(np.sum(np.asarray(want, dtype=np.float64) ** 2)))
 
 
 def bits_per_weight(bits: int, symmetric: bool, block: int, zero_bits: Optional[int] = None) -> float:

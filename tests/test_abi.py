@@ -159,6 +159,46 @@ def test_gemm_workspace_sizes_and_checks(lib):
     assert lib.w4a16_gemm(fake, 256, 15360, fake, fake, 3840, 128, fake, ctypes.c_void_p(0x1004), need,
                           None) == 1
     assert "aligned" in w4.w4_last_error()
+    # a misaligned workspace is refused even where the shape splits nothing
+    # (W4A8 above 128 rows may put the widened activations in it)
+    assert ws8(2048, 8192, 32768) > 0 and ws(2048, 8192, 32768) == 0
+    assert lib.w4a8_gemm(fake, 2048, 8192, fake, fake, 32768, 128, fake, fake, fake, ctypes.c_void_p(0x1008),
+                         ws8(2048, 8192, 32768), None) == 1
+    assert "aligned" in w4.w4_last_error()
+    assert lib.w4a16_gemm(fake, 2, 4096, fake, fake, 64, 128, fake, ctypes.c_void_p(0x1001), 4096, None) == 1
+
+
+def test_binding_checks_shapes_before_any_launch(lib):
+    # the ABI sees pointers only; the binding compares tensor sizes first and
+    # raises ValueError (CPU tensors: nothing here reaches a device)
+    import torch
+    import w4_dequant_gemm_amd as w4
+    N, K, G, M = 64, 4096, 128, 3
+    X = torch.zeros((M, K), dtype=torch.bfloat16)
+    wq = torch.zeros((N, K // 8), dtype=torch.int32)
+    sz = torch.zeros((N, K // G), dtype=torch.int32)
+    wq_14336 = torch.zeros((N, 14336 // 8), dtype=torch.int32)
+    with pytest.raises(ValueError, match="wq holds"):
+        w4.w4a16_gemm(X, wq_14336, sz, G)                       # K of X against a longer weight
+    with pytest.raises(ValueError, match="sz holds"):
+        w4.w4a16_gemm(X, wq, sz[:, :-1].contiguous(), G)
+    with pytest.raises(ValueError, match="sz holds"):
+        w4.w4a16_gemm(X, wq, sz, 32)                            # wrong group size for these scales
+    with pytest.raises(ValueError, match="output has shape"):
+        w4.w4a16_gemm(X, wq, sz, G, Y=torch.zeros((M, N + 1), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="xq must be"):
+        w4.w4a8_gemm(X, wq, sz, G, xq=torch.zeros((M, K - 8), dtype=torch.uint8))
+    with pytest.raises(ValueError, match="xscale has"):
+        w4.w4a8_gemm(X, wq, sz, G, xscale=torch.zeros((M + 1,), dtype=torch.float32))
+    gate = {"wq": wq, "sz": sz}
+    up = {"wq": torch.zeros((N + 16, K // 8), dtype=torch.int32), "sz": sz}
+    with pytest.raises(ValueError, match="up weight"):
+        w4.w4a16_gate_up(X, gate, up, G)
+    with pytest.raises(ValueError, match="up weight"):
+        w4.w4a8_gate_up(X, gate, {"wq": wq, "sz": torch.zeros((N, 2 * K // G), dtype=torch.int32)}, G)
+    # well-formed shapes get past the checks, to the device check
+    with pytest.raises(ValueError, match="device tensor"):
+        w4.w4a16_gemm(X, wq, sz, G)
 
 
 def test_per_channel_group_sizes(lib):

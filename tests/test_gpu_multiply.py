@@ -6,8 +6,9 @@ import pytest
 
 import oracle
 import synth
-from helpers import (REL_TOL, assert_bits_equal, bf16_dev, bits16, host, oracle_quant, prepack_dev,
-                     require_gpu, to_dev)
+from helpers import (REL_TOL, abs_products, assert_bits_equal, assert_gate_up_close, assert_outputs_close,
+                     bf16_dev, bits16, check_products, host, oracle_quant, prepack_dev, require_gpu, to_dev,
+                     w4a8_x64)
 
 pytestmark = pytest.mark.gpu
 
@@ -108,18 +109,18 @@ def test_products_match_oracle(case, kind):
         if kind == "w4a16":
             Y = w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G)
             torch.cuda.synchronize()
-            want = oracle.gemm_ref(oracle.bf16_bits_to_f64(Xb), q["packed"], q["scale"], q["zero"], G, mode,
-                                   rows=r, cols=c)
+            X64 = oracle.bf16_bits_to_f64(Xb)
+            want = oracle.gemm_ref(X64, q["packed"], q["scale"], q["zero"], G, mode, rows=r, cols=c)
         else:
             Y, xq, xs = w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G)
             torch.cuda.synchronize()
             want, rq, rs = oracle.w4a8_ref(Xb, q["packed"], q["scale"], q["zero"], G, mode, rows=r, cols=c)
             assert_bits_equal(host(xq), rq, "E4M3 activations")
             assert_bits_equal(host(xs).view(np.uint32), rs.view(np.uint32), "row scales")
+            X64 = w4a8_x64(rq, rs)
         got = Y.float().cpu().numpy()[np.ix_(r, c)]
-        err = oracle.rel_error(want, got)
+        err = check_products(want, got, X64, q, G, mode, f"{kind} {name} M={M}", rows=r, cols=c)
         print(f"    rel err {err:.3e}", flush=True)
-        assert err <= REL_TOL, f"{kind} {name} M={M}: relative error {err:.3e} > {REL_TOL}"
 
 
 @pytest.mark.parametrize("kind", ["w4a16", "w4a8"])
@@ -146,46 +147,84 @@ def test_70b_prefill_gemm_sampled(kind):
     if kind == "w4a16":
         Y = w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], 128)
         torch.cuda.synchronize()
-        want = oracle.gemm_ref(oracle.bf16_bits_to_f64(Xb[rows]), qs["packed"], qs["scale"], qs["zero"], 128, "asym")
+        X64 = oracle.bf16_bits_to_f64(Xb[rows])
+        want = oracle.gemm_ref(X64, qs["packed"], qs["scale"], qs["zero"], 128, "asym")
     else:
         Y, xq, xs = w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], 128)
         torch.cuda.synchronize()
         want, rq, rs = oracle.w4a8_ref(Xb[rows], qs["packed"], qs["scale"], qs["zero"], 128, "asym")
         assert_bits_equal(host(xq)[rows], rq, "E4M3 activations (sampled rows)")
+        X64 = w4a8_x64(rq, rs)
     got = Y.float().cpu().numpy()[np.ix_(rows, cols)]
-    err = oracle.rel_error(want, got)
+    err = check_products(want, got, X64, qs, 128, "asym", f"70B {kind}")
     print(f"    rel err {err:.3e}", flush=True)
-    assert err <= REL_TOL
 
 
+# One-hot activation rows (x = e_k) through every product kernel.  A W4A16
+# output is then bf16(W'[n, k]) exactly: the kernels round W' at most once to
+# bf16 (or keep it exact) and add a single nonzero product to zeros, also
+# across K splits.  W4A8 quantizes such a row to one code 448 with row scale
+# fl(1/448), so its outputs are W'[n, k] up to two bf16-sized roundings.  The
+# cases pick shapes whose schedule (checked through the workspace sizes)
+# reaches each kernel: the streaming kernel (dot and MFMA forms, its K split),
+# the 64 x 128 tiles with and without a K split, the 128 x 128 tiles (K not a
+# multiple of 64), the 256 x 256 tiles whole, all split, and with only the
+# last partial round split, for W4A8 also on widened activations.
+ONE_HOT_CASES = [
+    # label, N, K, G, mode, M, expected schedule
+    ("streaming", 576, 1536, 32, "asym", (1, 8, 16, 48), "stream"),
+    ("streaming G128", 1000, 8192, 128, "asym", (2, 16), "stream"),
+    ("streaming K split", 1000, 8192, 128, "asym", (40,), "stream-split"),
+    ("64x128 split", 1536, 1024, 128, "asym", (65, 100), "split"),
+    ("64x128 whole", 32768, 256, 32, "sym", (128,), "whole"),
+    ("128x128", 300, 1568, 32, "asym", (130,), "whole"),
+    ("256x256 all split", 1000, 1024, 128, "asym", (300,), "split"),
+    ("256x256 whole", 1000, 256, 64, "asym", (257,), "whole"),
+    ("256x256 last round split", 8448, 1024, 128, "asym", (2048,), "split"),
+]
+
+
+@pytest.mark.parametrize("case", ONE_HOT_CASES, ids=lambda c: c[0].replace(" ", "_"))
 @pytest.mark.parametrize("kind", ["w4a16", "w4a8"])
-def test_one_hot_rows_recover_dequantized_weights(kind):
-    # X = e_k: W4A16 output column k is bf16(W'[n, k]) exactly, since a single
-    # product of exact values is accumulated; W4A8 equals it after removing the
-    # row scale (one-hot rows quantize to a single 448 code)
+def test_one_hot_rows_recover_dequantized_weights(case, kind):
     require_gpu()
     import torch
     import w4_dequant_gemm_amd as w4
-    q = oracle_quant("smollm2_135m_mlp", 1, None, "asym", 32, 1)
-    pk, G = prepack_dev(q)
-    N, K = q["q"].shape
-    Wd = oracle.dequant(q["packed"], q["scale"], q["zero"], G, "asym")
-    for M in (1, 8, 16, 48):
-        ks = np.linspace(0, K - 1, M).astype(np.int64)
+    label, N, K, G, mode, Ms, sched = case
+    W = synth.normal_matrix(70 + N, N, K, 0.02)
+    q = oracle.quantize(W, G, mode)
+    pk, G2 = prepack_dev(q)
+    Wd = oracle.dequant(q["packed"], q["scale"], q["zero"], G2, mode)
+    for M in Ms:
+        need = w4.w4_gemm_workspace_bytes(M, K, N)
+        if sched == "whole":
+            assert need == 0, (label, M, need)
+        elif sched in ("split", "stream-split"):
+            assert need > 0, (label, M)
+        ks = (np.arange(M, dtype=np.int64) * 7919 + 3) % K          # every group position, tails included
         X = np.zeros((M, K), np.float32)
         X[np.arange(M), ks] = 1.0
         Xb = synth.to_bf16_bits(X)
-        want = synth.to_bf16_bits(Wd[:, ks].T.astype(np.float32))   # exact W' rounded once to bf16
+        want = Wd[:, ks].T                                           # exact float64 W'[n, k_m]
+        print(f"[one-hot {kind}] {label} M={M} N={N} K={K} G={G} workspace={need}", flush=True)
         if kind == "w4a16":
-            Y = w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G)
+            Y = w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G2)
             torch.cuda.synchronize()
-            assert_bits_equal(bits16(Y), want, f"one-hot W4A16 M={M}")
+            assert_bits_equal(bits16(Y), synth.to_bf16_bits(want.astype(np.float32)), f"one-hot W4A16 {label} M={M}")
         else:
-            Y, xq, xs = w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G)
-            torch.cuda.synchronize()
-            # xscale = 1/448, code 448: the product is W' * 448 * (1/448) in fp32
-            got = Y.float().cpu().numpy()
-            np.testing.assert_allclose(got, Wd[:, ks].T, rtol=2 ** -8, atol=0)
+            outs = []
+            ws_sizes = [None]
+            if M > 128 and w4.w4a8_gemm_workspace_bytes(M, K, N) > need:
+                ws_sizes.append(max(need, 16))      # the E4M3 kernel instead of the widened copy
+            for nb in ws_sizes:
+                ws = None if nb is None else torch.empty((nb,), dtype=torch.uint8, device="cuda")
+                Y, xq, xs = w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G2, workspace=ws)
+                torch.cuda.synchronize()
+                assert np.all(host(xq)[np.arange(M), ks] == 0x7E)    # the E4M3 code of 448
+                got = Y.float().cpu().numpy()
+                assert_outputs_close(want, got, np.zeros_like(want), f"one-hot W4A8 {label} M={M} ws={nb}",
+                                     tol=2.0 ** -8 * 1.01)
+                outs.append(got)
 
 
 def test_zero_rows_and_ragged_shapes():
@@ -208,8 +247,11 @@ def test_zero_rows_and_ragged_shapes():
             assert np.all(bits16(Y)[0] & 0x7FFF == 0)           # a zero row gives zeros
             assert np.all(bits16(Y8)[0] & 0x7FFF == 0)
             if M > 1:
-                assert oracle.rel_error(want[1:], Y.float().cpu().numpy()[1:]) <= REL_TOL
-                assert oracle.rel_error(want8[1:], Y8.float().cpu().numpy()[1:]) <= REL_TOL
+                rq, rs = oracle.row_quant_e4m3(Xb)
+                check_products(want[1:], Y.float().cpu().numpy()[1:], oracle.bf16_bits_to_f64(Xb)[1:], q, G2, mode,
+                               f"w4a16 {mode} M={M}")
+                check_products(want8[1:], Y8.float().cpu().numpy()[1:], w4a8_x64(rq, rs)[1:], q, G2, mode,
+                               f"w4a8 {mode} M={M}")
 
 
 def test_w4a8_decode_row_quant_in_product():
@@ -242,12 +284,12 @@ def test_w4a8_decode_row_quant_in_product():
             assert_bits_equal(host(xq), rq, f"E4M3 activations K={K} M={M}")
             assert_bits_equal(host(xs).view(np.uint32), rs.view(np.uint32), f"row scales K={K} M={M}")
             got = Y.float().cpu().numpy()
+            X64 = w4a8_x64(rq, rs)
             for i, r in enumerate(pick):
                 if r == 2:
                     assert np.all(bits16(Y)[i] & 0x7FFF == 0)
                 else:
-                    err = oracle.rel_error(want[i], got[i])
-                    assert err <= REL_TOL, f"K={K} M={M} row {i}: relative error {err:.3e}"
+                    check_products(want[i:i + 1], got[i:i + 1], X64[i:i + 1], q, G, "asym", f"K={K} M={M} row {i}")
 
 
 def test_split_k_products():
@@ -269,15 +311,16 @@ def test_split_k_products():
         print(f"[split-K] {kind} M={M} K={K} N={N}", flush=True)
         if kind == "w4a16":
             Y = w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G, workspace=ws)
-            want = oracle.gemm_ref(oracle.bf16_bits_to_f64(Xb), q["packed"], q["scale"], q["zero"], G, "asym")
+            X64 = oracle.bf16_bits_to_f64(Xb)
+            want = oracle.gemm_ref(X64, q["packed"], q["scale"], q["zero"], G, "asym")
         else:
             Y, xq, xs = w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G, workspace=ws)
             want, rq, rs = oracle.w4a8_ref(Xb, q["packed"], q["scale"], q["zero"], G, "asym")
             torch.cuda.synchronize()
             assert_bits_equal(host(xq), rq, "E4M3 activations")
+            X64 = w4a8_x64(rq, rs)
         torch.cuda.synchronize()
-        err = oracle.rel_error(want, Y.float().cpu().numpy())
-        assert err <= REL_TOL, f"{kind}: relative error {err:.3e}"
+        check_products(want, Y.float().cpu().numpy(), X64, q, G, "asym", f"split-K {kind}")
         # the same call again gives the same bits (fixed summation order)
         Y2 = (w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G, workspace=ws) if kind == "w4a16" else
               w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G, workspace=ws)[0])
@@ -323,12 +366,11 @@ def test_w4a8_widened_activations():
             assert_bits_equal(host(xq), rq, "E4M3 activations")
             assert_bits_equal(host(xs).view(np.uint32), rs.view(np.uint32), "row scales")
             got = Y.float().cpu().numpy()[np.ix_(r, c)]
-            err = oracle.rel_error(want, got)
-            assert err <= REL_TOL, f"{label} {name}: relative error {err:.3e}"
+            check_products(want, got, w4a8_x64(rq, rs), q, G, "asym", f"{label} {name}", rows=r, cols=c)
             outs.append(got)
         # the same activations and weights: the two kernels differ only in
         # the fp32 summation order
-        assert oracle.rel_error(outs[1].astype(np.float64), outs[0]) <= 1e-3
+        assert oracle.frobenius_gap(outs[1].astype(np.float64), outs[0]) <= 1e-3
 
 
 def test_split_last_round_products():
@@ -351,17 +393,17 @@ def test_split_last_round_products():
         print(f"[split last round] {kind} M={M} K={K} N={N}", flush=True)
         if kind == "w4a16":
             Y = w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G)
-            want = oracle.gemm_ref(oracle.bf16_bits_to_f64(Xb), q["packed"], q["scale"], q["zero"], G, "asym",
-                                   rows=rows, cols=cols)
+            X64 = oracle.bf16_bits_to_f64(Xb)
+            want = oracle.gemm_ref(X64, q["packed"], q["scale"], q["zero"], G, "asym", rows=rows, cols=cols)
         else:
             Y, _, _ = w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G)
-            want, _, _ = oracle.w4a8_ref(Xb, q["packed"], q["scale"], q["zero"], G, "asym", rows=rows, cols=cols)
+            want, rq, rs = oracle.w4a8_ref(Xb, q["packed"], q["scale"], q["zero"], G, "asym", rows=rows, cols=cols)
+            X64 = w4a8_x64(rq, rs)
         torch.cuda.synchronize()
         got = Y.float().cpu().numpy()[np.ix_(rows, cols)]
-        err = oracle.rel_error(want, got)
-        assert err <= REL_TOL, f"{kind}: relative error {err:.3e}"
+        check_products(want, got, X64, q, G, "asym", f"split last round {kind}", rows=rows, cols=cols)
         tail = np.ix_(rows >= 256, cols >= 32512)
-        err_t = oracle.rel_error(want[tail], got[tail])
+        err_t = oracle.frobenius_gap(want[tail], got[tail])
         assert err_t <= REL_TOL, f"{kind} split tiles: relative error {err_t:.3e}"
 
 
@@ -376,8 +418,9 @@ def test_group_size_64():
         Xb = _x("smollm2_135m_mlp", M, K)
         Y = w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G)
         torch.cuda.synchronize()
-        want = oracle.gemm_ref(oracle.bf16_bits_to_f64(Xb), q["packed"], q["scale"], q["zero"], G, "sym")
-        assert oracle.rel_error(want, Y.float().cpu().numpy()) <= REL_TOL
+        X64 = oracle.bf16_bits_to_f64(Xb)
+        want = oracle.gemm_ref(X64, q["packed"], q["scale"], q["zero"], G, "sym")
+        check_products(want, Y.float().cpu().numpy(), X64, q, G, "sym", f"G=64 M={M}")
 
 
 def test_invalid_arguments_raise():
@@ -412,12 +455,29 @@ def test_per_channel_products():
             Y = w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G)
             Y8, xq, xs = w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G)
             torch.cuda.synchronize()
-            want = oracle.gemm_ref(oracle.bf16_bits_to_f64(Xb), q["packed"], q["scale"], q["zero"], G, "asym")
+            X64 = oracle.bf16_bits_to_f64(Xb)
+            want = oracle.gemm_ref(X64, q["packed"], q["scale"], q["zero"], G, "asym")
             want8, rq, rs = oracle.w4a8_ref(Xb, q["packed"], q["scale"], q["zero"], G, "asym")
             assert_bits_equal(host(xq), rq, "E4M3 activations")
-            e16 = oracle.rel_error(want, Y.float().cpu().numpy())
-            e8 = oracle.rel_error(want8, Y8.float().cpu().numpy())
-            assert e16 <= REL_TOL and e8 <= REL_TOL, (M, e16, e8)
+            check_products(want, Y.float().cpu().numpy(), X64, q, G, "asym", f"per-channel w4a16 M={M}")
+            check_products(want8, Y8.float().cpu().numpy(), w4a8_x64(rq, rs), q, G, "asym", f"per-channel w4a8 M={M}")
+
+
+def _check_gate_up(H64, got, Xb, qg, qu, G, mode, act, kind, what, rows=None, cols=None):
+    """Frobenius check and per-output bound of a fused gate and up result."""
+    err = oracle.frobenius_gap(H64, got)
+    assert err <= REL_TOL, f"{what}: relative error {err:.3e} > {REL_TOL}"
+    if kind == "w4a16":
+        X64 = oracle.bf16_bits_to_f64(Xb)
+    else:
+        rq, rs = oracle.row_quant_e4m3(Xb)
+        X64 = w4a8_x64(rq, rs)
+    r = np.arange(Xb.shape[0]) if rows is None else np.asarray(rows)
+    g64 = oracle.gemm_ref(X64, qg["packed"], qg["scale"], qg["zero"], G, mode, rows=r, cols=cols)
+    u64 = oracle.gemm_ref(X64, qu["packed"], qu["scale"], qu["zero"], G, mode, rows=r, cols=cols)
+    ag = abs_products(X64[r], qg, G, mode, cols)
+    au = abs_products(X64[r], qu, G, mode, cols)
+    assert_gate_up_close(H64, got, g64, u64, ag, au, act, what)
 
 
 @pytest.mark.parametrize("kind", ["w4a16", "w4a8"])
@@ -458,8 +518,8 @@ def test_gate_up_products(kind):
                     assert_bits_equal(host(xq), rq, "E4M3 activations")
                     assert_bits_equal(host(xs).view(np.uint32), rs.view(np.uint32), "row scales")
                 torch.cuda.synchronize()
-                err = oracle.rel_error(want, H.float().cpu().numpy())
-                assert err <= REL_TOL, f"{kind} {act} M={M}: relative error {err:.3e}"
+                _check_gate_up(want, H.float().cpu().numpy(), Xb, qg, qu, G, mode, act, kind,
+                               f"{kind} {act} M={M}")
     # above 32 rows the tiled form needs K to be a multiple of 64
     Wr = synth.normal_matrix(62, 64, 1568, 0.05)
     qr = oracle.quantize(Wr, 32, "asym")
@@ -493,13 +553,13 @@ def test_mid_size_products():
             Y = w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G2, workspace=ws)
             Y8, xq, xs = w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G2, workspace=ws)
             torch.cuda.synchronize()
-            want = oracle.gemm_ref(oracle.bf16_bits_to_f64(Xb), q["packed"], q["scale"], q["zero"], G2, mode)
+            X64 = oracle.bf16_bits_to_f64(Xb)
+            want = oracle.gemm_ref(X64, q["packed"], q["scale"], q["zero"], G2, mode)
             want8, rq, rs = oracle.w4a8_ref(Xb, q["packed"], q["scale"], q["zero"], G2, mode)
             assert_bits_equal(host(xq), rq, "E4M3 activations")
             assert np.all(bits16(Y)[M // 2] & 0x7FFF == 0) and np.all(bits16(Y8)[M // 2] & 0x7FFF == 0)
-            e16 = oracle.rel_error(want, Y.float().cpu().numpy())
-            e8 = oracle.rel_error(want8, Y8.float().cpu().numpy())
-            assert e16 <= REL_TOL and e8 <= REL_TOL, (N, K, G, M, e16, e8)
+            check_products(want, Y.float().cpu().numpy(), X64, q, G2, mode, f"mid w4a16 N={N} K={K} M={M}")
+            check_products(want8, Y8.float().cpu().numpy(), w4a8_x64(rq, rs), q, G2, mode, f"mid w4a8 N={N} K={K} M={M}")
     # the 12B shapes at M = 128 (sampled rows and columns; K split 2 and 16 ways)
     wl = synth.WORKLOADS["gemma12b_w4a8"]
     rng = np.random.default_rng(61)
@@ -515,13 +575,13 @@ def test_mid_size_products():
         Y = w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G)
         Y8, _, _ = w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G)
         torch.cuda.synchronize()
-        want = oracle.gemm_ref(oracle.bf16_bits_to_f64(Xb), q["packed"], q["scale"], q["zero"], G, "asym",
-                               rows=rows, cols=cols)
-        want8, _, _ = oracle.w4a8_ref(Xb, q["packed"], q["scale"], q["zero"], G, "asym", rows=rows, cols=cols)
+        X64 = oracle.bf16_bits_to_f64(Xb)
+        want = oracle.gemm_ref(X64, q["packed"], q["scale"], q["zero"], G, "asym", rows=rows, cols=cols)
+        want8, rq, rs = oracle.w4a8_ref(Xb, q["packed"], q["scale"], q["zero"], G, "asym", rows=rows, cols=cols)
         got = Y.float().cpu().numpy()[np.ix_(rows, cols)]
         got8 = Y8.float().cpu().numpy()[np.ix_(rows, cols)]
-        assert oracle.rel_error(want, got) <= REL_TOL
-        assert oracle.rel_error(want8, got8) <= REL_TOL
+        check_products(want, got, X64, q, G, "asym", f"mid 12B[{idx}] w4a16", rows=rows, cols=cols)
+        check_products(want8, got8, w4a8_x64(rq, rs), q, G, "asym", f"mid 12B[{idx}] w4a8", rows=rows, cols=cols)
 
 
 def test_gate_up_full_8b_shapes_sampled():
@@ -551,8 +611,10 @@ def test_gate_up_full_8b_shapes_sampled():
         want = oracle.gate_up_ref(Xb, qg, qu, G, "asym", "silu", rows=rows, cols=cols)
         want8, rq, rs = oracle.gate_up_ref(Xb, qg, qu, G, "asym", "silu", kind="w4a8", rows=rows, cols=cols)
         assert_bits_equal(host(xq), rq, "E4M3 activations")
-        assert oracle.rel_error(want, H.float().cpu().numpy()[np.ix_(rows, cols)]) <= REL_TOL
-        assert oracle.rel_error(want8, H8.float().cpu().numpy()[np.ix_(rows, cols)]) <= REL_TOL
+        _check_gate_up(want, H.float().cpu().numpy()[np.ix_(rows, cols)], Xb, qg, qu, G, "asym", "silu", "w4a16",
+                       f"full 8B gate_up w4a16 M={M}", rows=rows, cols=cols)
+        _check_gate_up(want8, H8.float().cpu().numpy()[np.ix_(rows, cols)], Xb, qg, qu, G, "asym", "silu", "w4a8",
+                       f"full 8B gate_up w4a8 M={M}", rows=rows, cols=cols)
 
 
 def test_streaming_k_split_products():
@@ -581,13 +643,14 @@ def test_streaming_k_split_products():
         Y8s, xq, xs = w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G, workspace=ws)
         Y8u, _, _ = w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G, workspace=none)
         torch.cuda.synchronize()
-        want = oracle.gemm_ref(oracle.bf16_bits_to_f64(Xb), q["packed"], q["scale"], q["zero"], G, "asym")
-        want8, rq, _ = oracle.w4a8_ref(Xb, q["packed"], q["scale"], q["zero"], G, "asym")
+        X64 = oracle.bf16_bits_to_f64(Xb)
+        want = oracle.gemm_ref(X64, q["packed"], q["scale"], q["zero"], G, "asym")
+        want8, rq, rs = oracle.w4a8_ref(Xb, q["packed"], q["scale"], q["zero"], G, "asym")
         assert_bits_equal(host(xq), rq, "E4M3 activations")
-        for got, ref, what in ((Ys, want, "w4a16 split"), (Yu, want, "w4a16 unsplit"),
-                               (Y8s, want8, "w4a8 split"), (Y8u, want8, "w4a8 unsplit")):
-            err = oracle.rel_error(ref, got.float().cpu().numpy())
-            assert err <= REL_TOL, f"{what} M={M}: relative error {err:.3e}"
+        X8 = w4a8_x64(rq, rs)
+        for got, ref, xx, what in ((Ys, want, X64, "w4a16 split"), (Yu, want, X64, "w4a16 unsplit"),
+                                   (Y8s, want8, X8, "w4a8 split"), (Y8u, want8, X8, "w4a8 unsplit")):
+            check_products(ref, got.float().cpu().numpy(), xx, q, G, "asym", f"{what} M={M}")
         # the two schedules differ only in the order of fp32 additions
         d = (Ys.float() - Yu.float()).abs().max().item()
         assert d <= 2 ** -6 * Yu.float().abs().max().item()

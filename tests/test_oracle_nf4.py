@@ -101,11 +101,49 @@ def test_double_quantization_of_block_scales():
         grp = a[g * 256:(g + 1) * 256]
         assert q["absmax_q"][g * 256:(g + 1) * 256].max() == 255       # the group maximum uses the top code
         np.testing.assert_allclose(q["c2"][g], grp.max() / 255, rtol=2 ** -23)
-    # dequantized weights and the reference product
-    Wd = oracle.nf4_dequant(q["codes"], q["absmax_q"], q["c2"])
-    rel = np.linalg.norm(Wd - W) / np.linalg.norm(W)
-    assert rel < 0.15                                       # 4-bit normal-quantile grid
-    xb = (np.arange(W.shape[1]) % 7 == 0).astype(np.float32)
+
+
+def _normaldist_levels():
+    nd = NormalDist()
+    delta = 0.5 * (1 - 1 / 30) + 0.5 * (1 - 1 / 32)
+    pos = [nd.inv_cdf(delta + (0.5 - delta) * i / 8) for i in range(8)]
+    neg = [-nd.inv_cdf(delta + (0.5 - delta) * i / 7) for i in range(7)]
+    v = np.sort(np.array(pos + [0.0] + neg))
+    return (v / v.max()).astype(np.float32)
+
+
+def test_constructed_blocks_dequantize_exactly():
+    # Blocks built so that every stored quantity is known in advance: block b
+    # holds levels L[c] times a chosen absmax a_b = q_b / 256 (q_b an integer
+    # code, the largest 255, so the second-level constant is exactly
+    # 255/256 / 255 = 1/256), and each block contains a level of magnitude 1
+    # so that its absmax is a_b itself.  The quantizer must return the codes
+    # c, the scale codes q_b and c2 = 1/256; the dequantized weight must be
+    # L[c] * q_b / 256 exactly (levels from NormalDist, not the oracle); and a
+    # one-hot activation row must select one dequantized column exactly.
     import synth
+    L = _normaldist_levels()
+    rng = np.random.default_rng(5)
+    qb = np.array([255, 200, 17, 1, 128, 64, 3, 250], dtype=np.int64)
+    nblk = qb.size
+    codes = rng.integers(0, 16, size=(nblk, 64))
+    codes[:, 0] = np.where(np.arange(nblk) % 2 == 0, 15, 0)          # level +1 or -1 in every block
+    a = (qb.astype(np.float32) / np.float32(256)).astype(np.float32)
+    W = (L[codes] * a[:, None]).astype(np.float32).reshape(2, 4 * 64)
+    q = oracle.nf4_quantize(W)
+    np.testing.assert_array_equal(q["codes"], codes.reshape(2, 4 * 64))
+    np.testing.assert_array_equal(q["absmax"], a)
+    np.testing.assert_array_equal(q["absmax_q"], qb.astype(np.uint8))
+    assert q["c2"].tolist() == [1.0 / 256]
+    want = (L[codes].astype(np.float64) * (qb[:, None] / 256.0)).reshape(2, 4 * 64)
+    Wd = oracle.nf4_dequant(q["codes"], q["absmax_q"], q["c2"])
+    np.testing.assert_array_equal(Wd, want)
+    for k in (0, 77, 255):
+        x = np.zeros((1, 4 * 64), np.float32)
+        x[0, k] = 1.0
+        y = oracle.nf4_gemv_ref(synth.to_bf16_bits(x), q["codes"], q["absmax_q"], q["c2"])
+        np.testing.assert_array_equal(y, want[:, k])
+    # a 0/1 activation row sums the chosen dequantized columns (each term exact)
+    xb = (np.arange(W.shape[1]) % 7 == 0).astype(np.float32)
     y = oracle.nf4_gemv_ref(synth.to_bf16_bits(xb[None, :]), q["codes"], q["absmax_q"], q["c2"])
-    np.testing.assert_allclose(y, Wd[:, xb > 0].sum(axis=1), rtol=1e-12)
+    np.testing.assert_allclose(y, want[:, xb > 0].sum(axis=1), rtol=1e-15, atol=0)

@@ -39,8 +39,10 @@ def _recon(orc, r, G):
 
 def test_worked_block_minus02_to_1(orc):
     """gowda.ai "LLM fast inference", "The naive symmetric baseline" and
-    "Achievement 1": a block spanning [-0.2, 1.0]; symmetric step ~ 1/7 = 0.143,
-    affine step 1.2/15 = 0.08 before zero-point rounding."""
+    "Achievement 1": for a block whose values run from -0.2 to 1.0 the
+    max-abs grid has a step of about 0.143 (one seventh), while the affine grid
+    spreads the 1.2-wide range over 15 steps of 0.08 (the step is fixed before
+    the zero point is rounded)."""
     g = _golden("worked_blocks.txt")
     blk = np.array([[float(g["block_lo"]), 0.0, 0.5, float(g["block_hi"])]], dtype=np.float32)
     ra = orc.quantize(blk, 4, "asym")
@@ -157,8 +159,9 @@ def test_packing_nibble_order(orc):
 @pytest.mark.parametrize("G", [32, 128])
 def test_half_step_error_bound(orc, mode, G):
     """gsantana.dev "Scale and zero point" and nebelwolfi.xyz "The Basic
-    Arithmetic": the error per value is at most half a step, scale/2, for
-    every value inside the range the grid covers."""
+    Arithmetic": rounding to the nearest grid point can miss a weight by no
+    more than half the grid spacing, as long as the weight lies within the
+    grid's span (clipped weights excepted)."""
     w = synth.weight(synth.WORKLOADS["llama8b_decode"], 0, rows=64)
     r = orc.quantize(w, G, mode)
     wq, s, z = _recon(orc, r, G)
@@ -199,23 +202,25 @@ def test_code_space_use(orc):
 
 
 def test_group_locality(orc):
-    """gsantana.dev "One real weight matrix": a planted weight at 10x the tensor
-    max changes only the scale it shares; with groups, only its own group."""
+    """gsantana.dev "One real weight matrix": one outlying weight disturbs only
+    the weights that share its scale, so with groups nothing outside its own
+    group moves."""
     w = synth.normal_matrix(4, 32, 256, 0.2)
-    spiked = w.copy()
-    spiked[7, 100] = 10 * np.abs(w).max()
+    row, col = 19, 201                      # a planted negative outlier
+    planted = np.where(np.arange(w.size).reshape(w.shape) == row * w.shape[1] + col,
+                       np.float32(-25.0), w).astype(np.float32)
     for G, fr in ((32, None), (128, synth.FRACS_11), (256, None)):
         a = orc.quantize(w, G, "asym", fracs=fr)
-        b = orc.quantize(spiked, G, "asym", fracs=fr)
-        g = 100 // G
+        b = orc.quantize(planted, G, "asym", fracs=fr)
+        g = col // G
         mask = np.ones(a["scale"].shape, dtype=bool)
-        mask[7, g] = False
+        mask[row, g] = False
         np.testing.assert_array_equal(a["scale"][mask], b["scale"][mask])
         np.testing.assert_array_equal(a["zero"][mask], b["zero"][mask])
         np.testing.assert_array_equal(a["clip"][mask], b["clip"][mask])
         qmask = np.repeat(mask, G, axis=1)
         np.testing.assert_array_equal(a["q"][qmask], b["q"][qmask])
-        assert a["scale"][7, g] != b["scale"][7, g]
+        assert a["scale"][row, g] != b["scale"][row, g]
 
 
 def test_codes_are_nearest_grid_points_brute_force(orc):
@@ -271,30 +276,42 @@ def test_clip_search_selection_and_sse(orc):
     np.testing.assert_array_equal(r["q"][keep], r1["q"][keep])
 
 
-def test_clip_search_brute_force_tiny_blocks(orc):
-    # Exhaustive check on tiny blocks: for each candidate fraction, every
-    # (scale, zero) pair it could produce is enumerated independently as the
-    # fp16 neighbours of the exact-arithmetic scale, and the float64 optimum of
-    # the block error over candidates is compared with the oracle's choice.
-    # Where two candidates are within 1e-6 relative the case is a near-tie and
-    # is only counted, not failed.
-    rng = np.random.default_rng(21)
+@pytest.mark.parametrize("mode", ["asym", "sym"])
+def test_clip_search_brute_force_tiny_blocks(orc, mode):
+    # Exhaustive check on tiny blocks: for each candidate fraction the range,
+    # the fp16 scale, the zero point (asym), the codes and the block error are
+    # recomputed here in float64 straight from their definitions (asym: the
+    # range contracted about the midpoint, 15 steps, unclamped integer zero,
+    # codes clamped to 0..15; sym: [-f amax, f amax], 7 steps, codes clamped to
+    # -8..7), and the float64 optimum over the candidates is compared with the
+    # oracle's choice.  Near-ties (within 1e-6 relative) are counted, not
+    # failed; so are the rare blocks where float64 and the oracle's fp32 land
+    # on neighbouring fp16 scales (at most 2%).
+    rng = np.random.default_rng(21 if mode == "asym" else 22)
     fr = synth.FRACS_11
-    n_cases, agree, ties = 300, 0, 0
+    n_cases, agree, ties, picked_clip = 300, 0, 0, 0
     for _ in range(n_cases):
         G = int(rng.choice([4, 8]))
         blk = (rng.standard_t(2.5, size=G) * 0.1).astype(np.float32)
-        r = orc.quantize(blk[None, :], G, "asym", fracs=fr, want_sse=True)
+        r = orc.quantize(blk[None, :], G, mode, fracs=fr, want_sse=True)
         errs = []
         lo0, hi0 = float(blk.min()), float(blk.max())
+        amax = float(np.abs(blk).max())
         mid, h = (lo0 + hi0) / 2, (hi0 - lo0) / 2
         for f in fr.astype(np.float64):
-            lo, hi = (lo0, hi0) if f == 1.0 else (mid - f * h, mid + f * h)
-            s = np.float64(np.float16((hi - lo) / 15))
-            if s == 0:
-                s = 1.0
-            z = np.round(-lo / s)
-            q = np.clip(np.round(blk.astype(np.float64) / s) + z, 0, 15)
+            if mode == "asym":
+                lo, hi = (lo0, hi0) if f == 1.0 else (mid - f * h, mid + f * h)
+                s = np.float64(np.float16((hi - lo) / 15))
+                if s == 0:
+                    s = 1.0
+                z = np.round(-lo / s)
+                q = np.clip(np.round(blk.astype(np.float64) / s) + z, 0, 15)
+            else:
+                s = np.float64(np.float16(f * amax / 7))
+                if s == 0:
+                    s = 1.0
+                z = 0.0
+                q = np.clip(np.round(blk.astype(np.float64) / s), -8, 7)
             errs.append(float(np.sum((blk - (q - z) * s) ** 2)))
         errs = np.array(errs)
         best = int(np.argmin(errs))
@@ -303,7 +320,11 @@ def test_clip_search_brute_force_tiny_blocks(orc):
             ties += 1
             continue
         agree += int(r["clip"][0, 0] == best)
+        picked_clip += int(best > 0)
     assert agree >= (n_cases - ties) * 0.98, (agree, ties)
+    # heavy tails make contracted ranges win on a good share of these blocks,
+    # so the comparison exercises the search and not only the plain grid
+    assert picked_clip >= 0.08 * (n_cases - ties), picked_clip
 
 
 def test_padded_tree_for_groups_that_are_not_powers_of_two(orc):
@@ -379,12 +400,12 @@ def test_bits_per_weight_table(orc):
         assert f"{got:.2f}" == val, (key, got)
 
 
-def test_rel_error_metric(orc):
+def test_frobenius_gap_metric(orc):
     a = synth.normal_matrix(1, 16, 16)
-    assert orc.rel_error(a, a) == 0.0
-    assert orc.rel_error(a, np.zeros_like(a)) == pytest.approx(1.0)
-    assert orc.rel_error(a, 2 * a) == pytest.approx(1.0)
-    assert orc.rel_error(3 * a, 3 * a + 3e-3 * a) == pytest.approx(1e-3)
+    assert orc.frobenius_gap(a, a) == 0.0
+    assert orc.frobenius_gap(a, np.zeros_like(a)) == pytest.approx(1.0)
+    assert orc.frobenius_gap(a, 2 * a) == pytest.approx(1.0)
+    assert orc.frobenius_gap(3 * a, 3 * a + 3e-3 * a) == pytest.approx(1e-3)
 
 
 def test_granularity_ordering_on_synthetic_layer(orc):
@@ -397,9 +418,9 @@ def test_granularity_ordering_on_synthetic_layer(orc):
     err = {}
     for mode in ("sym", "asym"):
         for G in (32, 128, 1536):
-            err[(mode, G)] = orc.rel_error(w, orc.fake_quant(w, G, mode))
+            err[(mode, G)] = orc.frobenius_gap(w, orc.fake_quant(w, G, mode))
     flat = w.reshape(1, -1)
-    err[("sym", "tensor")] = orc.rel_error(flat, orc.fake_quant(flat, flat.shape[1], "sym"))
+    err[("sym", "tensor")] = orc.frobenius_gap(flat, orc.fake_quant(flat, flat.shape[1], "sym"))
     assert err[("sym", "tensor")] > 0.5
     assert err[("sym", 32)] < err[("sym", 128)] < err[("sym", 1536)] < err[("sym", "tensor")]
     assert err[("asym", 32)] < err[("sym", 32)]

@@ -154,6 +154,45 @@ def _empty(shape, dtype, device):
     return torch.empty(shape, dtype=dtype, device=device)
 
 
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _check_product_shapes(fn: str, X, wq, sz, G: int, Y=None, xq=None, xscale=None, up=None):
+    """Shape checks the C ABI cannot make (it sees only pointers): the GPU
+    layout of an [N, K] weight is N*K/2 bytes of codes and 4*N*K/G bytes of
+    scale/zero words; outputs and W4A8 buffers must match [M, N] and [M, K].
+    Raises ValueError before anything is launched."""
+    if X.dim() != 2:
+        raise ValueError(f"{fn}: X must be 2-D [M, K], got shape {tuple(X.shape)}")
+    M, K = X.shape
+    if wq.dim() != 2:
+        raise ValueError(f"{fn}: wq must be 2-D [N, K/8], got shape {tuple(wq.shape)}")
+    N = wq.shape[0]
+    if G <= 0 or K % G != 0 or K % 8 != 0:
+        raise ValueError(f"{fn}: K = {K} must be a multiple of 8 and of the group size G = {G}")
+    if _nbytes(wq) != N * K // 2:
+        raise ValueError(f"{fn}: wq holds {_nbytes(wq)} bytes; an [{N}, {K}] weight needs N*K/2 = {N * K // 2} "
+                         f"(K of X does not match the weight?)")
+    if _nbytes(sz) != 4 * N * (K // G):
+        raise ValueError(f"{fn}: sz holds {_nbytes(sz)} bytes; an [{N}, {K}] weight with G = {G} needs "
+                         f"{4 * N * (K // G)}")
+    if Y is not None and tuple(Y.shape) != (M, N):
+        raise ValueError(f"{fn}: output has shape {tuple(Y.shape)}, expected ({M}, {N})")
+    if xq is not None and (tuple(xq.shape) != (M, K) or xq.element_size() != 1):
+        raise ValueError(f"{fn}: xq must be one byte per element with shape ({M}, {K}), got "
+                         f"{tuple(xq.shape)} of {xq.dtype}")
+    if xscale is not None and xscale.numel() != M:
+        raise ValueError(f"{fn}: xscale has {xscale.numel()} elements, expected {M}")
+    if up is not None:
+        if tuple(up["wq"].shape) != tuple(wq.shape) or _nbytes(up["wq"]) != _nbytes(wq):
+            raise ValueError(f"{fn}: the up weight's wq {tuple(up['wq'].shape)} differs from the gate's "
+                             f"{tuple(wq.shape)}")
+        if _nbytes(up["sz"]) != _nbytes(sz):
+            raise ValueError(f"{fn}: the up weight's sz differs in size from the gate's")
+    return M, K, N
+
+
 def _workspace(M: int, K: int, N: int, device, workspace, stream, w4a8=False):
     """(pointer, bytes) of the product's workspace: the caller's tensor, or a
     new byte tensor of the fastest schedule's size when the shape uses one
@@ -337,8 +376,7 @@ def w4a16_gemm(X: torch.Tensor, wq: torch.Tensor, sz: torch.Tensor, G: int, *, Y
 
     ``workspace``: a device tensor of at least ``w4_gemm_workspace_bytes(M, K, N)``
     bytes; allocated here when omitted and the shape needs one."""
-    M, K = X.shape
-    N = wq.shape[0]
+    M, K, N = _check_product_shapes("w4a16_gemm", X, wq, sz, G, Y=Y)
     dev = X.device
     Y = _empty((M, N), torch.bfloat16, dev) if Y is None else Y
     ws, ws_bytes = _workspace(M, K, N, dev, workspace, stream)
@@ -351,8 +389,7 @@ def w4a16_gemm(X: torch.Tensor, wq: torch.Tensor, sz: torch.Tensor, G: int, *, Y
 def w4a8_gemm(X: torch.Tensor, wq: torch.Tensor, sz: torch.Tensor, G: int, *, Y=None, xq=None, xscale=None,
               workspace=None, stream=None):
     """W4A8: per-row E4M3 of ``X`` then ``Y = bf16(xscale * Xq . W'^T)``; returns (Y, xq, xscale)."""
-    M, K = X.shape
-    N = wq.shape[0]
+    M, K, N = _check_product_shapes("w4a8_gemm", X, wq, sz, G, Y=Y, xq=xq, xscale=xscale)
     dev = X.device
     Y = _empty((M, N), torch.bfloat16, dev) if Y is None else Y
     xq = _empty((M, K), torch.uint8, dev) if xq is None else xq
@@ -369,8 +406,7 @@ def w4a16_gate_up(X: torch.Tensor, gate: dict, up: dict, G: int, act="silu", *, 
     """Gate and up projections in one pass: ``H = bf16(act(X . Wg'^T) * (X . Wu'^T))``
     for bf16 ``X[M, K]`` (above 32 rows K must be a multiple of 64); ``gate`` and ``up`` are GPU layouts from
     ``w4_prepack`` (``wq``, ``sz``); ``act`` is ``"silu"`` or ``"gelu_tanh"``."""
-    M, K = X.shape
-    N = gate["wq"].shape[0]
+    M, K, N = _check_product_shapes("w4a16_gate_up", X, gate["wq"], gate["sz"], G, Y=H, up=up)
     dev = X.device
     H = _empty((M, N), torch.bfloat16, dev) if H is None else H
     rc = lib().w4a16_gate_up(_dev(X, "X", torch.bfloat16), M, K, _dev(gate["wq"], "gate wq"), _dev(gate["sz"], "gate sz"),
@@ -383,8 +419,8 @@ def w4a16_gate_up(X: torch.Tensor, gate: dict, up: dict, G: int, act="silu", *, 
 def w4a8_gate_up(X: torch.Tensor, gate: dict, up: dict, G: int, act="silu", *, H=None, xq=None, xscale=None,
                  stream=None):
     """W4A8 form of ``w4a16_gate_up``: per-row E4M3 of ``X`` first; returns (H, xq, xscale)."""
-    M, K = X.shape
-    N = gate["wq"].shape[0]
+    M, K, N = _check_product_shapes("w4a8_gate_up", X, gate["wq"], gate["sz"], G, Y=H, xq=xq, xscale=xscale,
+                                    up=up)
     dev = X.device
     H = _empty((M, N), torch.bfloat16, dev) if H is None else H
     xq = _empty((M, K), torch.uint8, dev) if xq is None else xq

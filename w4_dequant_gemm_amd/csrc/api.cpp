@@ -117,14 +117,15 @@ int mul_common(const char* fn, const uint16_t* X, int64_t M, int64_t K, const ui
     W4_REQUIRE_PTR(fn, wq);
     W4_REQUIRE_PTR(fn, sz);
     W4_REQUIRE_PTR(fn, Y);
+    // any workspace given is checked, whether or not this shape splits K: the
+    // row quantizer of W4A8 may also place the widened activations there
+    if (workspace && !aligned16(workspace)) return fail(W4_EINVAL, "%s: workspace is not 16-byte aligned", fn);
     const size_t need = M <= w4::kSkinnyMaxM ? 0 : w4::gemm_workspace_bytes(M, K, N);
     if (need > 0) {
         if (!workspace)
             return fail(W4_EINVAL, "%s: this shape needs a workspace of %zu bytes (w4_gemm_workspace_bytes)", fn, need);
         if (workspace_bytes < need)
             return fail(W4_EINVAL, "%s: workspace of %zu bytes, this shape needs %zu", fn, workspace_bytes, need);
-        if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
-            return fail(W4_EINVAL, "%s: workspace is not 16-byte aligned", fn);
     }
     return W4_OK;
 }
@@ -288,15 +289,21 @@ size_t w4a8_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
     return xw ? w4::gemm_xw_offset(M, K, N) + xw : w4::gemm_workspace_bytes(M, K, N);
 }
 
-int w4a16_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const uint32_t* sz, int64_t N,
-               int G, uint16_t* Y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    const char* fn = "w4a16_gemm";
+namespace {
+int w4a16_run(const char* fn, const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const uint32_t* sz,
+              int64_t N, int G, uint16_t* Y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     W4_TRY(mul_common(fn, X, M, K, wq, sz, N, G, Y, workspace, workspace_bytes));
     if (M == 0 || N == 0) return W4_OK;
     w4::MulParams p{X, nullptr, M, K, N, G, wq, sz, Y, false};
     if (M <= w4::kSkinnyMaxM)
         return hip_status(w4::launch_skinny(with_skinny_split(p, workspace, workspace_bytes), stream), fn);
     return hip_status(w4::launch_gemm(with_split(p, workspace), stream), fn);
+}
+}  // namespace
+
+int w4a16_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const uint32_t* sz, int64_t N,
+               int G, uint16_t* Y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return w4a16_run("w4a16_gemm", X, M, K, wq, sz, N, G, Y, workspace, workspace_bytes, stream);
 }
 
 int w4a8_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const uint32_t* sz, int64_t N,
