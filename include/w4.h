@@ -26,7 +26,8 @@
  *  - Every pointer argument is a DEVICE pointer on the current HIP device,
  *    owned by the caller, except where a parameter says "host".  The library
  *    allocates no memory.  Its state is a thread-local message for the last
- *    failed call and the NF4 level table; the products take their scratch
+ *    failed call, the NF4 level table, and one fixed scratch array per GPU
+ *    used only by w4a16_gemm_noalloc; the other products take their scratch
  *    memory from the caller (w4_gemm_workspace_bytes).
  *  - Device pointers must be 16-byte aligned.
  *  - Every call is asynchronous on `stream` (0 = the null stream).  Arguments
@@ -216,6 +217,25 @@ size_t w4a8_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
  */
 int w4a16_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const uint32_t* sz,
                int64_t N, int G, uint16_t* Y, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * w4a16_gemm_noalloc -- w4a16_gemm for callers that cannot allocate device
+ * memory (code under HIP graph capture, serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with the scratch memory of a K
+ * split taken from an array the library holds on each GPU
+ * (W4_NOALLOC_SCRATCH_BYTES, kept until the process ends) instead of a
+ * caller workspace.  The call allocates nothing; the caller passes X, the
+ * weights and Y as for w4a16_gemm.
+ *   A shape whose w4_gemm_workspace_bytes exceeds W4_NOALLOC_SCRATCH_BYTES
+ *   returns W4_EINVAL (64 MiB covers every shape: a K split never needs more
+ *   than 256 partial tiles of 256 x 256 fp32).
+ *   Every call on one GPU uses that GPU's one array: calls that can overlap
+ *   on a GPU (different streams or threads) race and must not be issued
+ *   together; calls in order on one stream are safe.
+ */
+#define W4_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int w4a16_gemm_noalloc(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const uint32_t* sz,
+                       int64_t N, int G, uint16_t* Y, hipStream_t stream);
 
 /*
  * w4a8_gemm -- W4A8: each activation row is quantized to E4M3 exactly as by

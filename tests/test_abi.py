@@ -33,8 +33,20 @@ def test_header_declares_the_boundary():
               "w4a16_gemm", "w4a8_gemm", "w4_gemm_workspace_bytes", "w4a8_gemm_workspace_bytes",
               "w4_status_string", "w4_last_error",
               "w4_abi_version", "w4_portable_save", "w4_portable_info_read", "w4_portable_load",
-              "w4a16_gate_up", "w4a8_gate_up", "w4_nf4_levels", "w4_nf4_quantize", "w4_nf4_gemv"):
+              "w4a16_gate_up", "w4a8_gate_up", "w4_nf4_levels", "w4_nf4_quantize", "w4_nf4_gemv",
+              "w4a16_gemm_noalloc"):
         assert n in names
+
+
+def test_noalloc_validation(lib):
+    # the no-alloc product checks its arguments like w4a16_gemm before it
+    # looks up its scratch array (no device needed for these)
+    fake = ctypes.c_void_p(0x1000)
+    f = lib.w4a16_gemm_noalloc
+    assert f(fake, 2, 96, fake, fake, 8, 48, fake, None) == 2          # unsupported group size
+    assert f(fake, -1, 96, fake, fake, 8, 32, fake, None) == 1         # negative M
+    assert f(None, 0, 96, None, None, 8, 32, None, None) == 0          # nothing to do
+    assert f(fake, 2, 100, fake, fake, 8, 32, fake, None) == 1         # K not a multiple of G
 
 
 def test_every_declared_symbol_is_exported(lib):

@@ -17,7 +17,7 @@ import torch
 __all__ = [
     "W4Error", "SYM", "ASYM", "MAX_FRACS", "lib", "library_path",
     "w4_quantize_blockwise", "w4_mse_clip_search", "w4_prepack", "w4_quantize_rows_e4m3",
-    "w4a16_gemm", "w4a8_gemm", "w4_gemm_workspace_bytes", "w4a8_gemm_workspace_bytes", "w4_status_string",
+    "w4a16_gemm", "w4a16_gemm_noalloc", "w4a8_gemm", "w4_gemm_workspace_bytes", "w4a8_gemm_workspace_bytes", "w4_status_string",
     "w4_last_error",
     "w4_abi_version", "w4_portable_save", "w4_portable_info_read", "w4_portable_load",
     "w4a16_gate_up", "w4a8_gate_up", "ACT_SILU", "ACT_GELU_TANH",
@@ -75,6 +75,8 @@ def lib():
     L.w4_quantize_rows_e4m3.argtypes = [P, i64, i64, P, P, P]
     sz_t = ctypes.c_size_t
     L.w4a16_gemm.argtypes = [P, i64, i64, P, P, i64, I, P, P, sz_t, P]
+    L.w4a16_gemm_noalloc.argtypes = [P, i64, i64, P, P, i64, I, P, P]
+    L.w4a16_gemm_noalloc.restype = I
     L.w4a8_gemm.argtypes = [P, i64, i64, P, P, i64, I, P, P, P, P, sz_t, P]
     L.w4_gemm_workspace_bytes.argtypes = [i64, i64, i64]
     L.w4_gemm_workspace_bytes.restype = sz_t
@@ -383,6 +385,19 @@ def w4a16_gemm(X: torch.Tensor, wq: torch.Tensor, sz: torch.Tensor, G: int, *, Y
     rc = lib().w4a16_gemm(_dev(X, "X", torch.bfloat16), M, K, _dev(wq, "wq"), _dev(sz, "sz"), N, G,
                           _dev(Y, "Y", torch.bfloat16), ws, ws_bytes, _stream(dev, stream))
     _check("w4a16_gemm", rc)
+    return Y
+
+
+def w4a16_gemm_noalloc(X: torch.Tensor, wq: torch.Tensor, sz: torch.Tensor, G: int, Y: torch.Tensor, *,
+                       stream=None):
+    """``w4a16_gemm`` into the caller's ``Y`` with the library's own scratch
+    memory (no allocation by the library or here); calls that overlap on one
+    GPU must not be issued together."""
+    M, K, N = _check_product_shapes("w4a16_gemm_noalloc", X, wq, sz, G, Y=Y)
+    dev = X.device
+    rc = lib().w4a16_gemm_noalloc(_dev(X, "X", torch.bfloat16), M, K, _dev(wq, "wq"), _dev(sz, "sz"), N, G,
+                                  _dev(Y, "Y", torch.bfloat16), _stream(dev, stream))
+    _check("w4a16_gemm_noalloc", rc)
     return Y
 
 

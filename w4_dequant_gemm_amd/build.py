@@ -22,7 +22,7 @@ PROBE_OUT = os.path.join(HERE, "libw4probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-KERNELS = ["quantize.hip", "prepack.hip", "rowquant.hip", "skinny.hip", "gemm.hip", "nf4.hip"]
+KERNELS = ["quantize.hip", "prepack.hip", "rowquant.hip", "skinny.hip", "gemm.hip", "nf4.hip", "noalloc.hip"]
 NO_CONTRACT = {"quantize.hip", "rowquant.hip", "nf4.hip"}
 HOST_SOURCES = ["api.cpp", "portable.cpp"]   # host C++ (argument checks, file I/O)
 

@@ -1,8 +1,9 @@
 // C ABI of the W4 library: argument checks, then the launches of the call on
 // the caller's stream (one kernel, or two where a row quantization or a split
 // sum goes with it).  No allocation, no state beyond a thread-local error
-// message and the NF4 level table (computed once), no fallback: anything the
-// kernels do not run is rejected before launch.
+// message, the NF4 level table (computed once) and the per-device address of
+// the no-alloc product's scratch array; no fallback: anything the kernels do
+// not run is rejected before launch.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -306,6 +307,21 @@ int w4a16_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, cons
     return w4a16_run("w4a16_gemm", X, M, K, wq, sz, N, G, Y, workspace, workspace_bytes, stream);
 }
 
+int w4a16_gemm_noalloc(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const uint32_t* sz,
+                       int64_t N, int G, uint16_t* Y, hipStream_t stream) {
+    const char* fn = "w4a16_gemm_noalloc";
+    W4_TRY(check_group(fn, N, K, G));
+    if (M < 0) return fail(W4_EINVAL, "%s: M = %lld must be >= 0", fn, static_cast<long long>(M));
+    if (M == 0 || N == 0) return W4_OK;
+    const size_t need = M <= w4::kSkinnyMaxM ? 0 : w4::gemm_workspace_bytes(M, K, N);
+    if (need > W4_NOALLOC_SCRATCH_BYTES)
+        return fail(W4_EINVAL, "%s: this shape needs %zu bytes of scratch; the library holds %zu", fn, need,
+                    static_cast<size_t>(W4_NOALLOC_SCRATCH_BYTES));
+    void* scratch = nullptr;
+    W4_TRY(hip_status(w4::noalloc_scratch(&scratch), fn));
+    return w4a16_run(fn, X, M, K, wq, sz, N, G, Y, scratch, W4_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 int w4a8_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const uint32_t* sz, int64_t N,
               int G, uint16_t* Y, uint8_t* xq, float* xscale, void* workspace, size_t workspace_bytes,
               hipStream_t stream) {
@@ -443,5 +459,7 @@ const char* w4_status_string(int status) {
 const char* w4_last_error(void) { return g_last_error; }
 
 int w4_abi_version(void) { return 2; }
+
+static_assert(W4_NOALLOC_SCRATCH_BYTES == w4::kNoAllocScratchBytes, "w4.h and the library agree on the scratch size");
 
 }  // extern "C"

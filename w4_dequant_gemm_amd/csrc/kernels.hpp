@@ -125,6 +125,13 @@ size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
 size_t gemm_xw_offset(int64_t M, int64_t K, int64_t N);
 size_t gemm_xw_bytes(int64_t M, int64_t K, int64_t N);
 
+// Library-held scratch of w4a16_gemm_noalloc: 64 MiB per GPU, the largest
+// K-split workspace any shape of the tiled GEMM takes (at most 256 partial
+// tiles of 256 x 256 fp32).  noalloc_scratch returns this GPU's address of it
+// (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = size_t{64} << 20;
+hipError_t noalloc_scratch(void** out);
+
 // NF4 comparator (normal-quantile levels, blocks of 64, double-quantized scales)
 constexpr int64_t kNf4MaxK = 32768;             // one 32-k chunk per lane of a 1024-lane workgroup
 struct Nf4QuantParams {
