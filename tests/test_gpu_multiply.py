@@ -654,3 +654,35 @@ def test_streaming_k_split_products():
         # the two schedules differ only in the order of fp32 additions
         d = (Ys.float() - Yu.float()).abs().max().item()
         assert d <= 2 ** -6 * Yu.float().abs().max().item()
+
+
+def test_zero_points_outside_the_code_range():
+    # Groups whose values are all of one sign have a zero point outside
+    # 0..15 (the range [lo, hi] excludes 0): all-positive groups get z < 0,
+    # all-negative ones z > 15.  Every product path must still use the exact
+    # W' = (u - z) s; the fp8 W4A8 kernel restores the part of z beyond its
+    # clamped operand separately.  Rows at 300 take the 256 x 256 tiles
+    # (W4A8: the fp8 kernel), 40 the streaming kernel, 100 the 64 x 128 tiles.
+    require_gpu()
+    import torch
+    import w4_dequant_gemm_amd as w4
+    N, K = 600, 2048
+    W = synth.normal_matrix(80, N, K, 0.02)
+    W[:, 128:256] += 1.0                     # group 1 of every row: all positive
+    W[::7, 1024:1152] -= 0.5                 # group 8 of every 7th row: all negative
+    q = oracle.quantize(W, 128, "asym")
+    z = oracle.f16_bits_to_f32(q["zero"])
+    assert (z < 0).sum() >= N and (z > 15).sum() >= N // 7
+    pk, G = prepack_dev(q)
+    for M in (300, 40, 100):
+        print(f"[zero outside 0..15] M={M}", flush=True)
+        Xb = synth.to_bf16_bits(synth.normal_matrix(81 + M, M, K))
+        Y = w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G)
+        Y8, xq, xs = w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G)
+        torch.cuda.synchronize()
+        X64 = oracle.bf16_bits_to_f64(Xb)
+        want = oracle.gemm_ref(X64, q["packed"], q["scale"], q["zero"], G, "asym")
+        want8, rq, rs = oracle.w4a8_ref(Xb, q["packed"], q["scale"], q["zero"], G, "asym")
+        assert_bits_equal(host(xq), rq, "E4M3 activations")
+        check_products(want, Y.float().cpu().numpy(), X64, q, G, "asym", f"w4a16 M={M}")
+        check_products(want8, Y8.float().cpu().numpy(), w4a8_x64(rq, rs), q, G, "asym", f"w4a8 M={M}")

@@ -22,8 +22,10 @@ PROBE_OUT = os.path.join(HERE, "libw4probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-KERNELS = ["quantize.hip", "prepack.hip", "rowquant.hip", "skinny.hip", "gemm.hip", "nf4.hip", "noalloc.hip"]
+KERNELS = ["quantize.hip", "prepack.hip", "rowquant.hip", "skinny.hip", "gemm.hip", "nf4.hip", "noalloc.hip", "gemm_f8.hip"]
 NO_CONTRACT = {"quantize.hip", "rowquant.hip", "nf4.hip"}
+# kernels whose MFMA results take VALU work: results in VGPRs, not AGPRs
+MFMA_VGPR = {"gemm_f8.hip"}
 HOST_SOURCES = ["api.cpp", "portable.cpp"]   # host C++ (argument checks, file I/O)
 
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
@@ -53,6 +55,8 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         flags = list(HIP_FLAGS)
         if src in NO_CONTRACT:
             flags.append("-ffp-contract=off")
+        if src in MFMA_VGPR:
+            flags += ["-mllvm", "-amdgpu-mfma-vgpr-form"]
         jobs_list.append([HIPCC, *flags, "-c", os.path.join(CSRC, src), "-o", obj])
     for host_src in HOST_SOURCES:
         obj = os.path.join(BUILD, host_src.replace(".cpp", ".o"))

@@ -339,7 +339,7 @@ int w4a8_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const
     // (w4a8_gemm_workspace_bytes) lets the row quantizer write them and the
     // bf16 tiled kernel run on them
     uint16_t* xw = nullptr;
-    const size_t xw_bytes = M > w4::kSkinnyMaxM ? w4::gemm_xw_bytes(M, K, N) : 0;
+    const size_t xw_bytes = M > w4::kSkinnyMaxM && !(w4::f8_eligible(M, K, G) && w4::f8_fits_buffers(M, K, N)) ? w4::gemm_xw_bytes(M, K, N) : 0;
     if (xw_bytes && workspace && workspace_bytes >= w4::gemm_xw_offset(M, K, N) + xw_bytes)
         xw = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + w4::gemm_xw_offset(M, K, N));
     w4::RowQuantParams rq{X, M, K, xq, xscale, xw};

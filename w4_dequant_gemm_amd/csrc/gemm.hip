@@ -1102,6 +1102,16 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(MulParams p) {
 #endif
 bool use_mid(int64_t M, int64_t K) { return M <= W4_MID_MAXM && K % big::BK == 0; }
 
+// The fp8-MFMA W4A8 kernel takes 128-k steps that each lie in one group:
+// groups of 128 (or per-channel rows) and K a multiple of 128.
+#ifndef W4_F8_GEMM
+#define W4_F8_GEMM 1
+#endif
+bool f8_eligible(int64_t M, int64_t K, int G) {
+    return W4_F8_GEMM && M > W4_MID_MAXM && K % kF8StepK == 0 && G % kF8StepK == 0;
+}
+bool use_f8(const MulParams& p) { return p.x_fp8 && f8_eligible(p.M, p.K, p.G) && f8_fits_buffers(p.M, p.K, p.N); }
+
 // Mid-size tiles: when there are fewer tiles than the target, every tile is
 // split along K (at most 16 ways, each of at least 4 steps of 64).
 GemmSplit gemm_split(int64_t M, int64_t K, int64_t N) {
@@ -1247,7 +1257,11 @@ hipError_t launch_gemm(const MulParams& p, hipStream_t stream) {
             return hipErrorInvalidValue;
         const int64_t wgs = q.split_t0 + (tiles - q.split_t0) * q.splits;
         const dim3 grid(static_cast<unsigned>(wgs));
-        if (q.x_fp8 && q.xw) {
+        if (q.x_fp8 && use_f8(q)) {
+            // W4A8 on the fp8 matrix cores (groups of 128 or whole rows)
+            const hipError_t e = launch_gemm_f8(q, wgs, stream);
+            if (e != hipSuccess) return e;
+        } else if (q.x_fp8 && q.xw) {
             // W4A8 on the widened activations: the bf16 kernel, row scales in
             // its epilogue (or in the split sum)
             q.X = q.xw;

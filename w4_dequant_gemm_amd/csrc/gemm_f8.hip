@@ -1,0 +1,421 @@
+// W4A8 on the fp8 matrix cores of gfx950 (groups of 128 k, or whole rows,
+// K a multiple of 128, M above the mid-size range).
+//
+// Both operands of v_mfma_f32_16x16x128_f8f6f4 are E4M3: the activation codes
+// of the row quantizer, and each weight as the exact integer u - z
+// (|u - z| <= 15 is an E4M3 value).  One 128-k step is one group, so one MFMA
+// gives a 16 x 16 output block's exact group sum T = sum_k xq (u - z), and the
+// group scale is applied to it per output, acc += s T; the row scale comes in
+// the epilogue (gowda.ai "LLM fast inference", "Achievement 2": FP8
+// operands, FP32 accumulation, the row scale in the epilogue; here the weight
+// codes stay exact instead of rounding (u - z) s to E4M3).
+//
+// Tile 256 x 256 of NW waves side by side: wave w owns output columns
+// (256 / NW) w .. for all 256 rows (16 row blocks of 16 x CB column blocks of
+// 16).  The accumulators take VALU multiply-adds, so they live in ordinary
+// VGPRs (the file is built with MFMA results in VGPRs) and a wave holds
+// 64 CB of them; with NW = 8 two waves share a SIMD and one wave's VALU work
+// runs under the other's MFMAs.
+//
+// The E4M3 activations go straight from global memory into LDS
+// (global_load_lds_dwordx4 into three 32 KB stages, two steps ahead; the
+// 16-byte chunk c of stage row r sits at position c ^ (r & 7)).  The weights
+// never pass through LDS: for a 16-column block, lane (c, q) loads the 16
+// bytes of 32-k tile 4 kt + q of its column (the 64 lanes read one contiguous
+// 1 KB of the blocked layout), two steps ahead, and converts them one step
+// ahead into its 32 B-operand bytes: per pair of codes one AND-OR into fp16
+// 1024 + u (or 1024 + 16 u), one packed fp16 add of -(1024 + z) (or
+// multiply-add by 1/16 and -(64 + z)), exact, and one
+// v_cvt_scalef32_pk_fp8_f16.  Lane (c, q) of the A operand holds bytes
+// 32 q .. 32 q + 31 of its row's 128-k step, so both operands pair the same k.
+// The group sums of a block are scaled two MFMA slots after their MFMA.
+//
+// A zero point outside 0..15 (possible only for a contracted range that
+// excludes 0) is clamped to zc for the MFMA operand, and the difference is
+// restored exactly: acc += s (zc - z) sum_k xq, with sum_k xq from one more
+// MFMA against ones, only in steps where some column of the wave needs it.
+#include <type_traits>
+
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace w4 {
+namespace {
+
+#ifndef W4_F8_NW
+#define W4_F8_NW 8
+#endif
+namespace f8 {
+constexpr int BM = 256, BN = 256, BK = 128, NW = W4_F8_NW, NT = 64 * NW;
+constexpr int STAGE = BM * BK;                 // bytes of one activation stage
+constexpr int ADMA = STAGE / (1024 * NW);      // direct-to-LDS loads per wave and step
+constexpr int RB = BM / 16;                    // 16-row blocks
+constexpr int WN = BN / NW;                    // columns per wave
+constexpr int CB = WN / 16;                    // 16-column blocks per wave
+constexpr int NSLOT = RB * CB;                 // MFMAs per wave and step
+constexpr int NCONV = CB * 4;                  // code words converted per lane and step
+constexpr int BLOAD = 2 * CB;                  // code and scale/zero loads per lane and step
+static_assert(BK == kF8StepK, "one K step of the fp8 kernel");
+static_assert(NSLOT % NCONV == 0 && NSLOT % BLOAD == 0 && NSLOT % ADMA == 0 && ADMA >= 1, "slot plan");
+}  // namespace f8
+
+typedef _Float16 half2v_t __attribute__((ext_vector_type(2)));
+typedef short short2v_t __attribute__((ext_vector_type(2)));
+
+// The work of one workgroup (1-D grid): workgroup b < split_t0 computes tile b
+// whole; the rest compute K range z of tile split_t0 + (b - split_t0) /
+// splits, z = (b - split_t0) % splits.  Tiles are row-major over the tile grid.
+struct F8Job {
+    int64_t m_base, n_base;
+    int kb, KT;        // first K step and number of K steps
+    int64_t part;      // partial-tile index in ws, or -1: write Y
+};
+__device__ __forceinline__ F8Job f8_job(const MulParams& p) {
+    using namespace f8;
+    const int64_t b = blockIdx.x;
+    const int64_t nt = (p.N + BN - 1) / BN;
+    const int KT_all = static_cast<int>(p.K / BK);
+    F8Job t;
+    int64_t tile;
+    if (b < p.split_t0) {
+        tile = b;
+        t.kb = 0;
+        t.KT = KT_all;
+        t.part = -1;
+    } else {
+        const int64_t j = (b - p.split_t0) / p.splits;
+        const int z = static_cast<int>((b - p.split_t0) % p.splits);
+        tile = p.split_t0 + j;
+        t.kb = z * KT_all / p.splits;
+        t.KT = (z + 1) * KT_all / p.splits - t.kb;
+        t.part = j * p.splits + z;
+    }
+    t.m_base = (tile / nt) * BM;
+    t.n_base = (tile % nt) * BN;
+    return t;
+}
+
+// One code word (codes k = 8j .. 8j + 7 of a column) as eight E4M3 bytes of
+// u - zc in k order, into o0 (k 0..3) and o1 (k 4..7).  nb = -(1024 + zc)
+// and nb16 = -(64 + zc) as fp16 pairs; bias = two fp16 1024.0 in a register.
+__device__ __forceinline__ void f8_word(uint32_t w, uint32_t bias, half2v_t nb, half2v_t nb16, uint32_t& o0,
+                                        uint32_t& o1) {
+    const half2v_t sixteenth = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(0.0625f)};
+    const uint32_t w8 = w >> 8;
+    const half2v_t e0 = __builtin_bit_cast(half2v_t, (w & 0x000F000Fu) | bias);     // 1024 + u: k 0, 1
+    const half2v_t e1 = __builtin_bit_cast(half2v_t, (w & 0x00F000F0u) | bias);     // 1024 + 16 u: k 2, 3
+    const half2v_t e2 = __builtin_bit_cast(half2v_t, (w8 & 0x000F000Fu) | bias);    // k 4, 5
+    const half2v_t e3 = __builtin_bit_cast(half2v_t, (w8 & 0x00F000F0u) | bias);    // k 6, 7
+    const half2v_t d0 = e0 + nb;
+    const half2v_t d1 = __builtin_elementwise_fma(e1, sixteenth, nb16);
+    const half2v_t d2 = e2 + nb;
+    const half2v_t d3 = __builtin_elementwise_fma(e3, sixteenth, nb16);
+    short2v_t r0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(short2v_t{0, 0}, d0, 1.0f, false);
+    r0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r0, d1, 1.0f, true);
+    short2v_t r1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(short2v_t{0, 0}, d2, 1.0f, false);
+    r1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r1, d3, 1.0f, true);
+    o0 = __builtin_bit_cast(uint32_t, r0);
+    o1 = __builtin_bit_cast(uint32_t, r1);
+}
+
+// A raw buffer descriptor (base, no stride, `bytes` records; reads past the
+// end return zeros), kept in SGPRs.
+__device__ __forceinline__ u32x4_t buffer_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return u32x4_t{static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a))),
+                   static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32))) & 0xFFFFu,
+                   bytes, 0x00020000u};
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t as_rsrc(const u32x4_t& r) {
+    return __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(static_cast<uint64_t>(r[0]) | (static_cast<uint64_t>(r[1]) << 32)), static_cast<short>(0),
+        static_cast<int>(r[2]), static_cast<int>(r[3]));
+}
+
+__device__ __forceinline__ float4_t mfma_f8_16x16x128(const int8x_t& a, const int8x_t& b) {
+    // formats 0 / 0: both operands E4M3; no block scales
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, float4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
+}
+
+__global__ void __launch_bounds__(f8::NT) gemm_f8_kernel(MulParams p) {
+    using namespace f8;
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a0[STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a1[STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a2[STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int c = lane & 15, q = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const F8Job job = f8_job(p);
+    const int64_t m_base = job.m_base, n_base = job.n_base;
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const int kb = job.kb, KT = job.KT;
+    const int g_shift = group_shift(p.G);
+
+    float4_t acc[RB][CB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int j = 0; j < CB; ++j) acc[i][j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // activations: load `it` of this wave fills stage rows 8 (wave ADMA + it)
+    // .. + 7; lane l writes row + l / 8 at chunk position l % 8, so it loads
+    // the chunk that the swizzle puts there, (l % 8) ^ (row & 7) (row & 7 is
+    // l / 8).  Buffer loads with a 32-bit lane offset: rows past M lie past
+    // the buffer's end and read as zeros (their outputs are never stored).
+    const int a_row0 = 8 * wave * ADMA + (lane >> 3);
+    const int a_chunk = (lane & 7) ^ (lane >> 3);
+    const u32x4_t a_rsrc = buffer_rsrc(p.X, static_cast<uint32_t>(M * K));
+    const uint32_t a_voff = static_cast<uint32_t>((m_base + a_row0) * K + a_chunk * 16);
+    auto dma_item = [&](int kt, uint8_t* stage, int it) {
+        kt = (kt < KT ? kt : KT - 1) + kb;
+        const uint32_t voff = a_voff + static_cast<uint32_t>(8 * it * K);
+        const uint32_t soff = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(kt * BK));
+        // Issued as plain instructions: the compiler cannot tell the three
+        // stages apart and would wait for every pending direct-to-LDS load
+        // before any LDS read.  No register result (the data goes to LDS at
+        // M0 + 16 lane); completion is covered by the wait at each step's end.
+        const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+            static_cast<uint32_t>(reinterpret_cast<uintptr_t>(stage + (wave * ADMA + it) * 1024)));
+        asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
+                     ::"v"(voff), "s"(a_rsrc), "s"(m0), "s"(soff) : "memory", "m0");
+    };
+
+    // weights: column n_base + WN wave + 16 cb + c, 32-k tile 4 kt + q.  In
+    // the blocked layout, block cb's 16 rows start at row r0 (uniform): the
+    // lane's 16 bytes of tile t are at word 4 nr t + 4 cc of the block and its
+    // scale/zero word of group g at nr g + cc (nr rows in the block, cc the
+    // lane's row, clamped to the block: columns past N repeat the last one,
+    // whose outputs are not stored).  Buffer loads: uniform block and step
+    // offsets, one lane offset per block.
+    const u32x4_t q_rsrc = buffer_rsrc(p.wq, static_cast<uint32_t>(N * K / 2));
+    const u32x4_t s_rsrc = buffer_rsrc(p.sz, static_cast<uint32_t>(N * (K / p.G) * 4));
+    uint32_t qblk[CB], sblk[CB], nrb[CB];      // uniform: block byte offsets, rows in the block
+    uint32_t qoff[CB], soff[CB];               // the lane's byte offsets in the block
+    const int64_t nblk_last = ((N - 1) / 16) * 16;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        int64_t r0 = n_base + WN * wave + 16 * cb;
+        r0 = r0 < N ? r0 : nblk_last;
+        const int nr = static_cast<int>(N - r0 < 16 ? N - r0 : 16);
+        const int cc = c < nr ? c : nr - 1;
+        qblk[cb] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(r0 * (K / 2)));
+        sblk[cb] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(r0 * (K / p.G) * 4));
+        nrb[cb] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(nr));
+        qoff[cb] = static_cast<uint32_t>(16 * nr * q + 16 * cc);
+        soff[cb] = static_cast<uint32_t>(4 * cc);
+    }
+    struct Regs {
+        u32x4_t q[CB];
+        uint32_t s[CB];
+    };
+    auto load_item = [&](int kt, Regs& r, int it) {
+        kt = (kt < KT ? kt : KT - 1) + kb;
+        if (it < CB) {
+            const uint32_t so = qblk[it] + static_cast<uint32_t>(kt) * (64u * nrb[it]);   // 4 tiles of 16 nr bytes
+            r.q[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      as_rsrc(q_rsrc), qoff[it], __builtin_amdgcn_readfirstlane(so), 0));
+        } else {
+            const int cb = it - CB;
+            // a 128-k step lies in one group (G is a multiple of 128)
+            const uint32_t g = static_cast<uint32_t>((static_cast<int64_t>(kt) * BK) >> g_shift);
+            const uint32_t so = sblk[cb] + g * (4u * nrb[cb]);
+            r.s[cb] = __builtin_amdgcn_raw_buffer_load_b32(as_rsrc(s_rsrc), soff[cb], __builtin_amdgcn_readfirstlane(so), 0);
+        }
+    };
+    // converted operands of one step: E4M3 bytes of u - zc, the group scale,
+    // and whether any column of the wave has zc != z
+    struct BOps {
+        int8x_t b[CB];
+        float s[CB];
+        uint32_t oor;
+    };
+    const uint32_t bias = opaque_vgpr(0x64006400u);   // two fp16 1024.0
+    half2v_t nbv[CB], nb16v[CB];
+    uint32_t oor_lane = 0;
+    auto conv_item = [&](int it, const Regs& r, BOps& o) {
+        const int cb = it >> 2, wi = it & 3;
+        if (wi == 0) {
+            const uint32_t szw = r.s[cb];
+            const float s = half_bits_to_float(szw);
+            const float z = half_bits_to_float(szw >> 16);
+            const float zc = fminf(fmaxf(z, 0.0f), 15.0f);
+            o.s[cb] = s;
+            const _Float16 e = static_cast<_Float16>(-(1024.0f + zc));
+            const _Float16 e16 = static_cast<_Float16>(-(64.0f + zc));
+            nbv[cb] = half2v_t{e, e};
+            nb16v[cb] = half2v_t{e16, e16};
+            oor_lane = (cb == 0 ? 0u : oor_lane) | (zc != z ? 1u : 0u);
+        }
+        uint32_t o0, o1;
+        f8_word(r.q[cb][wi], bias, nbv[cb], nb16v[cb], o0, o1);
+        // pinned here: the optimizer would otherwise sink the conversion
+        // (used only in the next step) past the MFMAs of this one
+        asm volatile("" : "+v"(o0), "+v"(o1));
+        o.b[cb][2 * wi] = static_cast<int>(o0);
+        o.b[cb][2 * wi + 1] = static_cast<int>(o1);
+        if (it == NCONV - 1)
+            o.oor = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(__builtin_amdgcn_ballot_w64(oor_lane != 0) != 0));
+    };
+
+    // A fragment of row block rb: stage row 16 rb + c, chunks 2 q and 2 q + 1
+    const uint32_t aoff0 = static_cast<uint32_t>(c * BK + 16 * ((2 * q) ^ (c & 7)));
+    const uint32_t aoff1 = static_cast<uint32_t>(c * BK + 16 * ((2 * q + 1) ^ (c & 7)));
+    auto frag_a = [&](const uint8_t* A, int rb) -> int8x_t {
+        const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(A + rb * (16 * BK) + aoff0);
+        const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(A + rb * (16 * BK) + aoff1);
+        return int8x_t{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]), static_cast<int>(lo[3]),
+                       static_cast<int>(hi[0]), static_cast<int>(hi[1]), static_cast<int>(hi[2]), static_cast<int>(hi[3])};
+    };
+    const int8x_t ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                          0x38383838, 0x38383838, 0x38383838, 0x38383838};   // E4M3 1.0
+
+    constexpr int kStepLoads = ADMA + BLOAD;
+    auto step_end3 = [&]() {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt((kStepLoads & 15) | (7 << 4) | ((kStepLoads >> 4) << 14));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    auto stage_a = [&](auto S) -> uint8_t* {
+        constexpr int s3 = decltype(S)::value;
+        return s3 == 0 ? lds_a0 : (s3 == 1 ? lds_a1 : lds_a2);
+    };
+    auto scale_add = [&](int v, const BOps& cur, const float4_t& t) {
+        const float sv = cur.s[v % CB];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[v / CB][v % CB][e] = fmaf(sv, t[e], acc[v / CB][v % CB][e]);
+    };
+    // step kt: MFMAs on `cur` (converted during step kt - 1) and the A stage
+    // of kt; `ready` (codes of step kt + 1) converted into `nxt`; the codes of
+    // step kt + 2 loaded into `next` and its activations sent to LDS
+#ifndef W4_F8_TROT
+#define W4_F8_TROT 2
+#endif
+    constexpr int TROT = W4_F8_TROT;   // group sums in flight: a block is scaled TROT - 1 slots after its MFMA
+    constexpr int CONV_EVERY = NSLOT / NCONV, LOAD_EVERY = NSLOT / BLOAD, DMA_EVERY = NSLOT / ADMA;
+    auto step3 = [&](int kt, auto SA, Regs& next, const Regs& ready, const BOps& cur, BOps& nxt) {
+        constexpr int sa = decltype(SA)::value;
+        const uint8_t* As = stage_a(std::integral_constant<int, sa>{});
+        uint8_t* Ad = stage_a(std::integral_constant<int, (sa + 2) % 3>{});
+        int8x_t fa = frag_a(As, 0);
+        float4_t T[TROT];
+#pragma unroll
+        for (int u = 0; u < NSLOT; ++u) {
+            const int rb = u / CB, cb = u % CB;
+            __builtin_amdgcn_sched_barrier(0);
+            T[u % TROT] = mfma_f8_16x16x128(fa, cur.b[cb]);
+            // the fragment is reloaded for the next row block right after its last use
+            if (cb == CB - 1 && rb + 1 < RB) fa = frag_a(As, rb + 1);
+            if (u >= TROT - 1) scale_add(u - (TROT - 1), cur, T[(u - (TROT - 1)) % TROT]);
+            if (u % CONV_EVERY == 1 % CONV_EVERY) conv_item(u / CONV_EVERY, ready, nxt);
+            if (u % LOAD_EVERY == LOAD_EVERY / 2 - 1) {
+                load_item(kt + 2, next, u / LOAD_EVERY);
+                asm volatile("" ::: "memory");
+            }
+            if (u % DMA_EVERY == DMA_EVERY - 1) dma_item(kt + 2, Ad, u / DMA_EVERY);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int v = NSLOT - (TROT - 1); v < NSLOT; ++v) scale_add(v, cur, T[v % TROT]);
+        if (cur.oor) {
+            // some column's zero point lies outside 0..15: add s (zc - z) sum_k xq,
+            // with the scale/zero words of this step read again
+            Regs rz;
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) load_item(kt, rz, CB + cb);
+            float corr[CB];
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                const float sc = half_bits_to_float(rz.s[cb]);
+                const float z = half_bits_to_float(rz.s[cb] >> 16);
+                corr[cb] = sc * (fminf(fmaxf(z, 0.0f), 15.0f) - z);
+            }
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const float4_t t1 = mfma_f8_16x16x128(frag_a(As, rb), ones);
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[rb][cb][e] = fmaf(corr[cb], t1[e], acc[rb][cb][e]);
+            }
+        }
+        step_end3();
+    };
+
+    Regs r0, r1;
+    BOps o0, o1;
+#pragma unroll
+    for (int it = 0; it < ADMA; ++it) dma_item(0, lds_a0, it);
+#pragma unroll
+    for (int it = 0; it < ADMA; ++it) dma_item(1, lds_a1, it);
+#pragma unroll
+    for (int it = 0; it < BLOAD; ++it) load_item(0, r0, it);
+#pragma unroll
+    for (int it = 0; it < BLOAD; ++it) load_item(1, r1, it);
+#pragma unroll
+    for (int it = 0; it < NCONV; ++it) conv_item(it, r0, o0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    // A stages cycle with period 3, code registers and operands with period 2
+    for (int kt = 0; kt < KT; kt += 6) {
+        step3(kt, I0{}, r0, r1, o0, o1);
+        if (kt + 1 < KT) step3(kt + 1, I1{}, r1, r0, o1, o0);
+        if (kt + 2 < KT) step3(kt + 2, I2{}, r0, r1, o0, o1);
+        if (kt + 3 < KT) step3(kt + 3, I0{}, r1, r0, o1, o0);
+        if (kt + 4 < KT) step3(kt + 4, I1{}, r0, r1, o0, o1);
+        if (kt + 5 < KT) step3(kt + 5, I2{}, r1, r0, o1, o0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("" ::: "memory");
+
+    // epilogue: register e of lane (c, q) in block (rb, cb) holds row
+    // 16 rb + 4 q + e, column WN wave + 16 cb + c
+    const bool whole = job.part < 0;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        float rsc[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t row = m_base + 16 * rb + 4 * q + e;
+            rsc[e] = whole && row < M ? p.xscale[row] : 1.0f;
+        }
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const int lc = WN * wave + 16 * cb + c;
+            const int64_t col = n_base + lc;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int lr = 16 * rb + 4 * q + e;
+                const int64_t row = m_base + lr;
+                if (!whole) p.ws[job.part * (BM * BN) + lr * BN + lc] = acc[rb][cb][e];
+                else if (row < M && col < N) p.Y[row * N + col] = float_to_bf16_bits(acc[rb][cb][e] * rsc[e]);
+            }
+        }
+    }
+}
+
+}  // namespace
+
+// byte offsets of the operands fit the 31-bit buffer records
+bool f8_fits_buffers(int64_t M, int64_t K, int64_t N) {
+    constexpr int64_t kMax = (int64_t{1} << 31) - 1;
+    return M * K <= kMax && N * K / 2 <= kMax && N * (K / f8::BK) * 4 <= kMax;
+}
+
+// grid of `wgs` workgroups over 256 x 256 tiles (the split schedule of
+// MulParams); the caller launches the split sum
+hipError_t launch_gemm_f8(const MulParams& p, int64_t wgs, hipStream_t stream) {
+    if (p.K % f8::BK != 0 || p.G % f8::BK != 0 || !p.x_fp8 || !p.xscale || !f8_fits_buffers(p.M, p.K, p.N))
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(gemm_f8_kernel, dim3(static_cast<unsigned>(wgs)), dim3(f8::NT), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace w4

@@ -124,6 +124,17 @@ size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
 // takes none
 size_t gemm_xw_offset(int64_t M, int64_t K, int64_t N);
 size_t gemm_xw_bytes(int64_t M, int64_t K, int64_t N);
+// true when a W4A8 product of this shape and group size runs on the fp8
+// matrix cores (above the mid-size range, K and G multiples of 128); it
+// takes the E4M3 activations as they are, never the widened copy
+bool f8_eligible(int64_t M, int64_t K, int G);
+// K step of the fp8 kernel (one group of 128 k)
+constexpr int kF8StepK = 128;
+// the fp8 kernel addresses its operands with 31-bit byte offsets
+bool f8_fits_buffers(int64_t M, int64_t K, int64_t N);
+// the fp8 W4A8 tiled kernel on `wgs` workgroups of 256 x 256 output tiles
+// (the split schedule of gemm_split in p); the split sum is launched apart
+hipError_t launch_gemm_f8(const MulParams& p, int64_t wgs, hipStream_t stream);
 
 // Library-held scratch of w4a16_gemm_noalloc: 64 MiB per GPU, the largest
 // K-split workspace any shape of the tiled GEMM takes (at most 256 partial
