@@ -270,14 +270,25 @@ int w4a8_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const
  * above, a tiled MFMA GEMM holds 128 columns of each weight per workgroup
  * (some of its waves sum the gate products, the others the up products of
  * the same outputs) and needs K to be a multiple of 64 (else W4_EUNSUPPORTED).
- * No workspace: the tiled form does not split K.  H feeds the down
- * projection (w4a8_gemm on one or two rows quantizes it to E4M3 inside its
- * own kernel).
+ * The tiled form does not split K.
  *   X            [M, K] bf16 in, M >= 0.
  *   wq_gate, sz_gate, wq_up, sz_up: two [N, K] weights in the GPU layout of
  *                w4_prepack, with the same G.
  *   H            [M, N] bf16 out.
  *   xq, xscale   (W4A8) as for w4a8_gemm.
+ * W4A8 only -- the down projection's input in the same pass (gowda.ai "LLM
+ * fast inference", "Machete, with credit where it is due", and "Achievement
+ * 2": per-row E4M3 activations at the input of the next FP8 product):
+ *   hq, hscale   [M, N] E4M3 bytes and [M] fp32 out, or both NULL: H's rows
+ *                quantized exactly as w4_quantize_rows_e4m3(H) would (same
+ *                codes and scales, bit for bit), for w4a8_gemm_e4m3 of the
+ *                down projection.  Each workgroup of the pass also records
+ *                the maximum |H| of every row over its columns, so the
+ *                quantization reads H once instead of twice.  Needs N a
+ *                multiple of 8.
+ *   workspace    with hq: at least w4a8_gate_up_workspace_bytes(M, K, N)
+ *                bytes, 16-byte aligned (the partial row maxima); else
+ *                ignored (may be NULL).
  */
 #define W4_ACT_SILU 1
 #define W4_ACT_GELU_TANH 2
@@ -286,7 +297,26 @@ int w4a16_gate_up(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq_ga
                   hipStream_t stream);
 int w4a8_gate_up(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq_gate, const uint32_t* sz_gate,
                  const uint32_t* wq_up, const uint32_t* sz_up, int64_t N, int G, int act, uint16_t* H, uint8_t* xq,
-                 float* xscale, hipStream_t stream);
+                 float* xscale, uint8_t* hq, float* hscale, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream);
+/* Bytes of workspace w4a8_gate_up needs to emit hq (M * tiles * 4: the
+ * partial row maxima of H, 16-column tiles up to 32 rows, 128-column tiles
+ * above); 0 for empty shapes. */
+size_t w4a8_gate_up_workspace_bytes(int64_t M, int64_t K, int64_t N);
+
+/*
+ * w4a8_gemm_e4m3 -- the W4A8 product on activations already quantized per
+ * row (the hq / hscale of w4a8_gate_up, or w4_quantize_rows_e4m3):
+ *   Y = bf16(xscale[m] * sum_k e4m3(xq[m, k]) * W'[n, k]), fp32 accumulation
+ * (gowda.ai "LLM fast inference", "Achievement 2").  Same kernels and result
+ * as w4a8_gemm after its row quantization.
+ *   xq [M, K] E4M3 bytes in;  xscale [M] fp32 in;  K a multiple of 16.
+ *   workspace: as for w4a16_gemm (w4_gemm_workspace_bytes).
+ *   Other arguments as for w4a8_gemm.
+ */
+int w4a8_gemm_e4m3(const uint8_t* xq, const float* xscale, int64_t M, int64_t K, const uint32_t* wq,
+                   const uint32_t* sz, int64_t N, int G, uint16_t* Y, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream);
 
 /*
  * NF4 comparator (gsantana.dev "Quantizing LLMs Without Guesswork",
@@ -366,7 +396,8 @@ const char* w4_status_string(int status);
  * (thread-local storage, valid until the next failing call). */
 const char* w4_last_error(void);
 
-/* Version of this ABI, currently 2. */
+/* Version of this ABI, currently 3 (3: w4a8_gate_up emits the down
+ * projection's E4M3 input; w4a8_gemm_e4m3; w4a16_gemm_noalloc). */
 int w4_abi_version(void);
 
 #ifdef __cplusplus

@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
               "w4_status_string", "w4_last_error",
               "w4_abi_version", "w4_portable_save", "w4_portable_info_read", "w4_portable_load",
               "w4a16_gate_up", "w4a8_gate_up", "w4_nf4_levels", "w4_nf4_quantize", "w4_nf4_gemv",
-              "w4a16_gemm_noalloc"):
+              "w4a16_gemm_noalloc", "w4a8_gate_up_workspace_bytes", "w4a8_gemm_e4m3"):
         assert n in names
 
 
@@ -76,7 +76,7 @@ def test_read_probe_library_is_separate(lib):
 
 def test_status_strings(lib):
     import w4_dequant_gemm_amd as w4
-    assert w4.w4_abi_version() == 2
+    assert w4.w4_abi_version() == 3
     assert w4.w4_status_string(0) == "ok"
     assert w4.w4_status_string(1) == "invalid argument"
     assert w4.w4_status_string(2) == "unsupported configuration"
@@ -240,7 +240,24 @@ def test_gate_up_validation(lib):
     assert g(fake, 1, 4096, fake, fake, fake, fake, 64, 128, 3, fake, None) == 1      # unknown activation
     assert g(fake, 1, 4096, fake, fake, None, fake, 64, 128, 1, fake, None) == 1      # no up weights
     assert g(None, 0, 4096, None, None, None, None, 64, 128, 1, None, None) == 0      # nothing to do
-    assert lib.w4a8_gate_up(fake, 1, 4096, fake, fake, fake, fake, 64, 128, 2, fake, None, fake, None) == 1
+    assert lib.w4a8_gate_up(fake, 1, 4096, fake, fake, fake, fake, 64, 128, 2, fake, None, fake, None, None, None,
+                            0, None) == 1
+    # emitting H's E4M3 form needs hscale and a workspace of the partial row maxima
+    gw = lib.w4a8_gate_up_workspace_bytes
+    assert gw(16, 4096, 14336) == 16 * (14336 // 16) * 4 and gw(2048, 4096, 14336) == 2048 * 112 * 4
+    assert gw(0, 4096, 64) == 0
+    assert lib.w4a8_gate_up(fake, 2, 4096, fake, fake, fake, fake, 64, 128, 1, fake, fake, fake, fake, None, fake,
+                            4096, None) == 1                                  # hq without hscale
+    assert lib.w4a8_gate_up(fake, 2, 4096, fake, fake, fake, fake, 64, 128, 1, fake, fake, fake, fake, fake, None,
+                            0, None) == 1                                     # no workspace
+    assert "workspace" in w4.w4_last_error()
+    assert lib.w4a8_gate_up(fake, 2, 4096, fake, fake, fake, fake, 64, 128, 1, fake, fake, fake, None, fake, None,
+                            0, None) == 1                                     # hscale without hq
+    assert lib.w4a8_gate_up(fake, 2, 4096, fake, fake, fake, fake, 60, 128, 1, fake, fake, fake, fake, fake, fake,
+                            4096, None) == 1                                  # N not a multiple of 8
+    # the product on E4M3 activations checks like the others
+    assert lib.w4a8_gemm_e4m3(fake, None, 2, 4096, fake, fake, 64, 128, fake, None, 0, None) == 1   # no xscale
+    assert lib.w4a8_gemm_e4m3(fake, fake, 2, 4096, fake, fake, 64, 48, fake, None, 0, None) == 2    # group size
 
 
 def test_nf4_levels_match_the_oracle(lib):

@@ -686,3 +686,49 @@ def test_zero_points_outside_the_code_range():
         assert_bits_equal(host(xq), rq, "E4M3 activations")
         check_products(want, Y.float().cpu().numpy(), X64, q, G, "asym", f"w4a16 M={M}")
         check_products(want8, Y8.float().cpu().numpy(), w4a8_x64(rq, rs), q, G, "asym", f"w4a8 M={M}")
+
+
+def test_gate_up_emits_the_down_projection_input():
+    # w4a8_gate_up with hq: the E4M3 rows of H and their scales, formed from
+    # the row maxima the pass leaves behind, must be bit for bit the oracle's
+    # row quantization of the bf16 H the same call returns; the down
+    # projection on them (w4a8_gemm_e4m3) must equal w4a8_gemm on H bit for
+    # bit and the oracle within the product bounds.  Streaming pass (1, 2,
+    # 16, 32 rows: 16-column tiles) and tiled pass (48, 300 rows: 128-column
+    # tiles), a zero activation row (H row 0: scale 1e-8, codes 0), a ragged N.
+    require_gpu()
+    import torch
+    import w4_dequant_gemm_amd as w4
+    wl = synth.WORKLOADS["llama8b_decode"]
+    W = synth.weight(wl, 0, rows=2 * 1056)
+    for N in (1024, 1056):
+        # N = 1056 leaves a partial last 128-column tile (the tiled pass) and
+        # gives the down weight [640, N] groups of 32
+        qg = oracle.quantize(np.ascontiguousarray(W[:N]), 128, "asym")
+        qu = oracle.quantize(np.ascontiguousarray(W[N:2 * N]), 128, "asym")
+        Gd = 128 if N % 128 == 0 else 32
+        qd = oracle.quantize(synth.normal_matrix(85, 640, N, 0.03), Gd, "asym")
+        pg, _ = prepack_dev(qg)
+        pu, _ = prepack_dev(qu)
+        pd, _ = prepack_dev(qd)
+        K = W.shape[1]
+        for M in (1, 2, 16, 32, 48, 300):
+            print(f"[gate_up e4m3] N={N} M={M}", flush=True)
+            Xb = _x("llama8b_decode", M, K)
+            Xb[0] = 0
+            H, xq, xs, hq, hs = w4.w4a8_gate_up(bf16_dev(Xb), pg, pu, 128, "silu", emit_e4m3=True)
+            torch.cuda.synchronize()
+            Hb = bits16(H)
+            rq, rs = oracle.row_quant_e4m3(Hb)
+            assert_bits_equal(host(hs).view(np.uint32), rs.view(np.uint32), f"H row scales M={M}")
+            assert_bits_equal(host(hq), rq, f"H E4M3 codes M={M}")
+            assert host(hs)[0] == np.float32(1e-8) and np.all(host(hq)[0] == 0)
+            # the down projection on the emitted codes
+            Yd = w4.w4a8_gemm_e4m3(hq, hs, pd["wq"], pd["sz"], Gd)
+            Yr, _, _ = w4.w4a8_gemm(H, pd["wq"], pd["sz"], Gd)
+            torch.cuda.synchronize()
+            assert np.array_equal(bits16(Yd), bits16(Yr)), f"w4a8_gemm_e4m3 differs from w4a8_gemm M={M}"
+            want, _, _ = oracle.w4a8_ref(Hb, qd["packed"], qd["scale"], qd["zero"], Gd, "asym")
+            if M > 1:
+                check_products(want[1:], Yd.float().cpu().numpy()[1:], w4a8_x64(rq, rs)[1:], qd, Gd, "asym",
+                               f"down on emitted codes M={M}")

@@ -20,7 +20,7 @@ __all__ = [
     "w4a16_gemm", "w4a16_gemm_noalloc", "w4a8_gemm", "w4_gemm_workspace_bytes", "w4a8_gemm_workspace_bytes", "w4_status_string",
     "w4_last_error",
     "w4_abi_version", "w4_portable_save", "w4_portable_info_read", "w4_portable_load",
-    "w4a16_gate_up", "w4a8_gate_up", "ACT_SILU", "ACT_GELU_TANH",
+    "w4a16_gate_up", "w4a8_gate_up", "w4a8_gate_up_workspace_bytes", "w4a8_gemm_e4m3", "ACT_SILU", "ACT_GELU_TANH",
     "w4_nf4_levels", "w4_nf4_quantize", "w4_nf4_gemv",
     "FRACS_PLAIN", "FRACS_11",
 ]
@@ -83,7 +83,11 @@ def lib():
     L.w4a8_gemm_workspace_bytes.argtypes = [i64, i64, i64]
     L.w4a8_gemm_workspace_bytes.restype = sz_t
     L.w4a16_gate_up.argtypes = [P, i64, i64, P, P, P, P, i64, I, I, P, P]
-    L.w4a8_gate_up.argtypes = [P, i64, i64, P, P, P, P, i64, I, I, P, P, P, P]
+    L.w4a8_gate_up.argtypes = [P, i64, i64, P, P, P, P, i64, I, I, P, P, P, P, P, P, sz_t, P]
+    L.w4a8_gate_up_workspace_bytes.argtypes = [i64, i64, i64]
+    L.w4a8_gate_up_workspace_bytes.restype = sz_t
+    L.w4a8_gemm_e4m3.argtypes = [P, P, i64, i64, P, P, i64, I, P, P, sz_t, P]
+    L.w4a8_gemm_e4m3.restype = I
     L.w4a16_gate_up.restype = I
     L.w4_nf4_levels.argtypes = [P]
     L.w4_nf4_quantize.argtypes = [P, i64, i64, P, P, P, P]
@@ -431,21 +435,61 @@ def w4a16_gate_up(X: torch.Tensor, gate: dict, up: dict, G: int, act="silu", *, 
     return H
 
 
+def w4a8_gate_up_workspace_bytes(M: int, K: int, N: int) -> int:
+    """Workspace bytes ``w4a8_gate_up`` needs to emit the E4M3 form of H."""
+    return int(lib().w4a8_gate_up_workspace_bytes(M, K, N))
+
+
 def w4a8_gate_up(X: torch.Tensor, gate: dict, up: dict, G: int, act="silu", *, H=None, xq=None, xscale=None,
-                 stream=None):
-    """W4A8 form of ``w4a16_gate_up``: per-row E4M3 of ``X`` first; returns (H, xq, xscale)."""
+                 emit_e4m3: bool = False, hq=None, hscale=None, workspace=None, stream=None):
+    """W4A8 form of ``w4a16_gate_up``: per-row E4M3 of ``X`` first; returns (H, xq, xscale).
+
+    With ``emit_e4m3`` (or ``hq`` given) the same pass also produces H's rows
+    quantized to E4M3 for the down projection (``w4a8_gemm_e4m3``) and
+    returns (H, xq, xscale, hq, hscale)."""
     M, K, N = _check_product_shapes("w4a8_gate_up", X, gate["wq"], gate["sz"], G, Y=H, xq=xq, xscale=xscale,
                                     up=up)
     dev = X.device
+    emit = emit_e4m3 or hq is not None
+    if emit:
+        if hq is not None and (tuple(hq.shape) != (M, N) or hq.element_size() != 1):
+            raise ValueError(f"w4a8_gate_up: hq must be one byte per element with shape ({M}, {N})")
+        if hscale is not None and hscale.numel() != M:
+            raise ValueError(f"w4a8_gate_up: hscale has {hscale.numel()} elements, expected {M}")
     H = _empty((M, N), torch.bfloat16, dev) if H is None else H
     xq = _empty((M, K), torch.uint8, dev) if xq is None else xq
     xscale = _empty((M,), torch.float32, dev) if xscale is None else xscale
+    ws, ws_bytes = None, 0
+    if emit:
+        hq = _empty((M, N), torch.uint8, dev) if hq is None else hq
+        hscale = _empty((M,), torch.float32, dev) if hscale is None else hscale
+        if workspace is None:
+            workspace = torch.empty((max(w4a8_gate_up_workspace_bytes(M, K, N), 16),), dtype=torch.uint8, device=dev)
+            if stream is not None:
+                workspace.record_stream(stream)
+        ws, ws_bytes = _dev(workspace, "workspace"), _nbytes(workspace)
     rc = lib().w4a8_gate_up(_dev(X, "X", torch.bfloat16), M, K, _dev(gate["wq"], "gate wq"), _dev(gate["sz"], "gate sz"),
                             _dev(up["wq"], "up wq"), _dev(up["sz"], "up sz"), N, G, _ACTS[act],
                             _dev(H, "H", torch.bfloat16), _dev(xq, "xq"), _dev(xscale, "xscale", torch.float32),
-                            _stream(dev, stream))
+                            _dev(hq, "hq") if emit else None, _dev(hscale, "hscale", torch.float32) if emit else None,
+                            ws, ws_bytes, _stream(dev, stream))
     _check("w4a8_gate_up", rc)
-    return H, xq, xscale
+    return (H, xq, xscale, hq, hscale) if emit else (H, xq, xscale)
+
+
+def w4a8_gemm_e4m3(xq: torch.Tensor, xscale: torch.Tensor, wq: torch.Tensor, sz: torch.Tensor, G: int, *, Y=None,
+                   workspace=None, stream=None):
+    """W4A8 product on activations already quantized per row: ``Y = bf16(xscale * Xq . W'^T)``."""
+    if xq.element_size() != 1:
+        raise ValueError("w4a8_gemm_e4m3: xq must hold one byte per element")
+    M, K, N = _check_product_shapes("w4a8_gemm_e4m3", xq, wq, sz, G, Y=Y, xscale=xscale)
+    dev = xq.device
+    Y = _empty((M, N), torch.bfloat16, dev) if Y is None else Y
+    ws, ws_bytes = _workspace(M, K, N, dev, workspace, stream)
+    rc = lib().w4a8_gemm_e4m3(_dev(xq, "xq"), _dev(xscale, "xscale", torch.float32), M, K, _dev(wq, "wq"),
+                              _dev(sz, "sz"), N, G, _dev(Y, "Y", torch.bfloat16), ws, ws_bytes, _stream(dev, stream))
+    _check("w4a8_gemm_e4m3", rc)
+    return Y
 
 
 # -------------------------------------------------------- NF4 comparator

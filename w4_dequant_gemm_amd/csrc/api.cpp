@@ -366,28 +366,43 @@ int w4a16_gate_up(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq_ga
     return hip_status(w4::launch_skinny(p, stream), fn);
 }
 
+size_t w4a8_gate_up_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+    if (M <= 0 || K <= 0 || N <= 0) return 0;
+    return static_cast<size_t>(M) * static_cast<size_t>(w4::gate_up_amax_tiles(M, N)) * sizeof(float);
+}
+
 int w4a8_gate_up(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq_gate, const uint32_t* sz_gate,
                  const uint32_t* wq_up, const uint32_t* sz_up, int64_t N, int G, int act, uint16_t* H, uint8_t* xq,
-                 float* xscale, hipStream_t stream) {
+                 float* xscale, uint8_t* hq, float* hscale, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream) {
     const char* fn = "w4a8_gate_up";
     W4_TRY(gate_up_common(fn, X, M, K, wq_gate, sz_gate, wq_up, sz_up, N, G, act, H));
     if (M == 0 || N == 0) return W4_OK;
     W4_REQUIRE_PTR(fn, xq);
     if (!xscale) return fail(W4_EINVAL, "%s: xscale is NULL", fn);
+    const bool emit = hq != nullptr;
+    if (emit) {
+        if (N % 8 != 0) return fail(W4_EINVAL, "%s: the E4M3 form of H needs N a multiple of 8 (N = %lld)", fn,
+                                    static_cast<long long>(N));
+        W4_REQUIRE_PTR(fn, hq);
+        if (!hscale) return fail(W4_EINVAL, "%s: hq given without hscale", fn);
+        const size_t need = w4a8_gate_up_workspace_bytes(M, K, N);
+        if (!workspace || workspace_bytes < need)
+            return fail(W4_EINVAL, "%s: emitting hq needs a workspace of %zu bytes (w4a8_gate_up_workspace_bytes)",
+                        fn, need);
+        if (!aligned16(workspace)) return fail(W4_EINVAL, "%s: workspace is not 16-byte aligned", fn);
+    } else if (hscale) {
+        return fail(W4_EINVAL, "%s: hscale given without hq", fn);
+    }
     w4::MulParams p{X, nullptr, M, K, N, G, wq_gate, sz_gate, H, true, xq, xscale};
     p.wq2 = wq_up;
     p.sz2 = sz_up;
     p.act = act;
-    if (M > w4::kGateUpMaxM) {
-        w4::RowQuantParams rq{X, M, K, xq, xscale};
-        W4_TRY(hip_status(w4::launch_rowquant(rq, stream), fn));
-        p.X = xq;
-        p.xscale = xscale;
-        p.xq_out = nullptr;
-        p.xscale_out = nullptr;
-        return hip_status(w4::launch_gemm_pair(p, stream), fn);
+    if (emit) {
+        p.amax_part = static_cast<float*>(workspace);
+        p.amax_tiles = w4::gate_up_amax_tiles(M, N);
     }
-    if (!w4::skinny_quantizes_rows(M, K)) {
+    if (M > w4::kGateUpMaxM || !w4::skinny_quantizes_rows(M, K)) {
         w4::RowQuantParams rq{X, M, K, xq, xscale};
         W4_TRY(hip_status(w4::launch_rowquant(rq, stream), fn));
         p.X = xq;
@@ -395,7 +410,27 @@ int w4a8_gate_up(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq_gat
         p.xq_out = nullptr;
         p.xscale_out = nullptr;
     }
-    return hip_status(w4::launch_skinny(p, stream), fn);
+    W4_TRY(hip_status(M > w4::kGateUpMaxM ? w4::launch_gemm_pair(p, stream) : w4::launch_skinny(p, stream), fn));
+    if (!emit) return W4_OK;
+    // H's rows quantized to E4M3 from the row maxima the pass left behind
+    w4::RowQuantParams hq_p{H, M, N, hq, hscale};
+    hq_p.amax_part = p.amax_part;
+    hq_p.amax_tiles = p.amax_tiles;
+    return hip_status(w4::launch_rowquant(hq_p, stream), fn);
+}
+
+int w4a8_gemm_e4m3(const uint8_t* xq, const float* xscale, int64_t M, int64_t K, const uint32_t* wq,
+                   const uint32_t* sz, int64_t N, int G, uint16_t* Y, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
+    const char* fn = "w4a8_gemm_e4m3";
+    W4_TRY(mul_common(fn, reinterpret_cast<const uint16_t*>(xq), M, K, wq, sz, N, G, Y, workspace, workspace_bytes));
+    if (M == 0 || N == 0) return W4_OK;
+    if (K % 16 != 0) return fail(W4_EINVAL, "%s: K = %lld must be a multiple of 16", fn, static_cast<long long>(K));
+    if (!xscale) return fail(W4_EINVAL, "%s: xscale is NULL", fn);
+    w4::MulParams p{xq, xscale, M, K, N, G, wq, sz, Y, true};
+    if (M <= w4::kSkinnyMaxM)
+        return hip_status(w4::launch_skinny(with_skinny_split(p, workspace, workspace_bytes), stream), fn);
+    return hip_status(w4::launch_gemm(with_split(p, workspace), stream), fn);
 }
 
 int w4_nf4_levels(float* levels) {
@@ -458,7 +493,7 @@ const char* w4_status_string(int status) {
 
 const char* w4_last_error(void) { return g_last_error; }
 
-int w4_abi_version(void) { return 2; }
+int w4_abi_version(void) { return 3; }
 
 static_assert(W4_NOALLOC_SCRATCH_BYTES == w4::kNoAllocScratchBytes, "w4.h and the library agree on the scratch size");
 

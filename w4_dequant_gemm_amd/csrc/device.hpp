@@ -120,6 +120,20 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// Maximum over each aligned group of 16 lanes; every lane gets its group's.
+__device__ __forceinline__ float max16(float v) {
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 16));
+    return v;
+}
+
+// Maximum over each half (32 lanes) of the wavefront.
+__device__ __forceinline__ float max32(float v) {
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 32));
+    return v;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));

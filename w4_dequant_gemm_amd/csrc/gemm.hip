@@ -717,7 +717,10 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_mid_kernel(MulParams p) {
         __syncthreads();
         if (wn == 0) {
 #pragma unroll
-            for (int i = 0; i < FI; ++i)
+            for (int i = 0; i < FI; ++i) {
+                float hmax[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) hmax[r] = 0.0f;
 #pragma unroll
                 for (int j = 0; j < FJ; ++j) {
                     const int64_t col = n_base + j * 32 + (lane & 31);
@@ -728,10 +731,23 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_mid_kernel(MulParams p) {
                             const float rs = XF8 ? p.xscale[row] : 1.0f;
                             const float g = acc[i][j][r] * rs;
                             const float u = up[((i * FJ + j) * 16 + r) * 64 + lane] * rs;
-                            p.Y[row * N + col] = float_to_bf16_bits(activation(p.act, g) * u);
+                            const uint16_t hb = float_to_bf16_bits(activation(p.act, g) * u);
+                            p.Y[row * N + col] = hb;
+                            hmax[r] = fmaxf(hmax[r], fabsf(bf16_lo(hb)));
                         }
                     }
                 }
+                if (p.amax_part) {
+                    // each row's maximum |H| over the tile's columns: the
+                    // 32 lanes of a half hold one row's columns
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float hv = max32(hmax[r]);
+                        const int64_t row = m_base + wm * TM + i * 32 + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
+                        if ((lane & 31) == 0 && row < M) p.amax_part[row * p.amax_tiles + n_base / OUTN] = hv;
+                    }
+                }
+            }
         }
         return;
     }
@@ -1236,6 +1252,8 @@ hipError_t launch_gemm_pair(const MulParams& p, hipStream_t stream) {
     if (p.M <= 64) return p.x_fp8 ? launch_pair_t<64, true>(p, stream) : launch_pair_t<64, false>(p, stream);
     return p.x_fp8 ? launch_pair_t<128, true>(p, stream) : launch_pair_t<128, false>(p, stream);
 }
+
+int64_t gate_up_amax_tiles(int64_t M, int64_t N) { return M <= kGateUpMaxM ? (N + 15) / 16 : (N + 127) / 128; }
 
 hipError_t launch_gemm(const MulParams& p, hipStream_t stream) {
     if (p.M == 0 || p.N == 0) return hipSuccess;

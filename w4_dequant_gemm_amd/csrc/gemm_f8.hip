@@ -176,8 +176,11 @@ __global__ void __launch_bounds__(f8::NT) gemm_f8_kernel(MulParams p) {
         // stages apart and would wait for every pending direct-to-LDS load
         // before any LDS read.  No register result (the data goes to LDS at
         // M0 + 16 lane); completion is covered by the wait at each step's end.
-        const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-            static_cast<uint32_t>(reinterpret_cast<uintptr_t>(stage + (wave * ADMA + it) * 1024)));
+        // the LDS byte address, as a uniform value (scalar arithmetic on the
+        // stage's constant address)
+        typedef __attribute__((address_space(3))) uint8_t lds_u8;
+        const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u8*)stage)) +
+                            static_cast<uint32_t>((wave * ADMA + it) * 1024);
         asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
                      ::"v"(voff), "s"(a_rsrc), "s"(m0), "s"(soff) : "memory", "m0");
     };
@@ -268,8 +271,6 @@ __global__ void __launch_bounds__(f8::NT) gemm_f8_kernel(MulParams p) {
         return int8x_t{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]), static_cast<int>(lo[3]),
                        static_cast<int>(hi[0]), static_cast<int>(hi[1]), static_cast<int>(hi[2]), static_cast<int>(hi[3])};
     };
-    const int8x_t ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                          0x38383838, 0x38383838, 0x38383838, 0x38383838};   // E4M3 1.0
 
     constexpr int kStepLoads = ADMA + BLOAD;
     auto step_end3 = [&]() {
@@ -294,7 +295,14 @@ __global__ void __launch_bounds__(f8::NT) gemm_f8_kernel(MulParams p) {
 #define W4_F8_TROT 2
 #endif
     constexpr int TROT = W4_F8_TROT;   // group sums in flight: a block is scaled TROT - 1 slots after its MFMA
-    constexpr int CONV_EVERY = NSLOT / NCONV, LOAD_EVERY = NSLOT / BLOAD, DMA_EVERY = NSLOT / ADMA;
+#ifndef W4_F8_CONV0
+#define W4_F8_CONV0 1
+#endif
+    // conversion items from slot CONV0 on, spread evenly over the rest of the
+    // step (a later start leaves the codes loaded a step before more time to arrive)
+    constexpr int CONV0 = W4_F8_CONV0;
+    constexpr int CONV_EVERY = (NSLOT - CONV0) / NCONV, LOAD_EVERY = NSLOT / BLOAD, DMA_EVERY = NSLOT / ADMA;
+    static_assert(CONV_EVERY >= 1, "conversion slots");
     auto step3 = [&](int kt, auto SA, Regs& next, const Regs& ready, const BOps& cur, BOps& nxt) {
         constexpr int sa = decltype(SA)::value;
         const uint8_t* As = stage_a(std::integral_constant<int, sa>{});
@@ -309,7 +317,8 @@ __global__ void __launch_bounds__(f8::NT) gemm_f8_kernel(MulParams p) {
             // the fragment is reloaded for the next row block right after its last use
             if (cb == CB - 1 && rb + 1 < RB) fa = frag_a(As, rb + 1);
             if (u >= TROT - 1) scale_add(u - (TROT - 1), cur, T[(u - (TROT - 1)) % TROT]);
-            if (u % CONV_EVERY == 1 % CONV_EVERY) conv_item(u / CONV_EVERY, ready, nxt);
+            if (u >= CONV0 && (u - CONV0) % CONV_EVERY == 0 && (u - CONV0) / CONV_EVERY < NCONV)
+                conv_item((u - CONV0) / CONV_EVERY, ready, nxt);
             if (u % LOAD_EVERY == LOAD_EVERY / 2 - 1) {
                 load_item(kt + 2, next, u / LOAD_EVERY);
                 asm volatile("" ::: "memory");
@@ -325,6 +334,9 @@ __global__ void __launch_bounds__(f8::NT) gemm_f8_kernel(MulParams p) {
             Regs rz;
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) load_item(kt, rz, CB + cb);
+            // E4M3 1.0 in every byte, made here (kept out of the loop's registers)
+            const int one = static_cast<int>(opaque_vgpr(0x38383838u));
+            const int8x_t ones = {one, one, one, one, one, one, one, one};
             float corr[CB];
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) {

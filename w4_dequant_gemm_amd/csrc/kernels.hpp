@@ -44,6 +44,10 @@ struct RowQuantParams {
     uint8_t* xq;             // [M, K] e4m3
     float* xscale;           // [M]
     uint16_t* xw = nullptr;  // [M, K] the same codes widened exactly to bf16, or null
+    // the rows' maxima of |x| already known as partial maxima [M][amax_tiles]
+    // (written by the product that produced X), or null: scan X for them
+    const float* amax_part = nullptr;
+    int64_t amax_tiles = 0;
 };
 hipError_t launch_rowquant(const RowQuantParams& p, hipStream_t stream);
 
@@ -84,10 +88,18 @@ struct MulParams {
     const uint32_t* wq2 = nullptr;
     const uint32_t* sz2 = nullptr;
     int act = 0;
+    // gate and up (W4A8): each workgroup also writes the maximum of |H| over
+    // its columns of every row to amax_part [M][amax_tiles] (tile = its
+    // column tile), for the row quantization of H that follows
+    float* amax_part = nullptr;
+    int64_t amax_tiles = 0;
 };
 // largest M of the streaming kernel's gate and up pass; above it the tiled
 // pair GEMM (K a multiple of 64) takes the fused product
 constexpr int64_t kGateUpMaxM = 32;
+// column tiles of the W4A8 gate and up pass (the partial row maxima of H it
+// writes per row): 16 columns in the streaming kernel, 128 in the tiled one
+int64_t gate_up_amax_tiles(int64_t M, int64_t N);
 // Which kernel runs a product: M <= kSkinnyMaxM: the weight-streaming
 // kernels (dot form for one or two rows, MFMA form above); larger M: the
 // tiled MFMA GEMM (64 x 128 tiles up to 128 rows, 256 x 256 above; 128 x 128

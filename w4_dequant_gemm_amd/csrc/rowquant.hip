@@ -7,7 +7,8 @@
 // another row resolution, and an all-zero row stays exactly zero.
 //
 // One 256-thread block per row: a max reduction (wavefront butterfly, then
-// LDS across the 4 waves), then a second pass over the row that divides
+// LDS across the 4 waves) over the row, or over the partial row maxima its
+// producer left (the fused gate and up pass), then a pass over the row that divides
 // (IEEE, correctly rounded), clamps to +-448 and converts pairs with
 // v_cvt_pk_fp8_f32 (OCP E4M3 on gfx950).  Rows are read 16 bytes per lane.
 #include "device.hpp"
@@ -25,13 +26,19 @@ __global__ void __launch_bounds__(256) rowquant_kernel(RowQuantParams p) {
     const uint4* x = reinterpret_cast<const uint4*>(p.X + m * p.K);
 
     float amax = 0.0f;
-    for (int64_t i = threadIdx.x; i < K8; i += blockDim.x) {
-        const uint4 v = x[i];
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    if (p.amax_part) {
+        // the producer of X left the row's maximum in partial maxima
+        const float* part = p.amax_part + m * p.amax_tiles;
+        for (int64_t i = threadIdx.x; i < p.amax_tiles; i += blockDim.x) amax = fmaxf(amax, part[i]);
+    } else {
+        for (int64_t i = threadIdx.x; i < K8; i += blockDim.x) {
+            const uint4 v = x[i];
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            amax = fmaxf(amax, fabsf(bf16_lo(w[j])));
-            amax = fmaxf(amax, fabsf(bf16_hi(w[j])));
+            for (int j = 0; j < 4; ++j) {
+                amax = fmaxf(amax, fabsf(bf16_lo(w[j])));
+                amax = fmaxf(amax, fabsf(bf16_hi(w[j])));
+            }
         }
     }
     amax = wave_max(amax);

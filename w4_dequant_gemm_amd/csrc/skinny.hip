@@ -585,9 +585,18 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
                     u += red_base[w * TILE + row * 16 * FJ + 16 + cc];
                 }
                 const int64_t n = n0 + cc;
+                float hv = 0.0f;
                 if (row < M && n < N) {
                     const float r = row_factor(row);
-                    p.Y[static_cast<int64_t>(row) * N + n] = float_to_bf16_bits(activation(p.act, g * r) * (u * r));
+                    const uint16_t hb = float_to_bf16_bits(activation(p.act, g * r) * (u * r));
+                    p.Y[static_cast<int64_t>(row) * N + n] = hb;
+                    hv = fabsf(bf16_lo(hb));
+                }
+                if (p.amax_part) {
+                    // the row's maximum |H| over this workgroup's 16 columns
+                    // (16 consecutive threads hold one row)
+                    hv = max16(hv);
+                    if (cc == 0 && row < M) p.amax_part[static_cast<int64_t>(row) * p.amax_tiles + blockIdx.x] = hv;
                 }
             }
             return;
@@ -626,9 +635,16 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
                 u += red[w * TILE + row * 16 * FJ + 16 + cc];
             }
             const int64_t n = n0 + cc;
+            float hv = 0.0f;
             if (row < M && n < N) {
                 const float r = XF8 ? p.xscale[row] : 1.0f;
-                p.Y[static_cast<int64_t>(row) * N + n] = float_to_bf16_bits(activation(p.act, g * r) * (u * r));
+                const uint16_t hb = float_to_bf16_bits(activation(p.act, g * r) * (u * r));
+                p.Y[static_cast<int64_t>(row) * N + n] = hb;
+                hv = fabsf(bf16_lo(hb));
+            }
+            if (p.amax_part) {
+                hv = max16(hv);
+                if (cc == 0 && row < M) p.amax_part[static_cast<int64_t>(row) * p.amax_tiles + blockIdx.x] = hv;
             }
         }
         return;
