@@ -266,14 +266,30 @@ def main():
             h8 = h[:M8]
             xq8 = torch.empty((M8, Ku), dtype=torch.uint8, device=dev)
             xs8 = torch.empty((M8,), dtype=torch.float32, device=dev)
+            hq8 = torch.empty((M8, Nu), dtype=torch.uint8, device=dev)
+            hs8 = torch.empty((M8,), dtype=torch.float32, device=dev)
+            wse = torch.empty((max(w4.w4a8_gate_up_workspace_bytes(M8, Ku, Nu), 16),), dtype=torch.uint8, device=dev)
 
             def fused8(x8=x8, h8=h8, xq8=xq8, xs8=xs8):
                 w4.w4a8_gate_up(x8, ups[0], ups[1], G, "silu", H=h8, xq=xq8, xscale=xs8)
+
+            def fused8e(x8=x8, h8=h8, xq8=xq8, xs8=xs8, hq8=hq8, hs8=hs8, wse=wse):
+                w4.w4a8_gate_up(x8, ups[0], ups[1], G, "silu", H=h8, xq=xq8, xscale=xs8, hq=hq8, hscale=hs8,
+                                workspace=wse)
+
+            def fused8_rq(x8=x8, h8=h8, xq8=xq8, xs8=xs8, hq8=hq8, hs8=hs8):
+                w4.w4a8_gate_up(x8, ups[0], ups[1], G, "silu", H=h8, xq=xq8, xscale=xs8)
+                w4.w4_quantize_rows_e4m3(h8, xq=hq8, xscale=hs8)
             ms8 = timer.time(fused8, 10, 3)
+            ms8e = timer.time(fused8e, 10, 3)
+            ms8r = timer.time(fused8_rq, 10, 3)
             fl8 = 2 * 2.0 * M8 * Nu * Ku
-            extra[f"w4a8_gate_up_8b_m{M8}"] = {"ms": round(ms8, 4), "TFLOP/s": round(fl8 / (ms8 * 1e-3) / 1e12, 1)}
-            log(f"[bench] W4A8 8B gate+up M={M8}: fused {ms8:.3f} ms ({fl8/(ms8*1e-3)/1e12:.1f} TFLOP/s, incl. row quant)")
-        del x, h, ya, yb, ws, x8, h8, xq8, xs8
+            extra[f"w4a8_gate_up_8b_m{M8}"] = {"ms": round(ms8, 4), "TFLOP/s": round(fl8 / (ms8 * 1e-3) / 1e12, 1),
+                                               "with_e4m3_H_ms": round(ms8e, 4),
+                                               "then_row_quantizer_on_H_ms": round(ms8r, 4)}
+            log(f"[bench] W4A8 8B gate+up M={M8}: fused {ms8:.3f} ms ({fl8/(ms8*1e-3)/1e12:.1f} TFLOP/s, incl. row "
+                f"quant); emitting E4M3 H {ms8e:.3f} ms; row quantizer on H after it {ms8r:.3f} ms")
+        del x, h, ya, yb, ws, x8, h8, xq8, xs8, hq8, hs8, wse
 
         # NF4 comparator at M = 1: the same up/down weights in NF4 (blocks of
         # 64, double-quantized scales), same rotation of copies
@@ -358,6 +374,38 @@ def main():
             del copies, base
             torch.cuda.empty_cache()
 
+    if args.only in ("all", "extra"):
+        # the small workloads (tiny, SmolLM2 MLP) and the quantizer on every
+        # workload: times only (launch-latency sized, no roofline claim)
+        for name, wl in synth.WORKLOADS.items():
+            if name == "llama70b_prefill":
+                continue
+            fr = tuple(float(f) for f in synth.workload_fracs(wl))
+            for idx, (N, K) in enumerate(wl.shapes):
+                Wt = torch.from_numpy(synth.weight(wl, idx)).to(dev)
+                for mode in wl.modes:
+                    out = w4.w4_quantize_blockwise(Wt, wl.group, mode, fr)
+
+                    def qrun(mode=mode, out=out):
+                        w4.w4_quantize_blockwise(Wt, wl.group, mode, fr, packed=out["packed"], scale=out["scale"],
+                                                 zero=out["zero"], clip_idx=out["clip_idx"])
+                    msq = timer.time(qrun, 20, 3)
+                    extra[f"quantize_{name}_{idx}_{mode}_n{len(fr)}"] = {
+                        "us": round(msq * 1e3, 2), "weights_per_s": round(N * K / (msq * 1e-3), 0)}
+                    if name in ("tiny", "smollm2_135m_mlp"):
+                        pk = w4.w4_prepack(out["packed"], out["scale"], out["zero"], wl.group, mode)
+                        for M in wl.ms:
+                            x = bf16(synth.activations_bf16_bits(wl, M, K))
+                            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+                            msm = timer.time(lambda: w4.w4a16_gemm(x, pk["wq"], pk["sz"], wl.group, Y=y), 50, 5)
+                            extra[f"w4a16_{name}_{idx}_{mode}_m{M}"] = {
+                                "us": round(msm * 1e3, 2),
+                                "GB/s": round(mul_bytes(M, N, K, wl.group) / (msm * 1e-3) / 1e9, 1)}
+                            log(f"[bench] {name}[{idx}] {mode} M={M}: {msm*1e3:.2f} us")
+                    del out
+                del Wt
+        torch.cuda.empty_cache()
+
     # ------------------------------------------------ 70B prefill GEMM + quantizer
     if args.only in ("all", "gemm", "quant"):
         wl70 = synth.WORKLOADS["llama70b_prefill"]
@@ -429,8 +477,15 @@ def main():
                                        "kernel": "gemm256_breg_kernel<false> + splitk_reduce_kernel<256, 256> (the whole W4A16 "
                                                  "call, M=2048: 768 tiles whole, the last 128 in two K halves)",
                                        "flops_per_launch": flops, "avg_launch_us": round(ms16 * 1e3, 1)}
+            result["roofline_w4a8"] = {"bound": "mfma", "achieved": round(t8, 1), "peak": FP8_PEAK_TFLOPS,
+                                       "unit": "TFLOP/s", "frac": round(t8 / FP8_PEAK_TFLOPS, 4),
+                                       "traffic": measured_traffic("gemm_f8_w4a8_70b_m2048"),
+                                       "kernel": "rowquant_kernel + gemm_f8_kernel + splitk_reduce_kernel<256, 256> "
+                                                 "(the whole W4A8 call, M=2048: fp8 MFMA 16x16x128 on E4M3 "
+                                                 "activations and exact u - z weight operands)",
+                                       "flops_per_launch": flops, "avg_launch_us": round(ms8 * 1e3, 1)}
             log(f"[bench] 70B GEMM M=2048: W4A16 {ms16:.3f} ms = {t16:.1f} TFLOP/s; "
-                f"W4A8 {ms8:.3f} ms = {t8:.1f} TFLOP/s")
+                f"W4A8 {ms8:.3f} ms = {t8:.1f} TFLOP/s ({t8 / FP8_PEAK_TFLOPS:.3f} of the fp8 peak)")
 
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib * (1 << 20) // 4
@@ -466,6 +521,7 @@ def main():
                    "step_bytes": result.get("step_bytes")},
         "roofline": result.get("roofline"),
         "roofline_gemm": result.get("roofline_gemm"),
+        "roofline_w4a8": result.get("roofline_w4a8"),
         "cpu_baseline": cpu,
         "extra": extra,
     }
@@ -501,8 +557,64 @@ def cpu_baseline(seconds: float):
     gbs = total_bytes / el / 1e9
     log(f"[bench] CPU oracle: {reps} x (up + down) in {el:.2f} s = {gbs:.3f} GB/s on {oracle.num_threads()} threads")
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{reps} decode passes (M=1) through one 8B up+down layer pair, float64 oracle product "
-                      f"({el:.1f} s)"}
+                      f"({el:.1f} s)",
+            "per_config": cpu_per_config()}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_per_config():
+    """The oracle on every workload: its quantizer (with the workload's clip
+    search) and its float64 product at every M, each on a bounded row sample,
+    reported as seconds for the whole call (sample time scaled by the sampled
+    fraction of rows) next to the sample that was timed."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    def timed(fn, min_s=0.05):
+        n, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= min_s:
+                return el / n
+    out = {}
+    for name, wl in synth.WORKLOADS.items():
+        fr = synth.workload_fracs(wl)
+        for idx, (N, K) in enumerate(wl.shapes):
+            # quantizer: up to 2^21 weights of whole rows
+            rows = max(1, min(N, (1 << 21) // K))
+            W = synth.weight(wl, idx, rows=rows)
+            for mode in wl.modes:
+                t = timed(lambda: oracle.quantize(W, wl.group, mode, fracs=fr))
+                out[f"{name}_{idx}_quantize_{mode}_n{len(fr)}"] = {
+                    "cpu_s_full": round(t * N / rows, 6), "sample_rows": rows, "rows": N}
+            q = oracle.quantize(W, wl.group, wl.modes[-1], fracs=fr)
+            del W
+            for M in wl.ms:
+                # product: at most 2^26 multiply-adds of the sample (whole sampled weight rows)
+                mr = max(1, min(M, (1 << 26) // (rows * K)))
+                X = oracle.bf16_bits_to_f64(synth.activations_bf16_bits(wl, mr, K))
+                t = timed(lambda: oracle.gemm_ref(X, q["packed"], q["scale"], q["zero"], wl.group, wl.modes[-1]))
+                full = t * (M / mr) * (N / rows)
+                out[f"{name}_{idx}_product_m{M}"] = {"cpu_s_full": round(full, 6), "sample_rows_x_cols": [mr, rows],
+                                                     "shape": [M, N, K]}
+    log(f"[bench] CPU oracle per workload: {len(out)} entries")
+    return out
 
 
 if __name__ == "__main__":
