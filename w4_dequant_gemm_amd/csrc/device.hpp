@@ -104,6 +104,22 @@ __device__ __forceinline__ TiledRow tiled_row(const uint32_t* wq, const uint32_t
     return r;
 }
 
+// XCD-aware order of whole output tiles.  Workgroups are handed to the 8
+// XCDs (each with its own L2) round-robin by workgroup index, so workgroup b
+// runs on XCD b % 8.  Of T tiles, the first T8 = 8 floor(T / 8) are dealt as
+// tile = (b % 8) (T8 / 8) + b / 8, which gives each XCD one contiguous range
+// of the row-major tile grid (its workgroups share activation row panels and
+// neighbouring weight panels in their L2); the last T - T8 keep their index.
+// A bijection on 0 .. T - 1.
+#ifndef W4_XCD_RASTER
+#define W4_XCD_RASTER 1
+#endif
+__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t T) {
+    const int64_t T8 = T & ~int64_t{7};
+    if (!W4_XCD_RASTER || b >= T8) return b;
+    return (b & 7) * (T8 >> 3) + (b >> 3);
+}
+
 // Activation of the gate projection in a gated MLP: SiLU x / (1 + e^-x)
 // (SwiGLU) or the tanh form of GELU, 0.5 x (1 + tanh(sqrt(2/pi) (x +
 // 0.044715 x^3))) (GeGLU), in fp32.

@@ -254,7 +254,7 @@ __device__ __forceinline__ TileJob tile_job(const MulParams& p) {
     TileJob t;
     int64_t tile;
     if (b < p.split_t0) {
-        tile = b;
+        tile = xcd_tile(b, p.split_t0);
         t.kb = 0;
         t.KT = KT_all;
         t.part = -1;
@@ -513,7 +513,7 @@ __device__ __forceinline__ big::TileJob tile_job_t(const MulParams& p) {
     big::TileJob t;
     int64_t tile;
     if (b < p.split_t0) {
-        tile = b;
+        tile = xcd_tile(b, p.split_t0);
         t.kb = 0;
         t.KT = KT_all;
         t.part = -1;
@@ -777,9 +777,10 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_mid_kernel(MulParams p) {
 // W4A16, M > 128: activations straight from global memory into LDS, weights
 // dequantized straight into MFMA operands.
 //
-// 256 x 256 tile, K step 64, four waves side by side: wave w owns output
-// columns 64 w .. 64 w + 63 for all 256 rows (8 x 2 blocks of
-// v_mfma_f32_32x32x16_bf16, 256 accumulators).  The bf16 activations never
+// 256 x 256 tile, K step 64, NW waves side by side: wave w owns output
+// columns 256 / NW of all 256 rows (NW = 4: 8 x 2 blocks of
+// v_mfma_f32_32x32x16_bf16, 256 accumulators, one wave per SIMD; NW = 8:
+// 8 x 1 blocks, 128 accumulators, two waves per SIMD).  The bf16 activations never
 // pass through registers: each wave issues global_load_lds_dwordx4 (lane l's
 // 16 bytes land at the instruction's LDS base + 16 l) two K steps ahead into
 // the free one of three 32 KB activation stages (chunk swizzle (row ^ row >>
@@ -806,20 +807,31 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_mid_kernel(MulParams p) {
 // w's gate sums register for register; after the loop both pass through LDS
 // in register order and H = bf16(act(gate) * up).  No K split.
 namespace breg {
-constexpr int BM = 256, BN = 256, BK = 64, NW = 4, NT = 64 * NW;
+constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int STAGE = BM * BK;                    // bf16 elements per activation stage
-constexpr int ADMA = BM * BK * 2 / (1024 * NW);   // direct-to-LDS loads per wave and step (8)
-constexpr int FJ = 2;                             // 32-column blocks per wave
-constexpr int BLOAD = 2 * FJ;                     // code and scale/zero loads per lane and step
+// NW waves side by side, each owning BN / NW columns (FJ 32-column blocks):
+// four waves of 64 columns (one per SIMD, 256 accumulators), or eight of 32
+// (two per SIMD, 128 accumulators: one wave's dequantization runs while the
+// other's MFMAs do)
+template <int NW>
+struct Geom {
+    static constexpr int NT = 64 * NW;
+    static constexpr int ADMA = BM * BK * 2 / (1024 * NW);   // direct-to-LDS loads per wave and step
+    static constexpr int FJ = BN / (32 * NW);                 // 32-column blocks per wave
+    static constexpr int BLOAD = 2 * FJ;                      // code and scale/zero loads per lane and step
+};
 #ifndef W4_DSWZ
 #define W4_DSWZ 3
 #endif
 __device__ __forceinline__ int swz(int row) { return big::swizzle_fn(W4_DSWZ, row); }
 }  // namespace breg
 
-template <bool PAIR>
-__global__ void __launch_bounds__(breg::NT) gemm256_breg_kernel(MulParams p) {
+template <bool PAIR, int NW = 4>
+__global__ void __launch_bounds__(64 * NW) gemm256_breg_kernel(MulParams p) {
     using namespace breg;
+    static_assert(!PAIR || NW == 4, "the pair form pairs waves w and w + 2");
+    constexpr int NT = Geom<NW>::NT, ADMA = Geom<NW>::ADMA, FJ = Geom<NW>::FJ, BLOAD = Geom<NW>::BLOAD;
+    constexpr int WNC = BN / NW;                      // columns per wave
     constexpr int FI = 8;
     __shared__ __attribute__((aligned(16))) uint16_t lds_a0[STAGE];
     __shared__ __attribute__((aligned(16))) uint16_t lds_a1[STAGE];
@@ -873,7 +885,7 @@ __global__ void __launch_bounds__(breg::NT) gemm256_breg_kernel(MulParams p) {
     // waves 2 and 3), clamped to N - 1 (its outputs are not stored); 32-k
     // chunk 2 kt + h of step kt
     const bool b_up = PAIR && wave >= 2;
-    const int wcol = PAIR ? 64 * (wave & 1) : 64 * wave;
+    const int wcol = PAIR ? 64 * (wave & 1) : WNC * wave;
     TiledRow brow[FJ];
 #pragma unroll
     for (int jb = 0; jb < FJ; ++jb) {
@@ -895,9 +907,11 @@ __global__ void __launch_bounds__(breg::NT) gemm256_breg_kernel(MulParams p) {
         u32x4_t b[BK / 16][FJ];
     };
     const uint32_t bias16 = opaque_vgpr(0x64006400u);
-    PairDequant dq[FJ] = {PairDequant{bias16}, PairDequant{bias16}};
+    PairDequant dq[FJ];
+#pragma unroll
+    for (int jb = 0; jb < FJ; ++jb) dq[jb] = PairDequant{bias16};
     auto b_pair = [&](int pr, const Regs& r, BOps& o) {
-        const int kk = pr >> 3, jb = (pr >> 2) & 1, i = pr & 3;
+        const int kk = pr / (4 * FJ), jb = (pr / 4) % FJ, i = pr % 4;
         if (kk == 0 && i == 0) dq[jb].group(r.s[jb]);
         o.b[kk][jb][i] = dq[jb].pair(r.q[jb][kk], i);
     };
@@ -921,7 +935,7 @@ __global__ void __launch_bounds__(breg::NT) gemm256_breg_kernel(MulParams p) {
         for (int i = 0; i < FI; ++i) a[i] = frag_a(A, kk, i);
     };
     constexpr int NSLOT = FI * FJ * (BK / 16);
-    static_assert(NSLOT == 64 && 4 * ADMA <= NSLOT && 4 * BLOAD <= NSLOT && NSLOT / 2 == 4 * FJ * (BK / 16), "slot plan");
+    static_assert(4 * ADMA <= NSLOT && 4 * BLOAD <= NSLOT && NSLOT / 2 == 4 * FJ * (BK / 16), "slot plan");
 
     constexpr int kStepLoads = ADMA + BLOAD;
     auto step_end3 = [&]() {
@@ -1051,7 +1065,7 @@ __global__ void __launch_bounds__(breg::NT) gemm256_breg_kernel(MulParams p) {
         }
 #pragma unroll
         for (int j = 0; j < FJ; ++j) {
-            const int lc = 64 * wave + 32 * j + (lane & 31);
+            const int lc = WNC * wave + 32 * j + (lane & 31);
             const int64_t col = n_base + lc;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -1191,6 +1205,13 @@ size_t gemm_xw_bytes(int64_t M, int64_t K, int64_t N) {
 #define W4_BIG_WN 2
 #endif
 constexpr int kBigWM = W4_BIG_WM, kBigWN = W4_BIG_WN;
+// Waves of the W4A16 256 x 256 kernel: eight of 32 columns (two per SIMD)
+// up to this many output tiles, four of 64 (one per SIMD) above.  Measured
+// on one MI355X: 12B up at M = 1024 (240 tiles) 118 us with eight against
+// 126 us with four; the 70B shape at M = 2048 (896 tiles) 823 against 817 us.
+#ifndef W4_BREG_NW8_MAX_TILES
+#define W4_BREG_NW8_MAX_TILES 512
+#endif
 
 template <int TBM, bool XF8>
 hipError_t launch_mid(const MulParams& p, hipStream_t stream) {
@@ -1246,7 +1267,8 @@ hipError_t launch_gemm_pair(const MulParams& p, hipStream_t stream) {
         q.splits = 1;
         q.split_t0 = tiles;
         q.ws = nullptr;
-        hipLaunchKernelGGL(gemm256_breg_kernel<true>, dim3(static_cast<unsigned>(tiles)), dim3(breg::NT), 0, stream, q);
+        hipLaunchKernelGGL((gemm256_breg_kernel<true, 4>), dim3(static_cast<unsigned>(tiles)), dim3(breg::Geom<4>::NT), 0,
+                           stream, q);
         return hipGetLastError();
     }
     if (p.M <= 64) return p.x_fp8 ? launch_pair_t<64, true>(p, stream) : launch_pair_t<64, false>(p, stream);
@@ -1283,11 +1305,17 @@ hipError_t launch_gemm(const MulParams& p, hipStream_t stream) {
             // W4A8 on the widened activations: the bf16 kernel, row scales in
             // its epilogue (or in the split sum)
             q.X = q.xw;
-            hipLaunchKernelGGL(gemm256_breg_kernel<false>, grid, dim3(breg::NT), 0, stream, q);
+            if (tiles <= W4_BREG_NW8_MAX_TILES)
+                hipLaunchKernelGGL((gemm256_breg_kernel<false, 8>), grid, dim3(breg::Geom<8>::NT), 0, stream, q);
+            else
+                hipLaunchKernelGGL((gemm256_breg_kernel<false, 4>), grid, dim3(breg::Geom<4>::NT), 0, stream, q);
         } else if (q.x_fp8) {
             hipLaunchKernelGGL((gemm256_kernel<kBigWM, kBigWN, true>), grid, dim3(64 * kBigWM * kBigWN), 0, stream, q);
         } else {
-            hipLaunchKernelGGL(gemm256_breg_kernel<false>, grid, dim3(breg::NT), 0, stream, q);
+            if (tiles <= W4_BREG_NW8_MAX_TILES)
+                hipLaunchKernelGGL((gemm256_breg_kernel<false, 8>), grid, dim3(breg::Geom<8>::NT), 0, stream, q);
+            else
+                hipLaunchKernelGGL((gemm256_breg_kernel<false, 4>), grid, dim3(breg::Geom<4>::NT), 0, stream, q);
         }
         if (q.splits > 1 && q.split_t0 < tiles) {
             const hipError_t e = hipGetLastError();

@@ -18,8 +18,9 @@
 // runs under the other's MFMAs.
 //
 // The E4M3 activations go straight from global memory into LDS
-// (global_load_lds_dwordx4 into three 32 KB stages, two steps ahead; the
-// 16-byte chunk c of stage row r sits at position c ^ (r & 7)).  The weights
+// (buffer_load_dwordx4 ... lds into three 32 KB stages, two steps ahead; the
+// 16-byte chunk c of stage row r sits at position c ^ ((r >> 1) & 7), so the
+// 16 rows of a fragment read spread over all 64 banks).  The weights
 // never pass through LDS: for a 16-column block, lane (c, q) loads the 16
 // bytes of 32-k tile 4 kt + q of its column (the 64 lanes read one contiguous
 // 1 KB of the blocked layout), two steps ahead, and converts them one step
@@ -78,7 +79,7 @@ __device__ __forceinline__ F8Job f8_job(const MulParams& p) {
     F8Job t;
     int64_t tile;
     if (b < p.split_t0) {
-        tile = b;
+        tile = xcd_tile(b, p.split_t0);
         t.kb = 0;
         t.KT = KT_all;
         t.part = -1;
@@ -160,17 +161,19 @@ __global__ void __launch_bounds__(f8::NT) gemm_f8_kernel(MulParams p) {
         for (int j = 0; j < CB; ++j) acc[i][j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
     // activations: load `it` of this wave fills stage rows 8 (wave ADMA + it)
-    // .. + 7; lane l writes row + l / 8 at chunk position l % 8, so it loads
-    // the chunk that the swizzle puts there, (l % 8) ^ (row & 7) (row & 7 is
-    // l / 8).  Buffer loads with a 32-bit lane offset: rows past M lie past
-    // the buffer's end and read as zeros (their outputs are never stored).
+    // .. + 7; lane l writes row r = 8 (wave ADMA + it) + l / 8 at chunk
+    // position l % 8, so it loads the chunk the swizzle puts there,
+    // (l % 8) ^ ((r >> 1) & 7) = (l % 8) ^ (l / 16) ^ (4 if wave ADMA + it is
+    // odd).  Buffer loads with a 32-bit lane offset: rows past M lie past the
+    // buffer's end and read as zeros (their outputs are never stored).
+    static_assert(ADMA % 2 == 0, "the chunk swizzle of a load depends on its parity only");
     const int a_row0 = 8 * wave * ADMA + (lane >> 3);
-    const int a_chunk = (lane & 7) ^ (lane >> 3);
+    const int a_chunk = (lane & 7) ^ (lane >> 4);
     const u32x4_t a_rsrc = buffer_rsrc(p.X, static_cast<uint32_t>(M * K));
     const uint32_t a_voff = static_cast<uint32_t>((m_base + a_row0) * K + a_chunk * 16);
     auto dma_item = [&](int kt, uint8_t* stage, int it) {
         kt = (kt < KT ? kt : KT - 1) + kb;
-        const uint32_t voff = a_voff + static_cast<uint32_t>(8 * it * K);
+        const uint32_t voff = (a_voff ^ ((it & 1) ? 64u : 0u)) + static_cast<uint32_t>(8 * it * K);
         const uint32_t soff = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(kt * BK));
         // Issued as plain instructions: the compiler cannot tell the three
         // stages apart and would wait for every pending direct-to-LDS load
@@ -263,8 +266,9 @@ __global__ void __launch_bounds__(f8::NT) gemm_f8_kernel(MulParams p) {
     };
 
     // A fragment of row block rb: stage row 16 rb + c, chunks 2 q and 2 q + 1
-    const uint32_t aoff0 = static_cast<uint32_t>(c * BK + 16 * ((2 * q) ^ (c & 7)));
-    const uint32_t aoff1 = static_cast<uint32_t>(c * BK + 16 * ((2 * q + 1) ^ (c & 7)));
+    // (swizzle ((16 rb + c) >> 1) & 7 = c >> 1, the same for every rb)
+    const uint32_t aoff0 = static_cast<uint32_t>(c * BK + 16 * ((2 * q) ^ (c >> 1)));
+    const uint32_t aoff1 = static_cast<uint32_t>(c * BK + 16 * ((2 * q + 1) ^ (c >> 1)));
     auto frag_a = [&](const uint8_t* A, int rb) -> int8x_t {
         const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(A + rb * (16 * BK) + aoff0);
         const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(A + rb * (16 * BK) + aoff1);
