@@ -64,6 +64,7 @@ def parse():
 # Source files that define the GEMV and GEMM kernels; a measured traffic figure
 # is used only while these files are unchanged since it was taken.
 KERNEL_SOURCES = ("w4_dequant_gemm_amd/csrc/skinny.hip", "w4_dequant_gemm_amd/csrc/gemm.hip",
+                  "w4_dequant_gemm_amd/csrc/gemm_f8.hip", "w4_dequant_gemm_amd/csrc/rowquant.hip",
                   "w4_dequant_gemm_amd/csrc/device.hpp", "w4_dequant_gemm_amd/csrc/kernels.hpp")
 
 

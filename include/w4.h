@@ -167,10 +167,10 @@ int w4_quantize_rows_e4m3(const uint16_t* X, int64_t M, int64_t K, uint8_t* xq, 
 
 /*
  * w4_gemm_workspace_bytes -- bytes of device workspace for the fastest
- * schedule of w4a16_gemm and w4a8_gemm on a product of M rows, reduction K
- * and N outputs (the scratch of the products that gowda.ai "LLM fast
- * inference", "Achievement 2", defines; FP32 partial sums of one output are
- * added in a fixed order): splits * M * N * 4 bytes of fp32 partial sums when the
+ * schedule of w4a16_gemm on a product of M rows, reduction K and N outputs
+ * (the scratch of the products that gowda.ai "LLM fast inference",
+ * "Achievement 2", defines; FP32 partial sums of one output are added in a
+ * fixed order): splits * M * N * 4 bytes of fp32 partial sums when the
  * product splits K across workgroups, else 0.  Above 64 rows the tiled GEMM
  * needs it (a product with few output tiles splits K).  From 3 to 64 rows it
  * is optional: with it, the weight-streaming kernel splits K when its widest
@@ -183,15 +183,21 @@ size_t w4_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
 
 /*
  * w4a8_gemm_workspace_bytes -- bytes of device workspace for the fastest
- * schedule of w4a8_gemm (gowda.ai "LLM fast inference", "Achievement 2"): w4_gemm_workspace_bytes, and above 128 rows (K a
- * multiple of 64, at least 256 output tiles of 256 x 256, i.e. a whole
- * round over the compute units) also room for the row-quantized activations widened
- * exactly to bf16 (M * K * 2 bytes after the split partials, at a 256-byte
- * aligned offset).  With that much, w4a8_gemm runs the bf16 tiled kernel on
- * the widened codes (same products: every finite E4M3 value is a bf16
- * value); with only w4_gemm_workspace_bytes it runs a kernel that widens
- * the E4M3 codes itself.  Both are exact widenings of the same activations;
- * results may differ in the fp32 summation order only.
+ * schedule of w4a8_gemm and w4a8_gemm_e4m3 with any group size (gowda.ai
+ * "LLM fast inference", "Achievement 2"), the larger of:
+ *  - groups of 128 or whole rows, K a multiple of 128, more than 32 rows: the
+ *    product runs on the fp8 matrix cores, on output tiles and a K split of
+ *    its own (the fp32 partial tiles of the split; 0 when it does not split);
+ *    this much is then required;
+ *  - other groups: w4_gemm_workspace_bytes, and above 128 rows (K a multiple
+ *    of 64, at least 256 output tiles of 256 x 256, i.e. a whole round over
+ *    the compute units) also room for the row-quantized activations widened
+ *    exactly to bf16 (M * K * 2 bytes after the split partials, at a 256-byte
+ *    aligned offset).  With that much, w4a8_gemm runs the bf16 tiled kernel
+ *    on the widened codes (same products: every finite E4M3 value is a bf16
+ *    value); with only w4_gemm_workspace_bytes it runs a kernel that widens
+ *    the E4M3 codes itself.  Both are exact widenings of the same
+ *    activations; results may differ in the fp32 summation order only.
  */
 size_t w4a8_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
 
@@ -243,12 +249,21 @@ int w4a16_gemm_noalloc(const uint16_t* X, int64_t M, int64_t K, const uint32_t* 
  * W'[n, k]) with fp32 accumulation.  Follows gowda.ai "LLM fast inference",
  * "Achievement 2: 8-bit activations without a calibration set" (per-row
  * dynamic E4M3, FP32 accumulation, the row scale in the epilogue, BF16
- * result).
+ * result).  With groups of 128 (or whole rows), K a multiple of 128 and more
+ * than 32 rows the product runs on the fp8 matrix cores: both MFMA operands
+ * E4M3, each weight as the exact integer u - z, one group per 128-k MFMA
+ * step, its sum scaled by the group scale in fp32.  Otherwise up to 64 rows
+ * the weight-streaming kernel and above them a tiled bf16-MFMA GEMM run on
+ * the E4M3 codes widened exactly to bf16.
  *   X  [M, K] bf16 in.
  *   xq [M, K] bytes and xscale [M] fp32: device buffers the call fills (they
  *      are the operands of the multiply and are left for the caller to read).
- *   workspace: at least w4_gemm_workspace_bytes(M, K, N) where that is
- *      required; w4a8_gemm_workspace_bytes(M, K, N) for the fastest schedule.
+ *   workspace: w4a8_gemm_workspace_bytes(M, K, N) bytes always suffice.
+ *      The least accepted is the fp32 partials of the kernel that runs: on
+ *      the fp8 kernel (groups of 128 or whole rows, K a multiple of 128, more
+ *      than 32 rows) those of its own K split, otherwise
+ *      w4_gemm_workspace_bytes(M, K, N) where that is required.  Too small or
+ *      NULL when needed: W4_EINVAL.
  *   Other arguments as for w4a16_gemm.
  */
 int w4a8_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const uint32_t* sz,
@@ -311,7 +326,7 @@ size_t w4a8_gate_up_workspace_bytes(int64_t M, int64_t K, int64_t N);
  * (gowda.ai "LLM fast inference", "Achievement 2").  Same kernels and result
  * as w4a8_gemm after its row quantization.
  *   xq [M, K] E4M3 bytes in;  xscale [M] fp32 in;  K a multiple of 16.
- *   workspace: as for w4a16_gemm (w4_gemm_workspace_bytes).
+ *   workspace: as for w4a8_gemm.
  *   Other arguments as for w4a8_gemm.
  */
 int w4a8_gemm_e4m3(const uint8_t* xq, const float* xscale, int64_t M, int64_t K, const uint32_t* wq,

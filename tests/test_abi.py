@@ -148,18 +148,25 @@ def test_gemm_workspace_sizes_and_checks(lib):
     assert ws(256, 96, 3840) == 0                            # K not a multiple of 64: 128 x 128 tiles
     assert ws(256, 512, 256) == 0                            # too few K steps to split
     assert ws(-1, 512, 256) == 0 and ws(256, 0, 256) == 0
-    # W4A8's fastest schedule above 128 rows (K % 64 == 0) with at least 256
-    # output tiles adds the widened activations, M * K * 2 bytes at a
-    # 256-byte aligned offset after the partials; elsewhere it is the same as
-    # the required workspace
+    # W4A8: the larger of the fp8 kernel's schedule (groups of 128, K a
+    # multiple of 128, above 32 rows) and the bf16 kernels' (w4_gemm_
+    # workspace_bytes, plus the widened activations, M * K * 2 bytes at a
+    # 256-byte aligned offset after the partials, above 128 rows with at
+    # least 256 output tiles of 256 x 256)
     ws8 = lib.w4a8_gemm_workspace_bytes
     assert ws8(2048, 8192, 28672) == 128 * 2 * tile + 2048 * 8192 * 2
     assert ws8(2048, 8192, 32768) == 2048 * 8192 * 2
     assert ws8(300, 4096, 33000) == 2 * 8 * tile + 300 * 4096 * 2       # 258 tiles
     assert ws8(1024, 512, 16384) == 1024 * 512 * 2                       # 256 tiles, none split
-    for shape in ((128, 3840, 15360), (64, 15360, 3840), (16, 14336, 4096), (256, 96, 3840), (1, 4096, 14336),
-                  (256, 15360, 3840), (256, 3840, 15360), (129, 128, 256), (1024, 512, 16128)):
+    # fp8 kernel: 64 x 128 tiles, 30 of them in 8 K ranges
+    assert ws8(64, 15360, 3840) == 30 * 8 * 64 * 128 * 4 > ws(64, 15360, 3840)
+    # 256 x 256 tiles, 30 of them in 8 K ranges
+    assert ws8(1056, 8192, 1500) == 30 * 8 * tile
+    for shape in ((128, 3840, 15360), (16, 14336, 4096), (256, 96, 3840), (1, 4096, 14336),
+                  (256, 15360, 3840), (256, 3840, 15360), (129, 128, 256)):
         assert ws8(*shape) == ws(*shape), shape
+    for shape in ((33, 1024, 1000), (520, 4096, 2000), (700, 2048, 1000), (800, 2048, 5000)):
+        assert ws8(*shape) >= ws(*shape), shape
     assert ws8(-1, 512, 256) == 0 and ws8(256, 512, 0) == 0
     # a shape that needs one: NULL or too small is rejected before any launch
     fake = ctypes.c_void_p(0x1000)

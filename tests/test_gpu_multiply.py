@@ -214,7 +214,7 @@ def test_one_hot_rows_recover_dequantized_weights(case, kind):
         else:
             outs = []
             ws_sizes = [None]
-            if M > 128 and w4.w4a8_gemm_workspace_bytes(M, K, N) > need:
+            if M > 128 and G2 % 128 != 0 and w4.w4a8_gemm_workspace_bytes(M, K, N) > need:
                 ws_sizes.append(max(need, 16))      # the E4M3 kernel instead of the widened copy
             for nb in ws_sizes:
                 ws = None if nb is None else torch.empty((nb,), dtype=torch.uint8, device="cuda")
@@ -332,18 +332,19 @@ def test_split_k_products():
 
 
 def test_w4a8_widened_activations():
-    # above 128 rows, with at least 256 output tiles, a workspace of
-    # w4a8_gemm_workspace_bytes lets the row quantizer also write the E4M3
-    # codes widened to bf16, and the bf16 tiled kernel runs on them (row
-    # scales in its epilogue or split sum); with the required minimum the
-    # E4M3 kernel runs.  Both match the oracle on sampled outputs, with the
-    # same codes and scales: 258 tiles of a ragged N with the last two split
-    # (workspace full of NaNs on entry), 256 whole tiles with G = 64, and the
-    # 12B down shape at M = 256, whose 15 tiles take no widened copy
+    # groups of 32 or 64 (no fp8 kernel): above 128 rows, with at least 256
+    # output tiles, a workspace of w4a8_gemm_workspace_bytes lets the row
+    # quantizer also write the E4M3 codes widened to bf16, and the bf16 tiled
+    # kernel runs on them (row scales in its epilogue or split sum); with the
+    # required minimum the E4M3 kernel runs.  Both match the oracle on
+    # sampled outputs, with the same codes and scales: 258 tiles of a ragged N
+    # with the last two split (workspace full of NaNs on entry) and 256 whole
+    # tiles.  The 12B down shape at M = 256 (groups of 128) takes the fp8
+    # kernel and no widened copy.
     require_gpu()
     import torch
     import w4_dequant_gemm_amd as w4
-    cases = [("258 tiles", synth.normal_matrix(54, 33000, 1024, 0.02), 300, 128, True),
+    cases = [("258 tiles", synth.normal_matrix(54, 33000, 1024, 0.02), 300, 64, True),
              ("256 tiles, G = 64", synth.normal_matrix(55, 16384, 512, 0.02), 1024, 64, True),
              ("12B down", synth.weight(synth.WORKLOADS["gemma12b_w4a8"], 1), 256, 128, False)]
     for name, W, M, G, widened in cases:
@@ -371,6 +372,63 @@ def test_w4a8_widened_activations():
         # the same activations and weights: the two kernels differ only in
         # the fp32 summation order
         assert oracle.frobenius_gap(outs[1].astype(np.float64), outs[0]) <= 1e-3
+
+
+# The fp8 W4A8 kernel's tile shapes, each whole and with a K split (the shape
+# chooses the tile and schedule; the expected one is pinned through the
+# workspace the call requires: its fp32 partial tiles).  Ragged M and N, and
+# K down to two 128-k steps.
+F8_TILE_CASES = [
+    # label, M, K, N, (tile rows, tile columns, tiles, whole tiles, splits)
+    ("256x256 whole", 1024, 256, 8200, (256, 256, 132, 132, 1)),
+    ("256x256 split", 1056, 8192, 1500, (256, 256, 30, 0, 8)),
+    ("128x256 whole", 800, 256, 8200, (128, 256, 231, 231, 1)),
+    ("128x256 split", 520, 4096, 2000, (128, 256, 40, 0, 6)),
+    ("256x128 whole", 800, 256, 5000, (256, 128, 160, 160, 1)),
+    ("256x128 split", 1024, 4096, 2080, (256, 128, 68, 0, 3)),
+    ("256x64 whole", 1024, 256, 2080, (256, 64, 132, 132, 1)),
+    ("256x64 split", 700, 2048, 1000, (256, 64, 48, 0, 4)),
+    ("256x64 last round split", 800, 2048, 5000, (256, 64, 316, 256, 4)),
+    ("64x128 whole", 33, 256, 1000, (64, 128, 8, 8, 1)),
+    ("64x128 split", 33, 1024, 1000, (64, 128, 8, 0, 2)),
+    ("128x64 whole", 400, 1024, 2080, (128, 64, 132, 132, 1)),
+    ("128x64 split", 65, 1024, 1056, (128, 64, 17, 0, 2)),
+]
+
+
+@pytest.mark.parametrize("case", F8_TILE_CASES, ids=lambda c: c[0].replace(" ", "_"))
+def test_w4a8_fp8_tiles(case):
+    require_gpu()
+    import torch
+    import w4_dequant_gemm_amd as w4
+    label, M, K, N, (bm, bn, tiles, t0, splits) = case
+    assert tiles == -(-M // bm) * -(-N // bn)
+    part = (tiles - t0) * splits * bm * bn * 4 if splits > 1 else 0
+    W = synth.normal_matrix(60 + M, N, K, 0.02)
+    q = oracle.quantize(W, 128, "asym")
+    del W
+    pk, G = prepack_dev(q)
+    Xb = synth.to_bf16_bits(synth.normal_matrix(61 + M, M, K))
+    r, c = _rows_cols(M, N, 48, 768, seed=M)
+    r = np.unique(np.concatenate([r, np.arange(max(M - 5, 0), M)]))     # the last (partial) row tile
+    c = np.unique(np.concatenate([c, np.arange(N - 9, N)]))              # the ragged last column tile
+    want, rq, rs = oracle.w4a8_ref(Xb, q["packed"], q["scale"], q["zero"], G, "asym", rows=r, cols=c)
+    X64 = w4a8_x64(rq, rs)
+    # exactly the partials' bytes (NaNs on entry) are enough; fewer are refused
+    ws = torch.full((max(part, 16) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    print(f"[w4a8 fp8 tiles] {label} M={M} K={K} N={N} partial bytes={part}", flush=True)
+    Y, xq, xs = w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G, workspace=ws)
+    torch.cuda.synchronize()
+    assert_bits_equal(host(xq), rq, "E4M3 activations")
+    got = Y.float().cpu().numpy()[np.ix_(r, c)]
+    check_products(want, got, X64, q, G, "asym", f"fp8 tiles {label}", rows=r, cols=c)
+    if part:
+        with pytest.raises(w4.W4Error):
+            w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G, workspace=ws.view(torch.uint8)[: part - 16])
+    # the product on the row-quantized activations directly: the same bits
+    Y2 = w4.w4a8_gemm_e4m3(xq, xs, pk["wq"], pk["sz"], G, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits16(Y), bits16(Y2))
 
 
 def test_split_last_round_products():
@@ -547,7 +605,7 @@ def test_mid_size_products():
         for M in Ms:
             Xb = synth.to_bf16_bits(synth.normal_matrix(M + K, M, K))
             Xb[M // 2] = 0
-            need = w4.w4_gemm_workspace_bytes(M, K, N)
+            need = max(w4.w4_gemm_workspace_bytes(M, K, N), w4.w4a8_gemm_workspace_bytes(M, K, N))
             ws = torch.full((need // 4 + 16,), float("nan"), dtype=torch.float32, device="cuda")
             print(f"[mid] N={N} K={K} G={G} {mode} M={M} workspace={need}", flush=True)
             Y = w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G2, workspace=ws)
@@ -623,7 +681,9 @@ def test_streaming_k_split_products():
     # partials, summed by a second kernel), without one it runs unsplit; both
     # against the oracle and against each other, on a ragged N (16 blocks of
     # 64 columns and 15 K ranges, or 32 of 32 and 8 for four row blocks),
-    # W4A16 and W4A8, NaNs in the workspace on entry
+    # W4A16 and W4A8, NaNs in the workspace on entry.  W4A8 above 32 rows
+    # (groups of 128) runs on the fp8 kernel instead, with the workspace its
+    # schedule requires.
     require_gpu()
     import torch
     import w4_dequant_gemm_amd as w4
@@ -632,16 +692,23 @@ def test_streaming_k_split_products():
     q = oracle.quantize(W, 128, "asym")
     pk, G = prepack_dev(q)
     none = torch.empty((0,), dtype=torch.uint8, device="cuda")
-    for M in (16, 40, 64):
+    for M in (16, 32, 40, 64):
         Xb = synth.to_bf16_bits(synth.normal_matrix(66 + M, M, K))
         need = w4.w4_gemm_workspace_bytes(M, K, N)
-        assert need == (15 if M <= 16 else 8) * M * N * 4      # 16 blocks of 64 columns, or 32 of 32
+        assert need == (15 if M <= 32 else 8) * M * N * 4      # 16 blocks of 64 columns, or 32 of 32
         ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device="cuda")
         print(f"[k-split] M={M} N={N} K={K} workspace={need}", flush=True)
         Ys = w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G, workspace=ws)
         Yu = w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G, workspace=none)
-        Y8s, xq, xs = w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G, workspace=ws)
-        Y8u, _, _ = w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G, workspace=none)
+        ws8 = torch.full((max(w4.w4a8_gemm_workspace_bytes(M, K, N), need) // 4,), float("nan"),
+                         dtype=torch.float32, device="cuda")
+        Y8s, xq, xs = w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G, workspace=ws8)
+        if M <= 32:
+            Y8u, _, _ = w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G, workspace=none)
+        else:
+            with pytest.raises(w4.W4Error):       # the fp8 kernel's split needs its partials
+                w4.w4a8_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G, workspace=none)
+            Y8u = Y8s
         torch.cuda.synchronize()
         X64 = oracle.bf16_bits_to_f64(Xb)
         want = oracle.gemm_ref(X64, q["packed"], q["scale"], q["zero"], G, "asym")

@@ -485,7 +485,7 @@ def w4a8_gemm_e4m3(xq: torch.Tensor, xscale: torch.Tensor, wq: torch.Tensor, sz:
     M, K, N = _check_product_shapes("w4a8_gemm_e4m3", xq, wq, sz, G, Y=Y, xscale=xscale)
     dev = xq.device
     Y = _empty((M, N), torch.bfloat16, dev) if Y is None else Y
-    ws, ws_bytes = _workspace(M, K, N, dev, workspace, stream)
+    ws, ws_bytes = _workspace(M, K, N, dev, workspace, stream, w4a8=True)
     rc = lib().w4a8_gemm_e4m3(_dev(xq, "xq"), _dev(xscale, "xscale", torch.float32), M, K, _dev(wq, "wq"),
                               _dev(sz, "sz"), N, G, _dev(Y, "Y", torch.bfloat16), ws, ws_bytes, _stream(dev, stream))
     _check("w4a8_gemm_e4m3", rc)

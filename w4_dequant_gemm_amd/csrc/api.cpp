@@ -109,8 +109,21 @@ int quantize_common(const char* fn, const float* W, int64_t N, int64_t K, int G,
     return hip_status(w4::launch_quantize(p, stream), fn);
 }
 
+// true when a W4A8 product of this shape runs on the fp8 kernel (its own
+// tiles and split schedule)
+bool f8_product(int64_t M, int64_t K, int64_t N, int G) {
+    return w4::f8_eligible(M, K, G) && w4::f8_fits_buffers(M, K, N);
+}
+
+// workspace the product's schedule needs (0: none)
+size_t split_bytes(int64_t M, int64_t K, int64_t N, int G, bool fp8) {
+    if (fp8 && f8_product(M, K, N, G)) return w4::f8_workspace_bytes(M, K, N);
+    return M <= w4::kSkinnyMaxM ? 0 : w4::gemm_workspace_bytes(M, K, N);
+}
+
 int mul_common(const char* fn, const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq,
-               const uint32_t* sz, int64_t N, int G, uint16_t* Y, void* workspace, size_t workspace_bytes) {
+               const uint32_t* sz, int64_t N, int G, uint16_t* Y, void* workspace, size_t workspace_bytes,
+               bool fp8) {
     W4_TRY(check_group(fn, N, K, G));
     if (M < 0) return fail(W4_EINVAL, "%s: M = %lld must be >= 0", fn, static_cast<long long>(M));
     if (M == 0 || N == 0) return W4_OK;
@@ -121,7 +134,7 @@ int mul_common(const char* fn, const uint16_t* X, int64_t M, int64_t K, const ui
     // any workspace given is checked, whether or not this shape splits K: the
     // row quantizer of W4A8 may also place the widened activations there
     if (workspace && !aligned16(workspace)) return fail(W4_EINVAL, "%s: workspace is not 16-byte aligned", fn);
-    const size_t need = M <= w4::kSkinnyMaxM ? 0 : w4::gemm_workspace_bytes(M, K, N);
+    const size_t need = split_bytes(M, K, N, G, fp8);
     if (need > 0) {
         if (!workspace)
             return fail(W4_EINVAL, "%s: this shape needs a workspace of %zu bytes (w4_gemm_workspace_bytes)", fn, need);
@@ -145,7 +158,8 @@ w4::MulParams with_skinny_split(w4::MulParams p, void* workspace, size_t workspa
 
 // the tiled-GEMM launch of a product, with the K split that its workspace was sized for
 w4::MulParams with_split(w4::MulParams p, void* workspace) {
-    const w4::GemmSplit g = w4::gemm_split(p.M, p.K, p.N);
+    const w4::GemmSplit g =
+        p.x_fp8 && f8_product(p.M, p.K, p.N, p.G) ? w4::f8_split(p.M, p.K, p.N) : w4::gemm_split(p.M, p.K, p.N);
     p.splits = g.splits;
     p.split_t0 = g.t0;
     p.ws = g.splits > 1 ? static_cast<float*>(workspace) : nullptr;
@@ -285,15 +299,21 @@ size_t w4_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
 
 size_t w4a8_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
     if (M <= 0 || K <= 0 || N <= 0) return 0;
-    if (M <= w4::kSkinnyMaxM) return w4::skinny_workspace_bytes(M, K, N);   // optional
-    const size_t xw = w4::gemm_xw_bytes(M, K, N);
-    return xw ? w4::gemm_xw_offset(M, K, N) + xw : w4::gemm_workspace_bytes(M, K, N);
+    // groups of 128 (or whole rows): the fp8 kernel's own schedule
+    const size_t f8 = f8_product(M, K, N, w4::kF8StepK) ? w4::f8_workspace_bytes(M, K, N) : 0;
+    // other groups: the bf16 kernels' schedule, with the widened activations
+    // where they pay
+    const size_t xw = M <= w4::kSkinnyMaxM ? 0 : w4::gemm_xw_bytes(M, K, N);
+    const size_t with_xw = xw ? w4::gemm_xw_offset(M, K, N) + xw : 0;
+    const size_t base = w4_gemm_workspace_bytes(M, K, N);
+    const size_t bf = with_xw > base ? with_xw : base;
+    return f8 > bf ? f8 : bf;
 }
 
 namespace {
 int w4a16_run(const char* fn, const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const uint32_t* sz,
               int64_t N, int G, uint16_t* Y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    W4_TRY(mul_common(fn, X, M, K, wq, sz, N, G, Y, workspace, workspace_bytes));
+    W4_TRY(mul_common(fn, X, M, K, wq, sz, N, G, Y, workspace, workspace_bytes, false));
     if (M == 0 || N == 0) return W4_OK;
     w4::MulParams p{X, nullptr, M, K, N, G, wq, sz, Y, false};
     if (M <= w4::kSkinnyMaxM)
@@ -326,7 +346,7 @@ int w4a8_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const
               int G, uint16_t* Y, uint8_t* xq, float* xscale, void* workspace, size_t workspace_bytes,
               hipStream_t stream) {
     const char* fn = "w4a8_gemm";
-    W4_TRY(mul_common(fn, X, M, K, wq, sz, N, G, Y, workspace, workspace_bytes));
+    W4_TRY(mul_common(fn, X, M, K, wq, sz, N, G, Y, workspace, workspace_bytes, true));
     if (M == 0 || N == 0) return W4_OK;
     W4_REQUIRE_PTR(fn, xq);
     if (!xscale) return fail(W4_EINVAL, "%s: xscale is NULL", fn);
@@ -339,14 +359,14 @@ int w4a8_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const
     // (w4a8_gemm_workspace_bytes) lets the row quantizer write them and the
     // bf16 tiled kernel run on them
     uint16_t* xw = nullptr;
-    const size_t xw_bytes = M > w4::kSkinnyMaxM && !(w4::f8_eligible(M, K, G) && w4::f8_fits_buffers(M, K, N)) ? w4::gemm_xw_bytes(M, K, N) : 0;
+    const size_t xw_bytes = M > w4::kSkinnyMaxM && !f8_product(M, K, N, G) ? w4::gemm_xw_bytes(M, K, N) : 0;
     if (xw_bytes && workspace && workspace_bytes >= w4::gemm_xw_offset(M, K, N) + xw_bytes)
         xw = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + w4::gemm_xw_offset(M, K, N));
     w4::RowQuantParams rq{X, M, K, xq, xscale, xw};
     W4_TRY(hip_status(w4::launch_rowquant(rq, stream), fn));
     w4::MulParams p{xq, xscale, M, K, N, G, wq, sz, Y, true};
     p.xw = xw;
-    if (M <= w4::kSkinnyMaxM)
+    if (M <= w4::kSkinnyMaxM && !f8_product(M, K, N, G))
         return hip_status(w4::launch_skinny(with_skinny_split(p, workspace, workspace_bytes), stream), fn);
     return hip_status(w4::launch_gemm(with_split(p, workspace), stream), fn);
 }
@@ -423,12 +443,13 @@ int w4a8_gemm_e4m3(const uint8_t* xq, const float* xscale, int64_t M, int64_t K,
                    const uint32_t* sz, int64_t N, int G, uint16_t* Y, void* workspace, size_t workspace_bytes,
                    hipStream_t stream) {
     const char* fn = "w4a8_gemm_e4m3";
-    W4_TRY(mul_common(fn, reinterpret_cast<const uint16_t*>(xq), M, K, wq, sz, N, G, Y, workspace, workspace_bytes));
+    W4_TRY(mul_common(fn, reinterpret_cast<const uint16_t*>(xq), M, K, wq, sz, N, G, Y, workspace, workspace_bytes,
+                      true));
     if (M == 0 || N == 0) return W4_OK;
     if (K % 16 != 0) return fail(W4_EINVAL, "%s: K = %lld must be a multiple of 16", fn, static_cast<long long>(K));
     if (!xscale) return fail(W4_EINVAL, "%s: xscale is NULL", fn);
     w4::MulParams p{xq, xscale, M, K, N, G, wq, sz, Y, true};
-    if (M <= w4::kSkinnyMaxM)
+    if (M <= w4::kSkinnyMaxM && !f8_product(M, K, N, G))
         return hip_status(w4::launch_skinny(with_skinny_split(p, workspace, workspace_bytes), stream), fn);
     return hip_status(w4::launch_gemm(with_split(p, workspace), stream), fn);
 }

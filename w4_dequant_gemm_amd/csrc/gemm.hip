@@ -1133,12 +1133,13 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(MulParams p) {
 bool use_mid(int64_t M, int64_t K) { return M <= W4_MID_MAXM && K % big::BK == 0; }
 
 // The fp8-MFMA W4A8 kernel takes 128-k steps that each lie in one group:
-// groups of 128 (or per-channel rows) and K a multiple of 128.
+// groups of 128 (or per-channel rows) and K a multiple of 128; it serves
+// every M above kF8MinM.
 #ifndef W4_F8_GEMM
 #define W4_F8_GEMM 1
 #endif
 bool f8_eligible(int64_t M, int64_t K, int G) {
-    return W4_F8_GEMM && M > W4_MID_MAXM && K % kF8StepK == 0 && G % kF8StepK == 0;
+    return W4_F8_GEMM && M > kF8MinM && K % kF8StepK == 0 && G % kF8StepK == 0;
 }
 bool use_f8(const MulParams& p) { return p.x_fp8 && f8_eligible(p.M, p.K, p.G) && f8_fits_buffers(p.M, p.K, p.N); }
 
@@ -1277,8 +1278,36 @@ hipError_t launch_gemm_pair(const MulParams& p, hipStream_t stream) {
 
 int64_t gate_up_amax_tiles(int64_t M, int64_t N) { return M <= kGateUpMaxM ? (N + 15) / 16 : (N + 127) / 128; }
 
+hipError_t launch_split_sum(const MulParams& q, int bm, int bn, int64_t tiles, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>((tiles - q.split_t0) * (static_cast<int64_t>(bm) * bn / 1024)));
+    if (bm == 256 && bn == 256)
+        hipLaunchKernelGGL((splitk_reduce_kernel<256, 256>), grid, dim3(256), 0, stream, q);
+    else if (bm == 128 && bn == 256)
+        hipLaunchKernelGGL((splitk_reduce_kernel<128, 256>), grid, dim3(256), 0, stream, q);
+    else if (bm == 64 && bn == 256)
+        hipLaunchKernelGGL((splitk_reduce_kernel<64, 256>), grid, dim3(256), 0, stream, q);
+    else if (bm == 64 && bn == 128)
+        hipLaunchKernelGGL((splitk_reduce_kernel<64, 128>), grid, dim3(256), 0, stream, q);
+    else if (bm == 256 && bn == 128)
+        hipLaunchKernelGGL((splitk_reduce_kernel<256, 128>), grid, dim3(256), 0, stream, q);
+    else if (bm == 256 && bn == 64)
+        hipLaunchKernelGGL((splitk_reduce_kernel<256, 64>), grid, dim3(256), 0, stream, q);
+    else if (bm == 128 && bn == 128)
+        hipLaunchKernelGGL((splitk_reduce_kernel<128, 128>), grid, dim3(256), 0, stream, q);
+    else if (bm == 64 && bn == 64)
+        hipLaunchKernelGGL((splitk_reduce_kernel<64, 64>), grid, dim3(256), 0, stream, q);
+    else if (bm == 128 && bn == 64)
+        hipLaunchKernelGGL((splitk_reduce_kernel<128, 64>), grid, dim3(256), 0, stream, q);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm(const MulParams& p, hipStream_t stream) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
+    // W4A8 on the fp8 matrix cores (groups of 128 or whole rows), on its own
+    // tiles and split schedule
+    if (use_f8(p)) return launch_gemm_f8(p, stream);
     if (use_mid(p.M, p.K)) {
         constexpr int bm = W4_MID_BM;
         return p.x_fp8 ? launch_mid<bm, true>(p, stream) : launch_mid<bm, false>(p, stream);
@@ -1297,11 +1326,7 @@ hipError_t launch_gemm(const MulParams& p, hipStream_t stream) {
             return hipErrorInvalidValue;
         const int64_t wgs = q.split_t0 + (tiles - q.split_t0) * q.splits;
         const dim3 grid(static_cast<unsigned>(wgs));
-        if (q.x_fp8 && use_f8(q)) {
-            // W4A8 on the fp8 matrix cores (groups of 128 or whole rows)
-            const hipError_t e = launch_gemm_f8(q, wgs, stream);
-            if (e != hipSuccess) return e;
-        } else if (q.x_fp8 && q.xw) {
+        if (q.x_fp8 && q.xw) {
             // W4A8 on the widened activations: the bf16 kernel, row scales in
             // its epilogue (or in the split sum)
             q.X = q.xw;

@@ -10,15 +10,17 @@
 // operands, FP32 accumulation, the row scale in the epilogue; here the weight
 // codes stay exact instead of rounding (u - z) s to E4M3).
 //
-// Tile 256 x 256 of NW waves side by side: wave w owns output columns
-// (256 / NW) w .. for all 256 rows (16 row blocks of 16 x CB column blocks of
-// 16).  The accumulators take VALU multiply-adds, so they live in ordinary
-// VGPRs (the file is built with MFMA results in VGPRs) and a wave holds
-// 64 CB of them; with NW = 8 two waves share a SIMD and one wave's VALU work
-// runs under the other's MFMAs.
+// Tile BM x BN (64 to 256 rows, 64 to 256 columns) of eight waves in a
+// WR x WC grid: wave (wr, wc) owns BM / WR rows (row blocks of 16) by
+// BN / WC columns (CB column blocks of 16).  The accumulators take VALU
+// multiply-adds, so they live in ordinary VGPRs (the file is built with MFMA
+// results in VGPRs); two waves share a SIMD and one wave's VALU work runs
+// under the other's MFMAs.  Large products take 256 x 256 tiles; products of
+// a few hundred rows or fewer take narrower or shorter tiles, which give
+// enough workgroups without splitting K (f8_split).
 //
 // The E4M3 activations go straight from global memory into LDS
-// (buffer_load_dwordx4 ... lds into three 32 KB stages, two steps ahead; the
+// (buffer_load_dwordx4 ... lds into three BM x 128-byte stages, two steps ahead; the
 // 16-byte chunk c of stage row r sits at position c ^ ((r >> 1) & 7), so the
 // 16 rows of a fragment read spread over all 64 banks).  The weights
 // never pass through LDS: for a 16-column block, lane (c, q) loads the 16
@@ -43,21 +45,24 @@
 namespace w4 {
 namespace {
 
-#ifndef W4_F8_NW
-#define W4_F8_NW 8
-#endif
 namespace f8 {
-constexpr int BM = 256, BN = 256, BK = 128, NW = W4_F8_NW, NT = 64 * NW;
-constexpr int STAGE = BM * BK;                 // bytes of one activation stage
-constexpr int ADMA = STAGE / (1024 * NW);      // direct-to-LDS loads per wave and step
-constexpr int RB = BM / 16;                    // 16-row blocks
-constexpr int WN = BN / NW;                    // columns per wave
-constexpr int CB = WN / 16;                    // 16-column blocks per wave
-constexpr int NSLOT = RB * CB;                 // MFMAs per wave and step
-constexpr int NCONV = CB * 4;                  // code words converted per lane and step
-constexpr int BLOAD = 2 * CB;                  // code and scale/zero loads per lane and step
+constexpr int BK = 128;
 static_assert(BK == kF8StepK, "one K step of the fp8 kernel");
-static_assert(NSLOT % NCONV == 0 && NSLOT % BLOAD == 0 && NSLOT % ADMA == 0 && ADMA >= 1, "slot plan");
+// BM x BN tile of WR x WC waves: wave (wr, wc) owns rows (BM / WR) wr ..
+// and columns (BN / WC) wc ..
+template <int BM_, int BN_, int WR_, int WC_>
+struct Geom {
+    static constexpr int BM = BM_, BN = BN_, WR = WR_, WC = WC_, NW = WR * WC, NT = 64 * NW;
+    static constexpr int STAGE = BM * BK;                 // bytes of one activation stage
+    static constexpr int ADMA = STAGE / (1024 * NW);      // direct-to-LDS loads per wave and step
+    static constexpr int RB = BM / 16 / WR;               // 16-row blocks per wave
+    static constexpr int WN = BN / WC;                    // columns per wave
+    static constexpr int CB = WN / 16;                    // 16-column blocks per wave
+    static constexpr int NSLOT = RB * CB;                 // MFMAs per wave and step
+    static constexpr int NCONV = CB * 4;                  // code words converted per lane and step
+    static constexpr int BLOAD = 2 * CB;                  // code and scale/zero loads per lane and step
+    static_assert(ADMA >= 1 && CB >= 1 && NSLOT % BLOAD == 0 && NSLOT % ADMA == 0, "slot plan");
+};
 }  // namespace f8
 
 typedef _Float16 half2v_t __attribute__((ext_vector_type(2)));
@@ -71,6 +76,7 @@ struct F8Job {
     int kb, KT;        // first K step and number of K steps
     int64_t part;      // partial-tile index in ws, or -1: write Y
 };
+template <int BM, int BN>
 __device__ __forceinline__ F8Job f8_job(const MulParams& p) {
     using namespace f8;
     const int64_t b = blockIdx.x;
@@ -138,8 +144,12 @@ __device__ __forceinline__ float4_t mfma_f8_16x16x128(const int8x_t& a, const in
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, float4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
 }
 
-__global__ void __launch_bounds__(f8::NT) gemm_f8_kernel(MulParams p) {
+template <int BM_, int BN_, int WR_, int WC_>
+__global__ void __launch_bounds__(64 * WR_ * WC_) gemm_f8_kernel(MulParams p) {
     using namespace f8;
+    using Gm = Geom<BM_, BN_, WR_, WC_>;
+    constexpr int BM = Gm::BM, BN = Gm::BN, WC = Gm::WC, STAGE = Gm::STAGE, ADMA = Gm::ADMA, RB = Gm::RB,
+                  WN = Gm::WN, CB = Gm::CB, NSLOT = Gm::NSLOT, NCONV = Gm::NCONV, BLOAD = Gm::BLOAD;
     __shared__ __attribute__((aligned(16))) uint8_t lds_a0[STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t lds_a1[STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t lds_a2[STAGE];
@@ -148,9 +158,12 @@ __global__ void __launch_bounds__(f8::NT) gemm_f8_kernel(MulParams p) {
     const int lane = tid & 63;
     const int c = lane & 15, q = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const F8Job job = f8_job(p);
+    const int wr = wave / WC, wc = wave % WC;
+    const int row0 = 16 * RB * wr;   // the wave's first tile row
+    const F8Job job = f8_job<BM, BN>(p);
     const int64_t m_base = job.m_base, n_base = job.n_base;
     const int64_t M = p.M, N = p.N, K = p.K;
+    __shared__ float lds_xs[BM];
     const int kb = job.kb, KT = job.KT;
     const int g_shift = group_shift(p.G);
 
@@ -166,9 +179,8 @@ __global__ void __launch_bounds__(f8::NT) gemm_f8_kernel(MulParams p) {
     // (l % 8) ^ ((r >> 1) & 7) = (l % 8) ^ (l / 16) ^ (4 if wave ADMA + it is
     // odd).  Buffer loads with a 32-bit lane offset: rows past M lie past the
     // buffer's end and read as zeros (their outputs are never stored).
-    static_assert(ADMA % 2 == 0, "the chunk swizzle of a load depends on its parity only");
     const int a_row0 = 8 * wave * ADMA + (lane >> 3);
-    const int a_chunk = (lane & 7) ^ (lane >> 4);
+    const int a_chunk = (lane & 7) ^ (lane >> 4) ^ ((wave * ADMA) & 1 ? 4 : 0);
     const u32x4_t a_rsrc = buffer_rsrc(p.X, static_cast<uint32_t>(M * K));
     const uint32_t a_voff = static_cast<uint32_t>((m_base + a_row0) * K + a_chunk * 16);
     auto dma_item = [&](int kt, uint8_t* stage, int it) {
@@ -188,7 +200,7 @@ __global__ void __launch_bounds__(f8::NT) gemm_f8_kernel(MulParams p) {
                      ::"v"(voff), "s"(a_rsrc), "s"(m0), "s"(soff) : "memory", "m0");
     };
 
-    // weights: column n_base + WN wave + 16 cb + c, 32-k tile 4 kt + q.  In
+    // weights: column n_base + WN wc + 16 cb + c, 32-k tile 4 kt + q.  In
     // the blocked layout, block cb's 16 rows start at row r0 (uniform): the
     // lane's 16 bytes of tile t are at word 4 nr t + 4 cc of the block and its
     // scale/zero word of group g at nr g + cc (nr rows in the block, cc the
@@ -202,7 +214,7 @@ __global__ void __launch_bounds__(f8::NT) gemm_f8_kernel(MulParams p) {
     const int64_t nblk_last = ((N - 1) / 16) * 16;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-        int64_t r0 = n_base + WN * wave + 16 * cb;
+        int64_t r0 = n_base + WN * wc + 16 * cb;
         r0 = r0 < N ? r0 : nblk_last;
         const int nr = static_cast<int>(N - r0 < 16 ? N - r0 : 16);
         const int cc = c < nr ? c : nr - 1;
@@ -265,10 +277,11 @@ __global__ void __launch_bounds__(f8::NT) gemm_f8_kernel(MulParams p) {
             o.oor = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(__builtin_amdgcn_ballot_w64(oor_lane != 0) != 0));
     };
 
-    // A fragment of row block rb: stage row 16 rb + c, chunks 2 q and 2 q + 1
-    // (swizzle ((16 rb + c) >> 1) & 7 = c >> 1, the same for every rb)
-    const uint32_t aoff0 = static_cast<uint32_t>(c * BK + 16 * ((2 * q) ^ (c >> 1)));
-    const uint32_t aoff1 = static_cast<uint32_t>(c * BK + 16 * ((2 * q + 1) ^ (c >> 1)));
+    // A fragment of the wave's row block rb: stage row row0 + 16 rb + c,
+    // chunks 2 q and 2 q + 1 (swizzle ((16 j + c) >> 1) & 7 = c >> 1, the same
+    // for every 16-row block j)
+    const uint32_t aoff0 = static_cast<uint32_t>((row0 + c) * BK + 16 * ((2 * q) ^ (c >> 1)));
+    const uint32_t aoff1 = static_cast<uint32_t>((row0 + c) * BK + 16 * ((2 * q + 1) ^ (c >> 1)));
     auto frag_a = [&](const uint8_t* A, int rb) -> int8x_t {
         const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(A + rb * (16 * BK) + aoff0);
         const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(A + rb * (16 * BK) + aoff1);
@@ -304,9 +317,13 @@ __global__ void __launch_bounds__(f8::NT) gemm_f8_kernel(MulParams p) {
 #endif
     // conversion items from slot CONV0 on, spread evenly over the rest of the
     // step (a later start leaves the codes loaded a step before more time to arrive)
-    constexpr int CONV0 = W4_F8_CONV0;
+    constexpr int CONV0 = NSLOT > 1 ? W4_F8_CONV0 : 0;
     constexpr int CONV_EVERY = (NSLOT - CONV0) / NCONV, LOAD_EVERY = NSLOT / BLOAD, DMA_EVERY = NSLOT / ADMA;
-    static_assert(CONV_EVERY >= 1, "conversion slots");
+    // conversion item i goes to slot conv_slot(i); with fewer slots than
+    // items, several share a slot
+    auto conv_slot = [](int i) constexpr {
+        return CONV_EVERY >= 1 ? CONV0 + i * CONV_EVERY : CONV0 + i * (NSLOT - CONV0) / NCONV;
+    };
     auto step3 = [&](int kt, auto SA, Regs& next, const Regs& ready, const BOps& cur, BOps& nxt) {
         constexpr int sa = decltype(SA)::value;
         const uint8_t* As = stage_a(std::integral_constant<int, sa>{});
@@ -321,8 +338,14 @@ __global__ void __launch_bounds__(f8::NT) gemm_f8_kernel(MulParams p) {
             // the fragment is reloaded for the next row block right after its last use
             if (cb == CB - 1 && rb + 1 < RB) fa = frag_a(As, rb + 1);
             if (u >= TROT - 1) scale_add(u - (TROT - 1), cur, T[(u - (TROT - 1)) % TROT]);
-            if (u >= CONV0 && (u - CONV0) % CONV_EVERY == 0 && (u - CONV0) / CONV_EVERY < NCONV)
-                conv_item((u - CONV0) / CONV_EVERY, ready, nxt);
+            if constexpr (CONV_EVERY >= 1) {
+                if (u >= CONV0 && (u - CONV0) % CONV_EVERY == 0 && (u - CONV0) / CONV_EVERY < NCONV)
+                    conv_item((u - CONV0) / CONV_EVERY, ready, nxt);
+            } else {
+#pragma unroll
+                for (int i = 0; i < NCONV; ++i)
+                    if (conv_slot(i) == u) conv_item(i, ready, nxt);
+            }
             if (u % LOAD_EVERY == LOAD_EVERY / 2 - 1) {
                 load_item(kt + 2, next, u / LOAD_EVERY);
                 asm volatile("" ::: "memory");
@@ -372,6 +395,9 @@ __global__ void __launch_bounds__(f8::NT) gemm_f8_kernel(MulParams p) {
     for (int it = 0; it < BLOAD; ++it) load_item(1, r1, it);
 #pragma unroll
     for (int it = 0; it < NCONV; ++it) conv_item(it, r0, o0);
+    // the tile's row scales for the epilogue of a whole tile (a partial tile
+    // leaves them to the split sum), fetched under the first steps' loads
+    for (int r = tid; r < BM; r += Gm::NT) lds_xs[r] = job.part < 0 && m_base + r < M ? p.xscale[m_base + r] : 1.0f;
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_s_barrier();
@@ -392,23 +418,20 @@ __global__ void __launch_bounds__(f8::NT) gemm_f8_kernel(MulParams p) {
     asm volatile("" ::: "memory");
 
     // epilogue: register e of lane (c, q) in block (rb, cb) holds row
-    // 16 rb + 4 q + e, column WN wave + 16 cb + c
+    // row0 + 16 rb + 4 q + e, column WN wc + 16 cb + c
     const bool whole = job.part < 0;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         float rsc[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int64_t row = m_base + 16 * rb + 4 * q + e;
-            rsc[e] = whole && row < M ? p.xscale[row] : 1.0f;
-        }
+        for (int e = 0; e < 4; ++e) rsc[e] = lds_xs[row0 + 16 * rb + 4 * q + e];
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
-            const int lc = WN * wave + 16 * cb + c;
+            const int lc = WN * wc + 16 * cb + c;
             const int64_t col = n_base + lc;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int lr = 16 * rb + 4 * q + e;
+                const int lr = row0 + 16 * rb + 4 * q + e;
                 const int64_t row = m_base + lr;
                 if (!whole) p.ws[job.part * (BM * BN) + lr * BN + lc] = acc[rb][cb][e];
                 else if (row < M && col < N) p.Y[row * N + col] = float_to_bf16_bits(acc[rb][cb][e] * rsc[e]);
@@ -425,13 +448,112 @@ bool f8_fits_buffers(int64_t M, int64_t K, int64_t N) {
     return M * K <= kMax && N * K / 2 <= kMax && N * (K / f8::BK) * 4 <= kMax;
 }
 
-// grid of `wgs` workgroups over 256 x 256 tiles (the split schedule of
-// MulParams); the caller launches the split sum
-hipError_t launch_gemm_f8(const MulParams& p, int64_t wgs, hipStream_t stream) {
+// Output tile and K split of the fp8 kernel for an [M, K] x [N, K] product.
+// Each tile shape gets the split schedule of the bf16 GEMM (with fewer tiles
+// than half the compute units every tile is split along K into as many
+// ranges as keep about one workgroup per compute unit, otherwise the tiles
+// of the last, partial round are split; at most 16 ranges of at least four
+// 128-k steps), and the shape with the least estimated time is taken:
+//   rounds of whole tiles x steps x the tile's time per step
+//   + the split tiles' steps x the same + the fp32 partials written and read.
+// The times per 128-k step are measured on one MI355X (one workgroup per
+// compute unit, all compute units busy); the partials cost about one
+// microsecond per 6 MB (written, then read by the split sum).
+#ifndef W4_F8_TILE
+#define W4_F8_TILE 0      // 0: chosen by the estimate; 1..6 forces one of the tiles
+#endif
+namespace {
+struct F8Tile {
+    int bm, bn, wr, wc;
+    double step_us;
+};
+constexpr F8Tile kF8Tiles[] = {{256, 256, 1, 8, 2.22}, {128, 256, 1, 8, 1.48}, {256, 128, 2, 4, 1.46},
+                               {256, 64, 2, 4, 0.83},  {64, 128, 1, 8, 0.59},  {128, 64, 2, 4, 0.59}};
+constexpr int kF8NTiles = sizeof(kF8Tiles) / sizeof(kF8Tiles[0]);
+
+GemmSplit f8_schedule(int t, int64_t M, int64_t K, int64_t N) {
+    constexpr int64_t kCUs = 256;
+    GemmSplit g{1, 0, 0, kF8Tiles[t].bm, kF8Tiles[t].bn};
+    g.tiles = ((M + g.bm - 1) / g.bm) * ((N + g.bn - 1) / g.bn);
+    g.t0 = g.tiles;
+    const int64_t rem = g.tiles < kCUs / 2 ? g.tiles : g.tiles % kCUs;
+    if (rem == 0) return g;
+    int64_t s = kCUs / rem;
+    if (s > (K / f8::BK) / 4) s = (K / f8::BK) / 4;
+    if (s > 16) s = 16;
+    if (s < 2) return g;
+    g.splits = static_cast<int>(s);
+    g.t0 = g.tiles - rem;
+    return g;
+}
+
+double f8_estimate_us(int t, const GemmSplit& g, int64_t K) {
+    constexpr int64_t kCUs = 256;
+    const int64_t KT = K / f8::BK;
+    double us = static_cast<double>((g.t0 + kCUs - 1) / kCUs) * KT * kF8Tiles[t].step_us;
+    if (g.splits > 1) {
+        us += static_cast<double>((KT + g.splits - 1) / g.splits) * kF8Tiles[t].step_us;
+        us += static_cast<double>(g.tiles - g.t0) * g.splits * g.bm * g.bn * 4 / 6.0e6 + 3.0;
+    }
+    return us;
+}
+
+int f8_tile(int64_t M, int64_t K, int64_t N) {
+    if (W4_F8_TILE >= 1 && W4_F8_TILE <= kF8NTiles) return W4_F8_TILE - 1;
+    int best = 0;
+    double best_us = 0.0;
+    for (int t = 0; t < kF8NTiles; ++t) {
+        const double us = f8_estimate_us(t, f8_schedule(t, M, K, N), K);
+        if (t == 0 || us < best_us) {
+            best = t;
+            best_us = us;
+        }
+    }
+    return best;
+}
+}  // namespace
+
+GemmSplit f8_split(int64_t M, int64_t K, int64_t N) {
+    if (M <= 0 || N <= 0 || K % f8::BK != 0) return GemmSplit{1, 0, 0, 256, 256};
+    return f8_schedule(f8_tile(M, K, N), M, K, N);
+}
+
+size_t f8_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+    const GemmSplit g = f8_split(M, K, N);
+    if (g.splits == 1) return 0;
+    return static_cast<size_t>(g.tiles - g.t0) * g.splits * g.bm * g.bn * sizeof(float);
+}
+
+// The product on the tile and split of f8_split (p.splits / p.split_t0 and
+// the workspace p.ws sized by f8_workspace_bytes, or splits = 1: unsplit),
+// then the split sum.
+hipError_t launch_gemm_f8(const MulParams& p, hipStream_t stream) {
     if (p.K % f8::BK != 0 || p.G % f8::BK != 0 || !p.x_fp8 || !p.xscale || !f8_fits_buffers(p.M, p.K, p.N))
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(gemm_f8_kernel, dim3(static_cast<unsigned>(wgs)), dim3(f8::NT), 0, stream, p);
-    return hipGetLastError();
+    if (p.M == 0 || p.N == 0) return hipSuccess;
+    const GemmSplit g = f8_split(p.M, p.K, p.N);
+    MulParams q = p;
+    if (q.splits <= 1) {
+        q.splits = 1;
+        q.split_t0 = g.tiles;
+        q.ws = nullptr;
+    } else if (q.splits != g.splits || q.split_t0 != g.t0 || !q.ws) {
+        return hipErrorInvalidValue;
+    }
+    const dim3 grid(static_cast<unsigned>(q.split_t0 + (g.tiles - q.split_t0) * q.splits));
+    const int t = f8_tile(p.M, p.K, p.N);
+    const dim3 block(static_cast<unsigned>(64 * kF8Tiles[t].wr * kF8Tiles[t].wc));
+    switch (t) {
+        case 0: hipLaunchKernelGGL((gemm_f8_kernel<256, 256, 1, 8>), grid, block, 0, stream, q); break;
+        case 1: hipLaunchKernelGGL((gemm_f8_kernel<128, 256, 1, 8>), grid, block, 0, stream, q); break;
+        case 2: hipLaunchKernelGGL((gemm_f8_kernel<256, 128, 2, 4>), grid, block, 0, stream, q); break;
+        case 3: hipLaunchKernelGGL((gemm_f8_kernel<256, 64, 2, 4>), grid, block, 0, stream, q); break;
+        case 4: hipLaunchKernelGGL((gemm_f8_kernel<64, 128, 1, 8>), grid, block, 0, stream, q); break;
+        default: hipLaunchKernelGGL((gemm_f8_kernel<128, 64, 2, 4>), grid, block, 0, stream, q); break;
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || q.splits == 1) return e;
+    return launch_split_sum(q, g.bm, g.bn, g.tiles, stream);
 }
 
 }  // namespace w4

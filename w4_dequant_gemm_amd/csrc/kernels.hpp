@@ -137,16 +137,29 @@ size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
 size_t gemm_xw_offset(int64_t M, int64_t K, int64_t N);
 size_t gemm_xw_bytes(int64_t M, int64_t K, int64_t N);
 // true when a W4A8 product of this shape and group size runs on the fp8
-// matrix cores (above the mid-size range, K and G multiples of 128); it
-// takes the E4M3 activations as they are, never the widened copy
+// matrix cores (M above kF8MinM, K and G multiples of 128); it takes the
+// E4M3 activations as they are, never the widened copy.  Up to kF8MinM rows
+// the weight-streaming kernel is faster.
+#ifndef W4_F8_MINM
+#define W4_F8_MINM 32
+#endif
+constexpr int64_t kF8MinM = W4_F8_MINM;
 bool f8_eligible(int64_t M, int64_t K, int G);
 // K step of the fp8 kernel (one group of 128 k)
 constexpr int kF8StepK = 128;
 // the fp8 kernel addresses its operands with 31-bit byte offsets
 bool f8_fits_buffers(int64_t M, int64_t K, int64_t N);
-// the fp8 W4A8 tiled kernel on `wgs` workgroups of 256 x 256 output tiles
-// (the split schedule of gemm_split in p); the split sum is launched apart
-hipError_t launch_gemm_f8(const MulParams& p, int64_t wgs, hipStream_t stream);
+// output tile (bm x bn) and K split of the fp8 kernel for this shape, and the
+// fp32 workspace bytes of its split partials
+GemmSplit f8_split(int64_t M, int64_t K, int64_t N);
+size_t f8_workspace_bytes(int64_t M, int64_t K, int64_t N);
+// the fp8 W4A8 tiled kernel on the schedule of f8_split (p.splits and
+// p.split_t0 from it, or splits = 1), then its split sum
+hipError_t launch_gemm_f8(const MulParams& p, hipStream_t stream);
+// the sum of K-split partial tiles (bm x bn of p.ws, p.splits per tile, from
+// tile p.split_t0 of `tiles` on), row scales applied for W4A8, into p.Y;
+// bm x bn one of 256 x 256, 128 x 256, 64 x 256, 64 x 128, 256 x 128, 256 x 64
+hipError_t launch_split_sum(const MulParams& p, int bm, int bn, int64_t tiles, hipStream_t stream);
 
 // Library-held scratch of w4a16_gemm_noalloc: 64 MiB per GPU, the largest
 // K-split workspace any shape of the tiled GEMM takes (at most 256 partial
