@@ -433,8 +433,10 @@ def test_w4a8_fp8_tiles(case):
 
 def test_split_last_round_products():
     # 258 output tiles over 256 compute units: the first 256 tiles whole, the
-    # last two (rows 256..299, columns 32512..32999, ragged in both) in eight
-    # K ranges each; sampled outputs cover both kinds of tile
+    # last two in eight K ranges each.  Tiles are numbered column by column
+    # over the two row tiles, so the split ones are the last column tile
+    # (columns 32768..32999, ragged, both row tiles, the second ragged);
+    # sampled outputs cover both kinds of tile
     require_gpu()
     import torch
     import w4_dequant_gemm_amd as w4
@@ -446,7 +448,7 @@ def test_split_last_round_products():
     Xb = synth.to_bf16_bits(synth.normal_matrix(55, M, K))
     rng = np.random.default_rng(56)
     rows = np.concatenate([np.arange(0, 8), np.arange(250, 300)]).astype(np.int64)
-    cols = np.unique(np.concatenate([rng.choice(32512, 256, replace=False), np.arange(32512, N, 2)])).astype(np.int64)
+    cols = np.unique(np.concatenate([rng.choice(32768, 256, replace=False), np.arange(32512, N, 2)])).astype(np.int64)
     for kind in ("w4a16", "w4a8"):
         print(f"[split last round] {kind} M={M} K={K} N={N}", flush=True)
         if kind == "w4a16":
@@ -460,7 +462,7 @@ def test_split_last_round_products():
         torch.cuda.synchronize()
         got = Y.float().cpu().numpy()[np.ix_(rows, cols)]
         check_products(want, got, X64, q, G, "asym", f"split last round {kind}", rows=rows, cols=cols)
-        tail = np.ix_(rows >= 256, cols >= 32512)
+        tail = np.ix_(rows >= 0, cols >= 32768)
         err_t = oracle.frobenius_gap(want[tail], got[tail])
         assert err_t <= REL_TOL, f"{kind} split tiles: relative error {err_t:.3e}"
 

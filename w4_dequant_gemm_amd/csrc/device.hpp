@@ -108,9 +108,8 @@ __device__ __forceinline__ TiledRow tiled_row(const uint32_t* wq, const uint32_t
 // XCDs (each with its own L2) round-robin by workgroup index, so workgroup b
 // runs on XCD b % 8.  Of T tiles, the first T8 = 8 floor(T / 8) are dealt as
 // tile = (b % 8) (T8 / 8) + b / 8, which gives each XCD one contiguous range
-// of the row-major tile grid (its workgroups share activation row panels and
-// neighbouring weight panels in their L2); the last T - T8 keep their index.
-// A bijection on 0 .. T - 1.
+// of tile numbers (tile_rc below places them on the grid); the last T - T8
+// keep their index.  A bijection on 0 .. T - 1.
 #ifndef W4_XCD_RASTER
 #define W4_XCD_RASTER 1
 #endif
@@ -118,6 +117,25 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t T) {
     const int64_t T8 = T & ~int64_t{7};
     if (!W4_XCD_RASTER || b >= T8) return b;
     return (b & 7) * (T8 >> 3) + (b >> 3);
+}
+
+// Position of output tile t in an mt x nt tile grid.  Tiles are numbered
+// super-row by super-row (kTileGroup row tiles each), column by column inside
+// a super-row: a run of consecutive tiles (one XCD's range above, or the
+// tiles in flight on it at one time) covers a few row tiles by many column
+// tiles, so its workgroups share activation row panels and weight column
+// panels in L2 instead of each reading a weight panel of its own.  A
+// bijection from 0 .. mt nt - 1 onto the grid.
+#ifndef W4_TILE_GROUP
+#define W4_TILE_GROUP 4
+#endif
+constexpr int64_t kTileGroup = W4_TILE_GROUP;
+__device__ __forceinline__ void tile_rc(int64_t t, int64_t mt, int64_t nt, int64_t& r, int64_t& c) {
+    const int64_t g = t / (kTileGroup * nt);
+    const int64_t j = t - g * (kTileGroup * nt);
+    const int64_t rows = mt - g * kTileGroup < kTileGroup ? mt - g * kTileGroup : kTileGroup;
+    c = j / rows;
+    r = g * kTileGroup + (j - c * rows);
 }
 
 // Activation of the gate projection in a gated MLP: SiLU x / (1 + e^-x)

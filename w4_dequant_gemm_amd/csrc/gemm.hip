@@ -239,9 +239,8 @@ __device__ __forceinline__ int lds_off(int row, int c) { return row * BK + ((c ^
 
 // The work of one workgroup of the 256 x 256 kernels (1-D grid): workgroup
 // b < split_t0 computes tile b whole; the rest compute K range z of tile
-// split_t0 + (b - split_t0) / splits, z = (b - split_t0) % splits.  Tiles are
-// row-major over the tile grid, so the 8 row tiles of a column tile land on
-// one XCD (workgroups go round-robin over the 8 XCDs; 112 column tiles).
+// split_t0 + (b - split_t0) / splits, z = (b - split_t0) % splits.  Tile
+// numbers map to the grid by tile_rc.
 struct TileJob {
     int64_t m_base, n_base;
     int kb, KT;        // first K step and number of K steps
@@ -266,8 +265,10 @@ __device__ __forceinline__ TileJob tile_job(const MulParams& p) {
         t.KT = (z + 1) * KT_all / p.splits - t.kb;
         t.part = j * p.splits + z;
     }
-    t.m_base = (tile / nt) * BM;
-    t.n_base = (tile % nt) * BN;
+    int64_t tr, tc;
+    tile_rc(tile, (p.M + BM - 1) / BM, nt, tr, tc);
+    t.m_base = tr * BM;
+    t.n_base = tc * BN;
     return t;
 }
 }  // namespace big
@@ -525,8 +526,10 @@ __device__ __forceinline__ big::TileJob tile_job_t(const MulParams& p) {
         t.KT = (z + 1) * KT_all / p.splits - t.kb;
         t.part = j * p.splits + z;
     }
-    t.m_base = (tile / nt) * TBM;
-    t.n_base = (tile % nt) * TBN;
+    int64_t tr, tc;
+    tile_rc(tile, (p.M + TBM - 1) / TBM, nt, tr, tc);
+    t.m_base = tr * TBM;
+    t.n_base = tc * TBN;
     return t;
 }
 
@@ -1089,7 +1092,9 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(MulParams p) {
     const int lr = static_cast<int>((e4 % (BM * BN)) / BN), lc = static_cast<int>(e4 % BN);
     const int64_t nt = (p.N + BN - 1) / BN;
     const int64_t tile = p.split_t0 + j;
-    const int64_t row = (tile / nt) * BM + lr, col = (tile % nt) * BN + lc;
+    int64_t tr, tc;
+    tile_rc(tile, (p.M + BM - 1) / BM, nt, tr, tc);
+    const int64_t row = tr * BM + lr, col = tc * BN + lc;
     if (row >= p.M || col >= p.N) return;
     const float* src = p.ws + j * p.splits * (BM * BN) + lr * BN + lc;
     float4 y = *reinterpret_cast<const float4*>(src);

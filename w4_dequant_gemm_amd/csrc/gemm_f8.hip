@@ -70,7 +70,7 @@ typedef short short2v_t __attribute__((ext_vector_type(2)));
 
 // The work of one workgroup (1-D grid): workgroup b < split_t0 computes tile b
 // whole; the rest compute K range z of tile split_t0 + (b - split_t0) /
-// splits, z = (b - split_t0) % splits.  Tiles are row-major over the tile grid.
+// splits, z = (b - split_t0) % splits.  Tile numbers map to the grid by tile_rc.
 struct F8Job {
     int64_t m_base, n_base;
     int kb, KT;        // first K step and number of K steps
@@ -97,8 +97,10 @@ __device__ __forceinline__ F8Job f8_job(const MulParams& p) {
         t.KT = (z + 1) * KT_all / p.splits - t.kb;
         t.part = j * p.splits + z;
     }
-    t.m_base = (tile / nt) * BM;
-    t.n_base = (tile % nt) * BN;
+    int64_t tr, tc;
+    tile_rc(tile, (p.M + BM - 1) / BM, nt, tr, tc);
+    t.m_base = tr * BM;
+    t.n_base = tc * BN;
     return t;
 }
 

@@ -73,7 +73,7 @@ struct MulParams {
     // K split across workgroups.  Streaming kernel (splits > 1, M >= 3): K
     // ranges of whole steps, partial sums in ws [range][M][N].  The 64 x 128
     // and 256 x 256 GEMMs: output
-    // tiles split_t0 .. tiles - 1 (row-major over the tile grid) are each
+    // tiles split_t0 .. tiles - 1 (numbered as tile_rc places them) are each
     // computed by `splits` workgroups over consecutive K ranges, which write
     // fp32 partial tiles to ws [tile - split_t0][split][tile rows x columns];
     // a second kernel adds them in split order, applies the row scale and
