@@ -174,6 +174,7 @@ ONE_HOT_CASES = [
     # label, N, K, G, mode, M, expected schedule
     ("streaming", 576, 1536, 32, "asym", (1, 8, 16, 48), "stream"),
     ("streaming G128", 1000, 8192, 128, "asym", (2, 16), "stream"),
+    ("streaming one row, 8B up width", 14336, 512, 128, "asym", (1,), "stream"),
     ("streaming K split", 1000, 8192, 128, "asym", (40,), "stream-split"),
     ("64x128 split", 1536, 1024, 128, "asym", (65, 100), "split"),
     ("64x128 whole", 32768, 256, 32, "sym", (128,), "whole"),

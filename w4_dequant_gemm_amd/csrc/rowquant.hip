@@ -10,7 +10,8 @@
 // LDS across the 4 waves) over the row, or over the partial row maxima its
 // producer left (the fused gate and up pass), then a pass over the row that divides
 // (IEEE, correctly rounded), clamps to +-448 and converts pairs with
-// v_cvt_pk_fp8_f32 (OCP E4M3 on gfx950).  Rows are read 16 bytes per lane.
+// v_cvt_pk_fp8_f32 (OCP E4M3 on gfx950).  Rows are read 16 bytes per lane,
+// once (kept in registers between the two passes) up to 32768 per row.
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -19,64 +20,92 @@
 namespace w4 {
 namespace {
 
+// Row of up to kRegRow * 256 16-byte pieces (K <= 32768): each thread keeps
+// its pieces in registers between the maximum and the quantizing pass, so
+// the row is read once; longer rows are read twice.
+constexpr int kRegRow = 16;
+
+__device__ __forceinline__ float amax8(uint4 v, float amax) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        amax = fmaxf(amax, fabsf(bf16_lo(w[j])));
+        amax = fmaxf(amax, fabsf(bf16_hi(w[j])));
+    }
+    return amax;
+}
+
+__device__ __forceinline__ void quant8(const RowQuantParams& p, int64_t m, int64_t i, uint4 v, float s) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float f[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f[2 * j] = fminf(fmaxf(bf16_lo(w[j]) / s, -448.0f), 448.0f);
+        f[2 * j + 1] = fminf(fmaxf(bf16_hi(w[j]) / s, -448.0f), 448.0f);
+    }
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
+    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
+    reinterpret_cast<uint2*>(p.xq + m * p.K)[i] = make_uint2(static_cast<uint32_t>(lo), static_cast<uint32_t>(hi));
+    if (p.xw) {
+        // the same codes widened to bf16 (exact: every finite E4M3 value is a
+        // bf16 value), two per conversion with scale 1
+        const uint32_t c[2] = {static_cast<uint32_t>(lo), static_cast<uint32_t>(hi)};
+        uint32_t wv[4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            wv[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[j], 1.0f, false));
+            wv[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[j], 1.0f, true));
+        }
+        reinterpret_cast<uint4*>(p.xw + m * p.K)[i] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    }
+}
+
 __global__ void __launch_bounds__(256) rowquant_kernel(RowQuantParams p) {
     __shared__ float red[4];
     const int64_t m = blockIdx.x;
     const int64_t K8 = p.K / 8;
     const uint4* x = reinterpret_cast<const uint4*>(p.X + m * p.K);
+    const int tid = threadIdx.x;
+    const bool in_regs = K8 <= kRegRow * 256;
 
     float amax = 0.0f;
+    uint4 v[kRegRow];
+    if (in_regs) {
+#pragma unroll
+        for (int r = 0; r < kRegRow; ++r) {
+            const int64_t i = tid + 256 * r;
+            v[r] = i < K8 ? x[i] : make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
     if (p.amax_part) {
         // the producer of X left the row's maximum in partial maxima
         const float* part = p.amax_part + m * p.amax_tiles;
-        for (int64_t i = threadIdx.x; i < p.amax_tiles; i += blockDim.x) amax = fmaxf(amax, part[i]);
-    } else {
-        for (int64_t i = threadIdx.x; i < K8; i += blockDim.x) {
-            const uint4 v = x[i];
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        for (int64_t i = tid; i < p.amax_tiles; i += blockDim.x) amax = fmaxf(amax, part[i]);
+    } else if (in_regs) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                amax = fmaxf(amax, fabsf(bf16_lo(w[j])));
-                amax = fmaxf(amax, fabsf(bf16_hi(w[j])));
-            }
-        }
+        for (int r = 0; r < kRegRow; ++r) amax = amax8(v[r], amax);
+    } else {
+        for (int64_t i = tid; i < K8; i += blockDim.x) amax = amax8(x[i], amax);
     }
     amax = wave_max(amax);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+    if ((tid & 63) == 0) red[tid >> 6] = amax;
     __syncthreads();
     amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 
     float s = amax / 448.0f;
     s = fmaxf(s, 1e-8f);
-    if (threadIdx.x == 0) p.xscale[m] = s;
+    if (tid == 0) p.xscale[m] = s;
 
-    uint2* out = reinterpret_cast<uint2*>(p.xq + m * p.K);
-    for (int64_t i = threadIdx.x; i < K8; i += blockDim.x) {
-        const uint4 v = x[i];
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        float f[8];
+    if (in_regs) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            f[2 * j] = fminf(fmaxf(bf16_lo(w[j]) / s, -448.0f), 448.0f);
-            f[2 * j + 1] = fminf(fmaxf(bf16_hi(w[j]) / s, -448.0f), 448.0f);
+        for (int r = 0; r < kRegRow; ++r) {
+            const int64_t i = tid + 256 * r;
+            if (i < K8) quant8(p, m, i, v[r], s);
         }
-        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
-        lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
-        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
-        hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
-        out[i] = make_uint2(static_cast<uint32_t>(lo), static_cast<uint32_t>(hi));
-        if (p.xw) {
-            // the same codes widened to bf16 (exact: every finite E4M3 value
-            // is a bf16 value), two per conversion with scale 1
-            const uint32_t c[2] = {static_cast<uint32_t>(lo), static_cast<uint32_t>(hi)};
-            uint32_t wv[4];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                wv[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[j], 1.0f, false));
-                wv[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[j], 1.0f, true));
-            }
-            reinterpret_cast<uint4*>(p.xw + m * p.K)[i] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-        }
+    } else {
+        for (int64_t i = tid; i < K8; i += blockDim.x) quant8(p, m, i, x[i], s);
     }
 }
 
