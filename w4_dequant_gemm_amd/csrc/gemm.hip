@@ -1256,8 +1256,9 @@ hipError_t launch_pair_t(const MulParams& p, hipStream_t stream) {
 }
 
 // Gate and up GEMM (M above the streaming kernel's pair range), no K split:
-// W4A16 above 256 rows on 256 x 128 output tiles of the direct-to-LDS
-// kernel; otherwise output tiles of 64 (M <= 64) or 128 rows by 128 columns.
+// W4A8 with groups of 128 on the fp8 kernel's pair form; W4A16 above 256
+// rows on 256 x 128 output tiles of the direct-to-LDS kernel; otherwise
+// output tiles of 64 (M <= 64) or 128 rows by 128 columns.
 // Measured on the 8B gate / up shapes (two 14336 x 4096): at M = 256 the
 // 128-row tiles take 98 us against 138 us for one row of 256-row tiles (224
 // workgroups against 112); from M = 384 the 256-row kernel is ahead
@@ -1266,6 +1267,8 @@ hipError_t launch_pair_t(const MulParams& p, hipStream_t stream) {
 hipError_t launch_gemm_pair(const MulParams& p, hipStream_t stream) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
     if (p.K % big::BK != 0 || !p.wq2 || !p.sz2) return hipErrorInvalidValue;
+    // W4A8 with groups of 128 (or whole rows): the fp8 kernel's pair form
+    if (use_f8(p)) return launch_gemm_f8_pair(p, stream);
     if (!p.x_fp8 && p.M > 256) {
         // W4A16: gemm256_breg_kernel on 256 x 128 output tiles
         const int64_t tiles = ((p.N + big::BN / 2 - 1) / (big::BN / 2)) * ((p.M + big::BM - 1) / big::BM);

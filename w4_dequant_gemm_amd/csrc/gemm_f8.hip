@@ -80,7 +80,7 @@ template <int BM, int BN>
 __device__ __forceinline__ F8Job f8_job(const MulParams& p) {
     using namespace f8;
     const int64_t b = blockIdx.x;
-    const int64_t nt = (p.N + BN - 1) / BN;
+    const int64_t nt = (p.N + BN - 1) / BN;     // BN: output columns of a tile
     const int KT_all = static_cast<int>(p.K / BK);
     F8Job t;
     int64_t tile;
@@ -146,7 +146,13 @@ __device__ __forceinline__ float4_t mfma_f8_16x16x128(const int8x_t& a, const in
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, float4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
 }
 
-template <int BM_, int BN_, int WR_, int WC_>
+// PAIR: the gate and up projections in one pass (p.wq2 / p.sz2 the up
+// weight): the tile holds BN / 2 output columns, waves wc < WC / 2 sum them
+// over the gate weight and the others over the up weight; the epilogue
+// combines the two through LDS into H = bf16(act(g) u) (both sums scaled by
+// the row scale first) and, with p.amax_part, records each row's maximum |H|
+// over the tile's columns.  Never split along K.
+template <int BM_, int BN_, int WR_, int WC_, bool PAIR = false>
 __global__ void __launch_bounds__(64 * WR_ * WC_) gemm_f8_kernel(MulParams p) {
     using namespace f8;
     using Gm = Geom<BM_, BN_, WR_, WC_>;
@@ -162,7 +168,9 @@ __global__ void __launch_bounds__(64 * WR_ * WC_) gemm_f8_kernel(MulParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wr = wave / WC, wc = wave % WC;
     const int row0 = 16 * RB * wr;   // the wave's first tile row
-    const F8Job job = f8_job<BM, BN>(p);
+    static_assert(!PAIR || (WR_ == 1 && WC_ % 2 == 0 && (BN_ / 2) % 64 == 0), "pair tiles");
+    constexpr int BNO = PAIR ? BN / 2 : BN;      // output columns of the tile
+    const F8Job job = f8_job<BM, BNO>(p);
     const int64_t m_base = job.m_base, n_base = job.n_base;
     const int64_t M = p.M, N = p.N, K = p.K;
     __shared__ float lds_xs[BM];
@@ -209,14 +217,17 @@ __global__ void __launch_bounds__(64 * WR_ * WC_) gemm_f8_kernel(MulParams p) {
     // lane's row, clamped to the block: columns past N repeat the last one,
     // whose outputs are not stored).  Buffer loads: uniform block and step
     // offsets, one lane offset per block.
-    const u32x4_t q_rsrc = buffer_rsrc(p.wq, static_cast<uint32_t>(N * K / 2));
-    const u32x4_t s_rsrc = buffer_rsrc(p.sz, static_cast<uint32_t>(N * (K / p.G) * 4));
+    // (PAIR: the up weight for waves wc >= WC / 2, at the same columns)
+    const bool up_wave = PAIR && wc >= WC / 2;
+    const int wcol = WN * (PAIR ? wc % (WC / 2) : wc);   // the wave's first column in the tile
+    const u32x4_t q_rsrc = buffer_rsrc(up_wave ? p.wq2 : p.wq, static_cast<uint32_t>(N * K / 2));
+    const u32x4_t s_rsrc = buffer_rsrc(up_wave ? p.sz2 : p.sz, static_cast<uint32_t>(N * (K / p.G) * 4));
     uint32_t qblk[CB], sblk[CB], nrb[CB];      // uniform: block byte offsets, rows in the block
     uint32_t qoff[CB], soff[CB];               // the lane's byte offsets in the block
     const int64_t nblk_last = ((N - 1) / 16) * 16;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-        int64_t r0 = n_base + WN * wc + 16 * cb;
+        int64_t r0 = n_base + wcol + 16 * cb;
         r0 = r0 < N ? r0 : nblk_last;
         const int nr = static_cast<int>(N - r0 < 16 ? N - r0 : 16);
         const int cc = c < nr ? c : nr - 1;
@@ -420,7 +431,79 @@ __global__ void __launch_bounds__(64 * WR_ * WC_) gemm_f8_kernel(MulParams p) {
     asm volatile("" ::: "memory");
 
     // epilogue: register e of lane (c, q) in block (rb, cb) holds row
-    // row0 + 16 rb + 4 q + e, column WN wc + 16 cb + c
+    // row0 + 16 rb + 4 q + e, column wcol + 16 cb + c
+    if constexpr (PAIR) {
+        // In two halves of the tile's rows: the up waves store their sums
+        // (fp32) in the free activation stages, 64 output columns to a stage
+        // ([BM / 2][64] each), the gate waves combine them with their own.
+        // A row's maximum |H| goes from 16 lanes to a wave, then through LDS
+        // across the gate waves.
+        __shared__ float lds_amax[WC / 2][BM];
+        auto su = [&](int oc, int lr) -> float& {
+            float* const st = reinterpret_cast<float*>(oc < 64 ? lds_a0 : lds_a1);
+            return st[lr * 64 + (oc & 63)];
+        };
+        static_assert(BM / 2 * 64 * 4 <= STAGE, "a half of the up sums fits a stage");
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            __syncthreads();
+            if (up_wave) {
+#pragma unroll
+                for (int rb = hh * RB / 2; rb < (hh + 1) * RB / 2; ++rb)
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) {
+                        const int oc = wcol + 16 * cb + c;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int lr = 16 * rb + 4 * q + e - hh * (BM / 2);
+                            su(oc, lr) = acc[rb][cb][e];
+                        }
+                    }
+            }
+            __syncthreads();
+            if (!up_wave) {
+#pragma unroll
+                for (int rb = hh * RB / 2; rb < (hh + 1) * RB / 2; ++rb) {
+                    float hmax[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) {
+                        const int oc = wcol + 16 * cb + c;
+                        const int64_t col = n_base + oc;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int lr = 16 * rb + 4 * q + e;
+                            const int64_t row = m_base + lr;
+                            const float r = lds_xs[lr];
+                            const float u = su(oc, lr - hh * (BM / 2));
+                            if (row < M && col < N) {
+                                const uint16_t hb = float_to_bf16_bits(activation(p.act, acc[rb][cb][e] * r) * (u * r));
+                                p.Y[row * N + col] = hb;
+                                hmax[e] = fmaxf(hmax[e], fabsf(bf16_lo(hb)));
+                            }
+                        }
+                    }
+                    if (p.amax_part) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float v = max16(hmax[e]);
+                            if (c == 0) lds_amax[wc][16 * rb + 4 * q + e] = v;
+                        }
+                    }
+                }
+            }
+        }
+        if (p.amax_part) {
+            __syncthreads();
+            const int64_t tcol = n_base / BNO;
+            for (int r = tid; r < BM; r += Gm::NT) {
+                float v = 0.0f;
+#pragma unroll
+                for (int w = 0; w < WC / 2; ++w) v = fmaxf(v, lds_amax[w][r]);
+                if (m_base + r < M) p.amax_part[(m_base + r) * p.amax_tiles + tcol] = v;
+            }
+        }
+        return;
+    }
     const bool whole = job.part < 0;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -429,7 +512,7 @@ __global__ void __launch_bounds__(64 * WR_ * WC_) gemm_f8_kernel(MulParams p) {
         for (int e = 0; e < 4; ++e) rsc[e] = lds_xs[row0 + 16 * rb + 4 * q + e];
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
-            const int lc = WN * wc + 16 * cb + c;
+            const int lc = wcol + 16 * cb + c;
             const int64_t col = n_base + lc;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -556,6 +639,31 @@ hipError_t launch_gemm_f8(const MulParams& p, hipStream_t stream) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || q.splits == 1) return e;
     return launch_split_sum(q, g.bm, g.bn, g.tiles, stream);
+}
+
+// Gate and up on the fp8 kernel: tiles of BM rows by 128 output columns
+// (256 weight columns: 128 of each weight), the most rows that still give
+// about one workgroup per compute unit; no K split.
+hipError_t launch_gemm_f8_pair(const MulParams& p, hipStream_t stream) {
+    if (p.K % f8::BK != 0 || p.G % f8::BK != 0 || !p.x_fp8 || !p.xscale || !p.wq2 || !p.sz2 ||
+        !f8_fits_buffers(p.M, p.K, p.N))
+        return hipErrorInvalidValue;
+    if (p.M == 0 || p.N == 0) return hipSuccess;
+    const int64_t nt = (p.N + 127) / 128;
+    const int bm = ((p.M + 255) / 256) * nt >= 224 ? 256 : (((p.M + 127) / 128) * nt >= 224 ? 128 : 64);
+    MulParams q = p;
+    const int64_t tiles = ((p.M + bm - 1) / bm) * nt;
+    q.splits = 1;
+    q.split_t0 = tiles;
+    q.ws = nullptr;
+    const dim3 grid(static_cast<unsigned>(tiles));
+    if (bm == 256)
+        hipLaunchKernelGGL((gemm_f8_kernel<256, 256, 1, 8, true>), grid, dim3(512), 0, stream, q);
+    else if (bm == 128)
+        hipLaunchKernelGGL((gemm_f8_kernel<128, 256, 1, 8, true>), grid, dim3(512), 0, stream, q);
+    else
+        hipLaunchKernelGGL((gemm_f8_kernel<64, 256, 1, 8, true>), grid, dim3(512), 0, stream, q);
+    return hipGetLastError();
 }
 
 }  // namespace w4

@@ -98,7 +98,7 @@ struct MulParams {
 // pair GEMM (K a multiple of 64) takes the fused product
 constexpr int64_t kGateUpMaxM = 32;
 // column tiles of the W4A8 gate and up pass (the partial row maxima of H it
-// writes per row): 16 columns in the streaming kernel, 128 in the tiled one
+// writes per row): 16 columns in the streaming kernel, 128 in the tiled ones
 int64_t gate_up_amax_tiles(int64_t M, int64_t N);
 // Which kernel runs a product: M <= kSkinnyMaxM: the weight-streaming
 // kernels (dot form for one or two rows, MFMA form above); larger M: the
@@ -156,6 +156,9 @@ size_t f8_workspace_bytes(int64_t M, int64_t K, int64_t N);
 // the fp8 W4A8 tiled kernel on the schedule of f8_split (p.splits and
 // p.split_t0 from it, or splits = 1), then its split sum
 hipError_t launch_gemm_f8(const MulParams& p, hipStream_t stream);
+// gate and up (p.wq2 / p.sz2 / p.act set) on the fp8 kernel: W4A8 with
+// groups of 128 (or whole rows), K a multiple of 128; no K split
+hipError_t launch_gemm_f8_pair(const MulParams& p, hipStream_t stream);
 // the sum of K-split partial tiles (bm x bn of p.ws, p.splits per tile, from
 // tile p.split_t0 of `tiles` on), row scales applied for W4A8, into p.Y;
 // bm x bn one of 256 x 256, 128 x 256, 64 x 256, 64 x 128, 256 x 128, 256 x 64
