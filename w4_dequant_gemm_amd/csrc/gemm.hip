@@ -938,6 +938,11 @@ __global__ void __launch_bounds__(64 * NW) gemm256_breg_kernel(MulParams p) {
         for (int i = 0; i < FI; ++i) a[i] = frag_a(A, kk, i);
     };
     constexpr int NSLOT = FI * FJ * (BK / 16);
+#ifndef W4_BREG_CONV0
+#define W4_BREG_CONV0 4     // in eighths of a step
+#endif
+    constexpr int BREG_CONV0 = NSLOT * W4_BREG_CONV0 / 8;
+    static_assert(BREG_CONV0 < NSLOT, "conversion slots");
     static_assert(4 * ADMA <= NSLOT && 4 * BLOAD <= NSLOT && NSLOT / 2 == 4 * FJ * (BK / 16), "slot plan");
 
     constexpr int kStepLoads = ADMA + BLOAD;
@@ -977,9 +982,14 @@ __global__ void __launch_bounds__(64 * NW) gemm256_breg_kernel(MulParams p) {
                     asm volatile("" ::: "memory");
                 }
                 if (u % 4 == 2 && u / 4 < ADMA) dma_item(kt + 2, Ad, u / 4);
-                // dequantization on the even slots (measured slightly ahead
-                // of the odd ones: 0.824 against 0.829 ms on the 70B shape)
-                if (u % 2 == 0) b_pair(u / 2, ready, nxt);
+                // dequantization of the NSLOT / 2 pairs spread over the
+                // second half of the step's slots, which gives the codes
+                // loaded during the step before half a step more to arrive
+                // (70B shape: 0.844 against 0.851 ms starting at slot 0,
+                // 0.847 from a quarter of the step)
+#pragma unroll
+                for (int pr = 0; pr < NSLOT / 2; ++pr)
+                    if (BREG_CONV0 + pr * (NSLOT - BREG_CONV0) / (NSLOT / 2) == u) b_pair(pr, ready, nxt);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
