@@ -475,7 +475,7 @@ def main():
             result["roofline_gemm"] = {"bound": "mfma", "achieved": round(t16, 1), "peak": BF16_PEAK_TFLOPS,
                                        "unit": "TFLOP/s", "frac": round(t16 / BF16_PEAK_TFLOPS, 4),
                                        "traffic": measured_traffic("gemm256_breg_w4a16_70b_m2048"),
-                                       "kernel": "gemm256_breg_kernel<false, 4> + splitk_reduce_kernel<256, 256> (the whole W4A16 "
+                                       "kernel": "gemm256_breg_kernel<false, 8> + splitk_reduce_kernel<256, 256> (the whole W4A16 "
                                                  "call, M=2048: 768 tiles whole, the last 128 in two K halves)",
                                        "flops_per_launch": flops, "avg_launch_us": round(ms16 * 1e3, 1)}
             result["roofline_w4a8"] = {"bound": "mfma", "achieved": round(t8, 1), "peak": FP8_PEAK_TFLOPS,

@@ -1221,13 +1221,12 @@ size_t gemm_xw_bytes(int64_t M, int64_t K, int64_t N) {
 #define W4_BIG_WN 2
 #endif
 constexpr int kBigWM = W4_BIG_WM, kBigWN = W4_BIG_WN;
-// Waves of the W4A16 256 x 256 kernel: eight of 32 columns (two per SIMD)
-// up to this many output tiles, four of 64 (one per SIMD) above.  Measured
-// on one MI355X: 12B up at M = 1024 (240 tiles) 118 us with eight against
-// 126 us with four; the 70B shape at M = 2048 (896 tiles) 823 against 817 us.
-#ifndef W4_BREG_NW8_MAX_TILES
-#define W4_BREG_NW8_MAX_TILES 512
-#endif
+// Waves of the W4A16 256 x 256 kernel: eight of 32 columns, two per SIMD, so
+// that one wave's dequantization and waits run under the other's MFMAs.
+// Measured on one MI355X against four of 64 columns (one per SIMD): 12B up
+// at M = 1024 (240 tiles) 118 against 126 us; the 70B shape at M = 2048
+// (896 tiles) 810-812 against 832 us (with the dequantization in the second
+// half of each step; 823 against 817 us before it).
 
 template <int TBM, bool XF8>
 hipError_t launch_mid(const MulParams& p, hipStream_t stream) {
@@ -1348,17 +1347,11 @@ hipError_t launch_gemm(const MulParams& p, hipStream_t stream) {
             // W4A8 on the widened activations: the bf16 kernel, row scales in
             // its epilogue (or in the split sum)
             q.X = q.xw;
-            if (tiles <= W4_BREG_NW8_MAX_TILES)
-                hipLaunchKernelGGL((gemm256_breg_kernel<false, 8>), grid, dim3(breg::Geom<8>::NT), 0, stream, q);
-            else
-                hipLaunchKernelGGL((gemm256_breg_kernel<false, 4>), grid, dim3(breg::Geom<4>::NT), 0, stream, q);
+            hipLaunchKernelGGL((gemm256_breg_kernel<false, 8>), grid, dim3(breg::Geom<8>::NT), 0, stream, q);
         } else if (q.x_fp8) {
             hipLaunchKernelGGL((gemm256_kernel<kBigWM, kBigWN, true>), grid, dim3(64 * kBigWM * kBigWN), 0, stream, q);
         } else {
-            if (tiles <= W4_BREG_NW8_MAX_TILES)
-                hipLaunchKernelGGL((gemm256_breg_kernel<false, 8>), grid, dim3(breg::Geom<8>::NT), 0, stream, q);
-            else
-                hipLaunchKernelGGL((gemm256_breg_kernel<false, 4>), grid, dim3(breg::Geom<4>::NT), 0, stream, q);
+            hipLaunchKernelGGL((gemm256_breg_kernel<false, 8>), grid, dim3(breg::Geom<8>::NT), 0, stream, q);
         }
         if (q.splits > 1 && q.split_t0 < tiles) {
             const hipError_t e = hipGetLastError();
