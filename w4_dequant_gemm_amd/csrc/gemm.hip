@@ -832,7 +832,7 @@ __device__ __forceinline__ int swz(int row) { return big::swizzle_fn(W4_DSWZ, ro
 template <bool PAIR, int NW = 4>
 __global__ void __launch_bounds__(64 * NW) gemm256_breg_kernel(MulParams p) {
     using namespace breg;
-    static_assert(!PAIR || NW == 4, "the pair form pairs waves w and w + 2");
+    static_assert(!PAIR || NW % 2 == 0, "the pair form pairs waves w and w + NW / 2");
     constexpr int NT = Geom<NW>::NT, ADMA = Geom<NW>::ADMA, FJ = Geom<NW>::FJ, BLOAD = Geom<NW>::BLOAD;
     constexpr int WNC = BN / NW;                      // columns per wave
     constexpr int FI = 8;
@@ -887,8 +887,8 @@ __global__ void __launch_bounds__(64 * NW) gemm256_breg_kernel(MulParams p) {
     // gate weight for waves 0 and 1, of the up weight at 64 (wave - 2) for
     // waves 2 and 3), clamped to N - 1 (its outputs are not stored); 32-k
     // chunk 2 kt + h of step kt
-    const bool b_up = PAIR && wave >= 2;
-    const int wcol = PAIR ? 64 * (wave & 1) : WNC * wave;
+    const bool b_up = PAIR && wave >= NW / 2;
+    const int wcol = PAIR ? WNC * (wave % (NW / 2)) : WNC * wave;
     TiledRow brow[FJ];
 #pragma unroll
     for (int jb = 0; jb < FJ; ++jb) {
@@ -1028,20 +1028,20 @@ __global__ void __launch_bounds__(64 * NW) gemm256_breg_kernel(MulParams p) {
 
     // epilogue: register r of lane l holds row (r%4) + 4(l/32) + 8(r/4), column l%32
     if constexpr (PAIR) {
-        // four rounds (w, hh): gate wave w and up wave 2 + w put the sums of
-        // their row blocks 4 hh .. 4 hh + 3 (32 KB each, register order) in
-        // lds_a0 and lds_a1; then all threads form the 128 x 64 outputs of
-        // the round row by row (coalesced stores, one copy of the
+        // rounds (w, hh): gate wave w and up wave NW / 2 + w put the sums of
+        // their row blocks 4 hh .. 4 hh + 3 (16 KB per 32 columns, register
+        // order) in lds_a0 and lds_a1; then all threads form the 128 x WNC
+        // outputs of the round row by row (coalesced stores, one copy of the
         // activation code)
-        constexpr int kQ = 4 * FJ * 16 * 64;      // floats per wave and round (32 KB)
+        constexpr int kQ = 4 * FJ * 16 * 64;      // floats per wave and round
         float* const g_l = reinterpret_cast<float*>(lds_a0);
         float* const u_l = reinterpret_cast<float*>(lds_a1);
 #pragma unroll
-        for (int w = 0; w < 2; ++w)
+        for (int w = 0; w < NW / 2; ++w)
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 __syncthreads();
-                if (wave == w || wave == 2 + w) {
+                if (wave == w || wave == NW / 2 + w) {
                     float* dst = wave == w ? g_l : u_l;
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
@@ -1052,8 +1052,8 @@ __global__ void __launch_bounds__(64 * NW) gemm256_breg_kernel(MulParams p) {
                 }
                 __syncthreads();
                 for (int o = tid; o < kQ; o += NT) {
-                    const int lr = o >> 6, lc = o & 63;          // row in the round's 128, column in the wave's 64
-                    const int64_t row = m_base + 128 * hh + lr, col = n_base + 64 * w + lc;
+                    const int lr = o / WNC, lc = o % WNC;        // row in the round's 128, column in the wave's WNC
+                    const int64_t row = m_base + 128 * hh + lr, col = n_base + WNC * w + lc;
                     if (row >= M || col >= N) continue;
                     // register order of (lr, lc): block (lr / 32, lc / 32), register
                     // (rr / 8) 4 + rr % 4 of lane ((rr / 4) % 2) 32 + lc % 32, rr = lr % 32
@@ -1266,13 +1266,19 @@ hipError_t launch_pair_t(const MulParams& p, hipStream_t stream) {
 
 // Gate and up GEMM (M above the streaming kernel's pair range), no K split:
 // W4A8 with groups of 128 on the fp8 kernel's pair form; W4A16 above 256
-// rows on 256 x 128 output tiles of the direct-to-LDS kernel; otherwise
+// rows on 256 x 128 output tiles of the direct-to-LDS kernel (eight waves,
+// four per weight); otherwise
 // output tiles of 64 (M <= 64) or 128 rows by 128 columns.
 // Measured on the 8B gate / up shapes (two 14336 x 4096): at M = 256 the
 // 128-row tiles take 98 us against 138 us for one row of 256-row tiles (224
 // workgroups against 112); from M = 384 the 256-row kernel is ahead
 // (151 / 179 us).  A 256-row form of the 128-row kernel spilled and ran
 // tens of times slower.
+// waves of the W4A16 pair kernel: eight (four per weight, two per SIMD);
+// 8B gate + up at M = 2048: 471-475 us against 516 us with four
+#ifndef W4_BREG_PAIR_NW
+#define W4_BREG_PAIR_NW 8
+#endif
 hipError_t launch_gemm_pair(const MulParams& p, hipStream_t stream) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
     if (p.K % big::BK != 0 || !p.wq2 || !p.sz2) return hipErrorInvalidValue;
@@ -1285,8 +1291,8 @@ hipError_t launch_gemm_pair(const MulParams& p, hipStream_t stream) {
         q.splits = 1;
         q.split_t0 = tiles;
         q.ws = nullptr;
-        hipLaunchKernelGGL((gemm256_breg_kernel<true, 4>), dim3(static_cast<unsigned>(tiles)), dim3(breg::Geom<4>::NT), 0,
-                           stream, q);
+        hipLaunchKernelGGL((gemm256_breg_kernel<true, W4_BREG_PAIR_NW>), dim3(static_cast<unsigned>(tiles)),
+                           dim3(breg::Geom<W4_BREG_PAIR_NW>::NT), 0, stream, q);
         return hipGetLastError();
     }
     if (p.M <= 64) return p.x_fp8 ? launch_pair_t<64, true>(p, stream) : launch_pair_t<64, false>(p, stream);
