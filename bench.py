@@ -247,8 +247,10 @@ def main():
         wsb = w4.w4_gemm_workspace_bytes(M, Ku, Nu)
         ws = torch.empty((max(wsb, 16),), dtype=torch.uint8, device=dev)
 
+        wsg = torch.empty((max(w4.w4a16_gate_up_workspace_bytes(M, Ku, Nu), 16),), dtype=torch.uint8, device=dev)
+
         def fused_p():
-            w4.w4a16_gate_up(x, ups[0], ups[1], G, "silu", H=h)
+            w4.w4a16_gate_up(x, ups[0], ups[1], G, "silu", H=h, workspace=wsg)
 
         def apart_p():
             w4.w4a16_gemm(x, ups[0]["wq"], ups[0]["sz"], G, Y=ya, workspace=ws)

@@ -285,7 +285,7 @@ int w4a8_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const
  * above, a tiled MFMA GEMM holds 128 columns of each weight per workgroup
  * (some of its waves sum the gate products, the others the up products of
  * the same outputs) and needs K to be a multiple of 64 (else W4_EUNSUPPORTED).
- * The tiled form does not split K.
+ * W4A8 with groups of 128 runs it on the fp8 matrix cores.
  *   X            [M, K] bf16 in, M >= 0.
  *   wq_gate, sz_gate, wq_up, sz_up: two [N, K] weights in the GPU layout of
  *                w4_prepack, with the same G.
@@ -304,12 +304,20 @@ int w4a8_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const
  *   workspace    with hq: at least w4a8_gate_up_workspace_bytes(M, K, N)
  *                bytes, 16-byte aligned (the partial row maxima); else
  *                ignored (may be NULL).
+ * W4A16 only -- an optional workspace (caller-owned, 16-byte aligned, its
+ * contents on entry irrelevant) of w4a16_gate_up_workspace_bytes(M, K, N)
+ * bytes lets the tiled form above 256 rows split the K range of the tiles of
+ * its last, partial round over the compute units (fp32 partial sums of both
+ * products, added in a fixed order by a second kernel that applies the
+ * activation); NULL or fewer bytes: the same outputs unsplit.  Calls in
+ * flight at the same time need separate workspaces.
  */
 #define W4_ACT_SILU 1
 #define W4_ACT_GELU_TANH 2
 int w4a16_gate_up(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq_gate, const uint32_t* sz_gate,
                   const uint32_t* wq_up, const uint32_t* sz_up, int64_t N, int G, int act, uint16_t* H,
-                  hipStream_t stream);
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+size_t w4a16_gate_up_workspace_bytes(int64_t M, int64_t K, int64_t N);
 int w4a8_gate_up(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq_gate, const uint32_t* sz_gate,
                  const uint32_t* wq_up, const uint32_t* sz_up, int64_t N, int G, int act, uint16_t* H, uint8_t* xq,
                  float* xscale, uint8_t* hq, float* hscale, void* workspace, size_t workspace_bytes,
@@ -411,7 +419,8 @@ const char* w4_status_string(int status);
  * (thread-local storage, valid until the next failing call). */
 const char* w4_last_error(void);
 
-/* Version of this ABI, currently 3 (3: w4a8_gate_up emits the down
+/* Version of this ABI, currently 4 (4: w4a16_gate_up takes an optional
+ * workspace, w4a16_gate_up_workspace_bytes; 3: w4a8_gate_up emits the down
  * projection's E4M3 input; w4a8_gemm_e4m3; w4a16_gemm_noalloc). */
 int w4_abi_version(void);
 

@@ -33,7 +33,8 @@ def test_header_declares_the_boundary():
               "w4a16_gemm", "w4a8_gemm", "w4_gemm_workspace_bytes", "w4a8_gemm_workspace_bytes",
               "w4_status_string", "w4_last_error",
               "w4_abi_version", "w4_portable_save", "w4_portable_info_read", "w4_portable_load",
-              "w4a16_gate_up", "w4a8_gate_up", "w4_nf4_levels", "w4_nf4_quantize", "w4_nf4_gemv",
+              "w4a16_gate_up", "w4a16_gate_up_workspace_bytes", "w4a8_gate_up", "w4_nf4_levels", "w4_nf4_quantize",
+              "w4_nf4_gemv",
               "w4a16_gemm_noalloc", "w4a8_gate_up_workspace_bytes", "w4a8_gemm_e4m3"):
         assert n in names
 
@@ -76,7 +77,7 @@ def test_read_probe_library_is_separate(lib):
 
 def test_status_strings(lib):
     import w4_dequant_gemm_amd as w4
-    assert w4.w4_abi_version() == 3
+    assert w4.w4_abi_version() == 4
     assert w4.w4_status_string(0) == "ok"
     assert w4.w4_status_string(1) == "invalid argument"
     assert w4.w4_status_string(2) == "unsupported configuration"
@@ -242,11 +243,20 @@ def test_gate_up_validation(lib):
     import w4_dequant_gemm_amd as w4
     fake = ctypes.c_void_p(0x1000)
     g = lib.w4a16_gate_up
-    assert g(fake, 33, 4000, fake, fake, fake, fake, 64, 32, 1, fake, None) == 2      # tiled form, K % 64 != 0
+    assert g(fake, 33, 4000, fake, fake, fake, fake, 64, 32, 1, fake, None, 0, None) == 2   # tiled, K % 64 != 0
     assert "multiple of 64" in w4.w4_last_error()
-    assert g(fake, 1, 4096, fake, fake, fake, fake, 64, 128, 3, fake, None) == 1      # unknown activation
-    assert g(fake, 1, 4096, fake, fake, None, fake, 64, 128, 1, fake, None) == 1      # no up weights
-    assert g(None, 0, 4096, None, None, None, None, 64, 128, 1, None, None) == 0      # nothing to do
+    assert g(fake, 1, 4096, fake, fake, fake, fake, 64, 128, 3, fake, None, 0, None) == 1   # unknown activation
+    assert g(fake, 1, 4096, fake, fake, None, fake, 64, 128, 1, fake, None, 0, None) == 1   # no up weights
+    assert g(None, 0, 4096, None, None, None, None, 64, 128, 1, None, None, 0, None) == 0   # nothing to do
+    assert g(fake, 300, 4096, fake, fake, fake, fake, 64, 128, 1, fake, ctypes.c_void_p(0x1004), 4096,
+             None) == 1                                                                 # misaligned workspace
+    # the optional split of the pair kernel's last round: 256 x 128 output
+    # tiles, partial tiles of 256 x 256 fp32 (both sums)
+    gw16 = lib.w4a16_gate_up_workspace_bytes
+    assert gw16(2048, 4096, 14336) == 128 * 2 * 256 * 256 * 4       # 896 tiles: the last 128 in halves
+    assert gw16(2048, 4096, 16384) == 0                              # 1024 tiles: four whole rounds
+    assert gw16(256, 4096, 14336) == 0 and gw16(32, 4096, 14336) == 0   # other kernels
+    assert gw16(300, 4096, 2000) == 32 * 8 * 256 * 256 * 4          # 32 tiles, each in 8 K ranges
     assert lib.w4a8_gate_up(fake, 1, 4096, fake, fake, fake, fake, 64, 128, 2, fake, None, fake, None, None, None,
                             0, None) == 1
     # emitting H's E4M3 form needs hscale and a workspace of the partial row maxima

@@ -678,6 +678,46 @@ def test_gate_up_full_8b_shapes_sampled():
                        f"full 8B gate_up w4a8 M={M}", rows=rows, cols=cols)
 
 
+def test_gate_up_split_last_round():
+    # W4A16 gate and up above 256 rows with the workspace of
+    # w4a16_gate_up_workspace_bytes: the pair kernel's 256 x 128 output tiles
+    # of the last partial round split along K (all 32 tiles of a 300 x 2000
+    # product in 8 ranges; of a 600 x 14336 product, 336 tiles, the last 80 in
+    # 3), NaNs in the workspace on entry; against the oracle on sampled
+    # outputs (split tiles included), and against the unsplit call (an empty
+    # workspace), which differs only in the fp32 order of additions
+    require_gpu()
+    import torch
+    import w4_dequant_gemm_amd as w4
+    for (M, N, K, parts) in ((300, 2000, 4096, (32, 0, 8)), (600, 14336, 4096, (336, 256, 3))):
+        Wg = synth.normal_matrix(70 + N, N, K, 0.02)
+        Wu = synth.normal_matrix(71 + N, N, K, 0.015)
+        qg = oracle.quantize(Wg, 128, "asym")
+        qu = oracle.quantize(Wu, 128, "asym")
+        del Wg, Wu
+        pg, G = prepack_dev(qg)
+        pu, _ = prepack_dev(qu)
+        tiles, t0, splits = parts
+        need = w4.w4a16_gate_up_workspace_bytes(M, K, N)
+        assert need == (tiles - t0) * splits * 256 * 256 * 4, (M, N, need)
+        Xb = synth.to_bf16_bits(synth.normal_matrix(72 + M, M, K))
+        rng = np.random.default_rng(73)
+        rows = np.unique(np.concatenate([rng.choice(M, 24, replace=False), np.arange(M - 4, M)]))
+        cols = np.unique(np.concatenate([rng.choice(N, 192, replace=False), np.arange(N - 8, N)]))
+        ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device="cuda")
+        print(f"[gate_up split] M={M} N={N} K={K} workspace={need}", flush=True)
+        Hs = w4.w4a16_gate_up(bf16_dev(Xb), pg, pu, G, "silu", workspace=ws)
+        Hu = w4.w4a16_gate_up(bf16_dev(Xb), pg, pu, G, "silu", workspace=torch.empty((0,), dtype=torch.uint8,
+                                                                                     device="cuda"))
+        torch.cuda.synchronize()
+        want = oracle.gate_up_ref(Xb, qg, qu, G, "asym", "silu", rows=rows, cols=cols)
+        for H, what in ((Hs, "split"), (Hu, "unsplit")):
+            _check_gate_up(want, H.float().cpu().numpy()[np.ix_(rows, cols)], Xb, qg, qu, G, "asym", "silu", "w4a16",
+                           f"gate_up {what} M={M} N={N}", rows=rows, cols=cols)
+        d = (Hs.float() - Hu.float()).abs().max().item()
+        assert d <= 2 ** -6 * Hu.float().abs().max().item()
+
+
 def test_streaming_k_split_products():
     # 3..64 rows whose widest column blocks are fewer than the compute units:
     # with a workspace the streaming kernel splits K into ranges (fp32

@@ -20,7 +20,7 @@ __all__ = [
     "w4a16_gemm", "w4a16_gemm_noalloc", "w4a8_gemm", "w4_gemm_workspace_bytes", "w4a8_gemm_workspace_bytes", "w4_status_string",
     "w4_last_error",
     "w4_abi_version", "w4_portable_save", "w4_portable_info_read", "w4_portable_load",
-    "w4a16_gate_up", "w4a8_gate_up", "w4a8_gate_up_workspace_bytes", "w4a8_gemm_e4m3", "ACT_SILU", "ACT_GELU_TANH",
+    "w4a16_gate_up", "w4a16_gate_up_workspace_bytes", "w4a8_gate_up", "w4a8_gate_up_workspace_bytes", "w4a8_gemm_e4m3", "ACT_SILU", "ACT_GELU_TANH",
     "w4_nf4_levels", "w4_nf4_quantize", "w4_nf4_gemv",
     "FRACS_PLAIN", "FRACS_11",
 ]
@@ -82,7 +82,9 @@ def lib():
     L.w4_gemm_workspace_bytes.restype = sz_t
     L.w4a8_gemm_workspace_bytes.argtypes = [i64, i64, i64]
     L.w4a8_gemm_workspace_bytes.restype = sz_t
-    L.w4a16_gate_up.argtypes = [P, i64, i64, P, P, P, P, i64, I, I, P, P]
+    L.w4a16_gate_up.argtypes = [P, i64, i64, P, P, P, P, i64, I, I, P, P, sz_t, P]
+    L.w4a16_gate_up_workspace_bytes.argtypes = [i64, i64, i64]
+    L.w4a16_gate_up_workspace_bytes.restype = sz_t
     L.w4a8_gate_up.argtypes = [P, i64, i64, P, P, P, P, i64, I, I, P, P, P, P, P, P, sz_t, P]
     L.w4a8_gate_up_workspace_bytes.argtypes = [i64, i64, i64]
     L.w4a8_gate_up_workspace_bytes.restype = sz_t
@@ -421,16 +423,30 @@ def w4a8_gemm(X: torch.Tensor, wq: torch.Tensor, sz: torch.Tensor, G: int, *, Y=
     return Y, xq, xscale
 
 
-def w4a16_gate_up(X: torch.Tensor, gate: dict, up: dict, G: int, act="silu", *, H=None, stream=None):
+def w4a16_gate_up_workspace_bytes(M: int, K: int, N: int) -> int:
+    """Workspace bytes that let ``w4a16_gate_up`` split K in its last round (0: no split)."""
+    return int(lib().w4a16_gate_up_workspace_bytes(M, K, N))
+
+
+def w4a16_gate_up(X: torch.Tensor, gate: dict, up: dict, G: int, act="silu", *, H=None, workspace=None,
+                  stream=None):
     """Gate and up projections in one pass: ``H = bf16(act(X . Wg'^T) * (X . Wu'^T))``
     for bf16 ``X[M, K]`` (above 32 rows K must be a multiple of 64); ``gate`` and ``up`` are GPU layouts from
-    ``w4_prepack`` (``wq``, ``sz``); ``act`` is ``"silu"`` or ``"gelu_tanh"``."""
+    ``w4_prepack`` (``wq``, ``sz``); ``act`` is ``"silu"`` or ``"gelu_tanh"``.  ``workspace``: a device
+    tensor (an empty one for none); by default one of ``w4a16_gate_up_workspace_bytes`` is allocated."""
     M, K, N = _check_product_shapes("w4a16_gate_up", X, gate["wq"], gate["sz"], G, Y=H, up=up)
     dev = X.device
     H = _empty((M, N), torch.bfloat16, dev) if H is None else H
+    if workspace is None:
+        need = w4a16_gate_up_workspace_bytes(M, K, N)
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev) if need else None
+        if workspace is not None and stream is not None:
+            workspace.record_stream(stream)
+    ws = _dev(workspace, "workspace") if workspace is not None and workspace.numel() else None
+    ws_bytes = _nbytes(workspace) if ws is not None else 0
     rc = lib().w4a16_gate_up(_dev(X, "X", torch.bfloat16), M, K, _dev(gate["wq"], "gate wq"), _dev(gate["sz"], "gate sz"),
                              _dev(up["wq"], "up wq"), _dev(up["sz"], "up sz"), N, G, _ACTS[act],
-                             _dev(H, "H", torch.bfloat16), _stream(dev, stream))
+                             _dev(H, "H", torch.bfloat16), ws, ws_bytes, _stream(dev, stream))
     _check("w4a16_gate_up", rc)
     return H
 

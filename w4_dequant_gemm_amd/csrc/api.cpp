@@ -372,16 +372,30 @@ int w4a8_gemm(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const
 }
 
 
+size_t w4a16_gate_up_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+    if (M <= 0 || K <= 0 || N <= 0) return 0;
+    return w4::pair_workspace_bytes(M, K, N);
+}
+
 int w4a16_gate_up(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq_gate, const uint32_t* sz_gate,
                   const uint32_t* wq_up, const uint32_t* sz_up, int64_t N, int G, int act, uint16_t* H,
-                  hipStream_t stream) {
+                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
     const char* fn = "w4a16_gate_up";
     W4_TRY(gate_up_common(fn, X, M, K, wq_gate, sz_gate, wq_up, sz_up, N, G, act, H));
     if (M == 0 || N == 0) return W4_OK;
+    if (workspace && !aligned16(workspace)) return fail(W4_EINVAL, "%s: workspace is not 16-byte aligned", fn);
     w4::MulParams p{X, nullptr, M, K, N, G, wq_gate, sz_gate, H, false};
     p.wq2 = wq_up;
     p.sz2 = sz_up;
     p.act = act;
+    // the optional split of the tiled form's last round
+    const size_t need = w4::pair_workspace_bytes(M, K, N);
+    if (M > w4::kGateUpMaxM && need > 0 && workspace && workspace_bytes >= need) {
+        const w4::GemmSplit g = w4::pair_split(M, K, N);
+        p.splits = g.splits;
+        p.split_t0 = g.t0;
+        p.ws = static_cast<float*>(workspace);
+    }
     if (M > w4::kGateUpMaxM) return hip_status(w4::launch_gemm_pair(p, stream), fn);
     return hip_status(w4::launch_skinny(p, stream), fn);
 }
@@ -514,7 +528,7 @@ const char* w4_status_string(int status) {
 
 const char* w4_last_error(void) { return g_last_error; }
 
-int w4_abi_version(void) { return 3; }
+int w4_abi_version(void) { return 4; }
 
 static_assert(W4_NOALLOC_SCRATCH_BYTES == w4::kNoAllocScratchBytes, "w4.h and the library agree on the scratch size");
 

@@ -1027,6 +1027,22 @@ __global__ void __launch_bounds__(64 * NW) gemm256_breg_kernel(MulParams p) {
     asm volatile("" ::: "memory");
 
     // epilogue: register r of lane l holds row (r%4) + 4(l/32) + 8(r/4), column l%32
+    if (PAIR && job.part >= 0) {
+        // a K range of a split pair tile: the fp32 sums of both weights as one
+        // 256 x 256 partial tile, gate columns 0..127 and up columns 128..255
+#pragma unroll
+        for (int i = 0; i < FI; ++i)
+#pragma unroll
+            for (int j = 0; j < FJ; ++j) {
+                const int lc = (b_up ? BN / 2 : 0) + wcol + 32 * j + (lane & 31);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int lr = i * 32 + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
+                    p.ws[job.part * (BM * BN) + lr * BN + lc] = acc[i][j][r];
+                }
+            }
+        return;
+    }
     if constexpr (PAIR) {
         // rounds (w, hh): gate wave w and up wave NW / 2 + w put the sums of
         // their row blocks 4 hh .. 4 hh + 3 (16 KB per 32 columns, register
@@ -1125,6 +1141,34 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(MulParams p) {
     } else {
         for (int e = 0; e < 4 && col + e < p.N; ++e) dst[e] = float_to_bf16_bits(yv[e]);
     }
+}
+
+// Sum of the K-split partials of the W4A16 gate and up pair on 256 x 128
+// output tiles: partial tile [256][256] holds the gate sums in columns
+// 0..127 and the up sums in 128..255; H = bf16(act(g) u) with g and u added
+// in split order.  A thread takes four consecutive output columns of a row.
+__global__ void __launch_bounds__(256) splitk_reduce_pair_kernel(MulParams p) {
+    constexpr int BM = big::BM, BN = big::BN, BNO = BN / 2;
+    const int64_t e4 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;   // output of the split tiles
+    const int64_t j = e4 / (BM * BNO);
+    const int lr = static_cast<int>((e4 % (BM * BNO)) / BNO), lc = static_cast<int>(e4 % BNO);
+    const int64_t nt = (p.N + BNO - 1) / BNO;
+    int64_t tr, tc;
+    tile_rc(p.split_t0 + j, (p.M + BM - 1) / BM, nt, tr, tc);
+    const int64_t row = tr * BM + lr, col = tc * BNO + lc;
+    if (row >= p.M || col >= p.N) return;
+    const float* src = p.ws + j * p.splits * (BM * BN) + lr * BN + lc;
+    float4 g = *reinterpret_cast<const float4*>(src);
+    float4 u = *reinterpret_cast<const float4*>(src + BNO);
+    for (int z = 1; z < p.splits; ++z) {
+        const float4 gv = *reinterpret_cast<const float4*>(src + z * (BM * BN));
+        const float4 uv = *reinterpret_cast<const float4*>(src + z * (BM * BN) + BNO);
+        g.x += gv.x; g.y += gv.y; g.z += gv.z; g.w += gv.w;
+        u.x += uv.x; u.y += uv.y; u.z += uv.z; u.w += uv.w;
+    }
+    const float gs[4] = {g.x, g.y, g.z, g.w}, us[4] = {u.x, u.y, u.z, u.w};
+    uint16_t* dst = p.Y + row * p.N + col;
+    for (int e = 0; e < 4 && col + e < p.N; ++e) dst[e] = float_to_bf16_bits(activation(p.act, gs[e]) * us[e]);
 }
 
 }  // namespace
@@ -1285,18 +1329,58 @@ hipError_t launch_gemm_pair(const MulParams& p, hipStream_t stream) {
     // W4A8 with groups of 128 (or whole rows): the fp8 kernel's pair form
     if (use_f8(p)) return launch_gemm_f8_pair(p, stream);
     if (!p.x_fp8 && p.M > 256) {
-        // W4A16: gemm256_breg_kernel on 256 x 128 output tiles
-        const int64_t tiles = ((p.N + big::BN / 2 - 1) / (big::BN / 2)) * ((p.M + big::BM - 1) / big::BM);
+        // W4A16: gemm256_breg_kernel on 256 x 128 output tiles, the tiles of
+        // the last, partial round split along K when the caller gave the
+        // workspace of pair_split (p.splits and p.split_t0 from it)
+        const GemmSplit g = pair_split(p.M, p.K, p.N);
         MulParams q = p;
-        q.splits = 1;
-        q.split_t0 = tiles;
-        q.ws = nullptr;
-        hipLaunchKernelGGL((gemm256_breg_kernel<true, W4_BREG_PAIR_NW>), dim3(static_cast<unsigned>(tiles)),
+        if (q.splits <= 1 || !q.ws) {
+            q.splits = 1;
+            q.split_t0 = g.tiles;
+            q.ws = nullptr;
+        } else if (q.splits != g.splits || q.split_t0 != g.t0) {
+            return hipErrorInvalidValue;
+        }
+        const int64_t wgs = q.split_t0 + (g.tiles - q.split_t0) * q.splits;
+        hipLaunchKernelGGL((gemm256_breg_kernel<true, W4_BREG_PAIR_NW>), dim3(static_cast<unsigned>(wgs)),
                            dim3(breg::Geom<W4_BREG_PAIR_NW>::NT), 0, stream, q);
+        if (q.splits > 1) {
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            const int64_t blocks = (g.tiles - q.split_t0) * (big::BM * big::BN / 2 / 1024);
+            hipLaunchKernelGGL(splitk_reduce_pair_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, q);
+        }
         return hipGetLastError();
     }
     if (p.M <= 64) return p.x_fp8 ? launch_pair_t<64, true>(p, stream) : launch_pair_t<64, false>(p, stream);
     return p.x_fp8 ? launch_pair_t<128, true>(p, stream) : launch_pair_t<128, false>(p, stream);
+}
+
+// K split of the W4A16 pair kernel (above 256 rows, K a multiple of 64):
+// the tiles of the last, partial round over the compute units in as many K
+// ranges as fill it (at most 16, each of at least 8 steps of 64), as for the
+// 256 x 256 GEMM; tiles of 256 x 128 outputs.
+GemmSplit pair_split(int64_t M, int64_t K, int64_t N) {
+    constexpr int64_t kCUs = 256;
+    GemmSplit g{1, 0, 0, big::BM, big::BN / 2};
+    if (M <= 256 || N <= 0 || K % big::BK != 0) return g;
+    g.tiles = ((N + big::BN / 2 - 1) / (big::BN / 2)) * ((M + big::BM - 1) / big::BM);
+    g.t0 = g.tiles;
+    const int64_t rem = g.tiles < kCUs / 2 ? g.tiles : g.tiles % kCUs;
+    if (rem == 0) return g;
+    int64_t s = kCUs / rem;
+    if (s > (K / big::BK) / 8) s = (K / big::BK) / 8;
+    if (s > 16) s = 16;
+    if (s < 2) return g;
+    g.splits = static_cast<int>(s);
+    g.t0 = g.tiles - rem;
+    return g;
+}
+
+size_t pair_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+    const GemmSplit g = pair_split(M, K, N);
+    if (g.splits == 1) return 0;
+    return static_cast<size_t>(g.tiles - g.t0) * g.splits * big::BM * big::BN * sizeof(float);
 }
 
 int64_t gate_up_amax_tiles(int64_t M, int64_t N) { return M <= kGateUpMaxM ? (N + 15) / 16 : (N + 127) / 128; }

@@ -130,6 +130,11 @@ struct GemmSplit {
 };
 GemmSplit gemm_split(int64_t M, int64_t K, int64_t N);
 size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
+// K split of the W4A16 gate and up pair kernel (above 256 rows): its last
+// partial round of 256 x 128 output tiles, and the fp32 workspace it needs
+// (partial tiles of 256 x 256: the gate and up sums side by side)
+GemmSplit pair_split(int64_t M, int64_t K, int64_t N);
+size_t pair_workspace_bytes(int64_t M, int64_t K, int64_t N);
 // W4A8 tiled product above 128 rows with at least 256 output tiles: byte
 // offset (after the split partials, 256-byte aligned) and size of the
 // widened activations in the workspace; gemm_xw_bytes is 0 where the product
