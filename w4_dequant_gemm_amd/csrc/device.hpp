@@ -39,6 +39,20 @@ __device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
     return static_cast<uint16_t>(pack_bf16x2(f, 0.0f) & 0xFFFFu);
 }
 
+// x / s for the E4M3 row quantization, without a division: with r = fl(1/s),
+// the product q1 = fl(x r) corrected once by its exact residual,
+// fl(q1 + fl(x - q1 s) r), with the sign of x (so that -0 stays -0).  For
+// every bf16 x and every row scale s = max(fl(a / 448), 1e-8) of a bf16
+// a >= |x|, clamping this to +-448 and rounding it to E4M3 (nearest even)
+// gives the same code as the correctly rounded fl(x / s) does; that was
+// checked on the host over all such pairs (tests/row_quotient_check.c).
+__device__ __forceinline__ float e4m3_quotient(float x, float s, float r) {
+#pragma clang fp contract(off)
+    const float q1 = x * r;
+    const float e = __builtin_fmaf(-q1, s, x);
+    return __builtin_copysignf(__builtin_fmaf(e, r, q1), x);
+}
+
 // sum_i a.bf16[i] * b.bf16[i] + c  (v_dot2_f32_bf16)
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
@@ -46,6 +60,7 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 }
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // 16-byte load marked non-temporal: streamed weights are read exactly once, so
 // they should not displace reused data (activations, scales) in the caches.

@@ -8,8 +8,10 @@
 //
 // One 256-thread block per row: a max reduction (wavefront butterfly, then
 // LDS across the 4 waves) over the row, or over the partial row maxima its
-// producer left (the fused gate and up pass), then a pass over the row that divides
-// (IEEE, correctly rounded), clamps to +-448 and converts pairs with
+// producer left (the fused gate and up pass), then a pass over the row that
+// divides (a reciprocal product with one exact-residual correction, which
+// gives the codes of the correctly rounded quotient: e4m3_quotient), clamps
+// to +-448 and converts pairs with
 // v_cvt_pk_fp8_f32 (OCP E4M3 on gfx950).  Rows are read 16 bytes per lane,
 // once (kept in registers between the two passes) up to 32768 per row.
 #include "device.hpp"
@@ -35,13 +37,13 @@ __device__ __forceinline__ float amax8(uint4 v, float amax) {
     return amax;
 }
 
-__device__ __forceinline__ void quant8(const RowQuantParams& p, int64_t m, int64_t i, uint4 v, float s) {
+__device__ __forceinline__ void quant8(const RowQuantParams& p, int64_t m, int64_t i, uint4 v, float s, float r) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     float f[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        f[2 * j] = fminf(fmaxf(bf16_lo(w[j]) / s, -448.0f), 448.0f);
-        f[2 * j + 1] = fminf(fmaxf(bf16_hi(w[j]) / s, -448.0f), 448.0f);
+        f[2 * j] = fminf(fmaxf(e4m3_quotient(bf16_lo(w[j]), s, r), -448.0f), 448.0f);
+        f[2 * j + 1] = fminf(fmaxf(e4m3_quotient(bf16_hi(w[j]), s, r), -448.0f), 448.0f);
     }
     int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
     lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
@@ -97,15 +99,16 @@ __global__ void __launch_bounds__(256) rowquant_kernel(RowQuantParams p) {
     float s = amax / 448.0f;
     s = fmaxf(s, 1e-8f);
     if (tid == 0) p.xscale[m] = s;
+    const float rs = 1.0f / s;
 
     if (in_regs) {
 #pragma unroll
         for (int r = 0; r < kRegRow; ++r) {
             const int64_t i = tid + 256 * r;
-            if (i < K8) quant8(p, m, i, v[r], s);
+            if (i < K8) quant8(p, m, i, v[r], s, rs);
         }
     } else {
-        for (int64_t i = tid; i < K8; i += blockDim.x) quant8(p, m, i, x[i], s);
+        for (int64_t i = tid; i < K8; i += blockDim.x) quant8(p, m, i, x[i], s, rs);
     }
 }
 

@@ -401,26 +401,27 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
         if constexpr (QX) {
             // W4A8 rows quantized here, with the arithmetic of the row
             // quantizer: scale = max(max |x| / 448, 1e-8), codes =
-            // e4m3(clamp(x / scale, +-448)) (correctly rounded division,
-            // round to nearest even); the codes, widened exactly to bf16,
-            // are what the products use.  Workgroup 0 also writes the codes
-            // and scales out.
+            // e4m3(clamp(x / scale, +-448)) (round to nearest even; the
+            // quotient from e4m3_quotient, whose codes are those of the
+            // correctly rounded one); the codes, widened exactly to bf16, are
+            // what the products use.  Workgroup 0 also writes the codes and
+            // scales out.  A lane takes one 16-byte unit (eight values)
+            // at a time; the four units of a quarter sit in four neighbouring
+            // lanes, which add their sums of the widened codes.  Those sums
+            // are exact in any order: 32 E4M3 values are multiples of 2^-9
+            // below 2^14 in magnitude, which fp32 holds exactly.
             __shared__ float wave_amax[kDotMaxM][16];
+            const int KU = 4 * KQ;                    // 16-byte units per row
             float amax[MB];
 #pragma unroll
             for (int m = 0; m < MB; ++m) {
                 amax[m] = 0.0f;
-                for (int q = threadIdx.x; q < KQ; q += blockDim.x) {
-                    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(p.X) + static_cast<int64_t>(m) * K + 32 * q);
-                    u32x4_t* dst = reinterpret_cast<u32x4_t*>(lds_x + m * (16 * KQ4) + 16 * q);
+                for (int u = threadIdx.x; u < KU; u += blockDim.x) {
+                    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(p.X) + static_cast<int64_t>(m) * K + 8 * u);
+                    *reinterpret_cast<u32x4_t*>(lds_x + m * (16 * KQ4) + 4 * u) = v;
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const u32x4_t v = src[t];
-                        dst[t] = v;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            amax[m] = fmaxf(fmaxf(amax[m], fabsf(bf16_lo(v[e]))), fabsf(bf16_hi(v[e])));
-                    }
+                    for (int e = 0; e < 4; ++e)
+                        amax[m] = fmaxf(fmaxf(amax[m], fabsf(bf16_lo(v[e]))), fabsf(bf16_hi(v[e])));
                 }
                 amax[m] = wave_max(amax[m]);
                 if (lane == 0) wave_amax[m][wave] = amax[m];
@@ -433,39 +434,39 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
                 float sc = a / 448.0f;
                 sc = fmaxf(sc, 1e-8f);
                 row_scale[m] = sc;
+                const float rsc = 1.0f / sc;
                 if (blockIdx.x == 0 && threadIdx.x == 0) p.xscale_out[m] = sc;
-                for (int q = threadIdx.x; q < KQ; q += blockDim.x) {
-                    u32x4_t* buf = reinterpret_cast<u32x4_t*>(lds_x + m * (16 * KQ4) + 16 * q);
-                    uint32_t codes[8];
-                    float t4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                // KU is a multiple of 4 and the stride a multiple of 64, so
+                // the four lanes of a quarter enter and leave together
+                for (int u = threadIdx.x; u < KU; u += blockDim.x) {
+                    u32x4_t* buf = reinterpret_cast<u32x4_t*>(lds_x + m * (16 * KQ4) + 4 * u);
+                    const u32x4_t v = *buf;
+                    u32x4_t wv;
+                    uint32_t codes[2];
+                    float t2[2] = {0.0f, 0.0f};
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const u32x4_t v = buf[t];
-                        u32x4_t wv;
-#pragma unroll
-                        for (int e = 0; e < 4; e += 2) {
-                            const float f0 = fminf(fmaxf(bf16_lo(v[e]) / sc, -448.0f), 448.0f);
-                            const float f1 = fminf(fmaxf(bf16_hi(v[e]) / sc, -448.0f), 448.0f);
-                            const float f2 = fminf(fmaxf(bf16_lo(v[e + 1]) / sc, -448.0f), 448.0f);
-                            const float f3 = fminf(fmaxf(bf16_hi(v[e + 1]) / sc, -448.0f), 448.0f);
-                            int c4 = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
-                            c4 = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, c4, true);
-                            codes[2 * t + e / 2] = static_cast<uint32_t>(c4);
-                            const float2_t g0 = __builtin_amdgcn_cvt_pk_f32_fp8(c4, false);
-                            const float2_t g1 = __builtin_amdgcn_cvt_pk_f32_fp8(c4, true);
-                            wv[e] = pack_bf16x2(g0[0], g0[1]);
-                            wv[e + 1] = pack_bf16x2(g1[0], g1[1]);
-                            t4[e] = dot2_bf16(wv[e], 0x3F803F80u, t4[e]);
-                            t4[e + 1] = dot2_bf16(wv[e + 1], 0x3F803F80u, t4[e + 1]);
-                        }
-                        buf[t] = wv;
+                    for (int e = 0; e < 4; e += 2) {
+                        const float f0 = fminf(fmaxf(e4m3_quotient(bf16_lo(v[e]), sc, rsc), -448.0f), 448.0f);
+                        const float f1 = fminf(fmaxf(e4m3_quotient(bf16_hi(v[e]), sc, rsc), -448.0f), 448.0f);
+                        const float f2 = fminf(fmaxf(e4m3_quotient(bf16_lo(v[e + 1]), sc, rsc), -448.0f), 448.0f);
+                        const float f3 = fminf(fmaxf(e4m3_quotient(bf16_hi(v[e + 1]), sc, rsc), -448.0f), 448.0f);
+                        int c4 = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
+                        c4 = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, c4, true);
+                        codes[e / 2] = static_cast<uint32_t>(c4);
+                        const float2_t g0 = __builtin_amdgcn_cvt_pk_f32_fp8(c4, false);
+                        const float2_t g1 = __builtin_amdgcn_cvt_pk_f32_fp8(c4, true);
+                        wv[e] = pack_bf16x2(g0[0], g0[1]);
+                        wv[e + 1] = pack_bf16x2(g1[0], g1[1]);
+                        t2[0] = dot2_bf16(wv[e], 0x3F803F80u, t2[0]);
+                        t2[1] = dot2_bf16(wv[e + 1], 0x3F803F80u, t2[1]);
                     }
-                    lds_xs[m * KQ4 + q] = (t4[0] + t4[1]) + (t4[2] + t4[3]);
-                    if (blockIdx.x == 0) {
-                        u32x4_t* out = reinterpret_cast<u32x4_t*>(p.xq_out + static_cast<int64_t>(m) * K + 32 * q);
-                        out[0] = u32x4_t{codes[0], codes[1], codes[2], codes[3]};
-                        out[1] = u32x4_t{codes[4], codes[5], codes[6], codes[7]};
-                    }
+                    *buf = wv;
+                    float qs = t2[0] + t2[1];
+                    qs += __shfl_xor(qs, 1, kWave);
+                    qs += __shfl_xor(qs, 2, kWave);
+                    if ((u & 3) == 0) lds_xs[m * KQ4 + (u >> 2)] = qs;
+                    if (blockIdx.x == 0)
+                        *reinterpret_cast<u32x2_t*>(p.xq_out + static_cast<int64_t>(m) * K + 8 * u) = u32x2_t{codes[0], codes[1]};
                 }
             }
         } else
