@@ -393,6 +393,29 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
         __builtin_amdgcn_sched_barrier(0);
     };
     int step = ks0 + wave;               // every wave has at least one step
+    // With staged activations their first loads go out before the weights':
+    // loads return in order, so the staging below waits for these alone and
+    // not for the weights in flight.  A thread's first quarter of each row
+    // (W4A8 with the rows quantized here: its first kPreQ 16-byte units).
+    constexpr int kPreQ = 2;
+    constexpr int kPre = QX ? kPreQ : (XF8 ? 2 : 4);
+    u32x4_t xpre[MB][kPre];
+    if constexpr (DOTL) {
+#pragma unroll
+        for (int m = 0; m < MB; ++m) {
+            const int64_t row = m < M ? m : M - 1;
+#pragma unroll
+            for (int i = 0; i < kPre; ++i) {
+                // unconditional (a piece past the row reloads its last one and
+                // is not used): a select would make the staging wait for the
+                // weights as well
+                int64_t piece = QX ? static_cast<int64_t>(threadIdx.x) + static_cast<int64_t>(i) * blockDim.x
+                                   : static_cast<int64_t>(threadIdx.x < static_cast<unsigned>(KQ) ? threadIdx.x : KQ - 1) * kPre + i;
+                if (QX && piece >= 4 * static_cast<int64_t>(KQ)) piece = 4 * static_cast<int64_t>(KQ) - 1;
+                xpre[m][i] = reinterpret_cast<const u32x4_t*>(static_cast<const uint8_t*>(p.X) + row * K * (XF8 && !QX ? 1 : 2))[piece];
+            }
+        }
+    }
     issue(step);
     if constexpr (DOTL) {
         // stage the activations while the first weights are in flight:
@@ -416,13 +439,19 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
 #pragma unroll
             for (int m = 0; m < MB; ++m) {
                 amax[m] = 0.0f;
-                for (int u = threadIdx.x; u < KU; u += blockDim.x) {
-                    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(p.X) + static_cast<int64_t>(m) * K + 8 * u);
+                auto take = [&](int u, const u32x4_t& v) {
                     *reinterpret_cast<u32x4_t*>(lds_x + m * (16 * KQ4) + 4 * u) = v;
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         amax[m] = fmaxf(fmaxf(amax[m], fabsf(bf16_lo(v[e]))), fabsf(bf16_hi(v[e])));
+                };
+#pragma unroll
+                for (int i = 0; i < kPreQ; ++i) {
+                    const int u = threadIdx.x + i * blockDim.x;
+                    if (u < KU) take(u, xpre[m][i]);
                 }
+                for (int u = threadIdx.x + kPreQ * blockDim.x; u < KU; u += blockDim.x)
+                    take(u, *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(p.X) + static_cast<int64_t>(m) * K + 8 * u));
                 amax[m] = wave_max(amax[m]);
                 if (lane == 0) wave_amax[m][wave] = amax[m];
             }
@@ -469,41 +498,51 @@ __global__ void __launch_bounds__((skinny_max_threads<MB, MODE>())) gemm_skinny_
                         *reinterpret_cast<u32x2_t*>(p.xq_out + static_cast<int64_t>(m) * K + 8 * u) = u32x2_t{codes[0], codes[1]};
                 }
             }
-        } else
+        } else {
+            // quarter q of row m from its 16-byte pieces (4 of bf16, 2 of E4M3)
+            auto stage = [&](int m, int q, const u32x4_t* vs) {
+                uint32_t w[16];
+                if constexpr (!XF8) {
 #pragma unroll
-        for (int m = 0; m < MB; ++m)
-        for (int q = threadIdx.x; q < KQ; q += blockDim.x) {
-            const int64_t row = m < M ? m : M - 1;
-            uint32_t w[16];
-            if constexpr (!XF8) {
-                const u32x4_t* src = reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(p.X) + row * K + 32 * q);
+                    for (int t = 0; t < 4; ++t)
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const u32x4_t v = src[t];
+                        for (int e = 0; e < 4; ++e) w[4 * t + e] = vs[t][e];
+                } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) w[4 * t + e] = v[e];
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float2_t f0 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(vs[t][e]), false);
+                            const float2_t f1 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(vs[t][e]), true);
+                            w[8 * t + 2 * e] = pack_bf16x2(f0[0], f0[1]);
+                            w[8 * t + 2 * e + 1] = pack_bf16x2(f1[0], f1[1]);
+                        }
                 }
-            } else {
-                const u32x4_t* src = reinterpret_cast<const u32x4_t*>(static_cast<const uint8_t*>(p.X) + row * K + 32 * q);
+                float t4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const u32x4_t v = src[t];
+                for (int i = 0; i < 16; ++i) t4[i & 3] = dot2_bf16(w[i], 0x3F803F80u, t4[i & 3]);
+                u32x4_t* dst = reinterpret_cast<u32x4_t*>(lds_x + m * (16 * KQ4) + 16 * q);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float2_t f0 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v[e]), false);
-                        const float2_t f1 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v[e]), true);
-                        w[8 * t + 2 * e] = pack_bf16x2(f0[0], f0[1]);
-                        w[8 * t + 2 * e + 1] = pack_bf16x2(f1[0], f1[1]);
-                    }
+                for (int t = 0; t < 4; ++t) dst[t] = u32x4_t{w[4 * t], w[4 * t + 1], w[4 * t + 2], w[4 * t + 3]};
+                lds_xs[m * KQ4 + q] = (t4[0] + t4[1]) + (t4[2] + t4[3]);
+            };
+            // the thread's first quarter, loaded before the weights, on its
+            // own (a later quarter's load waits for the weights in flight)
+#pragma unroll
+            for (int m = 0; m < MB; ++m)
+                if (static_cast<int>(threadIdx.x) < KQ) stage(m, threadIdx.x, xpre[m]);
+#pragma unroll
+            for (int m = 0; m < MB; ++m) {
+                const int64_t row = m < M ? m : M - 1;
+                for (int q = threadIdx.x + blockDim.x; q < KQ; q += blockDim.x) {
+                    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(static_cast<const uint8_t*>(p.X) +
+                                                                          (row * K + 32 * q) * (XF8 ? 1 : 2));
+                    u32x4_t vs[kPre];
+#pragma unroll
+                    for (int t = 0; t < kPre; ++t) vs[t] = src[t];
+                    stage(m, q, vs);
                 }
             }
-            float t4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int i = 0; i < 16; ++i) t4[i & 3] = dot2_bf16(w[i], 0x3F803F80u, t4[i & 3]);
-            u32x4_t* dst = reinterpret_cast<u32x4_t*>(lds_x + m * (16 * KQ4) + 16 * q);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) dst[t] = u32x4_t{w[4 * t], w[4 * t + 1], w[4 * t + 2], w[4 * t + 3]};
-            lds_xs[m * KQ4 + q] = (t4[0] + t4[1]) + (t4[2] + t4[3]);
         }
         // zero quarters past K up to a whole step
 #pragma unroll
