@@ -173,11 +173,14 @@ int w4_quantize_rows_e4m3(const uint16_t* X, int64_t M, int64_t K, uint8_t* xq, 
  * fixed order): splits * M * N * 4 bytes of fp32 partial sums when the
  * product splits K across workgroups, else 0.  Above 64 rows the tiled GEMM
  * needs it (a product with few output tiles splits K).  From 3 to 64 rows it
- * is optional: with it, the weight-streaming kernel splits K when its widest
- * column blocks are fewer than the compute units (wider blocks re-read the
- * activations less often); without it (NULL or fewer bytes) the same product
- * runs unsplit.  1 or 2 rows never use one.  Depends on the shape only; 0
- * for shapes the products reject.
+ * is optional.  From 33 to 64 rows with K a multiple of 64 it is the K split
+ * of the tiled GEMM's 64 x 128 tiles, which then take the product (they read
+ * the activations a quarter as often as the weight-streaming kernel).  Below
+ * 33 rows (or with K not a multiple of 64) the weight-streaming kernel splits
+ * K with it when its widest column blocks are fewer than the compute units.
+ * Without it (NULL or fewer bytes) the product runs unsplit on the
+ * weight-streaming kernel.  1 or 2 rows never use one.  Depends on the shape
+ * only; 0 for shapes the products reject.
  */
 size_t w4_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
 

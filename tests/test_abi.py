@@ -133,15 +133,19 @@ def test_gemm_workspace_sizes_and_checks(lib):
     assert ws(2048, 8192, 28672) == 128 * 2 * tile          # 896 tiles: the last 128 in halves
     assert ws(2048, 8192, 32768) == 0                        # 1024 tiles: four full rounds
     assert ws(300, 4096, 33000) == 2 * 8 * tile              # 258 tiles: the last 2 in eighths
-    assert ws(64, 3840, 15360) == 0                          # weight-streaming kernel, enough column blocks
-    assert ws(64, 15360, 3840) == 2 * 64 * 3840 * 4          # streaming kernel, optional K split in 2
+    # 33..64 rows, K a multiple of 64: the 64 x 128 tiles' K split (optional:
+    # without it the weight-streaming kernel runs the product unsplit)
+    mid = 64 * 128 * 4
+    assert ws(64, 3840, 15360) == 120 * 5 * mid              # 120 tiles: 5 splits
+    assert ws(64, 15360, 3840) == 30 * 16 * mid              # 30 tiles: 16 splits
+    assert ws(48, 96, 3840) == 0                             # K not a multiple of 64: streaming, no split
+    assert ws(32, 15360, 3840) == 4 * 32 * 3840 * 4          # streaming kernel, optional K split in 4
     assert ws(16, 14336, 4096) == 4 * 16 * 4096 * 4          # 64 blocks of 64 columns: 4 K ranges
     assert ws(2, 14336, 4096) == 0 and ws(1, 14336, 4096) == 0
     assert ws(16, 4096, 14336) == 0                          # 32-column blocks already: no split
     assert ws(8, 14336, 4096) == 0                           # activation re-reads below 4x the weights
     # 64 < M <= 128: 64 x 128 tiles, split along K towards 512 workgroups,
     # at most 16 ways and at least 4 K steps of 64 each
-    mid = 64 * 128 * 4
     assert ws(128, 3840, 15360) == 240 * 3 * mid             # 240 tiles: 3 splits
     assert ws(100, 15360, 3840) == 60 * 9 * mid              # 60 tiles: 9 splits
     assert ws(128, 576, 130) == 4 * 2 * mid                  # 9 K steps: 2 splits
@@ -159,8 +163,10 @@ def test_gemm_workspace_sizes_and_checks(lib):
     assert ws8(2048, 8192, 32768) == 2048 * 8192 * 2
     assert ws8(300, 4096, 33000) == 2 * 8 * tile + 300 * 4096 * 2       # 258 tiles
     assert ws8(1024, 512, 16384) == 1024 * 512 * 2                       # 256 tiles, none split
-    # fp8 kernel: 64 x 128 tiles, 30 of them in 8 K ranges
-    assert ws8(64, 15360, 3840) == 30 * 8 * 64 * 128 * 4 > ws(64, 15360, 3840)
+    # never less than the W4A16 size (one workspace serves both products):
+    # here the bf16 64 x 128 tiles' 16 K ranges of 30 tiles, more than the
+    # fp8 kernel's 8 ranges
+    assert ws8(64, 15360, 3840) == ws(64, 15360, 3840) == 30 * 16 * mid > 30 * 8 * mid
     # 256 x 256 tiles, 30 of them in 8 K ranges
     assert ws8(1056, 8192, 1500) == 30 * 8 * tile
     for shape in ((128, 3840, 15360), (16, 14336, 4096), (256, 96, 3840), (1, 4096, 14336),

@@ -167,16 +167,16 @@ def test_70b_prefill_gemm_sampled(kind):
 # fl(1/448), so its outputs are W'[n, k] up to two bf16-sized roundings.  The
 # cases pick shapes whose schedule (checked through the workspace sizes)
 # reaches each kernel: the streaming kernel (dot and MFMA forms, its K split),
-# the 64 x 128 tiles with and without a K split, the 128 x 128 tiles (K not a
+# the 64 x 128 tiles with and without a K split (W4A16 from 33 rows), the 128 x 128 tiles (K not a
 # multiple of 64), the 256 x 256 tiles whole, all split, and with only the
 # last partial round split, for W4A8 also on widened activations.
 ONE_HOT_CASES = [
     # label, N, K, G, mode, M, expected schedule
-    ("streaming", 576, 1536, 32, "asym", (1, 8, 16, 48), "stream"),
+    ("streaming", 576, 1536, 32, "asym", (1, 8, 16, 24), "stream"),
     ("streaming G128", 1000, 8192, 128, "asym", (2, 16), "stream"),
     ("streaming one row, 8B up width", 14336, 512, 128, "asym", (1,), "stream"),
-    ("streaming K split", 1000, 8192, 128, "asym", (40,), "stream-split"),
-    ("64x128 split", 1536, 1024, 128, "asym", (65, 100), "split"),
+    ("streaming K split", 1000, 8192, 128, "asym", (24,), "stream-split"),
+    ("64x128 split", 1536, 1024, 128, "asym", (40, 65, 100), "split"),
     ("64x128 whole", 32768, 256, 32, "sym", (128,), "whole"),
     ("128x128", 300, 1568, 32, "asym", (130,), "whole"),
     ("256x256 all split", 1000, 1024, 128, "asym", (300,), "split"),
@@ -723,10 +723,11 @@ def test_streaming_k_split_products():
     # with a workspace the streaming kernel splits K into ranges (fp32
     # partials, summed by a second kernel), without one it runs unsplit; both
     # against the oracle and against each other, on a ragged N (16 blocks of
-    # 64 columns and 15 K ranges, or 32 of 32 and 8 for four row blocks),
-    # W4A16 and W4A8, NaNs in the workspace on entry.  W4A8 above 32 rows
-    # (groups of 128) runs on the fp8 kernel instead, with the workspace its
-    # schedule requires.
+    # 64 columns and 15 K ranges), W4A16 and W4A8, NaNs in the workspace on
+    # entry.  Above 32 rows W4A16 with a workspace runs on the 64 x 128 tiles
+    # (their own K split) and W4A8 with groups of 128 on the fp8 kernel; the
+    # streaming kernel's four-row-block split (32 blocks of 32 columns, 8 K
+    # ranges) is then reached by W4A8 with groups of 64.
     require_gpu()
     import torch
     import w4_dequant_gemm_amd as w4
@@ -738,7 +739,10 @@ def test_streaming_k_split_products():
     for M in (16, 32, 40, 64):
         Xb = synth.to_bf16_bits(synth.normal_matrix(66 + M, M, K))
         need = w4.w4_gemm_workspace_bytes(M, K, N)
-        assert need == (15 if M <= 32 else 8) * M * N * 4      # 16 blocks of 64 columns, or 32 of 32
+        if M <= 32:
+            assert need == 15 * M * N * 4                       # 16 blocks of 64 columns
+        else:
+            assert need > 0                                     # the 64 x 128 tiles' split of K
         ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device="cuda")
         print(f"[k-split] M={M} N={N} K={K} workspace={need}", flush=True)
         Ys = w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G, workspace=ws)
@@ -764,6 +768,20 @@ def test_streaming_k_split_products():
         # the two schedules differ only in the order of fp32 additions
         d = (Ys.float() - Yu.float()).abs().max().item()
         assert d <= 2 ** -6 * Yu.float().abs().max().item()
+        if M > 32:
+            # W4A8, groups of 64: the streaming kernel's four row blocks, K
+            # split 8 ways with the workspace (32 blocks of 32 columns)
+            q64 = oracle.quantize(W, 64, "asym")
+            pk64, _ = prepack_dev(q64)
+            need64 = w4.w4a8_gemm_workspace_bytes(M, K, N)
+            assert need64 >= 8 * M * N * 4                      # (and the fp8 schedule's for groups of 128)
+            ws64 = torch.full((need64 // 4,), float("nan"), dtype=torch.float32, device="cuda")
+            Y64s, _, _ = w4.w4a8_gemm(bf16_dev(Xb), pk64["wq"], pk64["sz"], 64, workspace=ws64)
+            Y64u, _, _ = w4.w4a8_gemm(bf16_dev(Xb), pk64["wq"], pk64["sz"], 64, workspace=none)
+            torch.cuda.synchronize()
+            want64, _, _ = oracle.w4a8_ref(Xb, q64["packed"], q64["scale"], q64["zero"], 64, "asym")
+            for got, what in ((Y64s, "w4a8 G=64 split"), (Y64u, "w4a8 G=64 unsplit")):
+                check_products(want64, got.float().cpu().numpy(), X8, q64, 64, "asym", f"{what} M={M}")
 
 
 def test_zero_points_outside_the_code_range():
@@ -772,7 +790,8 @@ def test_zero_points_outside_the_code_range():
     # all-negative ones z > 15.  Every product path must still use the exact
     # W' = (u - z) s; the fp8 W4A8 kernel restores the part of z beyond its
     # clamped operand separately.  Rows at 300 take the 256 x 256 tiles
-    # (W4A8: the fp8 kernel), 40 the streaming kernel, 100 the 64 x 128 tiles.
+    # (W4A8: the fp8 kernel), 24 the streaming kernel, 40 and 100 the 64 x 128
+    # tiles (W4A8: the fp8 kernel).
     require_gpu()
     import torch
     import w4_dequant_gemm_amd as w4
@@ -784,7 +803,7 @@ def test_zero_points_outside_the_code_range():
     z = oracle.f16_bits_to_f32(q["zero"])
     assert (z < 0).sum() >= N and (z > 15).sum() >= N // 7
     pk, G = prepack_dev(q)
-    for M in (300, 40, 100):
+    for M in (300, 24, 40, 100):
         print(f"[zero outside 0..15] M={M}", flush=True)
         Xb = synth.to_bf16_bits(synth.normal_matrix(81 + M, M, K))
         Y = w4.w4a16_gemm(bf16_dev(Xb), pk["wq"], pk["sz"], G)

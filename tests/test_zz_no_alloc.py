@@ -14,10 +14,13 @@ from helpers import bf16_dev, bits16, check_products, require_gpu, to_dev
 pytestmark = pytest.mark.gpu
 
 # (label, N, K, M): a 16-way K split of 15 output tiles of 256 x 256 (60 MiB
-# of partial tiles), then a smaller 64 x 128-tile split, then the streaming
-# kernel's optional split, then a shape with no split at all
+# of partial tiles), then a smaller 64 x 128-tile split, then the same tiles
+# at 40 rows (below 65 rows they take the product only when the scratch
+# holds their split), then the streaming kernel's optional split, then a
+# shape with no split at all
 CASES = [("12B down M=256", 3840, 15360, 256), ("mid split", 1536, 1024, 100),
-         ("streaming split", 1000, 8192, 40), ("one row", 1000, 8192, 1)]
+         ("mid split at 40 rows", 1000, 8192, 40), ("streaming split", 1000, 8192, 24),
+         ("one row", 1000, 8192, 1)]
 
 
 def test_noalloc_matches_the_workspace_entry_point():

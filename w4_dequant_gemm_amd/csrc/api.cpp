@@ -293,7 +293,12 @@ int w4_quantize_rows_e4m3(const uint16_t* X, int64_t M, int64_t K, uint8_t* xq, 
 
 size_t w4_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
     if (M <= 0 || K <= 0 || N <= 0) return 0;
-    if (M <= w4::kSkinnyMaxM) return w4::skinny_workspace_bytes(M, K, N);   // optional
+    if (M <= w4::kSkinnyMaxM) {
+        // optional: the tiled kernel's split from kTiledFromM rows (K a
+        // multiple of 64), the streaming kernel's below
+        if (M >= w4::kTiledFromM && w4::use_mid(M, K)) return w4::gemm_workspace_bytes(M, K, N);
+        return w4::skinny_workspace_bytes(M, K, N);
+    }
     return w4::gemm_workspace_bytes(M, K, N);
 }
 
@@ -311,12 +316,22 @@ size_t w4a8_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
 }
 
 namespace {
+// W4A16 on the tiled kernel: always above the streaming kernel's rows; from
+// kTiledFromM rows on when K suits the 64 x 128 tiles and the workspace holds
+// their K split (the streaming kernel's workspace stays optional)
+bool w4a16_tiled(int64_t M, int64_t K, int64_t N, const void* workspace, size_t workspace_bytes) {
+    if (M > w4::kSkinnyMaxM) return true;
+    if (M < w4::kTiledFromM || !w4::use_mid(M, K)) return false;
+    const size_t need = w4::gemm_workspace_bytes(M, K, N);
+    return need == 0 || (workspace && aligned16(workspace) && workspace_bytes >= need);
+}
+
 int w4a16_run(const char* fn, const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq, const uint32_t* sz,
               int64_t N, int G, uint16_t* Y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     W4_TRY(mul_common(fn, X, M, K, wq, sz, N, G, Y, workspace, workspace_bytes, false));
     if (M == 0 || N == 0) return W4_OK;
     w4::MulParams p{X, nullptr, M, K, N, G, wq, sz, Y, false};
-    if (M <= w4::kSkinnyMaxM)
+    if (!w4a16_tiled(M, K, N, workspace, workspace_bytes))
         return hip_status(w4::launch_skinny(with_skinny_split(p, workspace, workspace_bytes), stream), fn);
     return hip_status(w4::launch_gemm(with_split(p, workspace), stream), fn);
 }

@@ -108,6 +108,16 @@ int64_t gate_up_amax_tiles(int64_t M, int64_t N);
 #define W4_SKINNY_MAX 64
 #endif
 constexpr int64_t kSkinnyMaxM = W4_SKINNY_MAX;
+// W4A16 from this many rows up to kSkinnyMaxM: the tiled kernel's 64 x 128
+// tiles (activations read once per 128 columns, against once per 32 in the
+// streaming kernel's four row blocks) when K is a multiple of 64 and the
+// caller's workspace holds their K split; otherwise the streaming kernel
+#ifndef W4_TILED_FROM_M
+#define W4_TILED_FROM_M 33
+#endif
+constexpr int64_t kTiledFromM = W4_TILED_FROM_M;
+// the 64 x 128-tile kernel serves this shape (M up to 128, K a multiple of 64)
+bool use_mid(int64_t M, int64_t K);
 hipError_t launch_skinny(const MulParams& p, hipStream_t stream);
 // K ranges of the streaming kernel's split for this shape and activation
 // width in bytes (1: no split), and the fp32 partial sums it needs (sized for
