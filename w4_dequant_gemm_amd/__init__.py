@@ -9,6 +9,7 @@ non-zero status, the function raises.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from typing import Optional, Sequence
 
@@ -144,13 +145,20 @@ def _dev(t: Optional[torch.Tensor], name: str, dtype=None):
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
-    return ctypes.c_void_p(t.data_ptr())
+    return t.data_ptr()
+
+
+# the current stream's handle as an integer, without building a Stream object
+# (about 2 us of host time per call otherwise, as much as a launch)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream(device, stream=None):
     if stream is None:
+        if _raw_stream is not None and device.index is not None:
+            return _raw_stream(device.index)
         stream = torch.cuda.current_stream(device)
-    return ctypes.c_void_p(stream.cuda_stream)
+    return stream.cuda_stream
 
 
 def _fracs(fracs: Sequence[float]):
@@ -201,11 +209,17 @@ def _check_product_shapes(fn: str, X, wq, sz, G: int, Y=None, xq=None, xscale=No
     return M, K, N
 
 
+@functools.lru_cache(maxsize=4096)
+def _need_bytes(M: int, K: int, N: int, w4a8: bool) -> int:
+    # a function of the shape only
+    return w4a8_gemm_workspace_bytes(M, K, N) if w4a8 else w4_gemm_workspace_bytes(M, K, N)
+
+
 def _workspace(M: int, K: int, N: int, device, workspace, stream, w4a8=False):
     """(pointer, bytes) of the product's workspace: the caller's tensor, or a
     new byte tensor of the fastest schedule's size when the shape uses one
     (kept alive on ``stream``)."""
-    need = w4a8_gemm_workspace_bytes(M, K, N) if w4a8 else w4_gemm_workspace_bytes(M, K, N)
+    need = _need_bytes(M, K, N, w4a8)
     if workspace is None:
         if need == 0:
             return None, 0
