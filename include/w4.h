@@ -211,15 +211,16 @@ size_t w4a8_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
  * "Weight-only methods: GPTQ, AWQ and the file formats" (weights dequantized
  * inside the matmul, arithmetic in 16-bit), "Scale and zero point" (the
  * reconstruction (q - z) s) and "The Problem & Context" (decode reads every
- * weight once).  One entry point for every M: up to 64 rows run a kernel that
+ * weight once).  One entry point for every M: up to 32 rows run a kernel that
  * streams the weights once (bandwidth bound), larger M a tiled bf16-MFMA
- * GEMM.
+ * GEMM; from 33 to 64 rows the tiled GEMM runs when the workspace holds its
+ * K split (K a multiple of 64), else the streaming kernel.
  *   X  [M, K] bf16 in;  wq, sz as written by w4_prepack;  Y [M, N] bf16 out.
  *   workspace: device memory of workspace_bytes >= w4_gemm_workspace_bytes(M,
  *      K, N) bytes, 16-byte aligned, owned by the caller; its contents on
  *      entry do not matter and are overwritten.  May be NULL when that size
- *      is 0, or when M <= 64 (the split is then not used).  Calls in flight
- *      at the same time need separate workspaces.
+ *      is 0, or when M <= 64 (the streaming kernel then runs unsplit).  Calls
+ *      in flight at the same time need separate workspaces.
  *      Too small or NULL when needed: W4_EINVAL.
  *   With a split K the partial sums are added in a fixed order: results do
  *   not depend on timing.
