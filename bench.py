@@ -235,14 +235,15 @@ def main():
         log(f"[bench] decode: {ms:.4f} ms/step, {value:.1f} GB/s, per launch {per_launch_ms*1e3:.2f} us")
 
     if args.only in ("all", "extra"):
-        # per-shape GEMV times at M = 1, 4, 16 (same rotation of weight copies)
-        for M in (1, 4, 16):
+        # per-shape GEMV times at M = 1, 4, 16 and 64 (same rotation of weight copies;
+        # 64 rows on the 64 x 128 tiles with their K split)
+        for M in (1, 4, 16, 64):
             xu = bf16(synth.activations_bf16_bits(wl8, M, Ku))
             xd = bf16(synth.activations_bf16_bits(wl8, M, Kd))
             yu = torch.empty((M, Nu), dtype=torch.bfloat16, device=dev)
             yd = torch.empty((M, Nd), dtype=torch.bfloat16, device=dev)
             for name, x, y, wts, N, K in (("up", xu, yu, ups, Nu, Ku), ("down", xd, yd, downs, Nd, Kd)):
-                # the optional workspace of the streaming kernel's K split
+                # the optional workspace of the K split (streaming kernel, or from 33 rows the tiles)
                 wsp = torch.empty((max(w4.w4_gemm_workspace_bytes(M, K, N), 16),), dtype=torch.uint8, device=dev)
 
                 def run(x=x, y=y, wts=wts, wsp=wsp):
