@@ -6,8 +6,8 @@
 // The scale is recomputed on every call, so one row's outlier never costs
 // another row resolution, and an all-zero row stays exactly zero.
 //
-// One 256-thread block per row: a max reduction (wavefront butterfly, then
-// LDS across the 4 waves) over the row, or over the partial row maxima its
+// One block per row (256 threads, 1024 for rows of 12288 or more values): a
+// max reduction (wavefront butterfly, then LDS across the waves) over the row, or over the partial row maxima its
 // producer left (the fused gate and up pass), then a pass over the row that
 // divides (a reciprocal product with one exact-residual correction, which
 // gives the codes of the correctly rounded quotient: e4m3_quotient), clamps
@@ -22,10 +22,9 @@
 namespace w4 {
 namespace {
 
-// Row of up to kRegRow * 256 16-byte pieces (K <= 32768): each thread keeps
-// its pieces in registers between the maximum and the quantizing pass, so
-// the row is read once; longer rows are read twice.
-constexpr int kRegRow = 16;
+// Row of up to REG * NT 16-byte pieces (K <= 32768 for both block sizes):
+// each thread keeps its pieces in registers between the maximum and the
+// quantizing pass, so the row is read once; longer rows are read twice.
 
 __device__ __forceinline__ float amax8(uint4 v, float amax) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -64,37 +63,41 @@ __device__ __forceinline__ void quant8(const RowQuantParams& p, int64_t m, int64
     }
 }
 
-__global__ void __launch_bounds__(256) rowquant_kernel(RowQuantParams p) {
-    __shared__ float red[4];
+template <int NT, int REG>
+__global__ void __launch_bounds__(NT) rowquant_kernel(RowQuantParams p) {
+    constexpr int NWV = NT / 64;
+    __shared__ float red[NWV];
     const int64_t m = blockIdx.x;
     const int64_t K8 = p.K / 8;
     const uint4* x = reinterpret_cast<const uint4*>(p.X + m * p.K);
     const int tid = threadIdx.x;
-    const bool in_regs = K8 <= kRegRow * 256;
+    const bool in_regs = K8 <= REG * NT;
 
     float amax = 0.0f;
-    uint4 v[kRegRow];
+    uint4 v[REG];
     if (in_regs) {
 #pragma unroll
-        for (int r = 0; r < kRegRow; ++r) {
-            const int64_t i = tid + 256 * r;
+        for (int r = 0; r < REG; ++r) {
+            const int64_t i = tid + NT * r;
             v[r] = i < K8 ? x[i] : make_uint4(0u, 0u, 0u, 0u);
         }
     }
     if (p.amax_part) {
         // the producer of X left the row's maximum in partial maxima
         const float* part = p.amax_part + m * p.amax_tiles;
-        for (int64_t i = tid; i < p.amax_tiles; i += blockDim.x) amax = fmaxf(amax, part[i]);
+        for (int64_t i = tid; i < p.amax_tiles; i += NT) amax = fmaxf(amax, part[i]);
     } else if (in_regs) {
 #pragma unroll
-        for (int r = 0; r < kRegRow; ++r) amax = amax8(v[r], amax);
+        for (int r = 0; r < REG; ++r) amax = amax8(v[r], amax);
     } else {
-        for (int64_t i = tid; i < K8; i += blockDim.x) amax = amax8(x[i], amax);
+        for (int64_t i = tid; i < K8; i += NT) amax = amax8(x[i], amax);
     }
     amax = wave_max(amax);
     if ((tid & 63) == 0) red[tid >> 6] = amax;
     __syncthreads();
-    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    amax = red[0];
+#pragma unroll
+    for (int w = 1; w < NWV; ++w) amax = fmaxf(amax, red[w]);
 
     float s = amax / 448.0f;
     s = fmaxf(s, 1e-8f);
@@ -103,12 +106,12 @@ __global__ void __launch_bounds__(256) rowquant_kernel(RowQuantParams p) {
 
     if (in_regs) {
 #pragma unroll
-        for (int r = 0; r < kRegRow; ++r) {
-            const int64_t i = tid + 256 * r;
+        for (int r = 0; r < REG; ++r) {
+            const int64_t i = tid + NT * r;
             if (i < K8) quant8(p, m, i, v[r], s, rs);
         }
     } else {
-        for (int64_t i = tid; i < K8; i += blockDim.x) quant8(p, m, i, x[i], s, rs);
+        for (int64_t i = tid; i < K8; i += NT) quant8(p, m, i, x[i], s, rs);
     }
 }
 
@@ -116,7 +119,17 @@ __global__ void __launch_bounds__(256) rowquant_kernel(RowQuantParams p) {
 
 hipError_t launch_rowquant(const RowQuantParams& p, hipStream_t stream) {
     if (p.M == 0) return hipSuccess;
-    hipLaunchKernelGGL(rowquant_kernel, dim3(static_cast<unsigned>(p.M)), dim3(256), 0, stream, p);
+#ifndef W4_RQ_WIDE_K
+#define W4_RQ_WIDE_K 12288
+#endif
+    // long rows: four times the threads, so that the quantizing pass of one
+    // row (all on one compute unit) takes a quarter of the time (M = 2048:
+    // K = 28672 38.2 -> 32.9 us; at K = 8192 the 256-thread blocks are 4%
+    // faster)
+    if (p.K >= W4_RQ_WIDE_K)
+        hipLaunchKernelGGL((rowquant_kernel<1024, 4>), dim3(static_cast<unsigned>(p.M)), dim3(1024), 0, stream, p);
+    else
+        hipLaunchKernelGGL((rowquant_kernel<256, 16>), dim3(static_cast<unsigned>(p.M)), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
