@@ -830,18 +830,23 @@ def test_gate_up_emits_the_down_projection_input():
     import w4_dequant_gemm_amd as w4
     wl = synth.WORKLOADS["llama8b_decode"]
     W = synth.weight(wl, 0, rows=2 * 1056)
-    for N in (1024, 1056):
+    for N in (1024, 1056, 12416):
         # N = 1056 leaves a partial last 128-column tile (the tiled pass) and
-        # gives the down weight [640, N] groups of 32
-        qg = oracle.quantize(np.ascontiguousarray(W[:N]), 128, "asym")
-        qu = oracle.quantize(np.ascontiguousarray(W[N:2 * N]), 128, "asym")
+        # gives the down weight [640, N] groups of 32; rows of H of 12416
+        # values take the row quantizer's 1024-thread blocks
+        if N > 1056:
+            qg = oracle.quantize(synth.weight(wl, 0, rows=N), 128, "asym")
+            qu = oracle.quantize(synth.normal_matrix(86, N, W.shape[1], 0.02), 128, "asym")
+        else:
+            qg = oracle.quantize(np.ascontiguousarray(W[:N]), 128, "asym")
+            qu = oracle.quantize(np.ascontiguousarray(W[N:2 * N]), 128, "asym")
         Gd = 128 if N % 128 == 0 else 32
         qd = oracle.quantize(synth.normal_matrix(85, 640, N, 0.03), Gd, "asym")
         pg, _ = prepack_dev(qg)
         pu, _ = prepack_dev(qu)
         pd, _ = prepack_dev(qd)
         K = W.shape[1]
-        for M in (1, 2, 16, 32, 48, 300):
+        for M in ((1, 2, 16, 32, 48, 300) if N <= 1056 else (1, 48)):
             print(f"[gate_up e4m3] N={N} M={M}", flush=True)
             Xb = _x("llama8b_decode", M, K)
             Xb[0] = 0
