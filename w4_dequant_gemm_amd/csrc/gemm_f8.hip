@@ -38,6 +38,7 @@
 // restored exactly: acc += s (zc - z) sum_k xq, with sum_k xq from one more
 // MFMA against ones, only in steps where some column of the wave needs it.
 #include <type_traits>
+#include <utility>
 
 #include "device.hpp"
 #include "kernels.hpp"
@@ -66,6 +67,21 @@ struct Geom {
 }  // namespace f8
 
 typedef _Float16 half2v_t __attribute__((ext_vector_type(2)));
+
+constexpr int gcd2(int a, int b) { return b == 0 ? a : gcd2(b, a % b); }
+constexpr int lcm3(int a, int b, int c) {
+    const int ab = a / gcd2(a, b) * b;
+    return ab / gcd2(ab, c) * c;
+}
+// f(integral_constant<int, 0>) .. f(integral_constant<int, N - 1>), in order
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 typedef short short2v_t __attribute__((ext_vector_type(2)));
 
 // The work of one workgroup (1-D grid): workgroup b < split_t0 computes tile b
@@ -128,12 +144,14 @@ __device__ __forceinline__ void f8_word(uint32_t w, uint32_t bias, half2v_t nb, 
 }
 
 // A raw buffer descriptor (base, no stride, `bytes` records; reads past the
-// end return zeros), kept in SGPRs.
+// end return zeros), kept in SGPRs: every word passes readfirstlane, since a
+// size computed with a division comes from the VALU, and a descriptor the
+// compiler cannot prove uniform wraps each load in a loop over its values.
 __device__ __forceinline__ u32x4_t buffer_rsrc(const void* base, uint32_t bytes) {
     const uint64_t a = reinterpret_cast<uint64_t>(base);
     return u32x4_t{static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a))),
                    static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32))) & 0xFFFFu,
-                   bytes, 0x00020000u};
+                   static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(bytes)), 0x00020000u};
 }
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t as_rsrc(const u32x4_t& r) {
     return __builtin_amdgcn_make_buffer_rsrc(
@@ -152,15 +170,38 @@ __device__ __forceinline__ float4_t mfma_f8_16x16x128(const int8x_t& a, const in
 // combines the two through LDS into H = bf16(act(g) u) (both sums scaled by
 // the row scale first) and, with p.amax_part, records each row's maximum |H|
 // over the tile's columns.  Never split along K.
-template <int BM_, int BN_, int WR_, int WC_, bool PAIR = false>
+//
+// SA activation stages and DW weight register sets: the activations of step
+// kt go out SA - 1 steps ahead, its codes DW steps ahead (converted one step
+// ahead).  A step ends waiting for the loads of all but its last SA - 2
+// steps, so codes loaded further ahead than SA steps would be waited for
+// early: DW <= SA.  Large tiles are compute-bound and take (3, 2); small ones
+// stream their weights at a few hundred rows or fewer and take deeper pipelines.
+template <int BM_, int BN_, int WR_, int WC_, bool PAIR = false, int SA_ = 3, int DW_ = 2>
 __global__ void __launch_bounds__(64 * WR_ * WC_) gemm_f8_kernel(MulParams p) {
     using namespace f8;
     using Gm = Geom<BM_, BN_, WR_, WC_>;
     constexpr int BM = Gm::BM, BN = Gm::BN, WC = Gm::WC, STAGE = Gm::STAGE, ADMA = Gm::ADMA, RB = Gm::RB,
                   WN = Gm::WN, CB = Gm::CB, NSLOT = Gm::NSLOT, NCONV = Gm::NCONV, BLOAD = Gm::BLOAD;
+    constexpr int SA = SA_, DW = DW_;
+    static_assert(SA >= 3 && DW >= 2 && DW <= SA, "pipeline depths");
+    // one array per stage (as separate objects their addresses stay constants)
     __shared__ __attribute__((aligned(16))) uint8_t lds_a0[STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t lds_a1[STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t lds_a2[STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a3[SA > 3 ? STAGE : 1];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a4[SA > 4 ? STAGE : 1];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a5[SA > 5 ? STAGE : 1];
+    static_assert(SA <= 6, "at most six stages");
+    auto stage_a = [&](auto S) -> uint8_t* {
+        constexpr int si = decltype(S)::value;
+        if constexpr (si == 0) return lds_a0;
+        else if constexpr (si == 1) return lds_a1;
+        else if constexpr (si == 2) return lds_a2;
+        else if constexpr (si == 3) return lds_a3;
+        else if constexpr (si == 4) return lds_a4;
+        else return lds_a5;
+    };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -302,16 +343,16 @@ __global__ void __launch_bounds__(64 * WR_ * WC_) gemm_f8_kernel(MulParams p) {
                        static_cast<int>(hi[0]), static_cast<int>(hi[1]), static_cast<int>(hi[2]), static_cast<int>(hi[3])};
     };
 
+    // a step ends with the activations of the next one in LDS: all loads
+    // done but those of the last SA - 2 steps (loads complete in order)
     constexpr int kStepLoads = ADMA + BLOAD;
-    auto step_end3 = [&]() {
+    constexpr int kLeft = (SA - 2) * kStepLoads;
+    static_assert(kLeft < 64, "vmcnt range");
+    auto step_end = [&]() {
         asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt((kStepLoads & 15) | (7 << 4) | ((kStepLoads >> 4) << 14));
+        __builtin_amdgcn_s_waitcnt((kLeft & 15) | (7 << 4) | ((kLeft >> 4) << 14));
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-    };
-    auto stage_a = [&](auto S) -> uint8_t* {
-        constexpr int s3 = decltype(S)::value;
-        return s3 == 0 ? lds_a0 : (s3 == 1 ? lds_a1 : lds_a2);
     };
     auto scale_add = [&](int v, const BOps& cur, const float4_t& t) {
         const float sv = cur.s[v % CB];
@@ -320,7 +361,8 @@ __global__ void __launch_bounds__(64 * WR_ * WC_) gemm_f8_kernel(MulParams p) {
     };
     // step kt: MFMAs on `cur` (converted during step kt - 1) and the A stage
     // of kt; `ready` (codes of step kt + 1) converted into `nxt`; the codes of
-    // step kt + 2 loaded into `next` and its activations sent to LDS
+    // step kt + DW loaded into `next`, the activations of step kt + SA - 1
+    // sent to LDS
 #ifndef W4_F8_TROT
 #define W4_F8_TROT 2
 #endif
@@ -337,10 +379,10 @@ __global__ void __launch_bounds__(64 * WR_ * WC_) gemm_f8_kernel(MulParams p) {
     auto conv_slot = [](int i) constexpr {
         return CONV_EVERY >= 1 ? CONV0 + i * CONV_EVERY : CONV0 + i * (NSLOT - CONV0) / NCONV;
     };
-    auto step3 = [&](int kt, auto SA, Regs& next, const Regs& ready, const BOps& cur, BOps& nxt) {
-        constexpr int sa = decltype(SA)::value;
+    auto step = [&](int kt, auto S, Regs& next, const Regs& ready, const BOps& cur, BOps& nxt) __attribute__((always_inline)) {
+        constexpr int sa = decltype(S)::value;
         const uint8_t* As = stage_a(std::integral_constant<int, sa>{});
-        uint8_t* Ad = stage_a(std::integral_constant<int, (sa + 2) % 3>{});
+        uint8_t* Ad = stage_a(std::integral_constant<int, (sa + SA - 1) % SA>{});
         int8x_t fa = frag_a(As, 0);
         float4_t T[TROT];
 #pragma unroll
@@ -360,10 +402,10 @@ __global__ void __launch_bounds__(64 * WR_ * WC_) gemm_f8_kernel(MulParams p) {
                     if (conv_slot(i) == u) conv_item(i, ready, nxt);
             }
             if (u % LOAD_EVERY == LOAD_EVERY / 2 - 1) {
-                load_item(kt + 2, next, u / LOAD_EVERY);
+                load_item(kt + DW, next, u / LOAD_EVERY);
                 asm volatile("" ::: "memory");
             }
-            if (u % DMA_EVERY == DMA_EVERY - 1) dma_item(kt + 2, Ad, u / DMA_EVERY);
+            if (u % DMA_EVERY == DMA_EVERY - 1) dma_item(kt + SA - 1, Ad, u / DMA_EVERY);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -393,21 +435,21 @@ __global__ void __launch_bounds__(64 * WR_ * WC_) gemm_f8_kernel(MulParams p) {
                     for (int e = 0; e < 4; ++e) acc[rb][cb][e] = fmaf(corr[cb], t1[e], acc[rb][cb][e]);
             }
         }
-        step_end3();
+        step_end();
     };
 
-    Regs r0, r1;
-    BOps o0, o1;
+    Regs rr[DW];
+    BOps oo[2];
+    static_for<SA - 1>([&](auto S) {
 #pragma unroll
-    for (int it = 0; it < ADMA; ++it) dma_item(0, lds_a0, it);
+        for (int it = 0; it < ADMA; ++it) dma_item(decltype(S)::value, stage_a(S), it);
+    });
 #pragma unroll
-    for (int it = 0; it < ADMA; ++it) dma_item(1, lds_a1, it);
+    for (int st = 0; st < DW; ++st)
 #pragma unroll
-    for (int it = 0; it < BLOAD; ++it) load_item(0, r0, it);
+        for (int it = 0; it < BLOAD; ++it) load_item(st, rr[st], it);
 #pragma unroll
-    for (int it = 0; it < BLOAD; ++it) load_item(1, r1, it);
-#pragma unroll
-    for (int it = 0; it < NCONV; ++it) conv_item(it, r0, o0);
+    for (int it = 0; it < NCONV; ++it) conv_item(it, rr[0], oo[0]);
     // the tile's row scales for the epilogue of a whole tile (a partial tile
     // leaves them to the split sum), fetched under the first steps' loads
     for (int r = tid; r < BM; r += Gm::NT) lds_xs[r] = job.part < 0 && m_base + r < M ? p.xscale[m_base + r] : 1.0f;
@@ -415,18 +457,28 @@ __global__ void __launch_bounds__(64 * WR_ * WC_) gemm_f8_kernel(MulParams p) {
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    // A stages cycle with period 3, code registers and operands with period 2
-    for (int kt = 0; kt < KT; kt += 6) {
-        step3(kt, I0{}, r0, r1, o0, o1);
-        if (kt + 1 < KT) step3(kt + 1, I1{}, r1, r0, o1, o0);
-        if (kt + 2 < KT) step3(kt + 2, I2{}, r0, r1, o0, o1);
-        if (kt + 3 < KT) step3(kt + 3, I0{}, r1, r0, o1, o0);
-        if (kt + 4 < KT) step3(kt + 4, I1{}, r0, r1, o0, o1);
-        if (kt + 5 < KT) step3(kt + 5, I2{}, r1, r0, o1, o0);
+    // A stages cycle with period SA, code registers with period DW and
+    // converted operands with period 2: the loop body is their common period.
+    // Whole rounds of U steps run with no branch between the steps, then the
+    // steps left over: with a branch around every step the compiler's waits
+    // for the code loads follow the worst of the joined paths, and a wave
+    // waited for every load in flight (those of the steps ahead included)
+    // early in each step.
+    constexpr int U = lcm3(SA, DW, 2);
+    int kt = 0;
+    for (; kt + U <= KT; kt += U) {
+        static_for<U>([&](auto I) __attribute__((always_inline)) {
+            constexpr int u = decltype(I)::value;
+            step(kt + u, std::integral_constant<int, u % SA>{}, rr[u % DW], rr[(u + 1) % DW], oo[u % 2],
+                 oo[(u + 1) % 2]);
+        });
     }
+    static_for<U - 1>([&](auto I) __attribute__((always_inline)) {
+        constexpr int u = decltype(I)::value;
+        if (kt + u < KT)
+            step(kt + u, std::integral_constant<int, u % SA>{}, rr[u % DW], rr[(u + 1) % DW], oo[u % 2],
+                 oo[(u + 1) % 2]);
+    });
     __builtin_amdgcn_s_waitcnt(0);
     asm volatile("" ::: "memory");
 
@@ -548,12 +600,27 @@ bool f8_fits_buffers(int64_t M, int64_t K, int64_t N) {
 #define W4_F8_TILE 0      // 0: chosen by the estimate; 1..6 forces one of the tiles
 #endif
 namespace {
+#ifndef W4_F8_DS
+#define W4_F8_DS 3        // pipeline depth (SA = DW) of the tiles of 64 or 128 rows
+#endif
+#ifndef W4_F8_DB
+#define W4_F8_DB 3        // the same for the 256-row tiles narrower than 256 columns (LDS: at most 4)
+#endif
 struct F8Tile {
     int bm, bn, wr, wc;
+    int sa, dw;          // activation stages, code register sets
     double step_us;
 };
-constexpr F8Tile kF8Tiles[] = {{256, 256, 1, 8, 2.22}, {128, 256, 1, 8, 1.48}, {256, 128, 2, 4, 1.46},
-                               {256, 64, 2, 4, 0.83},  {64, 128, 1, 8, 0.59},  {128, 64, 2, 4, 0.59}};
+#ifndef W4_F8_DSW
+#define W4_F8_DSW W4_F8_DS
+#endif
+#ifndef W4_F8_DBW
+#define W4_F8_DBW W4_F8_DB
+#endif
+constexpr int kDs = W4_F8_DS, kDb = W4_F8_DB, kDsw = W4_F8_DSW, kDbw = W4_F8_DBW;
+constexpr F8Tile kF8Tiles[] = {{256, 256, 1, 8, 3, 2, 2.22},         {128, 256, 1, 8, kDs, kDsw, 1.48},
+                               {256, 128, 2, 4, kDb, kDbw, 1.46},    {256, 64, 2, 4, kDb, kDbw, 0.83},
+                               {64, 128, 1, 8, kDs, kDsw, 0.59},     {128, 64, 2, 4, kDs, kDsw, 0.59}};
 constexpr int kF8NTiles = sizeof(kF8Tiles) / sizeof(kF8Tiles[0]);
 
 GemmSplit f8_schedule(int t, int64_t M, int64_t K, int64_t N) {
@@ -630,11 +697,16 @@ hipError_t launch_gemm_f8(const MulParams& p, hipStream_t stream) {
     const dim3 block(static_cast<unsigned>(64 * kF8Tiles[t].wr * kF8Tiles[t].wc));
     switch (t) {
         case 0: hipLaunchKernelGGL((gemm_f8_kernel<256, 256, 1, 8>), grid, block, 0, stream, q); break;
-        case 1: hipLaunchKernelGGL((gemm_f8_kernel<128, 256, 1, 8>), grid, block, 0, stream, q); break;
-        case 2: hipLaunchKernelGGL((gemm_f8_kernel<256, 128, 2, 4>), grid, block, 0, stream, q); break;
-        case 3: hipLaunchKernelGGL((gemm_f8_kernel<256, 64, 2, 4>), grid, block, 0, stream, q); break;
-        case 4: hipLaunchKernelGGL((gemm_f8_kernel<64, 128, 1, 8>), grid, block, 0, stream, q); break;
-        default: hipLaunchKernelGGL((gemm_f8_kernel<128, 64, 2, 4>), grid, block, 0, stream, q); break;
+#define W4_F8_LAUNCH(T)                                                                                         \
+    hipLaunchKernelGGL((gemm_f8_kernel<kF8Tiles[T].bm, kF8Tiles[T].bn, kF8Tiles[T].wr, kF8Tiles[T].wc, false,      \
+                                       kF8Tiles[T].sa, kF8Tiles[T].dw>),                                           \
+                       grid, block, 0, stream, q)
+        case 1: W4_F8_LAUNCH(1); break;
+        case 2: W4_F8_LAUNCH(2); break;
+        case 3: W4_F8_LAUNCH(3); break;
+        case 4: W4_F8_LAUNCH(4); break;
+        default: W4_F8_LAUNCH(5); break;
+#undef W4_F8_LAUNCH
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || q.splits == 1) return e;
