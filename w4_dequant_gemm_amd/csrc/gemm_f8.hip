@@ -135,9 +135,12 @@ __device__ __forceinline__ void f8_word(uint32_t w, uint32_t bias, half2v_t nb, 
     const half2v_t d1 = __builtin_elementwise_fma(e1, sixteenth, nb16);
     const half2v_t d2 = e2 + nb;
     const half2v_t d3 = __builtin_elementwise_fma(e3, sixteenth, nb16);
-    short2v_t r0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(short2v_t{0, 0}, d0, 1.0f, false);
+    // the first conversion of a pair writes the low half and keeps the high
+    // half of its first operand, which the second one overwrites: any
+    // register will do there (a zero would cost a move)
+    short2v_t r0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(__builtin_bit_cast(short2v_t, d1), d0, 1.0f, false);
     r0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r0, d1, 1.0f, true);
-    short2v_t r1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(short2v_t{0, 0}, d2, 1.0f, false);
+    short2v_t r1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(__builtin_bit_cast(short2v_t, d3), d2, 1.0f, false);
     r1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r1, d3, 1.0f, true);
     o0 = __builtin_bit_cast(uint32_t, r0);
     o1 = __builtin_bit_cast(uint32_t, r1);
@@ -595,7 +598,9 @@ bool f8_fits_buffers(int64_t M, int64_t K, int64_t N) {
 //   + the split tiles' steps x the same + the fp32 partials written and read.
 // The times per 128-k step are measured on one MI355X (one workgroup per
 // compute unit, all compute units busy); the partials cost about one
-// microsecond per 6 MB (written, then read by the split sum).
+// microsecond per 4 MB (written, then read by the split sum: fitted to every
+// tile timed on the 12B shapes from 40 to 384 rows, where it picks the
+// fastest tile or one within 0.6 us of it).
 #ifndef W4_F8_TILE
 #define W4_F8_TILE 0      // 0: chosen by the estimate; 1..6 forces one of the tiles
 #endif
@@ -645,7 +650,7 @@ double f8_estimate_us(int t, const GemmSplit& g, int64_t K) {
     double us = static_cast<double>((g.t0 + kCUs - 1) / kCUs) * KT * kF8Tiles[t].step_us;
     if (g.splits > 1) {
         us += static_cast<double>((KT + g.splits - 1) / g.splits) * kF8Tiles[t].step_us;
-        us += static_cast<double>(g.tiles - g.t0) * g.splits * g.bm * g.bn * 4 / 6.0e6 + 3.0;
+        us += static_cast<double>(g.tiles - g.t0) * g.splits * g.bm * g.bn * 4 / 4.0e6 + 3.0;
     }
     return us;
 }
