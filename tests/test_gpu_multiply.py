@@ -167,7 +167,9 @@ def test_70b_prefill_gemm_sampled(kind):
 # fl(1/448), so its outputs are W'[n, k] up to two bf16-sized roundings.  The
 # cases pick shapes whose schedule (checked through the workspace sizes)
 # reaches each kernel: the streaming kernel (dot and MFMA forms, its K split),
-# the 64 x 128 tiles with and without a K split (W4A16 from 33 rows), the 128 x 128 tiles (K not a
+# the 64 x 128 tiles with and without a K split (W4A16 from 33 rows; with
+# groups of 128 or per-channel rows on the fp8 kernel's bf16-activation form,
+# whose split rounds the ranges down), the 128 x 128 tiles (K not a
 # multiple of 64), the 256 x 256 tiles whole, all split, and with only the
 # last partial round split, for W4A8 also on widened activations.
 ONE_HOT_CASES = [
@@ -177,6 +179,7 @@ ONE_HOT_CASES = [
     ("streaming one row, 8B up width", 14336, 512, 128, "asym", (1,), "stream"),
     ("streaming K split", 1000, 8192, 128, "asym", (24,), "stream-split"),
     ("64x128 split", 1536, 1024, 128, "asym", (40, 65, 100), "split"),
+    ("64x128 per-channel", 700, 1024, 1024, "asym", (48, 128), "split"),
     ("64x128 whole", 32768, 256, 32, "sym", (128,), "whole"),
     ("128x128", 300, 1568, 32, "asym", (130,), "whole"),
     ("256x256 all split", 1000, 1024, 128, "asym", (300,), "split"),
@@ -591,16 +594,19 @@ def test_gate_up_products(kind):
 
 
 def test_mid_size_products():
-    # 64 < M <= 128 with K a multiple of 64: 64 x 128 output tiles, split
-    # along K into fp32 partials (a caller workspace holding NaNs on entry)
-    # when the tiles are few; both kinds, every group size, per-channel
-    # groups, ragged M and N, a zero row, and the 12B shapes at M = 128 on
+    # 64 < M <= 128 (and 33 with a workspace) with K a multiple of 64:
+    # 64 x 128 output tiles (W4A16 with groups of 128 or per-channel rows on
+    # the fp8 kernel's bf16-activation form), split along K into fp32
+    # partials (a caller workspace holding NaNs on entry) when the tiles are
+    # few; both kinds, every group size, per-channel groups, ragged M and N,
+    # a zero row, and the 12B shapes at M = 128 on
     # sampled outputs
     require_gpu()
     import torch
     import w4_dequant_gemm_amd as w4
     cases = [(200, 1024, 32, "asym", (65, 100)), (333, 2048, 64, "sym", (128,)),
-             (130, 576, 576, "asym", (97,)), (256, 4096, 128, "asym", (128, 70))]
+             (130, 576, 576, "asym", (97,)), (256, 4096, 128, "asym", (128, 70)),
+             (700, 1024, 1024, "sym", (33, 128))]
     for N, K, G, mode, Ms in cases:
         W = synth.normal_matrix(60 + N, N, K, 0.03)
         q = oracle.quantize(W, G, mode)

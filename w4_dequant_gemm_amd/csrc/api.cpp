@@ -158,8 +158,9 @@ w4::MulParams with_skinny_split(w4::MulParams p, void* workspace, size_t workspa
 
 // the tiled-GEMM launch of a product, with the K split that its workspace was sized for
 w4::MulParams with_split(w4::MulParams p, void* workspace) {
-    const w4::GemmSplit g =
-        p.x_fp8 && f8_product(p.M, p.K, p.N, p.G) ? w4::f8_split(p.M, p.K, p.N) : w4::gemm_split(p.M, p.K, p.N);
+    const w4::GemmSplit g = p.x_fp8 && f8_product(p.M, p.K, p.N, p.G) ? w4::f8_split(p.M, p.K, p.N)
+                            : w4::a16_runs(p.M, p.K, p.N, p.G, p.x_fp8) ? w4::a16_split(p.M, p.K, p.N)
+                                                                          : w4::gemm_split(p.M, p.K, p.N);
     p.splits = g.splits;
     p.split_t0 = g.t0;
     p.ws = g.splits > 1 ? static_cast<float*>(workspace) : nullptr;

@@ -1228,8 +1228,15 @@ bool f8_eligible(int64_t M, int64_t K, int G) {
 bool use_f8(const MulParams& p) { return p.x_fp8 && f8_eligible(p.M, p.K, p.G) && f8_fits_buffers(p.M, p.K, p.N); }
 
 // Mid-size tiles: when there are fewer tiles than the target, every tile is
-// split along K (at most 16 ways, each of at least 4 steps of 64).
-GemmSplit gemm_split(int64_t M, int64_t K, int64_t N) {
+// split along K (at most 16 ways, each of at least 4 steps of 64).  The
+// mid-size kernel takes the split count rounded up (more workgroups than the
+// target: two or three share a compute unit); the bf16-activation form of
+// the fp8 kernel (two 512-thread workgroups a compute unit) rounded down, so
+// that its workgroups fit one round (8B up at M = 64: 112 tiles in 4 ranges,
+// 448 workgroups, 27.3 -> 23.3 us; with 5 ranges 560 left a second round).
+// The workspace is sized for the larger, rounded-up split.
+namespace {
+GemmSplit mid_or_big_split(int64_t M, int64_t K, int64_t N, bool round_down) {
     constexpr int64_t kCUs = 256;
     GemmSplit g{1, 0, 0, big::BM, big::BN};
     if (N <= 0 || K % big::BK != 0) return g;
@@ -1238,7 +1245,7 @@ GemmSplit gemm_split(int64_t M, int64_t K, int64_t N) {
         g.bn = 128;
         g.tiles = ((N + g.bn - 1) / g.bn) * ((M + g.bm - 1) / g.bm);
         g.t0 = g.tiles;
-        int64_t s = (W4_MID_WGS + g.tiles - 1) / g.tiles;
+        int64_t s = round_down ? W4_MID_WGS / g.tiles : (W4_MID_WGS + g.tiles - 1) / g.tiles;
         if (s > (K / big::BK) / 4) s = (K / big::BK) / 4;
         if (s > 16) s = 16;
         if (s < 2) return g;
@@ -1262,6 +1269,16 @@ GemmSplit gemm_split(int64_t M, int64_t K, int64_t N) {
     g.t0 = g.tiles - rem;
     return g;
 }
+}  // namespace
+GemmSplit gemm_split(int64_t M, int64_t K, int64_t N) { return mid_or_big_split(M, K, N, false); }
+
+#ifndef W4_A16_MID
+#define W4_A16_MID 1
+#endif
+bool a16_runs(int64_t M, int64_t K, int64_t N, int G, bool x_fp8) {
+    return W4_A16_MID && W4_MID_BM == 64 && !x_fp8 && use_mid(M, K) && a16_eligible(M, K, N, G);
+}
+GemmSplit a16_split(int64_t M, int64_t K, int64_t N) { return mid_or_big_split(M, K, N, true); }
 
 size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
     const GemmSplit g = gemm_split(M, K, N);
@@ -1441,6 +1458,7 @@ hipError_t launch_gemm(const MulParams& p, hipStream_t stream) {
     // tiles and split schedule
     if (use_f8(p)) return launch_gemm_f8(p, stream);
     if (use_mid(p.M, p.K)) {
+        if (a16_runs(p.M, p.K, p.N, p.G, p.x_fp8)) return launch_gemm_a16(p, stream);
         constexpr int bm = W4_MID_BM;
         return p.x_fp8 ? launch_mid<bm, true>(p, stream) : launch_mid<bm, false>(p, stream);
     }

@@ -135,12 +135,9 @@ __device__ __forceinline__ void f8_word(uint32_t w, uint32_t bias, half2v_t nb, 
     const half2v_t d1 = __builtin_elementwise_fma(e1, sixteenth, nb16);
     const half2v_t d2 = e2 + nb;
     const half2v_t d3 = __builtin_elementwise_fma(e3, sixteenth, nb16);
-    // the first conversion of a pair writes the low half and keeps the high
-    // half of its first operand, which the second one overwrites: any
-    // register will do there (a zero would cost a move)
-    short2v_t r0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(__builtin_bit_cast(short2v_t, d1), d0, 1.0f, false);
+    short2v_t r0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(short2v_t{0, 0}, d0, 1.0f, false);
     r0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r0, d1, 1.0f, true);
-    short2v_t r1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(__builtin_bit_cast(short2v_t, d3), d2, 1.0f, false);
+    short2v_t r1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(short2v_t{0, 0}, d2, 1.0f, false);
     r1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r1, d3, 1.0f, true);
     o0 = __builtin_bit_cast(uint32_t, r0);
     o1 = __builtin_bit_cast(uint32_t, r1);
@@ -180,14 +177,25 @@ __device__ __forceinline__ float4_t mfma_f8_16x16x128(const int8x_t& a, const in
 // steps, so codes loaded further ahead than SA steps would be waited for
 // early: DW <= SA.  Large tiles are compute-bound and take (3, 2); small ones
 // stream their weights at a few hundred rows or fewer and take deeper pipelines.
-template <int BM_, int BN_, int WR_, int WC_, bool PAIR = false, int SA_ = 3, int DW_ = 2>
+//
+// A16: W4A16 on the same tiles (groups of 128): bf16 activations (two bytes
+// a k in the stages), the exact bf16 values 128 + u as the B operand of
+// v_mfma_f32_16x16x32_bf16 (four per 16 x 16 block and step; MFMA j takes,
+// from every quarter q, the 8 k at 32 q + 8 j, and the activation fragment
+// the same k), the row sums of the step's activations from four more MFMAs
+// against ones, and per group and output acc += s (T - (128 + z) X1): exact
+// weights, any zero point.
+template <int BM_, int BN_, int WR_, int WC_, bool PAIR = false, int SA_ = 3, int DW_ = 2, bool A16 = false>
 __global__ void __launch_bounds__(64 * WR_ * WC_) gemm_f8_kernel(MulParams p) {
     using namespace f8;
     using Gm = Geom<BM_, BN_, WR_, WC_>;
-    constexpr int BM = Gm::BM, BN = Gm::BN, WC = Gm::WC, STAGE = Gm::STAGE, ADMA = Gm::ADMA, RB = Gm::RB,
-                  WN = Gm::WN, CB = Gm::CB, NSLOT = Gm::NSLOT, NCONV = Gm::NCONV, BLOAD = Gm::BLOAD;
+    constexpr int AB = A16 ? 2 : 1;               // bytes per activation
+    constexpr int BM = Gm::BM, BN = Gm::BN, WC = Gm::WC, STAGE = Gm::STAGE * AB, ADMA = Gm::ADMA * AB,
+                  RB = Gm::RB, WN = Gm::WN, CB = Gm::CB, NSLOT = Gm::NSLOT, NCONV = Gm::NCONV, BLOAD = Gm::BLOAD;
     constexpr int SA = SA_, DW = DW_;
     static_assert(SA >= 3 && DW >= 2 && DW <= SA, "pipeline depths");
+    static_assert(NSLOT % ADMA == 0, "slot plan");
+    static_assert(!A16 || (!PAIR && RB <= 8), "bf16 activations: plain products of up to 8 row blocks a wave");
     // one array per stage (as separate objects their addresses stay constants)
     __shared__ __attribute__((aligned(16))) uint8_t lds_a0[STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t lds_a1[STAGE];
@@ -235,12 +243,21 @@ __global__ void __launch_bounds__(64 * WR_ * WC_) gemm_f8_kernel(MulParams p) {
     // buffer's end and read as zeros (their outputs are never stored).
     const int a_row0 = 8 * wave * ADMA + (lane >> 3);
     const int a_chunk = (lane & 7) ^ (lane >> 4) ^ ((wave * ADMA) & 1 ? 4 : 0);
-    const u32x4_t a_rsrc = buffer_rsrc(p.X, static_cast<uint32_t>(M * K));
+    const u32x4_t a_rsrc = buffer_rsrc(p.X, static_cast<uint32_t>(M * K * AB));
     const uint32_t a_voff = static_cast<uint32_t>((m_base + a_row0) * K + a_chunk * 16);
+    // A16: a 256-byte stage row of 16 chunks, chunk ch of row r at position
+    // ch ^ (r & 15); load `it` fills rows 4 (wave ADMA + it) .. + 3, lane l
+    // row 4 (wave ADMA + it) + l / 16 at position l % 16
     auto dma_item = [&](int kt, uint8_t* stage, int it) {
         kt = (kt < KT ? kt : KT - 1) + kb;
-        const uint32_t voff = (a_voff ^ ((it & 1) ? 64u : 0u)) + static_cast<uint32_t>(8 * it * K);
-        const uint32_t soff = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(kt * BK));
+        uint32_t voff;
+        if constexpr (A16) {
+            const int r = 4 * (wave * ADMA + it) + (lane >> 4);
+            voff = static_cast<uint32_t>((m_base + r) * (2 * K) + 16 * ((lane & 15) ^ (r & 15)));
+        } else {
+            voff = (a_voff ^ ((it & 1) ? 64u : 0u)) + static_cast<uint32_t>(8 * it * K);
+        }
+        const uint32_t soff = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(kt * BK * AB));
         // Issued as plain instructions: the compiler cannot tell the three
         // stages apart and would wait for every pending direct-to-LDS load
         // before any LDS read.  No register result (the data goes to LDS at
@@ -301,16 +318,39 @@ __global__ void __launch_bounds__(64 * WR_ * WC_) gemm_f8_kernel(MulParams p) {
     };
     // converted operands of one step: E4M3 bytes of u - zc, the group scale,
     // and whether any column of the wave has zc != z
-    struct BOps {
+    struct BOps8 {
         int8x_t b[CB];
         float s[CB];
         uint32_t oor;
     };
+    // A16: per block the four MFMA operands (bf16 pairs 128 + u), the group
+    // scale and 128 + z
+    struct BOps16 {
+        u32x4_t b[CB][4];
+        float s[CB];
+        float zb[CB];
+    };
+    using BOps = std::conditional_t<A16, BOps16, BOps8>;
+    [[maybe_unused]] uint32_t bias128 = 0;
+    if constexpr (A16) bias128 = opaque_vgpr(kBf16Bias128x2);
     const uint32_t bias = opaque_vgpr(0x64006400u);   // two fp16 1024.0
     half2v_t nbv[CB], nb16v[CB];
     uint32_t oor_lane = 0;
     auto conv_item = [&](int it, const Regs& r, BOps& o) {
         const int cb = it >> 2, wi = it & 3;
+        if constexpr (A16) {
+            if (wi == 0) {
+                const uint32_t szw = r.s[cb];
+                o.s[cb] = half_bits_to_float(szw);
+                o.zb[cb] = 128.0f + half_bits_to_float(szw >> 16);
+            }
+            const uint32_t w = r.q[cb][wi];
+            uint32_t b0 = nibble_pair_bf16(w, 0, bias128), b1 = nibble_pair_bf16(w, 1, bias128),
+                     b2 = nibble_pair_bf16(w, 2, bias128), b3 = nibble_pair_bf16(w, 3, bias128);
+            asm volatile("" : "+v"(b0), "+v"(b1), "+v"(b2), "+v"(b3));
+            o.b[cb][wi] = u32x4_t{b0, b1, b2, b3};
+            return;
+        } else {
         if (wi == 0) {
             const uint32_t szw = r.s[cb];
             const float s = half_bits_to_float(szw);
@@ -332,6 +372,7 @@ __global__ void __launch_bounds__(64 * WR_ * WC_) gemm_f8_kernel(MulParams p) {
         o.b[cb][2 * wi + 1] = static_cast<int>(o1);
         if (it == NCONV - 1)
             o.oor = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(__builtin_amdgcn_ballot_w64(oor_lane != 0) != 0));
+        }
     };
 
     // A fragment of the wave's row block rb: stage row row0 + 16 rb + c,
@@ -382,10 +423,73 @@ __global__ void __launch_bounds__(64 * WR_ * WC_) gemm_f8_kernel(MulParams p) {
     auto conv_slot = [](int i) constexpr {
         return CONV_EVERY >= 1 ? CONV0 + i * CONV_EVERY : CONV0 + i * (NSLOT - CONV0) / NCONV;
     };
+    // the conversions, code loads and activation loads of slot u (A16; the
+    // fp8 step spells the same plan out)
+    auto slot_work = [&](int u, int kt, Regs& next, const Regs& ready, BOps& nxt, uint8_t* Ad) __attribute__((always_inline)) {
+        if constexpr (CONV_EVERY >= 1) {
+            if (u >= CONV0 && (u - CONV0) % CONV_EVERY == 0 && (u - CONV0) / CONV_EVERY < NCONV)
+                conv_item((u - CONV0) / CONV_EVERY, ready, nxt);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NCONV; ++i)
+                if (conv_slot(i) == u) conv_item(i, ready, nxt);
+        }
+        if (u % LOAD_EVERY == LOAD_EVERY / 2 - 1) {
+            load_item(kt + DW, next, u / LOAD_EVERY);
+            asm volatile("" ::: "memory");
+        }
+        if (u % DMA_EVERY == DMA_EVERY - 1) dma_item(kt + SA - 1, Ad, u / DMA_EVERY);
+    };
+    // A16: fragment j of row block rb, stage row row0 + 16 rb + c (its low
+    // four bits are c), chunk 4 q + j at position (4 q + j) ^ c
+    auto frag_a16 = [&](const uint8_t* A, int rb, int j) -> bf16x8_t {
+        return *reinterpret_cast<const bf16x8_t*>(A + (row0 + 16 * rb + c) * (2 * BK) + 16 * ((4 * q + j) ^ c));
+    };
     auto step = [&](int kt, auto S, Regs& next, const Regs& ready, const BOps& cur, BOps& nxt) __attribute__((always_inline)) {
         constexpr int sa = decltype(S)::value;
         const uint8_t* As = stage_a(std::integral_constant<int, sa>{});
         uint8_t* Ad = stage_a(std::integral_constant<int, (sa + SA - 1) % SA>{});
+        if constexpr (A16) {
+            const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+            bf16x8_t fa[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) fa[j] = frag_a16(As, 0, j);
+            float4_t X1[RB], T[TROT];
+            auto scale_add16 = [&](int v, const float4_t& t) {
+                const int rb = v / CB, cb = v % CB;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc[rb][cb][e] = fmaf(cur.s[cb], fmaf(-cur.zb[cb], X1[rb][e], t[e]), acc[rb][cb][e]);
+            };
+#pragma unroll
+            for (int u = 0; u < NSLOT; ++u) {
+                const int rb = u / CB, cb = u % CB;
+                __builtin_amdgcn_sched_barrier(0);
+                if (cb == 0) {
+                    // the step's row sums of the block's 16 rows (every column alike)
+                    X1[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[0], ones, float4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+                    for (int j = 1; j < 4; ++j) X1[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[j], ones, X1[rb], 0, 0, 0);
+                }
+                T[u % TROT] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[0], __builtin_bit_cast(bf16x8_t, cur.b[cb][0]),
+                                                                      float4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+                for (int j = 1; j < 4; ++j)
+                    T[u % TROT] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[j], __builtin_bit_cast(bf16x8_t, cur.b[cb][j]),
+                                                                          T[u % TROT], 0, 0, 0);
+                if (cb == CB - 1 && rb + 1 < RB) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) fa[j] = frag_a16(As, rb + 1, j);
+                }
+                if (u >= TROT - 1) scale_add16(u - (TROT - 1), T[(u - (TROT - 1)) % TROT]);
+                slot_work(u, kt, next, ready, nxt, Ad);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int v = NSLOT - (TROT - 1); v < NSLOT; ++v) scale_add16(v, T[v % TROT]);
+            step_end();
+            return;
+        } else {
         int8x_t fa = frag_a(As, 0);
         float4_t T[TROT];
 #pragma unroll
@@ -439,6 +543,7 @@ __global__ void __launch_bounds__(64 * WR_ * WC_) gemm_f8_kernel(MulParams p) {
             }
         }
         step_end();
+        }
     };
 
     Regs rr[DW];
@@ -455,7 +560,7 @@ __global__ void __launch_bounds__(64 * WR_ * WC_) gemm_f8_kernel(MulParams p) {
     for (int it = 0; it < NCONV; ++it) conv_item(it, rr[0], oo[0]);
     // the tile's row scales for the epilogue of a whole tile (a partial tile
     // leaves them to the split sum), fetched under the first steps' loads
-    for (int r = tid; r < BM; r += Gm::NT) lds_xs[r] = job.part < 0 && m_base + r < M ? p.xscale[m_base + r] : 1.0f;
+    for (int r = tid; r < BM; r += Gm::NT) lds_xs[r] = !A16 && job.part < 0 && m_base + r < M ? p.xscale[m_base + r] : 1.0f;
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_s_barrier();
@@ -716,6 +821,32 @@ hipError_t launch_gemm_f8(const MulParams& p, hipStream_t stream) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || q.splits == 1) return e;
     return launch_split_sum(q, g.bm, g.bn, g.tiles, stream);
+}
+
+// W4A16 with groups of 128 on the same kernel's 64 x 128 tiles (bf16
+// activations, A16), in place of the mid-size kernel for up to 128 rows: its
+// tiles, its K split (fp32 partial tiles in the same layout, each range a
+// whole number of 128-k steps) and its workspace.
+bool a16_eligible(int64_t M, int64_t K, int64_t N, int G) {
+    return M > 0 && M <= 128 && K % f8::BK == 0 && G % f8::BK == 0 && f8_fits_buffers(2 * M, K, N);
+}
+hipError_t launch_gemm_a16(const MulParams& p, hipStream_t stream) {
+    if (p.x_fp8 || !a16_eligible(p.M, p.K, p.N, p.G)) return hipErrorInvalidValue;
+    constexpr int BM = 64, BN = 128;
+    const int64_t tiles = ((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM);
+    MulParams q = p;
+    if (q.splits <= 1) {
+        q.splits = 1;
+        q.split_t0 = tiles;
+        q.ws = nullptr;
+    }
+    if (q.splits > q.K / f8::BK || q.split_t0 < 0 || q.split_t0 > tiles || (q.splits > 1 && !q.ws))
+        return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>(q.split_t0 + (tiles - q.split_t0) * q.splits));
+    hipLaunchKernelGGL((gemm_f8_kernel<BM, BN, 1, 8, false, 3, 3, true>), grid, dim3(512), 0, stream, q);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || q.splits == 1) return e;
+    return launch_split_sum(q, BM, BN, tiles, stream);
 }
 
 // Gate and up on the fp8 kernel: tiles of BM rows by 128 output columns

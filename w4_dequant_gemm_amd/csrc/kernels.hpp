@@ -160,6 +160,15 @@ size_t gemm_xw_bytes(int64_t M, int64_t K, int64_t N);
 #endif
 constexpr int64_t kF8MinM = W4_F8_MINM;
 bool f8_eligible(int64_t M, int64_t K, int G);
+// W4A16 with groups of 128 (K a multiple of 128) up to 128 rows: the fp8
+// kernel's structure on bf16 activations, 64 x 128 tiles with the mid-size
+// K split (gemm_split)
+bool a16_eligible(int64_t M, int64_t K, int64_t N, int G);
+hipError_t launch_gemm_a16(const MulParams& p, hipStream_t stream);
+// true when the tiled W4A16 product of this shape runs that form, and its K
+// split (gemm_split's rounded down: it fits the workspace gemm_split sizes)
+bool a16_runs(int64_t M, int64_t K, int64_t N, int G, bool x_fp8);
+GemmSplit a16_split(int64_t M, int64_t K, int64_t N);
 // K step of the fp8 kernel (one group of 128 k)
 constexpr int kF8StepK = 128;
 // the fp8 kernel addresses its operands with 31-bit byte offsets
