@@ -326,9 +326,11 @@ int w4a8_gate_up(const uint16_t* X, int64_t M, int64_t K, const uint32_t* wq_gat
                  const uint32_t* wq_up, const uint32_t* sz_up, int64_t N, int G, int act, uint16_t* H, uint8_t* xq,
                  float* xscale, uint8_t* hq, float* hscale, void* workspace, size_t workspace_bytes,
                  hipStream_t stream);
-/* Bytes of workspace w4a8_gate_up needs to emit hq (M * tiles * 4: the
- * partial row maxima of H, 16-column tiles up to 32 rows, 128-column tiles
- * above); 0 for empty shapes. */
+/* Bytes of workspace w4a8_gate_up needs to emit hq, the down projection's
+ * per-row E4M3 input (gowda.ai "LLM fast inference", "Achievement 2": each
+ * activation row is scaled by its own maximum before the FP8 product): M *
+ * tiles * 4, the partial row maxima of H (16-column tiles up to 32 rows,
+ * 128-column tiles above); 0 for empty shapes. */
 size_t w4a8_gate_up_workspace_bytes(int64_t M, int64_t K, int64_t N);
 
 /*
