@@ -550,8 +550,9 @@ def test_gate_up_products(kind):
     # epilogue, against act(X Wg'^T) * (X Wu'^T) in float64: 8B-class rows
     # (gate and up are disjoint row ranges of the 8B up weight), one to 32
     # activation rows in the streaming kernel and 48 to 300 in the tiled pair
-    # GEMM (64-row tiles, 128-row tiles on both sides of M = 128 and at 256,
-    # and W4A16 at 300 the 256-row direct-to-LDS tiles), both activations;
+    # GEMM (W4A16 with G = 128 up to 256 rows: the fp8 kernel's
+    # bf16-activation pair form on 64-row tiles; W4A8: its fp8 pair form;
+    # W4A16 at 300 the 256-row direct-to-LDS tiles), both activations;
     # and a ragged
     # N with symmetric G = 32 weights (the dequantizing form for more than
     # two rows, and the tiled form at 70 rows)

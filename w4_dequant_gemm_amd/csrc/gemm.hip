@@ -1394,6 +1394,10 @@ hipError_t launch_gemm_pair(const MulParams& p, hipStream_t stream) {
         }
         return hipGetLastError();
     }
+#ifndef W4_A16_PAIR
+#define W4_A16_PAIR 1
+#endif
+    if (W4_A16_PAIR && !p.x_fp8 && a16_pair_eligible(p.M, p.K, p.N, p.G)) return launch_gemm_a16_pair(p, stream);
     if (p.M <= 64) return p.x_fp8 ? launch_pair_t<64, true>(p, stream) : launch_pair_t<64, false>(p, stream);
     return p.x_fp8 ? launch_pair_t<128, true>(p, stream) : launch_pair_t<128, false>(p, stream);
 }

@@ -195,7 +195,7 @@ __global__ void __launch_bounds__(64 * WR_ * WC_) gemm_f8_kernel(MulParams p) {
     constexpr int SA = SA_, DW = DW_;
     static_assert(SA >= 3 && DW >= 2 && DW <= SA, "pipeline depths");
     static_assert(NSLOT % ADMA == 0, "slot plan");
-    static_assert(!A16 || (!PAIR && RB <= 8), "bf16 activations: plain products of up to 8 row blocks a wave");
+    static_assert(!A16 || (WR_ == 1 && RB <= 8), "bf16 activations: one wave row of up to 8 row blocks");
     // one array per stage (as separate objects their addresses stay constants)
     __shared__ __attribute__((aligned(16))) uint8_t lds_a0[STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t lds_a1[STAGE];
@@ -847,6 +847,25 @@ hipError_t launch_gemm_a16(const MulParams& p, hipStream_t stream) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || q.splits == 1) return e;
     return launch_split_sum(q, BM, BN, tiles, stream);
+}
+
+// W4A16 gate and up with groups of 128 from 33 to 256 rows on the
+// bf16-activation form: 64-row tiles by 128 output columns (256 weight
+// columns, 128 of each weight), no K split, in place of the mid-size pair
+// kernel.
+bool a16_pair_eligible(int64_t M, int64_t K, int64_t N, int G) {
+    return M > 0 && M <= 256 && K % f8::BK == 0 && G % f8::BK == 0 && f8_fits_buffers(2 * M, K, N);
+}
+hipError_t launch_gemm_a16_pair(const MulParams& p, hipStream_t stream) {
+    if (p.x_fp8 || !p.wq2 || !p.sz2 || !a16_pair_eligible(p.M, p.K, p.N, p.G)) return hipErrorInvalidValue;
+    MulParams q = p;
+    const int64_t tiles = ((p.N + 127) / 128) * ((p.M + 63) / 64);
+    q.splits = 1;
+    q.split_t0 = tiles;
+    q.ws = nullptr;
+    hipLaunchKernelGGL((gemm_f8_kernel<64, 256, 1, 8, true, 3, 3, true>), dim3(static_cast<unsigned>(tiles)), dim3(512), 0,
+                       stream, q);
+    return hipGetLastError();
 }
 
 // Gate and up on the fp8 kernel: tiles of BM rows by 128 output columns

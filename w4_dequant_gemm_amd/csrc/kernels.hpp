@@ -168,6 +168,9 @@ hipError_t launch_gemm_a16(const MulParams& p, hipStream_t stream);
 // true when the tiled W4A16 product of this shape runs that form, and its K
 // split (gemm_split's rounded down: it fits the workspace gemm_split sizes)
 bool a16_runs(int64_t M, int64_t K, int64_t N, int G, bool x_fp8);
+// the W4A16 gate and up pair on that form (33 to 256 rows, groups of 128)
+bool a16_pair_eligible(int64_t M, int64_t K, int64_t N, int G);
+hipError_t launch_gemm_a16_pair(const MulParams& p, hipStream_t stream);
 GemmSplit a16_split(int64_t M, int64_t K, int64_t N);
 // K step of the fp8 kernel (one group of 128 k)
 constexpr int kF8StepK = 128;
