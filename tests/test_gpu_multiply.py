@@ -555,14 +555,16 @@ def test_gate_up_products(kind):
     # W4A16 at 300 the 256-row direct-to-LDS tiles), both activations;
     # and a ragged
     # N with symmetric G = 32 weights (the dequantizing form for more than
-    # two rows, and the tiled form at 70 rows)
+    # two rows, and the tiled form at 70 rows) and with G = 128 (the pair
+    # form's 64- and 128-row tiles)
     require_gpu()
     import torch
     import w4_dequant_gemm_amd as w4
     wl = synth.WORKLOADS["llama8b_decode"]
     W = synth.weight(wl, 0, rows=2048)
     cases = [(W[:1024], W[1024:], 128, "asym", (1, 2, 3, 16, 32, 48, 100, 200, 256, 300)),
-             (W[:1000, :1536], W[1000:2000, :1536], 32, "sym", (1, 2, 5, 70))]
+             (W[:1000, :1536], W[1000:2000, :1536], 32, "sym", (1, 2, 5, 70)),
+             (W[:1000, :1536], W[1000:2000, :1536], 128, "asym", (40, 130, 200))]
     for Wg, Wu, G, mode, Ms in cases:
         qg = oracle.quantize(np.ascontiguousarray(Wg), G, mode)
         qu = oracle.quantize(np.ascontiguousarray(Wu), G, mode)
