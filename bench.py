@@ -256,25 +256,28 @@ def main():
                 log(f"[bench] W4A16 8B {name} M={M}: {ms*1e3:.2f} us, {gbs:.1f} GB/s")
         # gated MLP front half at decode: gate and up (two 14336 x 4096 weights,
         # consecutive copies) in one pass with the SiLU-and-multiply epilogue,
-        # against the two products launched separately
-        for M in (1, 16):
+        # against the two products launched separately (from 33 rows with the
+        # products' split workspace, as a caller would pass it)
+        for M in (1, 16, 64, 256):
             x = bf16(synth.activations_bf16_bits(wl8, M, Ku))
             h = torch.empty((M, Nu), dtype=torch.bfloat16, device=dev)
             y2 = torch.empty((M, Nu), dtype=torch.bfloat16, device=dev)
+            wsm = torch.empty((max(w4.w4_gemm_workspace_bytes(M, Ku, Nu), 16),), dtype=torch.uint8, device=dev)
 
             def fused(x=x, h=h):
                 for i in range(0, L - 1, 2):
                     w4.w4a16_gate_up(x, ups[i], ups[i + 1], G, "silu", H=h)
 
-            def apart(x=x, h=h, y2=y2):
+            def apart(x=x, h=h, y2=y2, wsm=wsm):
                 for i in range(0, L - 1, 2):
-                    w4.w4a16_gemm(x, ups[i]["wq"], ups[i]["sz"], G, Y=h)
-                    w4.w4a16_gemm(x, ups[i + 1]["wq"], ups[i + 1]["sz"], G, Y=y2)
+                    w4.w4a16_gemm(x, ups[i]["wq"], ups[i]["sz"], G, Y=h, workspace=wsm)
+                    w4.w4a16_gemm(x, ups[i + 1]["wq"], ups[i + 1]["sz"], G, Y=y2, workspace=wsm)
             pairs = L // 2
             msf = timer.time(captured(torch, fused, [h]), 20, 3) / pairs
             msa = timer.time(captured(torch, apart, [h, y2]), 20, 3) / pairs
             by = 2 * mul_bytes(M, Nu, Ku, G) - M * Ku * 2 - M * Nu * 2    # x read once, one output
             extra[f"w4a16_gate_up_8b_m{M}"] = {"us": round(msf * 1e3, 3), "GB/s": round(by / (msf * 1e-3) / 1e9, 1),
+                                               "TFLOP/s": round(4.0 * M * Nu * Ku / (msf * 1e-3) / 1e12, 2),
                                                "two_products_us": round(msa * 1e3, 3)}
             log(f"[bench] W4A16 8B gate+up M={M}: fused {msf*1e3:.2f} us ({by/(msf*1e-3)/1e9:.1f} GB/s), "
                 f"two products {msa*1e3:.2f} us")
