@@ -1278,7 +1278,26 @@ GemmSplit gemm_split(int64_t M, int64_t K, int64_t N) { return mid_or_big_split(
 bool a16_runs(int64_t M, int64_t K, int64_t N, int G, bool x_fp8) {
     return W4_A16_MID && W4_MID_BM == 64 && !x_fp8 && use_mid(M, K) && a16_eligible(M, K, N, G);
 }
-GemmSplit a16_split(int64_t M, int64_t K, int64_t N) { return mid_or_big_split(M, K, N, true); }
+GemmSplit a16_split(int64_t M, int64_t K, int64_t N) {
+    GemmSplit g = mid_or_big_split(M, K, N, true);
+    const int bm = a16_tile_rows(M);
+    if (bm == g.bm || g.tiles == 0) return g;
+    // taller tiles: their own count and split, within the workspace sized
+    // for the 64-row tiles' rounded-up split
+    const size_t ws = gemm_workspace_bytes(M, K, N);
+    GemmSplit t{1, 0, 0, bm, 128};
+    t.tiles = ((N + 127) / 128) * ((M + bm - 1) / bm);
+    t.t0 = t.tiles;
+    int64_t s = (W4_MID_WGS / 2) / t.tiles;   // one such workgroup a compute unit (twice the LDS)
+    if (s > (K / big::BK) / 4) s = (K / big::BK) / 4;
+    if (s > 16) s = 16;
+    const int64_t fit = static_cast<int64_t>(ws / (static_cast<size_t>(t.tiles) * bm * 128 * sizeof(float)));
+    if (s > fit) s = fit;
+    if (s < 2) return t;
+    t.splits = static_cast<int>(s);
+    t.t0 = 0;
+    return t;
+}
 
 size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
     const GemmSplit g = gemm_split(M, K, N);

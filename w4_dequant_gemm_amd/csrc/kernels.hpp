@@ -172,6 +172,7 @@ bool a16_runs(int64_t M, int64_t K, int64_t N, int G, bool x_fp8);
 bool a16_pair_eligible(int64_t M, int64_t K, int64_t N, int G);
 hipError_t launch_gemm_a16_pair(const MulParams& p, hipStream_t stream);
 GemmSplit a16_split(int64_t M, int64_t K, int64_t N);
+int a16_tile_rows(int64_t M);   // 64, or 128 from the rows it is set for
 // K step of the fp8 kernel (one group of 128 k)
 constexpr int kF8StepK = 128;
 // the fp8 kernel addresses its operands with 31-bit byte offsets
