@@ -144,6 +144,9 @@ def test_gemm_workspace_sizes_and_checks(lib):
     assert ws(2, 14336, 4096) == 0 and ws(1, 14336, 4096) == 0
     assert ws(16, 4096, 14336) == 0                          # 32-column blocks already: no split
     assert ws(8, 14336, 4096) == 0                           # activation re-reads below 4x the weights
+    # K = 1536, N = 576 (9 blocks of 64 columns): four-step ranges allow 3
+    # splits, 27 workgroups, so the product runs unsplit
+    assert ws(16, 1536, 576) == 0 and ws(32, 1536, 576) == 0
     # 64 < M <= 128: 64 x 128 tiles, split along K towards 512 workgroups,
     # at most 16 ways and at least 4 K steps of 64 each
     assert ws(128, 3840, 15360) == 240 * 3 * mid             # 240 tiles: 3 splits

@@ -773,6 +773,9 @@ hipError_t launch_skinny_m(const MulParams& p, int fj, int wk, hipStream_t strea
 #ifndef W4_SK_SPLIT_MINSTEPS
 #define W4_SK_SPLIT_MINSTEPS 4
 #endif
+#ifndef W4_SK_SPLIT_MINWG
+#define W4_SK_SPLIT_MINWG 120
+#endif
 
 // K split of the MFMA forms (3 <= M <= 64).  Every workgroup reads the whole
 // activation block [M, K] from L2, once per column block; the unsplit
@@ -782,7 +785,11 @@ hipError_t launch_skinny_m(const MulParams& p, int fj, int wk, hipStream_t strea
 // instead: the widest column blocks the registers allow (64 columns, 32 for
 // four row blocks), one workgroup per (block, range), at most 16 ranges of
 // at least four 128-k steps, and a second kernel sums the ranges (below
-// that ratio its launch costs more than the reads save).  The ranges depend
+// that ratio its launch costs more than the reads save).  A split that the
+// four-step minimum keeps below 120 workgroups is dropped: there the unsplit
+// schedule's several waves per workgroup do better than fewer one-wave
+// workgroups and a second launch (SmolLM2-sized down projection, K = 1536,
+// N = 576, at M = 16 / 32: 10.7 / 14.4 -> 4.4 / 5.9 us).  The ranges depend
 // on the shape and the activation width; the workspace is sized for bf16,
 // the wider.
 int skinny_splits(int64_t M, int64_t K, int64_t N, int xbytes) {
@@ -798,6 +805,9 @@ int skinny_splits(int64_t M, int64_t K, int64_t N, int xbytes) {
     int64_t s = (W4_SK_MINBLK + nblk - 1) / nblk;
     if (s > ks / W4_SK_SPLIT_MINSTEPS) s = ks / W4_SK_SPLIT_MINSTEPS;
     if (s > 16) s = 16;
+    // too few steps to reach the workgroup count: the split would leave
+    // fewer, one-wave workgroups and a second launch
+    if (nblk * s < W4_SK_SPLIT_MINWG) return 1;
     return s < 2 ? 1 : static_cast<int>(s);
 }
 
